@@ -1,0 +1,346 @@
+"""Plain float64 CPU oracle for the HARP rotated low-bit linear.
+
+TEST INFRASTRUCTURE ONLY.  This module exists to check the HIP library.  Only
+``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import it.  The library under ``rotated_bit_amd/`` never
+imports, links or calls anything here, and nothing here imports the library.
+
+What it computes, and where each step comes from
+------------------------------------------------
+Source page: "HARP: Hadamard-Preconditioned Adaptive Rotation Processor for
+Extreme LLM Quantization" (gist.science technical summary of arXiv 2605.29843).
+
+* Technical summary §2.1: the orthogonal map is a product of sparse stages,
+  each a block-diagonal orthogonal matrix acting on coordinates that are a
+  stride apart ("separated by stride permutations").  With every radix equal
+  to 2 there are L = log2(b) stages, each made of b/2 independent 2x2 blocks.
+* Technical summary §2.2: each block is B = Q(phi) G_2, where G_2 is the
+  normalised 2x2 Sylvester Hadamard and Q a Givens rotation; at phi = 0 the
+  whole map is the fixed randomized Hadamard transform (RHT).
+* Technical summary §1 and §2.4: RHT costs O(d log d); the stages are applied
+  in place, without materialising the permutation.
+* Technical summary §5: the processor is an exact change of basis: the model
+  y = U (U^T W V) V^T x is unchanged before quantization.
+
+Readings taken where the page is silent (all listed with reasons in the
+repository's design notes):
+
+* Block form.  Q(phi) G_2 = [[cos t, sin t], [sin t, -cos t]] with
+  t = pi/4 + phi (``paper_block`` and ``block``).  The library takes the block
+  as the float32 pair (cos t, sin t).
+* Pairing.  Stage s pairs coordinate i (bit s clear) with i + 2^s; the block
+  index of that pair is i with bit s deleted.  Stages run s = 0, 1, ..., L-1.
+* Signs.  One random +-1 diagonal per side, applied before the stages:
+  F = B_{L-1} ... B_0 D.  The input side computes x~ = F_V x, the output side
+  y = F_U^T y'.  Offline, W' = F_U W F_V^T.
+* Dimensions that are not one power of two are block-diagonal: independent
+  butterflies of size b, each with its own angles and sign slice.
+* Quantizer stand-in (the page leaves the codebook to QuIP#/QTIP): per row
+  and per group of 64 consecutive inputs, asymmetric min-max with zero forced
+  into the range, fp16 scale s, integer zero z stored in fp16, round half to
+  even, codes clamped to [0, 2^B - 1]; dequantized weight (q - z) s.
+* Packing: 2- and 4-bit codes least-significant-bits first, 32/B per uint32
+  word; 3-bit codes as a 96-bit little-endian bit stream per 32 weights
+  (three words).
+* Rounding points of the batched (bf16 matrix-core) path: the rotated input
+  and the dequantized weight are rounded to bf16, round to nearest even.
+
+Every routine is written for clarity, not speed: numpy float64, one library
+matrix product for the contraction, no blocking or fusion.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 64
+
+
+# ---------------------------------------------------------------------------
+# Fixed base mixer (technical summary §2.2: normalised Sylvester Hadamard)
+# ---------------------------------------------------------------------------
+
+def sylvester_hadamard(b: int) -> np.ndarray:
+    """Unnormalised Sylvester Hadamard matrix of order b (b a power of two).
+
+    H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]].
+    """
+    if b < 1 or b & (b - 1):
+        raise ValueError("b must be a power of two")
+    h = np.ones((1, 1), dtype=np.float64)
+    while h.shape[0] < b:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def paper_block(phi: float) -> np.ndarray:
+    """The page's learnable 2x2 block Q(phi) G_2 (technical summary §2.2).
+
+    Q is the Givens rotation [[cos, -sin], [sin, cos]] and G_2 the normalised
+    2x2 Hadamard.  Built as a literal matrix product so that tests can pin the
+    (cos t, sin t) form used everywhere else against it.
+    """
+    q = np.array([[np.cos(phi), -np.sin(phi)], [np.sin(phi), np.cos(phi)]])
+    g2 = sylvester_hadamard(2) / np.sqrt(2.0)
+    return q @ g2
+
+
+def block(c: float, s: float) -> np.ndarray:
+    """2x2 block for the pair (cos t, sin t): [[c, s], [s, -c]]."""
+    return np.array([[c, s], [s, -c]], dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Boundary formats (decoders only)
+# ---------------------------------------------------------------------------
+
+def decode_signs(sign_bits: np.ndarray, d: int) -> np.ndarray:
+    """+-1 diagonal from the bitmask: bit i of word i//32 set means d_i = -1."""
+    words = np.asarray(sign_bits, dtype=np.uint32)
+    i = np.arange(d)
+    bit = (words[i >> 5] >> (i & 31).astype(np.uint32)) & np.uint32(1)
+    return 1.0 - 2.0 * bit.astype(np.float64)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) to float64 values (exact)."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """fp16 bit patterns (uint16) to float64 values (exact)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value, ties to even.
+
+    bf16 keeps 8 significant bits.  Written with frexp so that the rounding is
+    taken once, straight from float64 (no detour through float32).  Values
+    here are normal numbers well inside the bf16 range.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                      # x = m * 2**e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
+# ---------------------------------------------------------------------------
+# Butterfly (technical summary §2.1-2.2)
+# ---------------------------------------------------------------------------
+
+def _log2(b: int) -> int:
+    if b < 2 or b & (b - 1):
+        raise ValueError("block size must be a power of two >= 2")
+    return b.bit_length() - 1
+
+
+def apply_stage(u: np.ndarray, cos_s: np.ndarray, sin_s: np.ndarray,
+                s: int) -> np.ndarray:
+    """One stage on the last axis of u (length b); returns a new array.
+
+    Pairs (i, i + 2^s) for every i with bit s clear.  Writing
+    i = hi * 2^(s+1) + lo with lo < 2^s, the pair's block index is
+    hi * 2^s + lo (i with bit s deleted).  cos_s and sin_s have shape
+    (..., b/2) and broadcast against the leading axes of u.
+    """
+    b = u.shape[-1]
+    h = 1 << s
+    v = u.reshape(u.shape[:-1] + (b // (2 * h), 2, h))
+    a = v[..., 0, :]                     # coordinate i
+    p = v[..., 1, :]                     # coordinate i + 2^s
+    c = cos_s.reshape(cos_s.shape[:-1] + (b // (2 * h), h))
+    sn = sin_s.reshape(sin_s.shape[:-1] + (b // (2 * h), h))
+    out = np.empty_like(v)
+    out[..., 0, :] = c * a + sn * p
+    out[..., 1, :] = sn * a - c * p
+    return out.reshape(u.shape)
+
+
+def _as_blocks(cs: np.ndarray, d: int, b: int):
+    cs = np.asarray(cs, dtype=np.float64)
+    L = _log2(b)
+    if d % b:
+        raise ValueError("dimension must be a multiple of the block size")
+    if cs.shape != (d // b, L, b // 2, 2):
+        raise ValueError(f"cs must have shape {(d // b, L, b // 2, 2)}")
+    return cs, L
+
+
+def forward(x: np.ndarray, cs: np.ndarray, sign_bits: np.ndarray,
+            b: int) -> np.ndarray:
+    """F x = blockdiag_j(B^(j)_{L-1} ... B^(j)_0) D x, on the last axis of x.
+
+    x: (..., d).  cs: (d/b, L, b/2, 2) holding (cos t, sin t) per stage and
+    block.  sign_bits: bitmask of D.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    cs, L = _as_blocks(cs, d, b)
+    u = x * decode_signs(sign_bits, d)
+    u = u.reshape(x.shape[:-1] + (d // b, b))
+    for s in range(L):
+        u = apply_stage(u, cs[:, s, :, 0], cs[:, s, :, 1], s)
+    return u.reshape(x.shape)
+
+
+def transpose(y: np.ndarray, cs: np.ndarray, sign_bits: np.ndarray,
+              b: int) -> np.ndarray:
+    """F^T y: stages L-1 down to 0 (each stage is symmetric), then D."""
+    y = np.asarray(y, dtype=np.float64)
+    d = y.shape[-1]
+    cs, L = _as_blocks(cs, d, b)
+    u = y.reshape(y.shape[:-1] + (d // b, b))
+    for s in reversed(range(L)):
+        u = apply_stage(u, cs[:, s, :, 0], cs[:, s, :, 1], s)
+    return u.reshape(y.shape) * decode_signs(sign_bits, d)
+
+
+def rotation_matrix(cs: np.ndarray, sign_bits: np.ndarray, d: int,
+                    b: int) -> np.ndarray:
+    """Dense F (d x d): column j is F e_j."""
+    return forward(np.eye(d), cs, sign_bits, b).T
+
+
+# ---------------------------------------------------------------------------
+# Offline preparation (technical summary §2.4: rotate, then quantize)
+# ---------------------------------------------------------------------------
+
+def rotate_weight(W: np.ndarray, cs_u, signs_u, b_u, cs_v, signs_v,
+                  b_v) -> np.ndarray:
+    """W' = F_U W F_V^T for W stored as [N][K] (out x in)."""
+    W = np.asarray(W, dtype=np.float64)
+    rows = forward(W, cs_v, signs_v, b_v)          # each row: F_V w_n
+    return forward(rows.T, cs_u, signs_u, b_u).T   # each column: F_U
+
+
+def quantize(Wp: np.ndarray, bits: int, group: int = GROUP):
+    """Per-row, per-group uniform asymmetric quantizer (stand-in reading).
+
+    Returns (q uint8 [N][K], scale fp16 [N][K/group], zero fp16 [N][K/group]).
+    For one group w: lo = min(min w, 0), hi = max(max w, 0) (lo = -1, hi = 1
+    when both are 0); s = fp16((hi - lo) / (2^B - 1)), at least 2^-14;
+    z = clamp(rint(-lo / s), 0, 2^B - 1); q = clamp(rint(w / s) + z, 0, 2^B - 1).
+    rint rounds half to even.
+    """
+    Wp = np.asarray(Wp, dtype=np.float64)
+    n, k = Wp.shape
+    if k % group:
+        raise ValueError("K must be a multiple of the group size")
+    qmax = (1 << bits) - 1
+    g = Wp.reshape(n, k // group, group)
+    lo = np.minimum(g.min(axis=2), 0.0)
+    hi = np.maximum(g.max(axis=2), 0.0)
+    flat = hi == lo
+    lo = np.where(flat, -1.0, lo)
+    hi = np.where(flat, 1.0, hi)
+    s16 = ((hi - lo) / qmax).astype(np.float16)
+    s16 = np.maximum(s16, np.float16(2.0 ** -14))
+    s = s16.astype(np.float64)
+    z = np.clip(np.rint(-lo / s), 0, qmax)
+    q = np.clip(np.rint(g / s[..., None]) + z[..., None], 0, qmax)
+    return (q.reshape(n, k).astype(np.uint8), s16,
+            z.astype(np.float16))
+
+
+def pack(q: np.ndarray, bits: int) -> np.ndarray:
+    """Pack codes [N][K] into uint32 words [N][K*bits/32] (LSB first)."""
+    q = np.asarray(q, dtype=np.uint64)
+    n, k = q.shape
+    if bits in (2, 4):
+        per = 32 // bits
+        if k % per:
+            raise ValueError("K must fill whole words")
+        f = q.reshape(n, k // per, per)
+        shifts = (np.arange(per, dtype=np.uint64) * np.uint64(bits))
+        return (f << shifts).sum(axis=2).astype(np.uint32)
+    if bits == 3:
+        if k % 32:
+            raise ValueError("3-bit rows pack 32 codes into 3 words")
+        f = q.reshape(n, k // 32, 32)
+        words = np.zeros((n, k // 32, 3), dtype=np.uint64)
+        for j in range(32):
+            pos = 3 * j                          # bit position in the 96-bit run
+            w, off = divmod(pos, 32)
+            words[:, :, w] |= (f[:, :, j] << np.uint64(off)) & np.uint64(0xFFFFFFFF)
+            if off > 29:                         # field straddles two words
+                words[:, :, w + 1] |= f[:, :, j] >> np.uint64(32 - off)
+        return words.reshape(n, k // 32 * 3).astype(np.uint32)
+    raise ValueError("bits must be 2, 3 or 4")
+
+
+def unpack(words: np.ndarray, bits: int, K: int) -> np.ndarray:
+    """Codes [N][K] from packed words [N][K*bits/32]; inverse of ``pack``."""
+    w = np.asarray(words, dtype=np.uint64)
+    n = w.shape[0]
+    if w.shape[1] * 32 != K * bits:
+        raise ValueError("word count does not match K and bits")
+    mask = np.uint64((1 << bits) - 1)
+    if bits in (2, 4):
+        per = 32 // bits
+        shifts = np.arange(per, dtype=np.uint64) * np.uint64(bits)
+        q = (w[:, :, None] >> shifts) & mask
+        return q.reshape(n, K).astype(np.uint8)
+    if bits == 3:
+        t = w.reshape(n, K // 32, 3)
+        run = t[:, :, 0] | (t[:, :, 1] << np.uint64(32))   # low 64 bits
+        high = t[:, :, 2]                                    # bits 64..95
+        q = np.empty((n, K // 32, 32), dtype=np.uint64)
+        for j in range(32):
+            pos = 3 * j
+            if pos + 3 <= 64:
+                q[:, :, j] = (run >> np.uint64(pos)) & mask
+            elif pos >= 64:
+                q[:, :, j] = (high >> np.uint64(pos - 64)) & mask
+            else:                                            # bits 63..65
+                lo_bits = 64 - pos
+                q[:, :, j] = ((run >> np.uint64(pos)) |
+                              (high << np.uint64(lo_bits))) & mask
+        return q.reshape(n, K).astype(np.uint8)
+    raise ValueError("bits must be 2, 3 or 4")
+
+
+def dequant(q: np.ndarray, scale: np.ndarray, zero: np.ndarray,
+            group: int = GROUP) -> np.ndarray:
+    """w_hat[n][k] = (q[n][k] - z[n][k/64]) * s[n][k/64], in float64.
+
+    scale and zero are fp16 values (float16 arrays or already-decoded
+    floats).  |q - z| <= 15 and s has 11 significant bits, so the product is
+    exact in float64 and in float32.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    s = np.repeat(np.asarray(scale, dtype=np.float64), group, axis=1)
+    z = np.repeat(np.asarray(zero, dtype=np.float64), group, axis=1)
+    return (q - z) * s
+
+
+# ---------------------------------------------------------------------------
+# The online linear (technical summary §2.4 and §5): y = U W_hat V^T x
+# ---------------------------------------------------------------------------
+
+def linear(x: np.ndarray, words: np.ndarray, scale: np.ndarray,
+           zero: np.ndarray, bits: int, cs_v, signs_v, b_v, cs_u, signs_u,
+           b_u, mfma_contract: bool = False) -> np.ndarray:
+    """y = F_U^T (W_hat (F_V x)) for x of shape (M, K); returns (M, N).
+
+    x holds the values the device received (decoded to float64).  With
+    ``mfma_contract`` the two rounding points of the bf16 matrix-core path are
+    modelled: x~ and w_hat are rounded to bf16 (round to nearest even) before
+    the float64 contraction.  Everything else is float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    K = x.shape[-1]
+    w_hat = dequant(unpack(words, bits, K), scale, zero)
+    xt = forward(x, cs_v, signs_v, b_v)
+    if mfma_contract:
+        xt = bf16_round(xt)
+        w_hat = bf16_round(w_hat)
+    yp = xt @ w_hat.T
+    return transpose(yp, cs_u, signs_u, b_u)
+
+
+def rel_l2(a: np.ndarray, ref: np.ndarray) -> float:
+    """||a - ref||_2 / ||ref||_2 over the whole array."""
+    a = np.asarray(a, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.linalg.norm(a - ref) / np.linalg.norm(ref))

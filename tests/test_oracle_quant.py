@@ -1,0 +1,160 @@
+"""Pins for the oracle's quantizer, packing, dequantization and bf16 rounding.
+
+The pages leave the codebook open; the stand-in grid, its packing and its
+dequantization are fixed by the stated reading and pinned here by hand-derived
+layout fixtures (tests/golden/pack_layout.txt), exact-recovery constructions,
+error bounds and library conversions (numpy fp16, torch bf16).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import harp_oracle as O
+
+rng0 = np.random.default_rng(99)
+
+
+def load_layout_fixtures(golden_dir):
+    cases = []
+    with open(os.path.join(golden_dir, "pack_layout.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            parts = line.split()
+            bits, K, spec = int(parts[0]), int(parts[1]), parts[2]
+            words = [int(w, 16) for w in parts[3:]]
+            if spec.startswith("mod:"):
+                P = int(spec[4:])
+                codes = [k % P for k in range(K)]
+            else:
+                pos, val = spec[4:].split("=")
+                codes = [0] * K
+                codes[int(pos)] = int(val)
+            cases.append((bits, K, codes, words))
+    return cases
+
+
+def test_pack_layout_fixtures(golden_dir):
+    cases = load_layout_fixtures(golden_dir)
+    assert len(cases) >= 8
+    for bits, K, codes, words in cases:
+        q = np.array([codes], dtype=np.uint8)
+        got = O.pack(q, bits)
+        assert got.shape == (1, K * bits // 32)
+        assert [int(w) for w in got[0]] == words, (bits, codes)
+        assert np.array_equal(O.unpack(got, bits, K), q)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_pack_unpack_roundtrip(bits):
+    q = rng0.integers(0, 1 << bits, size=(5, 256)).astype(np.uint8)
+    w = O.pack(q, bits)
+    assert w.dtype == np.uint32 and w.shape == (5, 256 * bits // 32)
+    assert np.array_equal(O.unpack(w, bits, 256), q)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_unpack_random_words_in_range(bits):
+    w = rng0.integers(0, 2 ** 32, size=(3, 64 * bits // 32 * 4), dtype=np.uint64)
+    w = w.astype(np.uint32)
+    q = O.unpack(w, bits, 256)
+    assert q.max() <= (1 << bits) - 1
+    # every bit of every word is used exactly once: repacking reproduces it
+    assert np.array_equal(O.pack(q, bits), w)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_quantizer_bounds(bits):
+    qmax = (1 << bits) - 1
+    W = rng0.normal(0, 0.02, size=(16, 512))
+    W[:, 7] *= 20
+    q, s16, z16 = O.quantize(W, bits)
+    assert q.max() <= qmax
+    s = s16.astype(np.float64)
+    z = z16.astype(np.float64)
+    assert np.all(z == np.rint(z)) and z.min() >= 0 and z.max() <= qmax
+    w_hat = O.dequant(q, s16, z16)
+    sr = np.repeat(s, 64, axis=1)
+    zr = np.repeat(z, 64, axis=1)
+    lo_grid = -zr * sr
+    hi_grid = (qmax - zr) * sr
+    inside = (W >= lo_grid) & (W <= hi_grid)
+    err = np.abs(W - w_hat)
+    assert np.all(err[inside] <= sr[inside] / 2 * (1 + 1e-12))
+    # outside the grid, the clamp costs at most one more half step
+    # (z rounding) plus fp16 rounding of s over qmax steps
+    assert np.all(err <= sr * (1.0 + qmax * 2.0 ** -11) + 1e-15)
+    # zero is on the grid: codes equal to z dequantize to exactly 0
+    assert np.all(w_hat[q == zr] == 0.0)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_quantizer_exact_recovery(bits):
+    """A group that lies on a grid spanning its own min and max is recovered."""
+    qmax = (1 << bits) - 1
+    n, G = 6, 4
+    s0 = (rng0.integers(600, 1400, size=(n, G)) * 2.0 ** -16)  # fp16-exact
+    z0 = rng0.integers(0, qmax + 1, size=(n, G)).astype(np.float64)
+    q0 = rng0.integers(0, qmax + 1, size=(n, G, 64))
+    q0[..., 0] = 0
+    q0[..., 1] = qmax
+    W = (q0 - z0[..., None]) * s0[..., None]
+    q, s16, z16 = O.quantize(W.reshape(n, G * 64), bits)
+    assert np.array_equal(s16.astype(np.float64), s0)
+    assert np.array_equal(z16.astype(np.float64), z0)
+    assert np.array_equal(q, q0.reshape(n, G * 64))
+
+
+def test_quantizer_degenerate_group():
+    W = np.zeros((2, 128))
+    W[1, 64:] = 0.5
+    q, s16, z16 = O.quantize(W, 2)
+    assert float(s16[0, 0]) == float(np.float16(2.0 / 3.0))
+    assert np.all(O.dequant(q, s16, z16)[0] == 0.0)
+    # all-positive group: lo forced to 0 -> z = 0, top code hits max exactly
+    assert float(z16[1, 1]) == 0.0 and np.all(q[1, 64:] == 3)
+
+
+def test_quantizer_scale_floor():
+    W = np.full((1, 64), 1e-9)
+    _, s16, _ = O.quantize(W, 2)
+    assert float(s16[0, 0]) == 2.0 ** -14
+
+
+def test_dequant_exact_in_float32():
+    """(q - z) s is exact in float32 for every code, zero and fp16 scale."""
+    s_bits = rng0.integers(0x0400, 0x7BFF, size=(64, 8)).astype(np.uint16)
+    s16 = s_bits.view(np.float16)
+    for bits in (2, 3, 4):
+        qmax = (1 << bits) - 1
+        q = rng0.integers(0, qmax + 1, size=(64, 512)).astype(np.uint8)
+        z16 = rng0.integers(0, qmax + 1, size=(64, 8)).astype(np.float16)
+        ref = O.dequant(q, s16, z16)
+        q32 = q.astype(np.float32)
+        s32 = np.repeat(s16.astype(np.float32), 64, axis=1)
+        z32 = np.repeat(z16.astype(np.float32), 64, axis=1)
+        f32 = (q32 - z32) * s32
+        assert np.array_equal(f32.astype(np.float64), ref)
+
+
+def test_bf16_round_matches_torch():
+    x = rng0.normal(0, 3, size=4096).astype(np.float32)
+    # add exact ties: low 16 bits = 0x8000, with even and odd upper halves
+    u = x.view(np.uint32).copy()
+    u[:64] = (u[:64] & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    u[64:128] = (u[64:128] & np.uint32(0xFFFE0000)) | np.uint32(0x18000)
+    x = u.view(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.bf16_round(x.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+def test_f16_and_bf16_decoders():
+    v = rng0.normal(size=100).astype(np.float16)
+    assert np.array_equal(O.f16_bits_to_f64(v.view(np.uint16)), v.astype(np.float64))
+    t = torch.from_numpy(rng0.normal(size=100).astype(np.float32)).to(torch.bfloat16)
+    bits = t.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.bf16_bits_to_f64(bits), t.to(torch.float64).numpy())
