@@ -1,0 +1,192 @@
+/*
+ * harp.h -- C ABI of libharp: the inference hot path of HARP, a two-sided
+ * learnable structured orthogonal processor around a low-bit linear layer,
+ *
+ *     y = U . deq(Wq) . V^T . x        with  V^T = F_V,  U = F_U^T.
+ *
+ * Source: "HARP: Hadamard-Preconditioned Adaptive Rotation Processor for
+ * Extreme LLM Quantization" (gist.science technical summary of arXiv
+ * 2605.29843).  Technical summary §2.4 describes the processor as a
+ * drop-in replacement for the fixed randomized-Hadamard pre-processing of
+ * QuIP#/QTIP pipelines; this ABI mirrors that role: rotate in, quantized
+ * matmul, rotate out, plus the whole linear in one call.
+ *
+ * One side's rotation (technical summary §2.1-2.2), for a vector of length
+ * dim split into dim/b independent blocks of size b = 2^L:
+ *
+ *     F = blockdiag_j( B^(j)_{L-1} ... B^(j)_0 ) . D
+ *
+ * D is a +-1 diagonal; stage s of block j pairs coordinates (i, i + 2^s) for
+ * every i with bit s clear and applies [[c, s], [s, -c]] with
+ * (c, s) = (cos t, sin t) of that pair's angle.  This is the page's
+ * Hadamard-preconditioned block Q(phi) G_2 with t = pi/4 + phi, so zero
+ * angles phi give the randomized Hadamard transform (technical summary
+ * §2.2).  The pair's index within the stage is i with bit s deleted.
+ *
+ * Weights (stand-in quantizer; the pages leave the codebook open): per
+ * output row n and per group g of 64 consecutive inputs,
+ *     w_hat[n][k] = (q[n][k] - z[n][g]) * s[n][g],   g = k / 64,
+ * with q a B-bit code, s an fp16 scale and z an integer-valued fp16 zero.
+ *
+ * Conventions for every call
+ * --------------------------
+ * Ownership: the caller owns every buffer.  The library never allocates or
+ *   frees device memory and keeps no state beyond a per-thread HIP error.
+ * Memory: all data pointers are device pointers, 16-byte aligned, row-major,
+ *   without padding.  Outputs must not overlap inputs.
+ * Streams: work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *   stream); calls return once it is enqueued.
+ * Errors: arguments are checked before anything is launched.  A failed check
+ *   returns its status, launches nothing and leaves the outputs untouched.
+ *   A failed launch returns HARP_ERR_HIP; harp_last_hip_error() then holds
+ *   the hipError_t.  No C++ exception crosses this ABI.
+ * Empty input: M == 0 is valid and does nothing; data pointers may then be
+ *   NULL (the structure pointers and their fields are still checked).
+ * Determinism: results are bitwise reproducible run to run for identical
+ *   inputs and launch configuration (no floating-point atomics).
+ * Threads: every call is thread-safe; calls on different streams may run
+ *   concurrently.
+ */
+#ifndef HARP_H
+#define HARP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum harp_status {
+  HARP_OK = 0,
+  HARP_ERR_NULL = 1,         /* a required pointer is NULL                    */
+  HARP_ERR_SHAPE = 2,        /* inconsistent or out-of-range dimension        */
+  HARP_ERR_DTYPE = 3,        /* dtype value not in harp_dtype                 */
+  HARP_ERR_ALIGN = 4,        /* a data pointer is not 16-byte aligned         */
+  HARP_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required       */
+  HARP_ERR_UNSUPPORTED = 6,  /* bits not in {2,3,4}, group != 64, b > 8192    */
+  HARP_ERR_HIP = 7           /* a HIP launch failed; see harp_last_hip_error  */
+} harp_status;
+
+typedef enum harp_dtype {
+  HARP_F32 = 0,              /* IEEE binary32                                 */
+  HARP_BF16 = 1              /* bfloat16, stored as uint16 bit patterns       */
+} harp_dtype;
+
+typedef void *harp_stream;   /* hipStream_t */
+
+/* Largest dimension, block and batch the library accepts. */
+#define HARP_MAX_DIM 262144
+#define HARP_MAX_BLOCK 8192
+#define HARP_MAX_M 65536
+
+/*
+ * One side of the processor (technical summary §2.1-2.2).
+ *   dim        vector length (K on the input side, N on the output side)
+ *   block      b: power of two, 2 <= b <= 8192, dim % b == 0
+ *   cs         [dim/b][log2 b][b/2][2] float32: (cos t, sin t) for block j,
+ *              stage s, pair index c (i with bit s deleted)
+ *   sign_bits  [ceil(dim/32)] uint32: bit i of word i/32 set means D_ii = -1
+ */
+typedef struct harp_rotation {
+  int32_t dim;
+  int32_t block;
+  const float *cs;
+  const uint32_t *sign_bits;
+} harp_rotation;
+
+/*
+ * Packed low-bit weight W_hat [N][K] (out x in).
+ *   bits     2, 3 or 4;  group must be 64;  K % 64 == 0
+ *   qweight  [N][K*bits/32] uint32.  bits 2 and 4: code k in word k/(32/bits)
+ *            at bits bits*(k % (32/bits)), least significant first.  bits 3:
+ *            each run of 32 codes is a 96-bit little-endian integer in three
+ *            words (first word = bits 0..31), code k of the run at bits 3k.
+ *   scale    [N][K/64] fp16 bit patterns
+ *   zero     [N][K/64] fp16 bit patterns holding integers in [0, 2^bits-1]
+ */
+typedef struct harp_qweight {
+  int32_t N;
+  int32_t K;
+  int32_t bits;
+  int32_t group;
+  const uint32_t *qweight;
+  const uint16_t *scale;
+  const uint16_t *zero;
+} harp_qweight;
+
+/*
+ * x~ = F_V x for each of M rows (technical summary §2.1-2.2: sign flip, then
+ * stages 0..L-1 in place; §2.4: stride stages without a materialised
+ * permutation).
+ *   x   [M][V->dim] of x_dt;  xt  [M][V->dim] of xt_dt.
+ * Arithmetic is float32; a bf16 xt is rounded to nearest even at the end.
+ */
+harp_status harp_rotate_in(const harp_rotation *V, const void *x,
+                           harp_dtype x_dt, void *xt, harp_dtype xt_dt,
+                           int32_t M, harp_stream stream);
+
+/*
+ * y = F_U^T y' for each of M rows: stages L-1..0 (each stage is its own
+ * transpose), then the sign flip.
+ *   yt  [M][U->dim] float32;  y  [M][U->dim] of y_dt (bf16: nearest even).
+ */
+harp_status harp_rotate_out(const harp_rotation *U, const float *yt, void *y,
+                            harp_dtype y_dt, int32_t M, harp_stream stream);
+
+/*
+ * y'[m][n] = sum_k w_hat[n][k] x~[m][k] on the vector ALUs, float32
+ * throughout: w_hat is exact in float32 and x~ is not rounded.  Meant for
+ * decode batches (M < 64); any M is accepted.
+ *   xt  [M][W->K] float32;  yt  [M][W->N] float32.
+ */
+harp_status harp_deq_gemv(const harp_qweight *W, const float *xt, float *yt,
+                          int32_t M, harp_stream stream);
+
+/*
+ * y'[m][n] = sum_k bf16(w_hat[n][k]) x~[m][k] on the bf16 matrix cores with
+ * float32 accumulation; bf16(w_hat) rounds to nearest even.  Meant for
+ * prefill batches (M >= 64); any M is accepted.
+ *   xt_bf16  [M][W->K] bf16;  yt  [M][W->N] float32.
+ */
+harp_status harp_deq_gemm(const harp_qweight *W, const uint16_t *xt_bf16,
+                          float *yt, int32_t M, harp_stream stream);
+
+/* Workspace bytes harp_linear_fused needs for M rows of a K -> N linear;
+ * 0 when an argument is out of range. */
+size_t harp_linear_workspace_bytes(int32_t M, int32_t N, int32_t K);
+
+/*
+ * y = F_U^T deq(W) F_V x, the whole linear (technical summary §2.4 and §5).
+ * M < 64 runs rotate-in (float32 x~), the vector-ALU product and rotate-out;
+ * M >= 64 runs rotate-in with a bf16 x~, the matrix-core product and
+ * rotate-out.  Requires V->dim == W->K and U->dim == W->N.
+ *   x  [M][K] of x_dt;  y  [M][N] of y_dt;
+ *   workspace  at least harp_linear_workspace_bytes(M, N, K) bytes, 256-byte
+ *              aligned, owned by the caller, clobbered by the call.
+ */
+harp_status harp_linear_fused(const harp_rotation *V, const harp_qweight *W,
+                              const harp_rotation *U, const void *x,
+                              harp_dtype x_dt, void *y, harp_dtype y_dt,
+                              int32_t M, void *workspace, size_t ws_bytes,
+                              harp_stream stream);
+
+/*
+ * Test hook, not on the hot path: writes the dense w_hat [N][K] as float32
+ * (exact) or bf16 (nearest even), through the same device unpack and
+ * dequant code the products use.
+ */
+harp_status harp_dequant(const harp_qweight *W, void *out, harp_dtype out_dt,
+                         harp_stream stream);
+
+/* Static string naming a status. */
+const char *harp_status_string(harp_status status);
+
+/* hipError_t of this thread's last failed launch (0 if none). */
+int32_t harp_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HARP_H */

@@ -1,0 +1,191 @@
+"""ctypes binding of libharp.so (include/harp.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  torch is used for device memory and the current stream.  The
+functions carry the C names; tensors are passed by ``data_ptr()`` on
+``torch.cuda.current_stream()`` unless a stream handle is given.
+
+If libharp.so is missing this module raises on import: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import c_int32, c_size_t, c_void_p, c_char_p
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libharp.so")
+
+HARP_OK = 0
+HARP_ERR_NULL = 1
+HARP_ERR_SHAPE = 2
+HARP_ERR_DTYPE = 3
+HARP_ERR_ALIGN = 4
+HARP_ERR_WORKSPACE = 5
+HARP_ERR_UNSUPPORTED = 6
+HARP_ERR_HIP = 7
+
+HARP_F32 = 0
+HARP_BF16 = 1
+
+EXPORTED = (
+    "harp_rotate_in", "harp_rotate_out", "harp_deq_gemv", "harp_deq_gemm",
+    "harp_linear_workspace_bytes", "harp_linear_fused", "harp_dequant",
+    "harp_status_string", "harp_last_hip_error",
+)
+
+
+class HarpError(RuntimeError):
+    def __init__(self, status: int, where: str, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        msg = f"{where}: {status_string(status)}"
+        if status == HARP_ERR_HIP:
+            msg += f" (hipError_t {hip_error})"
+        super().__init__(msg)
+
+
+class harp_rotation(ctypes.Structure):
+    _fields_ = [("dim", c_int32), ("block", c_int32),
+                ("cs", c_void_p), ("sign_bits", c_void_p)]
+
+
+class harp_qweight(ctypes.Structure):
+    _fields_ = [("N", c_int32), ("K", c_int32), ("bits", c_int32),
+                ("group", c_int32), ("qweight", c_void_p), ("scale", c_void_p),
+                ("zero", c_void_p)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m rotated_bit_amd.build` "
+            "(or __graft_entry__.build()). There is no fallback path.")
+    lib = ctypes.CDLL(LIB_PATH)
+    R = ctypes.POINTER(harp_rotation)
+    Q = ctypes.POINTER(harp_qweight)
+    sig = {
+        "harp_rotate_in": (c_int32, [R, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p]),
+        "harp_rotate_out": (c_int32, [R, c_void_p, c_void_p, c_int32, c_int32, c_void_p]),
+        "harp_deq_gemv": (c_int32, [Q, c_void_p, c_void_p, c_int32, c_void_p]),
+        "harp_deq_gemm": (c_int32, [Q, c_void_p, c_void_p, c_int32, c_void_p]),
+        "harp_linear_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
+        "harp_linear_fused": (c_int32, [R, Q, R, c_void_p, c_int32, c_void_p, c_int32,
+                                        c_int32, c_void_p, c_size_t, c_void_p]),
+        "harp_dequant": (c_int32, [Q, c_void_p, c_int32, c_void_p]),
+        "harp_status_string": (c_char_p, [c_int32]),
+        "harp_last_hip_error": (c_int32, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.harp_status_string(status).decode()
+
+
+# ---------------------------------------------------------------------------
+# torch-facing marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else c_void_p(t.data_ptr())
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return HARP_F32
+    if t.dtype == torch.bfloat16:
+        return HARP_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _stream(stream):
+    if stream is None:
+        return c_void_p(_torch().cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return c_void_p(stream)
+    return c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != HARP_OK:
+        raise HarpError(status, where, lib.harp_last_hip_error())
+
+
+class Rotation:
+    """One side: cs float32 [dim/b][log2 b][b/2][2], sign_bits int32/uint32 [ceil(dim/32)]."""
+
+    def __init__(self, cs, sign_bits, dim: int, block: int):
+        self.cs, self.sign_bits, self.dim, self.block = cs, sign_bits, dim, block
+        self.c = harp_rotation(dim, block, cs.data_ptr(), sign_bits.data_ptr())
+
+
+class QWeight:
+    """Packed weight: qweight int32 [N][K*bits/32], scale/zero int16 or fp16 [N][K/64]."""
+
+    def __init__(self, qweight, scale, zero, N: int, K: int, bits: int, group: int = 64):
+        self.qweight, self.scale, self.zero = qweight, scale, zero
+        self.N, self.K, self.bits, self.group = N, K, bits, group
+        self.c = harp_qweight(N, K, bits, group, qweight.data_ptr(),
+                              scale.data_ptr(), zero.data_ptr())
+
+
+def harp_rotate_in(V: Rotation, x, xt, M: int | None = None, stream=None) -> None:
+    M = x.shape[0] if M is None else M
+    _check(lib.harp_rotate_in(ctypes.byref(V.c), _ptr(x), _dtype_code(x), _ptr(xt),
+                              _dtype_code(xt), M, _stream(stream)), "harp_rotate_in")
+
+
+def harp_rotate_out(U: Rotation, yt, y, M: int | None = None, stream=None) -> None:
+    M = yt.shape[0] if M is None else M
+    _check(lib.harp_rotate_out(ctypes.byref(U.c), _ptr(yt), _ptr(y), _dtype_code(y), M,
+                               _stream(stream)), "harp_rotate_out")
+
+
+def harp_deq_gemv(W: QWeight, xt, yt, M: int | None = None, stream=None) -> None:
+    M = xt.shape[0] if M is None else M
+    _check(lib.harp_deq_gemv(ctypes.byref(W.c), _ptr(xt), _ptr(yt), M, _stream(stream)),
+           "harp_deq_gemv")
+
+
+def harp_deq_gemm(W: QWeight, xt_bf16, yt, M: int | None = None, stream=None) -> None:
+    M = xt_bf16.shape[0] if M is None else M
+    _check(lib.harp_deq_gemm(ctypes.byref(W.c), _ptr(xt_bf16), _ptr(yt), M,
+                             _stream(stream)), "harp_deq_gemm")
+
+
+def harp_linear_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib.harp_linear_workspace_bytes(M, N, K))
+
+
+def harp_linear_fused(V: Rotation, W: QWeight, U: Rotation, x, y, workspace,
+                      M: int | None = None, stream=None) -> None:
+    M = x.shape[0] if M is None else M
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.harp_linear_fused(ctypes.byref(V.c), ctypes.byref(W.c), ctypes.byref(U.c),
+                                 _ptr(x), _dtype_code(x), _ptr(y), _dtype_code(y), M,
+                                 _ptr(workspace), ws_bytes, _stream(stream)),
+           "harp_linear_fused")
+
+
+def harp_dequant(W: QWeight, out, stream=None) -> None:
+    _check(lib.harp_dequant(ctypes.byref(W.c), _ptr(out), _dtype_code(out), _stream(stream)),
+           "harp_dequant")
+
+
+def harp_last_hip_error() -> int:
+    return int(lib.harp_last_hip_error())

@@ -1,0 +1,100 @@
+// extern "C" entry points of libharp (declared in include/harp.h): check the
+// arguments, pick the kernels, launch them on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include "../../include/harp.h"
+#include "launch.hpp"
+#include "validate.hpp"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+harp_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return HARP_OK;
+  g_last_hip_error = static_cast<int32_t>(e);
+  return HARP_ERR_HIP;
+}
+
+hipStream_t as_stream(harp_stream s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+harp_status harp_rotate_in(const harp_rotation* V, const void* x,
+                           harp_dtype x_dt, void* xt, harp_dtype xt_dt,
+                           int32_t M, harp_stream stream) {
+  const harp_status st = harp::validate_rotate_in(V, x, x_dt, xt, xt_dt, M);
+  if (st != HARP_OK || M == 0) return st;
+  return from_hip(harp::launch_rotate(*V, x, x_dt, xt, xt_dt, M, false,
+                                      as_stream(stream)));
+}
+
+harp_status harp_rotate_out(const harp_rotation* U, const float* yt, void* y,
+                            harp_dtype y_dt, int32_t M, harp_stream stream) {
+  const harp_status st = harp::validate_rotate_out(U, yt, y, y_dt, M);
+  if (st != HARP_OK || M == 0) return st;
+  return from_hip(harp::launch_rotate(*U, yt, HARP_F32, y, y_dt, M, true,
+                                      as_stream(stream)));
+}
+
+harp_status harp_deq_gemv(const harp_qweight* W, const float* xt, float* yt,
+                          int32_t M, harp_stream stream) {
+  const harp_status st = harp::validate_gemv(W, xt, yt, M);
+  if (st != HARP_OK || M == 0) return st;
+  return from_hip(harp::launch_gemv(*W, xt, yt, M, as_stream(stream)));
+}
+
+harp_status harp_deq_gemm(const harp_qweight* W, const uint16_t* xt_bf16,
+                          float* yt, int32_t M, harp_stream stream) {
+  const harp_status st = harp::validate_gemm(W, xt_bf16, yt, M);
+  if (st != HARP_OK || M == 0) return st;
+  return from_hip(harp::launch_gemm(*W, xt_bf16, yt, M, as_stream(stream)));
+}
+
+size_t harp_linear_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  return harp::workspace_bytes(M, N, K);
+}
+
+harp_status harp_linear_fused(const harp_rotation* V, const harp_qweight* W,
+                              const harp_rotation* U, const void* x,
+                              harp_dtype x_dt, void* y, harp_dtype y_dt,
+                              int32_t M, void* workspace, size_t ws_bytes,
+                              harp_stream stream) {
+  const harp_status st = harp::validate_fused(V, W, U, x, x_dt, y, y_dt, M,
+                                              workspace, ws_bytes);
+  if (st != HARP_OK || M == 0) return st;
+  const hipStream_t s = as_stream(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* yp = reinterpret_cast<float*>(ws + harp::workspace_yp_offset(M, W->K));
+  if (M < harp::kGemmMinM) {
+    float* xt = reinterpret_cast<float*>(ws);
+    harp_status r = from_hip(harp::launch_rotate(*V, x, x_dt, xt, HARP_F32, M, false, s));
+    if (r != HARP_OK) return r;
+    r = from_hip(harp::launch_gemv(*W, xt, yp, M, s));
+    if (r != HARP_OK) return r;
+  } else {
+    uint16_t* xt = reinterpret_cast<uint16_t*>(ws);
+    harp_status r = from_hip(harp::launch_rotate(*V, x, x_dt, xt, HARP_BF16, M, false, s));
+    if (r != HARP_OK) return r;
+    r = from_hip(harp::launch_gemm(*W, xt, yp, M, s));
+    if (r != HARP_OK) return r;
+  }
+  return from_hip(harp::launch_rotate(*U, yp, HARP_F32, y, y_dt, M, true, s));
+}
+
+harp_status harp_dequant(const harp_qweight* W, void* out, harp_dtype out_dt,
+                         harp_stream stream) {
+  const harp_status st = harp::validate_dequant(W, out, out_dt);
+  if (st != HARP_OK) return st;
+  return from_hip(harp::launch_dequant(*W, out, out_dt, as_stream(stream)));
+}
+
+const char* harp_status_string(harp_status status) {
+  return harp::status_string(status);
+}
+
+int32_t harp_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

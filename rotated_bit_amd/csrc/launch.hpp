@@ -1,0 +1,29 @@
+// Internal kernel launchers (C++ linkage, not exported).  Arguments have
+// already been validated by harp_api.cpp when these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/harp.h"
+
+namespace harp {
+
+// xt = F x (transpose == false) or y = F^T y' (transpose == true) for M rows.
+hipError_t launch_rotate(const harp_rotation& R, const void* in, int in_dt,
+                         void* out, int out_dt, int M, bool transpose,
+                         hipStream_t stream);
+
+// yt = w_hat xt on the vector ALUs, float32.
+hipError_t launch_gemv(const harp_qweight& W, const float* xt, float* yt,
+                       int M, hipStream_t stream);
+
+// yt = bf16(w_hat) xt_bf16 on the matrix cores, float32 accumulation.
+hipError_t launch_gemm(const harp_qweight& W, const uint16_t* xt, float* yt,
+                       int M, hipStream_t stream);
+
+// Dense w_hat [N][K], float32 or bf16.
+hipError_t launch_dequant(const harp_qweight& W, void* out, int out_dt,
+                          hipStream_t stream);
+
+}  // namespace harp

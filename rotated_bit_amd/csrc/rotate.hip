@@ -1,0 +1,230 @@
+// Butterfly rotation kernels: x~ = F x and y = F^T y'.
+//
+// HARP technical summary §2.1-2.2 ("HARP: Hadamard-Preconditioned Adaptive
+// Rotation Processor for Extreme LLM Quantization", gist.science): the map
+// is a product of L = log2(b) sparse stages; stage s applies a 2x2 block
+// [[c, s], [s, -c]] to every pair (i, i + 2^s) with bit s of i clear, and
+// the pair's index in the stage is i with bit s deleted.  F = B_{L-1} .. B_0 D
+// and F^T = D B_0 .. B_{L-1}.  Technical summary §2.4: the stride stages are
+// applied without materialising a permutation.
+//
+// gfx950 mapping.  One workgroup slot owns one length-b block of one row.
+// Each thread holds E = 8 elements in registers, so up to three consecutive
+// stages run in registers per round (a radix-8 sub-butterfly over the
+// strides 2^s0, 2^(s0+1), 2^(s0+2)); rounds exchange through LDS with one
+// barrier each.  The first round reads global memory and the last writes
+// it, so b = 4096 needs three LDS exchanges for twelve stages.  All of a
+// thread's (cos, sin) pairs are loaded into registers before the first
+// round, so their memory latency is paid once.
+#include "launch.hpp"
+#include "device_common.hpp"
+
+namespace harp {
+namespace {
+
+template <int LOGB>
+struct Plan {
+  static constexpr int L = LOGB;
+  static constexpr int EL = LOGB < 3 ? LOGB : 3;      // log2 elements/thread
+  static constexpr int E = 1 << EL;
+  static constexpr int B = 1 << LOGB;
+  static constexpr int TPB = B >> EL;                  // threads per block row
+  static constexpr int NR = (L + EL - 1) / EL;         // register rounds
+  static constexpr int SLOTS = TPB >= 256 ? 1 : 256 / TPB;
+  static constexpr int THREADS = TPB * SLOTS;
+};
+
+__host__ __device__ constexpr int round_width(int r, int EL, int L) {
+  return (L - r * EL) < EL ? (L - r * EL) : EL;
+}
+
+// Index inside the block of local element j of thread t in a round that
+// covers stages s0 .. s0+R-1: the low R bits of j select the position along
+// those strides, the remaining bits (thread index, high bits of j) fill the
+// other index bits in order.
+template <int E>
+__device__ __forceinline__ int elem_index(int t, int j, int s0, int R) {
+  const int rest = t * (E >> R) + (j >> R);
+  const int jl = j & ((1 << R) - 1);
+  const int lo = rest & ((1 << s0) - 1);
+  const int hi = rest >> s0;
+  return (hi << (s0 + R)) | (jl << s0) | lo;
+}
+
+__device__ __forceinline__ int insert_zero_bit(int p, int k) {
+  return ((p >> k) << (k + 1)) | (p & ((1 << k) - 1));
+}
+
+__device__ __forceinline__ int delete_bit(int i, int s) {
+  return ((i >> (s + 1)) << s) | (i & ((1 << s) - 1));
+}
+
+__device__ __forceinline__ float load_elem(const void* p, size_t idx, int dt) {
+  if (dt == HARP_BF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[idx]);
+  return static_cast<const float*>(p)[idx];
+}
+
+__device__ __forceinline__ void store_elem(void* p, size_t idx, int dt, float v) {
+  if (dt == HARP_BF16)
+    static_cast<uint16_t*>(p)[idx] = f32_to_bf16(v);
+  else
+    static_cast<float*>(p)[idx] = v;
+}
+
+template <int LOGB, bool TRANSPOSE>
+__global__ __launch_bounds__(Plan<LOGB>::THREADS) void rotate_kernel(
+    const void* __restrict__ in, int in_dt, void* __restrict__ out, int out_dt,
+    const float2* __restrict__ cs, const uint32_t* __restrict__ sign, int dim,
+    int M, int rows_per_slot) {
+  using P = Plan<LOGB>;
+  constexpr int B = P::B;
+  constexpr int E = P::E;
+  constexpr int EL = P::EL;
+  constexpr int L = P::L;
+  constexpr int NR = P::NR;
+  extern __shared__ float lds[];
+
+  const int tid = threadIdx.x;
+  const int slot = tid / P::TPB;
+  const int t = tid - slot * P::TPB;
+  const int blk = blockIdx.x;
+  float* u = lds + slot * B;
+
+  // (cos, sin) of every pair this thread touches, stage-major.
+  float2 cf[L][E / 2];
+  const float2* csb = cs + static_cast<size_t>(blk) * L * (B / 2);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int s0 = r * EL;
+    const int R = round_width(r, EL, L);
+#pragma unroll
+    for (int k = 0; k < EL; ++k) {
+      if (k < R) {
+        const int s = s0 + k;
+#pragma unroll
+        for (int p = 0; p < E / 2; ++p) {
+          const int i = elem_index<E>(t, insert_zero_bit(p, k), s0, R);
+          cf[s][p] = csb[s * (B / 2) + delete_bit(i, s)];
+        }
+      }
+    }
+  }
+
+  for (int it = 0; it < rows_per_slot; ++it) {
+    const int row = (blockIdx.y * rows_per_slot + it) * P::SLOTS + slot;
+    const bool active = row < M;
+    const size_t base = static_cast<size_t>(active ? row : 0) * dim +
+                        static_cast<size_t>(blk) * B;
+    if (NR > 1 && it > 0) __syncthreads();   // LDS reuse across rows
+    float v[E];
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      const int r = TRANSPOSE ? NR - 1 - q : q;
+      const int s0 = r * EL;
+      const int R = round_width(r, EL, L);
+      if (q == 0) {
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+          const int i = elem_index<E>(t, j, s0, R);
+          float x = active ? load_elem(in, base + i, in_dt) : 0.0f;
+          if (!TRANSPOSE) {
+            const int g = blk * B + i;
+            x = flip_sign(x, (sign[g >> 5] >> (g & 31)) & 1u);
+          }
+          v[j] = x;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < E; ++j) v[j] = u[elem_index<E>(t, j, s0, R)];
+      }
+      // stages of this round, ascending for F, descending for F^T
+#pragma unroll
+      for (int kk = 0; kk < EL; ++kk) {
+        const int k = TRANSPOSE ? EL - 1 - kk : kk;
+        if (k < R) {
+          const int s = s0 + k;
+#pragma unroll
+          for (int p = 0; p < E / 2; ++p) {
+            const int j = insert_zero_bit(p, k);
+            const int j2 = j | (1 << k);
+            const float a = v[j];
+            const float b = v[j2];
+            const float c = cf[s][p].x;
+            const float sn = cf[s][p].y;
+            v[j] = fmaf(c, a, sn * b);
+            v[j2] = fmaf(sn, a, -(c * b));
+          }
+        }
+      }
+      if (q == NR - 1) {
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+          const int i = elem_index<E>(t, j, s0, R);
+          float y = v[j];
+          if (TRANSPOSE) {
+            const int g = blk * B + i;
+            y = flip_sign(y, (sign[g >> 5] >> (g & 31)) & 1u);
+          }
+          if (active) store_elem(out, base + i, out_dt, y);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < E; ++j) u[elem_index<E>(t, j, s0, R)] = v[j];
+        __syncthreads();
+      }
+    }
+  }
+}
+
+template <int LOGB>
+hipError_t launch_logb(const harp_rotation& R, const void* in, int in_dt,
+                       void* out, int out_dt, int M, bool transpose,
+                       hipStream_t stream) {
+  using P = Plan<LOGB>;
+  const int nblk = R.dim >> LOGB;
+  const int ygroups = (M + P::SLOTS - 1) / P::SLOTS;
+  // Rows per slot: keep about 1024 workgroups in flight; reuse the
+  // coefficient registers across rows when there are more.
+  int rps = (nblk * ygroups) / 1024;
+  if (rps < 1) rps = 1;
+  if (rps > 8) rps = 8;
+  const int need = (ygroups + 65534) / 65535;
+  if (rps < need) rps = need;
+  const dim3 grid(nblk, (ygroups + rps - 1) / rps);
+  const size_t shmem = P::NR > 1 ? sizeof(float) * P::SLOTS * P::B : 0;
+  const float2* cs = reinterpret_cast<const float2*>(R.cs);
+  if (transpose)
+    hipLaunchKernelGGL((rotate_kernel<LOGB, true>), grid, dim3(P::THREADS),
+                       shmem, stream, in, in_dt, out, out_dt, cs, R.sign_bits,
+                       R.dim, M, rps);
+  else
+    hipLaunchKernelGGL((rotate_kernel<LOGB, false>), grid, dim3(P::THREADS),
+                       shmem, stream, in, in_dt, out, out_dt, cs, R.sign_bits,
+                       R.dim, M, rps);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rotate(const harp_rotation& R, const void* in, int in_dt,
+                         void* out, int out_dt, int M, bool transpose,
+                         hipStream_t stream) {
+  switch (__builtin_ctz(static_cast<unsigned>(R.block))) {
+    case 1: return launch_logb<1>(R, in, in_dt, out, out_dt, M, transpose, stream);
+    case 2: return launch_logb<2>(R, in, in_dt, out, out_dt, M, transpose, stream);
+    case 3: return launch_logb<3>(R, in, in_dt, out, out_dt, M, transpose, stream);
+    case 4: return launch_logb<4>(R, in, in_dt, out, out_dt, M, transpose, stream);
+    case 5: return launch_logb<5>(R, in, in_dt, out, out_dt, M, transpose, stream);
+    case 6: return launch_logb<6>(R, in, in_dt, out, out_dt, M, transpose, stream);
+    case 7: return launch_logb<7>(R, in, in_dt, out, out_dt, M, transpose, stream);
+    case 8: return launch_logb<8>(R, in, in_dt, out, out_dt, M, transpose, stream);
+    case 9: return launch_logb<9>(R, in, in_dt, out, out_dt, M, transpose, stream);
+    case 10: return launch_logb<10>(R, in, in_dt, out, out_dt, M, transpose, stream);
+    case 11: return launch_logb<11>(R, in, in_dt, out, out_dt, M, transpose, stream);
+    case 12: return launch_logb<12>(R, in, in_dt, out, out_dt, M, transpose, stream);
+    case 13: return launch_logb<13>(R, in, in_dt, out, out_dt, M, transpose, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace harp

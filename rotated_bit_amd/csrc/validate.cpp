@@ -1,0 +1,147 @@
+// Argument checks of the C ABI (see validate.hpp).  Order of checks, which
+// fixes the status returned when several arguments are wrong: structure
+// pointers and their fields (NULL), unsupported formats, shapes, dtypes,
+// batch range, data pointers (NULL when M > 0), alignment, workspace.
+#include "validate.hpp"
+
+namespace harp {
+namespace {
+
+bool pow2(int32_t v) { return v > 0 && (v & (v - 1)) == 0; }
+bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+bool bad_dtype(int dt) { return dt != HARP_F32 && dt != HARP_BF16; }
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+harp_status check_m(int32_t M) {
+  return (M < 0 || M > HARP_MAX_M) ? HARP_ERR_SHAPE : HARP_OK;
+}
+
+// A data buffer of a call with M rows: NULL allowed only when M == 0.
+harp_status check_data(const void* p, int32_t M) {
+  if (M == 0) return HARP_OK;
+  if (p == nullptr) return HARP_ERR_NULL;
+  return aligned(p, 16) ? HARP_OK : HARP_ERR_ALIGN;
+}
+
+#define HARP_TRY(expr)                      \
+  do {                                      \
+    const harp_status st_ = (expr);         \
+    if (st_ != HARP_OK) return st_;         \
+  } while (0)
+
+}  // namespace
+
+harp_status check_rotation(const harp_rotation* R) {
+  if (R == nullptr || R->cs == nullptr || R->sign_bits == nullptr)
+    return HARP_ERR_NULL;
+  if (pow2(R->block) && R->block > HARP_MAX_BLOCK) return HARP_ERR_UNSUPPORTED;
+  if (!pow2(R->block) || R->block < 2) return HARP_ERR_SHAPE;
+  if (R->dim < 1 || R->dim > HARP_MAX_DIM || R->dim % R->block != 0)
+    return HARP_ERR_SHAPE;
+  if (!aligned(R->cs, 16) || !aligned(R->sign_bits, 16)) return HARP_ERR_ALIGN;
+  return HARP_OK;
+}
+
+harp_status check_qweight(const harp_qweight* W) {
+  if (W == nullptr || W->qweight == nullptr || W->scale == nullptr ||
+      W->zero == nullptr)
+    return HARP_ERR_NULL;
+  if (W->bits != 2 && W->bits != 3 && W->bits != 4) return HARP_ERR_UNSUPPORTED;
+  if (W->group != 64) return HARP_ERR_UNSUPPORTED;
+  if (W->N < 1 || W->N > HARP_MAX_DIM || W->K < 64 || W->K > HARP_MAX_DIM ||
+      W->K % 64 != 0)
+    return HARP_ERR_SHAPE;
+  if (!aligned(W->qweight, 16) || !aligned(W->scale, 16) || !aligned(W->zero, 16))
+    return HARP_ERR_ALIGN;
+  return HARP_OK;
+}
+
+harp_status validate_rotate_in(const harp_rotation* V, const void* x, int x_dt,
+                               const void* xt, int xt_dt, int32_t M) {
+  HARP_TRY(check_rotation(V));
+  if (bad_dtype(x_dt) || bad_dtype(xt_dt)) return HARP_ERR_DTYPE;
+  HARP_TRY(check_m(M));
+  HARP_TRY(check_data(x, M));
+  HARP_TRY(check_data(xt, M));
+  return HARP_OK;
+}
+
+harp_status validate_rotate_out(const harp_rotation* U, const void* yt,
+                                const void* y, int y_dt, int32_t M) {
+  HARP_TRY(check_rotation(U));
+  if (bad_dtype(y_dt)) return HARP_ERR_DTYPE;
+  HARP_TRY(check_m(M));
+  HARP_TRY(check_data(yt, M));
+  HARP_TRY(check_data(y, M));
+  return HARP_OK;
+}
+
+harp_status validate_gemv(const harp_qweight* W, const void* xt, const void* yt,
+                          int32_t M) {
+  HARP_TRY(check_qweight(W));
+  HARP_TRY(check_m(M));
+  HARP_TRY(check_data(xt, M));
+  HARP_TRY(check_data(yt, M));
+  return HARP_OK;
+}
+
+harp_status validate_gemm(const harp_qweight* W, const void* xt, const void* yt,
+                          int32_t M) {
+  return validate_gemv(W, xt, yt, M);
+}
+
+harp_status validate_fused(const harp_rotation* V, const harp_qweight* W,
+                           const harp_rotation* U, const void* x, int x_dt,
+                           const void* y, int y_dt, int32_t M,
+                           const void* workspace, size_t ws_bytes) {
+  HARP_TRY(check_rotation(V));
+  HARP_TRY(check_qweight(W));
+  HARP_TRY(check_rotation(U));
+  if (V->dim != W->K || U->dim != W->N) return HARP_ERR_SHAPE;
+  if (bad_dtype(x_dt) || bad_dtype(y_dt)) return HARP_ERR_DTYPE;
+  HARP_TRY(check_m(M));
+  HARP_TRY(check_data(x, M));
+  HARP_TRY(check_data(y, M));
+  if (M == 0) return HARP_OK;
+  if (workspace == nullptr) return HARP_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return HARP_ERR_ALIGN;
+  if (ws_bytes < workspace_bytes(M, W->N, W->K)) return HARP_ERR_WORKSPACE;
+  return HARP_OK;
+}
+
+harp_status validate_dequant(const harp_qweight* W, const void* out, int out_dt) {
+  HARP_TRY(check_qweight(W));
+  if (bad_dtype(out_dt)) return HARP_ERR_DTYPE;
+  HARP_TRY(check_data(out, 1));
+  return HARP_OK;
+}
+
+size_t workspace_yp_offset(int32_t M, int32_t K) {
+  const size_t xt_elem = M < kGemmMinM ? 4 : 2;
+  return align256(static_cast<size_t>(M) * K * xt_elem);
+}
+
+size_t workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  if (M < 0 || M > HARP_MAX_M || N < 1 || N > HARP_MAX_DIM || K < 1 ||
+      K > HARP_MAX_DIM)
+    return 0;
+  return workspace_yp_offset(M, K) + align256(static_cast<size_t>(M) * N * 4);
+}
+
+const char* status_string(harp_status s) {
+  switch (s) {
+    case HARP_OK: return "HARP_OK";
+    case HARP_ERR_NULL: return "HARP_ERR_NULL: a required pointer is NULL";
+    case HARP_ERR_SHAPE: return "HARP_ERR_SHAPE: inconsistent or out-of-range dimension";
+    case HARP_ERR_DTYPE: return "HARP_ERR_DTYPE: unknown dtype";
+    case HARP_ERR_ALIGN: return "HARP_ERR_ALIGN: pointer not aligned (16 B data, 256 B workspace)";
+    case HARP_ERR_WORKSPACE: return "HARP_ERR_WORKSPACE: workspace missing or too small";
+    case HARP_ERR_UNSUPPORTED: return "HARP_ERR_UNSUPPORTED: bits not in {2,3,4}, group != 64 or block > 8192";
+    case HARP_ERR_HIP: return "HARP_ERR_HIP: a HIP launch failed";
+  }
+  return "unknown harp_status";
+}
+
+}  // namespace harp

@@ -1,0 +1,164 @@
+"""The C ABI on the host: libharp.so loads, exports every function that
+include/harp.h declares, and rejects bad arguments with the documented
+status before any HIP call (no compute call is made here; pointers are
+fake but never dereferenced because every call below fails validation or
+has M == 0)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from rotated_bit_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "harp.h")
+
+FAKE = 0x10000           # 256-byte aligned, never dereferenced
+MISALIGNED = 0x10004
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(harp_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    decl = declared_functions()
+    assert decl == sorted(L.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported():
+    for name in declared_functions():
+        assert hasattr(L.lib, name), name
+        assert ctypes.cast(getattr(L.lib, name), ctypes.c_void_p).value
+
+
+def rot(dim=256, block=256, cs=FAKE, sb=FAKE):
+    return L.harp_rotation(dim, block, cs, sb)
+
+
+def qw(N=256, K=256, bits=2, group=64, q=FAKE, s=FAKE, z=FAKE):
+    return L.harp_qweight(N, K, bits, group, q, s, z)
+
+
+def rot_in(R, x=FAKE, xdt=0, xt=FAKE, xtdt=0, M=1):
+    return L.lib.harp_rotate_in(ctypes.byref(R) if R is not None else None,
+                                x, xdt, xt, xtdt, M, None)
+
+
+@pytest.mark.parametrize("R,expect", [
+    (rot(cs=0), L.HARP_ERR_NULL),
+    (rot(sb=0), L.HARP_ERR_NULL),
+    (rot(block=3), L.HARP_ERR_SHAPE),
+    (rot(block=1), L.HARP_ERR_SHAPE),
+    (rot(block=0), L.HARP_ERR_SHAPE),
+    (rot(block=-4), L.HARP_ERR_SHAPE),
+    (rot(dim=16384, block=16384), L.HARP_ERR_UNSUPPORTED),
+    (rot(dim=300, block=256), L.HARP_ERR_SHAPE),
+    (rot(dim=0, block=2), L.HARP_ERR_SHAPE),
+    (rot(dim=262144 * 2, block=256), L.HARP_ERR_SHAPE),
+    (rot(cs=MISALIGNED), L.HARP_ERR_ALIGN),
+    (rot(sb=MISALIGNED), L.HARP_ERR_ALIGN),
+])
+def test_rotation_checks(R, expect):
+    assert rot_in(R) == expect
+
+
+def test_rotate_in_other_checks():
+    assert rot_in(None) == L.HARP_ERR_NULL
+    assert rot_in(rot(), xdt=2) == L.HARP_ERR_DTYPE
+    assert rot_in(rot(), xtdt=-1) == L.HARP_ERR_DTYPE
+    assert rot_in(rot(), M=-1) == L.HARP_ERR_SHAPE
+    assert rot_in(rot(), M=65537) == L.HARP_ERR_SHAPE
+    assert rot_in(rot(), x=0) == L.HARP_ERR_NULL
+    assert rot_in(rot(), xt=0) == L.HARP_ERR_NULL
+    assert rot_in(rot(), x=MISALIGNED) == L.HARP_ERR_ALIGN
+    # empty input: a no-op, NULL data allowed
+    assert rot_in(rot(), x=0, xt=0, M=0) == L.HARP_OK
+
+
+def test_rotate_out_checks():
+    f = L.lib.harp_rotate_out
+    R = rot()
+    assert f(None, FAKE, FAKE, 0, 1, None) == L.HARP_ERR_NULL
+    assert f(ctypes.byref(R), FAKE, FAKE, 5, 1, None) == L.HARP_ERR_DTYPE
+    assert f(ctypes.byref(R), 0, FAKE, 0, 1, None) == L.HARP_ERR_NULL
+    assert f(ctypes.byref(R), FAKE, MISALIGNED, 0, 1, None) == L.HARP_ERR_ALIGN
+    assert f(ctypes.byref(R), 0, 0, 0, 0, None) == L.HARP_OK
+
+
+@pytest.mark.parametrize("W,expect", [
+    (qw(q=0), L.HARP_ERR_NULL),
+    (qw(s=0), L.HARP_ERR_NULL),
+    (qw(z=0), L.HARP_ERR_NULL),
+    (qw(bits=1), L.HARP_ERR_UNSUPPORTED),
+    (qw(bits=8), L.HARP_ERR_UNSUPPORTED),
+    (qw(group=128), L.HARP_ERR_UNSUPPORTED),
+    (qw(K=100), L.HARP_ERR_SHAPE),
+    (qw(K=0), L.HARP_ERR_SHAPE),
+    (qw(N=0), L.HARP_ERR_SHAPE),
+    (qw(N=-5), L.HARP_ERR_SHAPE),
+    (qw(q=MISALIGNED), L.HARP_ERR_ALIGN),
+    (qw(s=FAKE + 2), L.HARP_ERR_ALIGN),
+])
+def test_qweight_checks(W, expect):
+    assert L.lib.harp_deq_gemv(ctypes.byref(W), FAKE, FAKE, 1, None) == expect
+    assert L.lib.harp_deq_gemm(ctypes.byref(W), FAKE, FAKE, 1, None) == expect
+    assert L.lib.harp_dequant(ctypes.byref(W), FAKE, 0, None) == expect
+
+
+def test_product_data_checks():
+    W = qw()
+    for f in (L.lib.harp_deq_gemv, L.lib.harp_deq_gemm):
+        assert f(None, FAKE, FAKE, 1, None) == L.HARP_ERR_NULL
+        assert f(ctypes.byref(W), 0, FAKE, 1, None) == L.HARP_ERR_NULL
+        assert f(ctypes.byref(W), FAKE, 0, 3, None) == L.HARP_ERR_NULL
+        assert f(ctypes.byref(W), FAKE, MISALIGNED, 3, None) == L.HARP_ERR_ALIGN
+        assert f(ctypes.byref(W), FAKE, FAKE, -2, None) == L.HARP_ERR_SHAPE
+        assert f(ctypes.byref(W), 0, 0, 0, None) == L.HARP_OK
+    assert L.lib.harp_dequant(ctypes.byref(W), 0, 0, None) == L.HARP_ERR_NULL
+    assert L.lib.harp_dequant(ctypes.byref(W), FAKE, 3, None) == L.HARP_ERR_DTYPE
+
+
+def test_workspace_bytes():
+    f = L.harp_linear_workspace_bytes
+    assert f(1, 4096, 4096) == 4096 * 4 + 4096 * 4
+    assert f(63, 100, 64) == 16128 + 25344      # 63*100*4 = 25200 rounds up to 25344
+    assert f(64, 4096, 4096) == 64 * 4096 * 2 + 64 * 4096 * 4
+    assert f(0, 4096, 4096) == 0
+    assert f(-1, 4096, 4096) == 0
+    assert f(1, 0, 4096) == 0
+
+
+def fused(V, W, U, x=FAKE, xdt=1, y=FAKE, ydt=0, M=1, ws=FAKE, wsb=1 << 30):
+    b = lambda s: ctypes.byref(s) if s is not None else None
+    return L.lib.harp_linear_fused(b(V), b(W), b(U), x, xdt, y, ydt, M, ws, wsb, None)
+
+
+def test_fused_checks():
+    V, U = rot(dim=256), rot(dim=512, block=256)
+    W = qw(N=512, K=256)
+    assert fused(None, W, U) == L.HARP_ERR_NULL
+    assert fused(V, None, U) == L.HARP_ERR_NULL
+    assert fused(V, W, None) == L.HARP_ERR_NULL
+    assert fused(V, qw(N=512, K=512), U) == L.HARP_ERR_SHAPE          # V.dim != K
+    assert fused(V, qw(N=256, K=256), U) == L.HARP_ERR_SHAPE          # U.dim != N
+    assert fused(V, W, U, xdt=9) == L.HARP_ERR_DTYPE
+    assert fused(V, W, U, ydt=9) == L.HARP_ERR_DTYPE
+    assert fused(V, W, U, M=70000) == L.HARP_ERR_SHAPE
+    assert fused(V, W, U, x=0) == L.HARP_ERR_NULL
+    assert fused(V, W, U, ws=0) == L.HARP_ERR_WORKSPACE
+    assert fused(V, W, U, ws=FAKE + 16) == L.HARP_ERR_ALIGN
+    need = L.harp_linear_workspace_bytes(1, 512, 256)
+    assert fused(V, W, U, wsb=need - 1) == L.HARP_ERR_WORKSPACE
+    assert fused(V, W, U, x=0, y=0, ws=0, wsb=0, M=0) == L.HARP_OK
+    assert fused(V, qw(N=512, K=256, bits=5), U) == L.HARP_ERR_UNSUPPORTED
+
+
+def test_status_strings():
+    for s in range(8):
+        assert L.status_string(s).startswith("HARP_")
+    assert "unknown" in L.status_string(42)
+    assert L.harp_last_hip_error() == 0
