@@ -58,6 +58,10 @@ class harp_qweight(ctypes.Structure):
 
 
 def _load() -> ctypes.CDLL:
+    # torch first: its bundled HIP runtime (soname libamdhip64.so.7) must be
+    # the one loaded, so that torch's streams and allocations and this
+    # library's kernels live in a single runtime.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is not built; run `python -m rotated_bit_amd.build` "

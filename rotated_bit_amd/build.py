@@ -24,8 +24,10 @@ ARCH = os.environ.get("HARP_OFFLOAD_ARCH", "gfx950")
 HIP_SOURCES = ["rotate.hip", "gemv.hip", "gemm.hip", "dequant.hip", "harp_api.cpp"]
 CXX_SOURCES = ["validate.cpp"]
 
+# Code object v5: loadable by the HIP runtime that ships inside torch, which
+# is the runtime the library shares with its caller (one runtime per process).
 HIP_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-version=5",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
@@ -46,6 +48,16 @@ def _run(cmd):
     if p.returncode != 0:
         raise RuntimeError(f"build step failed ({p.returncode}): {' '.join(cmd)}\n{out}")
     return out
+
+
+def torch_lib_dir():
+    """torch's lib directory (holds the HIP runtime torch uses), or None."""
+    import importlib.util
+    spec = importlib.util.find_spec("torch")
+    if spec is None or not spec.origin:
+        return None
+    d = os.path.join(os.path.dirname(spec.origin), "lib")
+    return d if os.path.exists(os.path.join(d, "libamdhip64.so")) else None
 
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
@@ -70,7 +82,13 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
             if o.strip():
                 print(o)
     tmp = LIB + ".tmp"
-    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs])
+    link = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-version=5"]
+    tl = torch_lib_dir()
+    if tl:
+        # Resolve libamdhip64.so.7 to torch's copy when loaded on its own;
+        # when torch is already loaded the loader reuses its copy (same soname).
+        link += [f"-L{tl}", f"-Wl,-rpath,{tl}"]
+    _run(link + ["-o", tmp, *objs])
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)
