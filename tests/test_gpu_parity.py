@@ -26,6 +26,16 @@ pytestmark = pytest.mark.gpu
 CONTRACT_TOL = 1e-3
 BUTTERFLY_TOL = 1e-5
 FP32_PATH_TOL = 2e-5
+# bf16 matrix-core path: the device rounds a float32 x~ to bf16, the oracle
+# the float64 x~; values within the float32 error (<= 1e-5 relative, the
+# butterfly bar) of a rounding boundary round one ulp apart.  Flip rate
+# p <= 2e-5 / 2^-8 ~ 5e-3, each flip one ulp (2^-8 relative), so the
+# output error is <= sqrt(p) 2^-8 ~ 2.8e-4.
+MFMA_PATH_TOL = 3e-4
+
+
+def path_tol(M):
+    return FP32_PATH_TOL if M < 64 else MFMA_PATH_TOL
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -269,7 +279,7 @@ def test_fused_configs(cfg, lin, bits, M):
     ref, _ = oracle_linear_rows(li, D().x_f64(li.x, li.x_dtype), mfma)
     r = report(f"fused {cfg}[{lin}] b{bits} M={M}", y, ref)
     assert r <= CONTRACT_TOL
-    assert r <= FP32_PATH_TOL
+    assert r <= path_tol(M)
 
 
 L70B_CASES = [(0, 2), (0, 3), (0, 4), (1, 2), (1, 3), (1, 4), (2, 2)]
@@ -315,9 +325,9 @@ def test_fused_batch_edges_and_bf16_out(M):
     ref, _ = oracle_linear_rows(li, D().x_f64(li.x, "bf16"), M >= 64)
     y = D().host(run_fused(li))
     r = report(f"edge M={M}", y, ref)
-    assert r <= CONTRACT_TOL and r <= FP32_PATH_TOL
+    assert r <= CONTRACT_TOL and r <= path_tol(M)
     assert_bf16_rounding_close(D().host(run_fused(li, torch.bfloat16)), ref,
-                               FP32_PATH_TOL)
+                               path_tol(M))
 
 
 @pytest.mark.parametrize("M", [1, 16, 512])
