@@ -7,9 +7,10 @@
 // (64) per step: the x~ tile is copied to LDS, and the packed weight tile is
 // unpacked, dequantized to float32 (exact), rounded to bf16 and written to
 // LDS, so each weight is dequantized once per tile.  LDS rows are padded to
-// 144 bytes to spread the 16-byte fragment reads over the banks.  Global
-// loads for the next step are issued before the barrier that retires the
-// current step's matrix-core reads.
+// 144 bytes to spread the 16-byte fragment reads over the banks.  The
+// K loop is software-pipelined: the global loads of step k+1 are issued
+// right after step k is in LDS and complete while the matrix cores work on
+// step k; LDS is double-buffered, so one barrier per step suffices.
 #include "launch.hpp"
 #include "unpack.hpp"
 
@@ -21,13 +22,68 @@ constexpr int BN = 128;
 constexpr int BK = kGroup;
 constexpr int LDK = BK + 8;   // bf16 elements per padded LDS row
 
+// Global operands of one K step, held in registers between the load and
+// the LDS store (the software-pipelined prefetch).
+template <int BITS>
+struct StepRegs {
+  uint4 a[4];        // 32 bf16 of x~ (row lr, half lh)
+  uint32_t w[BITS];  // 32 codes of weight row lr, half lh
+  uint16_t s, z;
+};
+
+template <int BITS>
+__device__ __forceinline__ void load_step(StepRegs<BITS>& r, int kt,
+                                          const uint16_t* arow, bool a_ok,
+                                          const uint32_t* brow, bool b_ok,
+                                          const uint16_t* __restrict__ sc,
+                                          const uint16_t* __restrict__ zr,
+                                          size_t sz_row, int lh) {
+  if (a_ok) {
+    const uint4* p = reinterpret_cast<const uint4*>(arow + static_cast<size_t>(kt) * BK);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.a[i] = p[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.a[i] = make_uint4(0, 0, 0, 0);
+  }
+  if (b_ok) {
+    load_run32<BITS>(brow, (2 * kt + lh) * BITS, r.w);
+    r.s = sc[sz_row + kt];
+    r.z = zr[sz_row + kt];
+  } else {
+#pragma unroll
+    for (int i = 0; i < BITS; ++i) r.w[i] = 0u;
+    r.s = 0;   // scale 0: the padded rows dequantize to 0
+    r.z = 0;
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_step(const StepRegs<BITS>& r, uint16_t* sA,
+                                           uint16_t* sB, int lr, int lh) {
+  float f[32];
+  dequant_run32<BITS>(r.w, f16_to_f32(r.s), f16_to_f32(r.z), f);
+  uint4* da = reinterpret_cast<uint4*>(sA + lr * LDK + lh * 32);
+  uint4* db = reinterpret_cast<uint4*>(sB + lr * LDK + lh * 32);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    da[i] = r.a[i];
+    db[i] = make_uint4(pack_bf16x2(f[8 * i + 0], f[8 * i + 1]),
+                       pack_bf16x2(f[8 * i + 2], f[8 * i + 3]),
+                       pack_bf16x2(f[8 * i + 4], f[8 * i + 5]),
+                       pack_bf16x2(f[8 * i + 6], f[8 * i + 7]));
+  }
+}
+
 template <int BITS>
 __global__ __launch_bounds__(256) void gemm_kernel(
     const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
     const uint16_t* __restrict__ zr, const uint16_t* __restrict__ xt,
     float* __restrict__ yt, int N, int K, int M) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[BN * LDK];
+  // two LDS stages: step kt is read from stage kt & 1 while step kt + 1 is
+  // written to the other
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDK];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -61,56 +117,27 @@ __global__ __launch_bounds__(256) void gemm_kernel(
   const int frag_row = lane & 31;
   const int frag_k = 8 * (lane >> 5);
 
+  StepRegs<BITS> regs;
+  load_step<BITS>(regs, 0, arow, a_ok, brow, b_ok, sc, zr, sz_row, lh);
   for (int kt = 0; kt < G; ++kt) {
-    uint4 av[4];
-    if (a_ok) {
-      const uint4* p = reinterpret_cast<const uint4*>(arow + static_cast<size_t>(kt) * BK);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = p[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = make_uint4(0, 0, 0, 0);
-    }
-    uint32_t w[BITS];
-    float s = 0.0f, z = 0.0f;
-    if (b_ok) {
-      load_run32<BITS>(brow, (2 * kt + lh) * BITS, w);
-      s = f16_to_f32(sc[sz_row + kt]);
-      z = f16_to_f32(zr[sz_row + kt]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < BITS; ++i) w[i] = 0u;
-    }
-    float f[32];
-    dequant_run32<BITS>(w, s, z, f);
-    uint4 bv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      bv[i].x = pack_bf16x2(f[8 * i + 0], f[8 * i + 1]);
-      bv[i].y = pack_bf16x2(f[8 * i + 2], f[8 * i + 3]);
-      bv[i].z = pack_bf16x2(f[8 * i + 4], f[8 * i + 5]);
-      bv[i].w = pack_bf16x2(f[8 * i + 6], f[8 * i + 7]);
-    }
-    __syncthreads();   // the previous step's fragment reads are done
-    uint4* da = reinterpret_cast<uint4*>(sA + lr * LDK + lh * 32);
-    uint4* db = reinterpret_cast<uint4*>(sB + lr * LDK + lh * 32);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      da[i] = av[i];
-      db[i] = bv[i];
-    }
-    __syncthreads();
+    const int st = kt & 1;
+    store_step<BITS>(regs, sA[st], sB[st], lr, lh);
+    __syncthreads();   // stage st complete; stage st^1 no longer read
+    if (kt + 1 < G)
+      load_step<BITS>(regs, kt + 1, arow, a_ok, brow, b_ok, sc, zr, sz_row, lh);
+    const uint16_t* pa = sA[st];
+    const uint16_t* pb = sB[st];
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       bf16x8 a[2], b[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         a[i] = *reinterpret_cast<const bf16x8*>(
-            sA + (wm + 32 * i + frag_row) * LDK + kk * 16 + frag_k);
+            pa + (wm + 32 * i + frag_row) * LDK + kk * 16 + frag_k);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         b[j] = *reinterpret_cast<const bf16x8*>(
-            sB + (wn + 32 * j + frag_row) * LDK + kk * 16 + frag_k);
+            pb + (wn + 32 * j + frag_row) * LDK + kk * 16 + frag_k);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll

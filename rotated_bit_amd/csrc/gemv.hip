@@ -7,7 +7,8 @@
 // = three words); thread t takes units t, t+256, ...  For each unit it loads
 // x~ once (coalesced across threads) and streams the unit's words of all
 // ROWS rows, so every weight byte is read once and x~ is read once per
-// workgroup.  Per group the product is factored as
+// workgroup.  The workgroup's fp16 scales and zeros are staged in LDS with
+// one coalesced pass.  Per group the product is factored as
 //     sum_k (q_k - z) s x~_k = s (sum_k q_k x~_k - z sum_k x~_k),
 // which leaves one convert and MT fused multiply-adds per code.  The
 // ROWS*MT partial sums are combined with a transposing wave reduction and
@@ -52,6 +53,91 @@ __device__ __forceinline__ void unit_codes(const uint32_t (&w)[NW], float (&q)[K
   }
 }
 
+// One K unit of the operands: x~ for MT rows, the unit's words, scales and
+// zeros for ROWS weight rows.  Loaded as a batch so that every load of a
+// unit is in flight before the first use.
+template <int BITS, int MT, int ROWS>
+struct UnitData {
+  static constexpr int KU = GemvUnit<BITS>::KU;
+  static constexpr int NW = GemvUnit<BITS>::NW;
+  float xv[MT][KU];
+  uint32_t w[ROWS][NW];
+};
+
+template <int BITS, int MT, int ROWS>
+__device__ __forceinline__ void load_unit(UnitData<BITS, MT, ROWS>& d, int u,
+                                          const uint32_t* __restrict__ qw,
+                                          const float* __restrict__ xt, int N,
+                                          int K, int M, int row0, int m0,
+                                          size_t WPR) {
+  constexpr int KU = GemvUnit<BITS>::KU;
+  constexpr int NW = GemvUnit<BITS>::NW;
+  const int k0 = u * KU;
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    const int n = min(row0 + r, N - 1);
+    const uint32_t* wp = qw + static_cast<size_t>(n) * WPR + static_cast<size_t>(u) * NW;
+    if constexpr (NW == 2) {
+      const uint2 v2 = *reinterpret_cast<const uint2*>(wp);
+      d.w[r][0] = v2.x;
+      d.w[r][1] = v2.y;
+    } else {
+#pragma unroll
+      for (int i = 0; i < NW; ++i) d.w[r][i] = wp[i];
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int mm = min(m0 + m, M - 1);     // rows past M: loaded, never stored
+    const float4* p = reinterpret_cast<const float4*>(xt + static_cast<size_t>(mm) * K + k0);
+#pragma unroll
+    for (int c = 0; c < KU / 4; ++c) {
+      const float4 f = p[c];
+      d.xv[m][4 * c + 0] = f.x;
+      d.xv[m][4 * c + 1] = f.y;
+      d.xv[m][4 * c + 2] = f.z;
+      d.xv[m][4 * c + 3] = f.w;
+    }
+  }
+}
+
+// s_lds / z_lds: the workgroup's scales and zeros, [ROWS][G] fp16 bits.
+template <int BITS, int MT, int ROWS>
+__device__ __forceinline__ void compute_unit(const UnitData<BITS, MT, ROWS>& d,
+                                             int u, const uint16_t* s_lds,
+                                             const uint16_t* z_lds, int G,
+                                             float (&acc)[ROWS * MT]) {
+  constexpr int KU = GemvUnit<BITS>::KU;
+  constexpr int NW = GemvUnit<BITS>::NW;
+  float sx[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    float t = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KU; ++j) t += d.xv[m][j];
+    sx[m] = t;
+  }
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    float q[KU];
+    unit_codes<BITS, NW, KU>(d.w[r], q);
+    float dot[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) dot[m] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KU; ++j) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) dot[m] = fmaf(q[j], d.xv[m][j], dot[m]);
+    }
+    const int gi = r * G + u * KU / kGroup;
+    const float s = f16_to_f32(s_lds[gi]);
+    const float z = f16_to_f32(z_lds[gi]);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      acc[r * MT + m] = fmaf(s, fmaf(-z, sx[m], dot[m]), acc[r * MT + m]);
+  }
+}
+
 template <int BITS, int MT, int ROWS>
 __global__ __launch_bounds__(256) void gemv_kernel(
     const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
@@ -59,9 +145,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(
     float* __restrict__ yt, int N, int K, int M) {
   using U = GemvUnit<BITS>;
   constexpr int KU = U::KU;
-  constexpr int NW = U::NW;
   constexpr int V = ROWS * MT;
   __shared__ float red[4][kWave];
+  extern __shared__ uint16_t sz_lds[];   // [2][ROWS][G]: scales, then zeros
 
   const int NU = K / KU;
   const size_t WPR = static_cast<size_t>(K) * BITS / 32;
@@ -76,62 +162,39 @@ __global__ __launch_bounds__(256) void gemv_kernel(
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.0f;
 
-  for (int u = tid; u < NU; u += 256) {
-    const int k0 = u * KU;
-    const int g = k0 / kGroup;
-    float xv[MT][KU];
-    float sx[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if (m0 + m < M) {
-        const float4* p = reinterpret_cast<const float4*>(
-            xt + static_cast<size_t>(m0 + m) * K + k0);
-#pragma unroll
-        for (int c = 0; c < KU / 4; ++c) {
-          const float4 f = p[c];
-          xv[m][4 * c + 0] = f.x;
-          xv[m][4 * c + 1] = f.y;
-          xv[m][4 * c + 2] = f.z;
-          xv[m][4 * c + 3] = f.w;
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < KU; ++j) xv[m][j] = 0.0f;
-      }
-      float s = 0.0f;
-#pragma unroll
-      for (int j = 0; j < KU; ++j) s += xv[m][j];
-      sx[m] = s;
+  // First unit's operands in flight, then this workgroup's scales and zeros
+  // (ROWS consecutive rows = one contiguous run of ROWS*G halves) to LDS.
+  int u = tid;
+  UnitData<BITS, MT, ROWS> cur;
+  if (u < NU) load_unit<BITS, MT, ROWS>(cur, u, qw, xt, N, K, M, row0, m0, WPR);
+  {
+    const int rows = min(ROWS, N - row0);
+    const size_t base = static_cast<size_t>(row0) * G;
+    for (int i = tid; i < ROWS * G; i += 256) {
+      const bool ok = i < rows * G;
+      sz_lds[i] = ok ? sc[base + i] : uint16_t(0);
+      sz_lds[ROWS * G + i] = ok ? zr[base + i] : uint16_t(0);
     }
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      const int n = min(row0 + r, N - 1);
-      const uint32_t* wp = qw + static_cast<size_t>(n) * WPR + static_cast<size_t>(u) * NW;
-      uint32_t w[NW];
-      if constexpr (NW == 2) {
-        const uint2 v2 = *reinterpret_cast<const uint2*>(wp);
-        w[0] = v2.x;
-        w[1] = v2.y;
+  }
+  __syncthreads();
+  const uint16_t* s_lds = sz_lds;
+  const uint16_t* z_lds = sz_lds + ROWS * G;
+
+  // Software pipeline over this thread's K units: the next unit's loads
+  // are issued before the current unit is computed.
+  if (u < NU) {
+    for (;;) {
+      const int un = u + 256;
+      if (un < NU) {
+        UnitData<BITS, MT, ROWS> nxt;
+        load_unit<BITS, MT, ROWS>(nxt, un, qw, xt, N, K, M, row0, m0, WPR);
+        compute_unit<BITS, MT, ROWS>(cur, u, s_lds, z_lds, G, acc);
+        cur = nxt;
+        u = un;
       } else {
-#pragma unroll
-        for (int i = 0; i < NW; ++i) w[i] = wp[i];
+        compute_unit<BITS, MT, ROWS>(cur, u, s_lds, z_lds, G, acc);
+        break;
       }
-      const size_t gi = static_cast<size_t>(n) * G + g;
-      const float s = f16_to_f32(sc[gi]);
-      const float z = f16_to_f32(zr[gi]);
-      float q[KU];
-      unit_codes<BITS, NW, KU>(w, q);
-      float dot[MT];
-#pragma unroll
-      for (int m = 0; m < MT; ++m) dot[m] = 0.0f;
-#pragma unroll
-      for (int j = 0; j < KU; ++j) {
-#pragma unroll
-        for (int m = 0; m < MT; ++m) dot[m] = fmaf(q[j], xv[m][j], dot[m]);
-      }
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-        acc[r * MT + m] = fmaf(s, fmaf(-z, sx[m], dot[m]), acc[r * MT + m]);
     }
   }
 
@@ -152,7 +215,8 @@ template <int BITS, int MT, int ROWS>
 hipError_t launch_cfg(const harp_qweight& W, const float* xt, float* yt, int M,
                       hipStream_t stream) {
   const dim3 grid((W.N + ROWS - 1) / ROWS, (M + MT - 1) / MT);
-  hipLaunchKernelGGL((gemv_kernel<BITS, MT, ROWS>), grid, dim3(256), 0, stream,
+  const size_t shmem = sizeof(uint16_t) * 2 * ROWS * (W.K / kGroup);
+  hipLaunchKernelGGL((gemv_kernel<BITS, MT, ROWS>), grid, dim3(256), shmem, stream,
                      W.qweight, W.scale, W.zero, xt, yt, W.N, W.K, M);
   return hipGetLastError();
 }
@@ -160,10 +224,11 @@ hipError_t launch_cfg(const harp_qweight& W, const float* xt, float* yt, int M,
 template <int BITS>
 hipError_t launch_bits(const harp_qweight& W, const float* xt, float* yt, int M,
                        hipStream_t stream) {
-  if (M == 1) return launch_cfg<BITS, 1, 16>(W, xt, yt, M, stream);
+  // MT x~ rows per pass (grid.y passes); more rows per pass would spill
+  // the double-buffered operands.
+  if (M == 1) return launch_cfg<BITS, 1, 8>(W, xt, yt, M, stream);
   if (M == 2) return launch_cfg<BITS, 2, 16>(W, xt, yt, M, stream);
-  if (M <= 4 || BITS == 3) return launch_cfg<BITS, 4, 8>(W, xt, yt, M, stream);
-  return launch_cfg<BITS, (BITS == 3 ? 4 : 8), 8>(W, xt, yt, M, stream);
+  return launch_cfg<BITS, 4, 8>(W, xt, yt, M, stream);
 }
 
 }  // namespace

@@ -59,21 +59,35 @@ __device__ __forceinline__ int delete_bit(int i, int s) {
   return ((i >> (s + 1)) << s) | (i & ((1 << s) - 1));
 }
 
-__device__ __forceinline__ float load_elem(const void* p, size_t idx, int dt) {
-  if (dt == HARP_BF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[idx]);
-  return static_cast<const float*>(p)[idx];
+// Element access in the boundary dtypes (float32, or bf16 as uint16).
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
+__device__ __forceinline__ void from_f32(float& d, float v) { d = v; }
+__device__ __forceinline__ void from_f32(uint16_t& d, float v) { d = f32_to_bf16(v); }
+
+// E contiguous elements starting at p (E-aligned), as one or two vector
+// accesses.
+template <typename T, int E>
+struct alignas(sizeof(T) * E < 16 ? sizeof(T) * E : 16) Pack { T v[E]; };
+
+template <typename T, int E>
+__device__ __forceinline__ void load_contig(const T* p, float (&v)[E]) {
+  const Pack<T, E> pk = *reinterpret_cast<const Pack<T, E>*>(p);
+#pragma unroll
+  for (int j = 0; j < E; ++j) v[j] = to_f32(pk.v[j]);
 }
 
-__device__ __forceinline__ void store_elem(void* p, size_t idx, int dt, float v) {
-  if (dt == HARP_BF16)
-    static_cast<uint16_t*>(p)[idx] = f32_to_bf16(v);
-  else
-    static_cast<float*>(p)[idx] = v;
+template <typename T, int E>
+__device__ __forceinline__ void store_contig(T* p, const float (&v)[E]) {
+  Pack<T, E> pk;
+#pragma unroll
+  for (int j = 0; j < E; ++j) from_f32(pk.v[j], v[j]);
+  *reinterpret_cast<Pack<T, E>*>(p) = pk;
 }
 
-template <int LOGB, bool TRANSPOSE>
+template <int LOGB, bool TRANSPOSE, typename TIn, typename TOut>
 __global__ __launch_bounds__(Plan<LOGB>::THREADS) void rotate_kernel(
-    const void* __restrict__ in, int in_dt, void* __restrict__ out, int out_dt,
+    const TIn* __restrict__ in, TOut* __restrict__ out,
     const float2* __restrict__ cs, const uint32_t* __restrict__ sign, int dim,
     int M, int rows_per_slot) {
   using P = Plan<LOGB>;
@@ -90,7 +104,8 @@ __global__ __launch_bounds__(Plan<LOGB>::THREADS) void rotate_kernel(
   const int blk = blockIdx.x;
   float* u = lds + slot * B;
 
-  // (cos, sin) of every pair this thread touches, stage-major.
+  // (cos, sin) of every pair this thread touches, stage-major, and the E
+  // sign bits of its contiguous elements t*E .. t*E+E-1 (one word).
   float2 cf[L][E / 2];
   const float2* csb = cs + static_cast<size_t>(blk) * L * (B / 2);
 #pragma unroll
@@ -109,6 +124,8 @@ __global__ __launch_bounds__(Plan<LOGB>::THREADS) void rotate_kernel(
       }
     }
   }
+  const int g0 = blk * B + t * E;
+  const uint32_t sbits = sign[g0 >> 5] >> (g0 & 31);
 
   for (int it = 0; it < rows_per_slot; ++it) {
     const int row = (blockIdx.y * rows_per_slot + it) * P::SLOTS + slot;
@@ -123,15 +140,21 @@ __global__ __launch_bounds__(Plan<LOGB>::THREADS) void rotate_kernel(
       const int s0 = r * EL;
       const int R = round_width(r, EL, L);
       if (q == 0) {
+        if (s0 == 0) {
+          if (active) {
+            load_contig<TIn, E>(in + base + t * E, v);
+          } else {
 #pragma unroll
-        for (int j = 0; j < E; ++j) {
-          const int i = elem_index<E>(t, j, s0, R);
-          float x = active ? load_elem(in, base + i, in_dt) : 0.0f;
-          if (!TRANSPOSE) {
-            const int g = blk * B + i;
-            x = flip_sign(x, (sign[g >> 5] >> (g & 31)) & 1u);
+            for (int j = 0; j < E; ++j) v[j] = 0.0f;
           }
-          v[j] = x;
+          if (!TRANSPOSE) {
+#pragma unroll
+            for (int j = 0; j < E; ++j) v[j] = flip_sign(v[j], (sbits >> j) & 1u);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < E; ++j)
+            v[j] = active ? to_f32(in[base + elem_index<E>(t, j, s0, R)]) : 0.0f;
         }
       } else {
 #pragma unroll
@@ -157,15 +180,16 @@ __global__ __launch_bounds__(Plan<LOGB>::THREADS) void rotate_kernel(
         }
       }
       if (q == NR - 1) {
-#pragma unroll
-        for (int j = 0; j < E; ++j) {
-          const int i = elem_index<E>(t, j, s0, R);
-          float y = v[j];
+        if (s0 == 0) {
           if (TRANSPOSE) {
-            const int g = blk * B + i;
-            y = flip_sign(y, (sign[g >> 5] >> (g & 31)) & 1u);
+#pragma unroll
+            for (int j = 0; j < E; ++j) v[j] = flip_sign(v[j], (sbits >> j) & 1u);
           }
-          if (active) store_elem(out, base + i, out_dt, y);
+          if (active) store_contig<TOut, E>(out + base + t * E, v);
+        } else if (active) {
+#pragma unroll
+          for (int j = 0; j < E; ++j)
+            from_f32(out[base + elem_index<E>(t, j, s0, R)], v[j]);
         }
       } else {
 #pragma unroll
@@ -176,10 +200,9 @@ __global__ __launch_bounds__(Plan<LOGB>::THREADS) void rotate_kernel(
   }
 }
 
-template <int LOGB>
-hipError_t launch_logb(const harp_rotation& R, const void* in, int in_dt,
-                       void* out, int out_dt, int M, bool transpose,
-                       hipStream_t stream) {
+template <int LOGB, bool TRANSPOSE, typename TIn, typename TOut>
+hipError_t launch_typed(const harp_rotation& R, const void* in, void* out, int M,
+                        hipStream_t stream) {
   using P = Plan<LOGB>;
   const int nblk = R.dim >> LOGB;
   const int ygroups = (M + P::SLOTS - 1) / P::SLOTS;
@@ -192,16 +215,28 @@ hipError_t launch_logb(const harp_rotation& R, const void* in, int in_dt,
   if (rps < need) rps = need;
   const dim3 grid(nblk, (ygroups + rps - 1) / rps);
   const size_t shmem = P::NR > 1 ? sizeof(float) * P::SLOTS * P::B : 0;
-  const float2* cs = reinterpret_cast<const float2*>(R.cs);
-  if (transpose)
-    hipLaunchKernelGGL((rotate_kernel<LOGB, true>), grid, dim3(P::THREADS),
-                       shmem, stream, in, in_dt, out, out_dt, cs, R.sign_bits,
-                       R.dim, M, rps);
-  else
-    hipLaunchKernelGGL((rotate_kernel<LOGB, false>), grid, dim3(P::THREADS),
-                       shmem, stream, in, in_dt, out, out_dt, cs, R.sign_bits,
-                       R.dim, M, rps);
+  hipLaunchKernelGGL((rotate_kernel<LOGB, TRANSPOSE, TIn, TOut>), grid,
+                     dim3(P::THREADS), shmem, stream,
+                     static_cast<const TIn*>(in), static_cast<TOut*>(out),
+                     reinterpret_cast<const float2*>(R.cs), R.sign_bits, R.dim,
+                     M, rps);
   return hipGetLastError();
+}
+
+template <int LOGB>
+hipError_t launch_logb(const harp_rotation& R, const void* in, int in_dt,
+                       void* out, int out_dt, int M, bool transpose,
+                       hipStream_t stream) {
+  const bool ib = in_dt == HARP_BF16;
+  const bool ob = out_dt == HARP_BF16;
+  if (transpose) {   // y' is always float32
+    if (ob) return launch_typed<LOGB, true, float, uint16_t>(R, in, out, M, stream);
+    return launch_typed<LOGB, true, float, float>(R, in, out, M, stream);
+  }
+  if (ib && ob) return launch_typed<LOGB, false, uint16_t, uint16_t>(R, in, out, M, stream);
+  if (ib) return launch_typed<LOGB, false, uint16_t, float>(R, in, out, M, stream);
+  if (ob) return launch_typed<LOGB, false, float, uint16_t>(R, in, out, M, stream);
+  return launch_typed<LOGB, false, float, float>(R, in, out, M, stream);
 }
 
 }  // namespace
