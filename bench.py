@@ -154,6 +154,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=512 figure")
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graph")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (the known-size "
+                         "reference for the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -216,6 +219,15 @@ def main():
     log(f"step: {count} fused linears in {ms:.3f} ms "
         f"({ms * 1e3 / count:.2f} us per linear)")
     value = count * per_call / (ms * 1e-3) / 1e9
+
+    if args.calibrate_copy:
+        src = torch.empty(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration: 3 x 256 MiB device copies done")
+        del src, dst
 
     # per-kernel launch durations: each kernel alone, graph of `count` launches
     kern = {}
