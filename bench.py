@@ -77,8 +77,11 @@ class Instance:
                            lin.N, lin.K, li.bits)
         self.x = dev(li.x).view(torch.bfloat16)
         self.y = torch.empty((li.M, lin.N), dtype=y_dtype, device="cuda")
-        self.ws = torch.empty(max(256, H.harp_linear_workspace_bytes(li.M, lin.N, lin.K)),
+        # zero-filled: the GEMM arrival counters in its tail must start at 0
+        self.ws = torch.zeros(max(256, H.harp_linear_workspace_bytes(li.M, lin.N, lin.K)),
                               dtype=torch.uint8, device="cuda")
+        gb = H.harp_deq_gemm_workspace_bytes(li.M, lin.N, lin.K)
+        self.gws = torch.zeros(gb, dtype=torch.uint8, device="cuda") if gb else None
         self.xt32 = torch.empty((li.M, lin.K), dtype=torch.float32, device="cuda")
         self.xt16 = torch.empty((li.M, lin.K), dtype=torch.bfloat16, device="cuda")
         self.yp = torch.empty((li.M, lin.N), dtype=torch.float32, device="cuda")
@@ -258,7 +261,7 @@ def main():
         flops = 2.0 * 512 * 4096 * 4096
         for it in pre:
             H.harp_rotate_in(it.V, it.x, it.xt16)
-        ms_gm, _ = time_graph(torch, lambda: [H.harp_deq_gemm(i.W, i.xt16, i.yp) for i in pre], 10)
+        ms_gm, _ = time_graph(torch, lambda: [H.harp_deq_gemm(i.W, i.xt16, i.yp, i.gws) for i in pre], 10)
         ms_fu, _ = time_graph(torch, lambda: [H.harp_linear_fused(i.V, i.W, i.U, i.x, i.y, i.ws)
                                               for i in pre], 10)
         us_gm, us_fu = ms_gm * 1e3 / len(pre), ms_fu * 1e3 / len(pre)

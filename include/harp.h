@@ -147,10 +147,22 @@ harp_status harp_deq_gemv(const harp_qweight *W, const float *xt, float *yt,
  * y'[m][n] = sum_k bf16(w_hat[n][k]) x~[m][k] on the bf16 matrix cores with
  * float32 accumulation; bf16(w_hat) rounds to nearest even.  Meant for
  * prefill batches (M >= 64); any M is accepted.
- *   xt_bf16  [M][W->K] bf16;  yt  [M][W->N] float32.
+ *   xt_bf16    [M][W->K] bf16;  yt  [M][W->N] float32.
+ *   workspace  optional.  NULL runs the product as one K slice.  Otherwise
+ *              at least harp_deq_gemm_workspace_bytes(M, N, K) bytes,
+ *              256-byte aligned: the K dimension is split into slices that
+ *              run concurrently and are summed in a fixed slice order
+ *              (bitwise reproducible).  The workspace must be zero-filled
+ *              before its first use; every call leaves it zero-filled.
+ *              Calls that share a workspace must not overlap in time.
  */
 harp_status harp_deq_gemm(const harp_qweight *W, const uint16_t *xt_bf16,
-                          float *yt, int32_t M, harp_stream stream);
+                          float *yt, int32_t M, void *workspace,
+                          size_t ws_bytes, harp_stream stream);
+
+/* Workspace bytes harp_deq_gemm uses for M rows of a K -> N product (0: the
+ * product runs as one K slice and needs none); 0 for out-of-range sizes. */
+size_t harp_deq_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
 
 /* Workspace bytes harp_linear_fused needs for M rows of a K -> N linear;
  * 0 when an argument is out of range. */
@@ -163,7 +175,10 @@ size_t harp_linear_workspace_bytes(int32_t M, int32_t N, int32_t K);
  * rotate-out.  Requires V->dim == W->K and U->dim == W->N.
  *   x  [M][K] of x_dt;  y  [M][N] of y_dt;
  *   workspace  at least harp_linear_workspace_bytes(M, N, K) bytes, 256-byte
- *              aligned, owned by the caller, clobbered by the call.
+ *              aligned, owned by the caller.  Zero-filled before its first
+ *              use (its last part holds the GEMM arrival counters, which
+ *              every call leaves at zero); the rest is clobbered.  Calls
+ *              that share a workspace must not overlap in time.
  */
 harp_status harp_linear_fused(const harp_rotation *V, const harp_qweight *W,
                               const harp_rotation *U, const void *x,

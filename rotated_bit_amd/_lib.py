@@ -31,7 +31,7 @@ HARP_BF16 = 1
 
 EXPORTED = (
     "harp_rotate_in", "harp_rotate_out", "harp_deq_gemv", "harp_deq_gemm",
-    "harp_linear_workspace_bytes", "harp_linear_fused", "harp_dequant",
+    "harp_deq_gemm_workspace_bytes", "harp_linear_workspace_bytes", "harp_linear_fused", "harp_dequant",
     "harp_status_string", "harp_last_hip_error",
 )
 
@@ -64,7 +64,7 @@ def _load() -> ctypes.CDLL:
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m rotated_bit_amd.build` "
+            f"{LIB_PATH} is not built; run `python rotated_bit_amd/build.py` "
             "(or __graft_entry__.build()). There is no fallback path.")
     lib = ctypes.CDLL(LIB_PATH)
     R = ctypes.POINTER(harp_rotation)
@@ -73,7 +73,9 @@ def _load() -> ctypes.CDLL:
         "harp_rotate_in": (c_int32, [R, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p]),
         "harp_rotate_out": (c_int32, [R, c_void_p, c_void_p, c_int32, c_int32, c_void_p]),
         "harp_deq_gemv": (c_int32, [Q, c_void_p, c_void_p, c_int32, c_void_p]),
-        "harp_deq_gemm": (c_int32, [Q, c_void_p, c_void_p, c_int32, c_void_p]),
+        "harp_deq_gemm": (c_int32, [Q, c_void_p, c_void_p, c_int32, c_void_p, c_size_t,
+                                    c_void_p]),
+        "harp_deq_gemm_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
         "harp_linear_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
         "harp_linear_fused": (c_int32, [R, Q, R, c_void_p, c_int32, c_void_p, c_int32,
                                         c_int32, c_void_p, c_size_t, c_void_p]),
@@ -166,10 +168,16 @@ def harp_deq_gemv(W: QWeight, xt, yt, M: int | None = None, stream=None) -> None
            "harp_deq_gemv")
 
 
-def harp_deq_gemm(W: QWeight, xt_bf16, yt, M: int | None = None, stream=None) -> None:
+def harp_deq_gemm(W: QWeight, xt_bf16, yt, workspace=None, M: int | None = None,
+                  stream=None) -> None:
     M = xt_bf16.shape[0] if M is None else M
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.harp_deq_gemm(ctypes.byref(W.c), _ptr(xt_bf16), _ptr(yt), M,
-                             _stream(stream)), "harp_deq_gemm")
+                             _ptr(workspace), ws_bytes, _stream(stream)), "harp_deq_gemm")
+
+
+def harp_deq_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib.harp_deq_gemm_workspace_bytes(M, N, K))
 
 
 def harp_linear_workspace_bytes(M: int, N: int, K: int) -> int:

@@ -1,6 +1,8 @@
 """Build libharp.so in-tree for gfx950 with hipcc.
 
-    python -m rotated_bit_amd.build          # or  __graft_entry__.build()
+    python rotated_bit_amd/build.py          # or  __graft_entry__.build()
+
+(Run it as a file: importing the package loads the library.)
 
 Every HIP source is compiled with packed-FP32 instructions disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``).  The argument checks

@@ -9,8 +9,12 @@ namespace harp {
 constexpr int kWave = 64;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+// Native 16-byte vector (HIP's uint4 class does not stay in registers when
+// held in arrays across a pipelined loop).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
@@ -21,10 +25,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
-// Two floats to a packed bf16 pair (low half = a).
+// Two floats to a packed bf16 pair (low half = a), round to nearest even;
+// one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) |
-         (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+  const bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {

@@ -32,7 +32,7 @@ __device__ __forceinline__ void unit_codes(const uint32_t (&w)[NW], float (&q)[K
   if constexpr (BITS == 2) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const uint32_t m = (w[0] >> (2 * t)) & 0x03030303u;   // codes t, t+4, t+8, t+12
+      const uint32_t m = opaque((w[0] >> (2 * t)) & 0x03030303u);  // codes t, t+4, t+8, t+12
 #pragma unroll
       for (int i = 0; i < 4; ++i) q[t + 4 * i] = static_cast<float>((m >> (8 * i)) & 0xffu);
     }
@@ -41,7 +41,7 @@ __device__ __forceinline__ void unit_codes(const uint32_t (&w)[NW], float (&q)[K
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const uint32_t m = (w[h] >> (4 * t)) & 0x0f0f0f0fu;  // codes 8h+t, +2, +4, +6
+        const uint32_t m = opaque((w[h] >> (4 * t)) & 0x0f0f0f0fu);  // codes 8h+t, +2, +4, +6
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           q[8 * h + t + 2 * i] = static_cast<float>((m >> (8 * i)) & 0xffu);

@@ -47,10 +47,20 @@ harp_status harp_deq_gemv(const harp_qweight* W, const float* xt, float* yt,
 }
 
 harp_status harp_deq_gemm(const harp_qweight* W, const uint16_t* xt_bf16,
-                          float* yt, int32_t M, harp_stream stream) {
-  const harp_status st = harp::validate_gemm(W, xt_bf16, yt, M);
+                          float* yt, int32_t M, void* workspace, size_t ws_bytes,
+                          harp_stream stream) {
+  const harp_status st = harp::validate_gemm(W, xt_bf16, yt, M, workspace, ws_bytes);
   if (st != HARP_OK || M == 0) return st;
-  return from_hip(harp::launch_gemm(*W, xt_bf16, yt, M, as_stream(stream)));
+  const int splits = workspace ? harp::gemm_splits(M, W->N, W->K) : 1;
+  return from_hip(harp::launch_gemm(*W, xt_bf16, yt, M, splits, workspace,
+                                    as_stream(stream)));
+}
+
+size_t harp_deq_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  if (M < 0 || M > HARP_MAX_M || N < 1 || N > HARP_MAX_DIM || K < 64 ||
+      K > HARP_MAX_DIM)
+    return 0;
+  return harp::gemm_workspace_bytes(M, N, K);
 }
 
 size_t harp_linear_workspace_bytes(int32_t M, int32_t N, int32_t K) {
@@ -78,7 +88,8 @@ harp_status harp_linear_fused(const harp_rotation* V, const harp_qweight* W,
     uint16_t* xt = reinterpret_cast<uint16_t*>(ws);
     harp_status r = from_hip(harp::launch_rotate(*V, x, x_dt, xt, HARP_BF16, M, false, s));
     if (r != HARP_OK) return r;
-    r = from_hip(harp::launch_gemm(*W, xt, yp, M, s));
+    r = from_hip(harp::launch_gemm(*W, xt, yp, M, harp::gemm_splits(M, W->N, W->K),
+                                   ws + harp::workspace_gemm_offset(M, W->N, W->K), s));
     if (r != HARP_OK) return r;
   }
   return from_hip(harp::launch_rotate(*U, yp, HARP_F32, y, y_dt, M, true, s));

@@ -18,9 +18,11 @@ hipError_t launch_rotate(const harp_rotation& R, const void* in, int in_dt,
 hipError_t launch_gemv(const harp_qweight& W, const float* xt, float* yt,
                        int M, hipStream_t stream);
 
-// yt = bf16(w_hat) xt_bf16 on the matrix cores, float32 accumulation.
+// yt = bf16(w_hat) xt_bf16 on the matrix cores, float32 accumulation, in
+// `splits` K slices (splits > 1 needs the GEMM workspace, zero-filled
+// before its first use and left zero-filled).
 hipError_t launch_gemm(const harp_qweight& W, const uint16_t* xt, float* yt,
-                       int M, hipStream_t stream);
+                       int M, int splits, void* workspace, hipStream_t stream);
 
 // Dense w_hat [N][K], float32 or bf16.
 hipError_t launch_dequant(const harp_qweight& W, void* out, int out_dt,

@@ -22,10 +22,14 @@
 namespace harp {
 namespace {
 
-template <int LOGB>
+// EL_ = log2 elements per thread (stages per register round).  The default
+// 3 keeps 8 elements per thread; 2 gives a b = 4096 block 1024 threads,
+// which is what a single CU needs to pull a block's 196 KB of (cos, sin)
+// pairs at full rate when only a few blocks are in flight.
+template <int LOGB, int EL_ = (LOGB < 3 ? LOGB : 3)>
 struct Plan {
   static constexpr int L = LOGB;
-  static constexpr int EL = LOGB < 3 ? LOGB : 3;      // log2 elements/thread
+  static constexpr int EL = EL_;
   static constexpr int E = 1 << EL;
   static constexpr int B = 1 << LOGB;
   static constexpr int TPB = B >> EL;                  // threads per block row
@@ -85,12 +89,12 @@ __device__ __forceinline__ void store_contig(T* p, const float (&v)[E]) {
   *reinterpret_cast<Pack<T, E>*>(p) = pk;
 }
 
-template <int LOGB, bool TRANSPOSE, typename TIn, typename TOut>
-__global__ __launch_bounds__(Plan<LOGB>::THREADS) void rotate_kernel(
+template <int LOGB, int EL_, bool TRANSPOSE, typename TIn, typename TOut>
+__global__ __launch_bounds__((Plan<LOGB, EL_>::THREADS)) void rotate_kernel(
     const TIn* __restrict__ in, TOut* __restrict__ out,
     const float2* __restrict__ cs, const uint32_t* __restrict__ sign, int dim,
     int M, int rows_per_slot) {
-  using P = Plan<LOGB>;
+  using P = Plan<LOGB, EL_>;
   constexpr int B = P::B;
   constexpr int E = P::E;
   constexpr int EL = P::EL;
@@ -104,12 +108,15 @@ __global__ __launch_bounds__(Plan<LOGB>::THREADS) void rotate_kernel(
   const int blk = blockIdx.x;
   float* u = lds + slot * B;
 
-  // (cos, sin) of every pair this thread touches, stage-major, and the E
-  // sign bits of its contiguous elements t*E .. t*E+E-1 (one word).
+  // (cos, sin) of every pair this thread touches, stage-major.  Rounds are
+  // loaded in execution order; when they would not all fit in registers
+  // next to the data (b = 8192 at 1024 threads), the last ones are loaded
+  // once the first round has released its registers.
   float2 cf[L][E / 2];
   const float2* csb = cs + static_cast<size_t>(blk) * L * (B / 2);
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
+  constexpr int kEarly = (L * E) > 96 ? 3 : NR;   // rounds loaded up front
+  auto load_round = [&](int q) {
+    const int r = TRANSPOSE ? NR - 1 - q : q;
     const int s0 = r * EL;
     const int R = round_width(r, EL, L);
 #pragma unroll
@@ -123,7 +130,10 @@ __global__ __launch_bounds__(Plan<LOGB>::THREADS) void rotate_kernel(
         }
       }
     }
-  }
+  };
+#pragma unroll
+  for (int q = 0; q < kEarly; ++q) load_round(q);
+  // the E sign bits of this thread's contiguous elements t*E .. t*E+E-1
   const int g0 = blk * B + t * E;
   const uint32_t sbits = sign[g0 >> 5] >> (g0 & 31);
 
@@ -139,6 +149,10 @@ __global__ __launch_bounds__(Plan<LOGB>::THREADS) void rotate_kernel(
       const int r = TRANSPOSE ? NR - 1 - q : q;
       const int s0 = r * EL;
       const int R = round_width(r, EL, L);
+      if (q == 1 && it == 0) {
+#pragma unroll
+        for (int ql = kEarly; ql < NR; ++ql) load_round(ql);
+      }
       if (q == 0) {
         if (s0 == 0) {
           if (active) {
@@ -200,22 +214,22 @@ __global__ __launch_bounds__(Plan<LOGB>::THREADS) void rotate_kernel(
   }
 }
 
-template <int LOGB, bool TRANSPOSE, typename TIn, typename TOut>
+template <int LOGB, int EL_, bool TRANSPOSE, typename TIn, typename TOut>
 hipError_t launch_typed(const harp_rotation& R, const void* in, void* out, int M,
                         hipStream_t stream) {
-  using P = Plan<LOGB>;
+  using P = Plan<LOGB, EL_>;
   const int nblk = R.dim >> LOGB;
   const int ygroups = (M + P::SLOTS - 1) / P::SLOTS;
-  // Rows per slot: keep about 1024 workgroups in flight; reuse the
-  // coefficient registers across rows when there are more.
-  int rps = (nblk * ygroups) / 1024;
+  // Rows per slot: about one workgroup per CU; beyond that, a workgroup
+  // reuses its coefficient registers over several rows.
+  int rps = (nblk * ygroups) / 256;
   if (rps < 1) rps = 1;
   if (rps > 8) rps = 8;
   const int need = (ygroups + 65534) / 65535;
   if (rps < need) rps = need;
   const dim3 grid(nblk, (ygroups + rps - 1) / rps);
   const size_t shmem = P::NR > 1 ? sizeof(float) * P::SLOTS * P::B : 0;
-  hipLaunchKernelGGL((rotate_kernel<LOGB, TRANSPOSE, TIn, TOut>), grid,
+  hipLaunchKernelGGL((rotate_kernel<LOGB, EL_, TRANSPOSE, TIn, TOut>), grid,
                      dim3(P::THREADS), shmem, stream,
                      static_cast<const TIn*>(in), static_cast<TOut*>(out),
                      reinterpret_cast<const float2*>(R.cs), R.sign_bits, R.dim,
@@ -223,20 +237,33 @@ hipError_t launch_typed(const harp_rotation& R, const void* in, void* out, int M
   return hipGetLastError();
 }
 
+template <int LOGB, int EL_>
+hipError_t launch_el(const harp_rotation& R, const void* in, int in_dt,
+                     void* out, int out_dt, int M, bool transpose,
+                     hipStream_t stream) {
+  const bool ib = in_dt == HARP_BF16;
+  const bool ob = out_dt == HARP_BF16;
+  if (transpose) {   // y' is always float32
+    if (ob) return launch_typed<LOGB, EL_, true, float, uint16_t>(R, in, out, M, stream);
+    return launch_typed<LOGB, EL_, true, float, float>(R, in, out, M, stream);
+  }
+  if (ib && ob) return launch_typed<LOGB, EL_, false, uint16_t, uint16_t>(R, in, out, M, stream);
+  if (ib) return launch_typed<LOGB, EL_, false, uint16_t, float>(R, in, out, M, stream);
+  if (ob) return launch_typed<LOGB, EL_, false, float, uint16_t>(R, in, out, M, stream);
+  return launch_typed<LOGB, EL_, false, float, float>(R, in, out, M, stream);
+}
+
 template <int LOGB>
 hipError_t launch_logb(const harp_rotation& R, const void* in, int in_dt,
                        void* out, int out_dt, int M, bool transpose,
                        hipStream_t stream) {
-  const bool ib = in_dt == HARP_BF16;
-  const bool ob = out_dt == HARP_BF16;
-  if (transpose) {   // y' is always float32
-    if (ob) return launch_typed<LOGB, true, float, uint16_t>(R, in, out, M, stream);
-    return launch_typed<LOGB, true, float, float>(R, in, out, M, stream);
+  if constexpr (LOGB == 12) {
+    // few b = 4096 blocks in flight: 1024 threads per block (see Plan)
+    if ((R.dim >> LOGB) * M <= 64)
+      return launch_el<LOGB, 2>(R, in, in_dt, out, out_dt, M, transpose, stream);
   }
-  if (ib && ob) return launch_typed<LOGB, false, uint16_t, uint16_t>(R, in, out, M, stream);
-  if (ib) return launch_typed<LOGB, false, uint16_t, float>(R, in, out, M, stream);
-  if (ob) return launch_typed<LOGB, false, float, uint16_t>(R, in, out, M, stream);
-  return launch_typed<LOGB, false, float, float>(R, in, out, M, stream);
+  return launch_el<LOGB, (LOGB < 3 ? LOGB : 3)>(R, in, in_dt, out, out_dt, M,
+                                                 transpose, stream);
 }
 
 }  // namespace

@@ -45,14 +45,84 @@ __device__ __forceinline__ void load_run32(const uint32_t* __restrict__ row,
   }
 }
 
-// Dequantize one 32-code run to float32 (exact).
+// Keeps a masked dword opaque to the optimizer, so that its byte lanes are
+// converted with v_cvt_f32_ubyte0..3 instead of being re-extracted one
+// field at a time.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm("" : "+v"(v));
+  return v;
+}
+
+// Codes of one 32-code run as floats.  2- and 4-bit codes are masked four
+// at a time into byte lanes, each then a single byte-to-float convert.
+template <int BITS>
+__device__ __forceinline__ void codes_run32(const uint32_t (&w)[BITS], float (&q)[32]) {
+  if constexpr (BITS == 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t m = opaque((w[h] >> (2 * t)) & 0x03030303u);  // codes t, t+4, t+8, t+12
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          q[16 * h + t + 4 * i] = static_cast<float>((m >> (8 * i)) & 0xffu);
+      }
+    }
+  } else if constexpr (BITS == 4) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t m = opaque((w[h] >> (4 * t)) & 0x0f0f0f0fu);  // codes t, t+2, t+4, t+6
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          q[8 * h + t + 2 * i] = static_cast<float>((m >> (8 * i)) & 0xffu);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) q[j] = static_cast<float>(code_at<BITS, BITS>(w, j));
+  }
+}
+
+// 16 consecutive codes (a quarter of a group) as floats: one word of
+// 2-bit codes or two words of 4-bit codes, masked into byte lanes.
+template <int BITS>
+__device__ __forceinline__ void codes_16(const uint32_t* w, float (&q)[16]) {
+  static_assert(BITS == 2 || BITS == 4, "16-code parts exist for 2 and 4 bits");
+  if constexpr (BITS == 2) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t m = opaque((w[0] >> (2 * t)) & 0x03030303u);  // codes t, t+4, t+8, t+12
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[t + 4 * i] = static_cast<float>((m >> (8 * i)) & 0xffu);
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t m = opaque((w[h] >> (4 * t)) & 0x0f0f0f0fu);  // codes t, t+2, t+4, t+6
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          q[8 * h + t + 2 * i] = static_cast<float>((m >> (8 * i)) & 0xffu);
+      }
+    }
+  }
+}
+
+// Dequantize one 32-code run to float32, exactly: q*s and z*s are exact
+// (at most 4 + 11 significant bits) and so is their difference, so the
+// fused multiply-add q*s - z*s equals (q - z)*s in every evaluation order.
 template <int BITS>
 __device__ __forceinline__ void dequant_run32(const uint32_t (&w)[BITS],
                                               float s, float z,
                                               float (&out)[32]) {
+  float q[32];
+  codes_run32<BITS>(w, q);
+  const float nzs = -z * s;
 #pragma unroll
-  for (int j = 0; j < 32; ++j)
-    out[j] = (static_cast<float>(code_at<BITS, BITS>(w, j)) - z) * s;
+  for (int j = 0; j < 32; ++j) out[j] = fmaf(q[j], s, nzs);
 }
 
 }  // namespace harp

@@ -88,8 +88,12 @@ harp_status validate_gemv(const harp_qweight* W, const void* xt, const void* yt,
 }
 
 harp_status validate_gemm(const harp_qweight* W, const void* xt, const void* yt,
-                          int32_t M) {
-  return validate_gemv(W, xt, yt, M);
+                          int32_t M, const void* workspace, size_t ws_bytes) {
+  HARP_TRY(validate_gemv(W, xt, yt, M));
+  if (M == 0 || workspace == nullptr) return HARP_OK;   // no workspace: one K slice
+  if (!aligned(workspace, 256)) return HARP_ERR_ALIGN;
+  if (ws_bytes < gemm_workspace_bytes(M, W->N, W->K)) return HARP_ERR_WORKSPACE;
+  return HARP_OK;
 }
 
 harp_status validate_fused(const harp_rotation* V, const harp_qweight* W,
@@ -118,16 +122,41 @@ harp_status validate_dequant(const harp_qweight* W, const void* out, int out_dt)
   return HARP_OK;
 }
 
+int32_t gemm_splits(int32_t M, int32_t N, int32_t K) {
+  if (M < 1 || N < 1 || K < 64) return 1;
+  const int64_t tiles = static_cast<int64_t>((M + kGemmTile - 1) / kGemmTile) *
+                        ((N + kGemmTile - 1) / kGemmTile);
+  int32_t s = static_cast<int32_t>((256 + tiles / 2) / tiles);
+  const int32_t groups = K / 64;
+  if (s > 4) s = 4;
+  if (s > groups / 8) s = groups / 8;
+  return s < 1 ? 1 : s;
+}
+
+size_t gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  const int32_t s = gemm_splits(M, N, K);
+  if (s <= 1) return 0;
+  const size_t tiles = static_cast<size_t>((M + kGemmTile - 1) / kGemmTile) *
+                       ((N + kGemmTile - 1) / kGemmTile);
+  return align256(static_cast<size_t>(s) * tiles * kGemmTile * kGemmTile * 4) +
+         align256(tiles * 4);
+}
+
 size_t workspace_yp_offset(int32_t M, int32_t K) {
   const size_t xt_elem = M < kGemmMinM ? 4 : 2;
   return align256(static_cast<size_t>(M) * K * xt_elem);
+}
+
+size_t workspace_gemm_offset(int32_t M, int32_t N, int32_t K) {
+  return workspace_yp_offset(M, K) + align256(static_cast<size_t>(M) * N * 4);
 }
 
 size_t workspace_bytes(int32_t M, int32_t N, int32_t K) {
   if (M < 0 || M > HARP_MAX_M || N < 1 || N > HARP_MAX_DIM || K < 1 ||
       K > HARP_MAX_DIM)
     return 0;
-  return workspace_yp_offset(M, K) + align256(static_cast<size_t>(M) * N * 4);
+  const size_t gemm = M >= kGemmMinM ? gemm_workspace_bytes(M, N, K) : 0;
+  return workspace_gemm_offset(M, N, K) + gemm;
 }
 
 const char* status_string(harp_status s) {

@@ -20,18 +20,29 @@ harp_status validate_rotate_out(const harp_rotation* U, const void* yt,
 harp_status validate_gemv(const harp_qweight* W, const void* xt, const void* yt,
                           int32_t M);
 harp_status validate_gemm(const harp_qweight* W, const void* xt, const void* yt,
-                          int32_t M);
+                          int32_t M, const void* workspace, size_t ws_bytes);
 harp_status validate_fused(const harp_rotation* V, const harp_qweight* W,
                            const harp_rotation* U, const void* x, int x_dt,
                            const void* y, int y_dt, int32_t M,
                            const void* workspace, size_t ws_bytes);
 harp_status validate_dequant(const harp_qweight* W, const void* out, int out_dt);
 
-// Workspace layout of the fused linear: x~ first, then y' (both 256-byte
-// aligned).  x~ is float32 below kGemmMinM rows and bf16 from there on.
+// Matrix-core GEMM tiling and its split over K: the number of K slices is
+// chosen so that about one 128 x 128 output tile slice runs per CU (256 on
+// MI355X), at most 4, each slice at least 8 quantization groups.  With
+// slices > 1 the GEMM needs a workspace: per slice and tile a float32
+// partial tile, then one uint32 arrival counter per tile.
+constexpr int32_t kGemmTile = 128;
+int32_t gemm_splits(int32_t M, int32_t N, int32_t K);
+size_t gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
+
+// Workspace layout of the fused linear: x~, then y', then (M >= kGemmMinM)
+// the GEMM workspace, each 256-byte aligned.  x~ is float32 below kGemmMinM
+// rows and bf16 from there on.
 constexpr int32_t kGemmMinM = 64;
 size_t workspace_bytes(int32_t M, int32_t N, int32_t K);
 size_t workspace_yp_offset(int32_t M, int32_t K);
+size_t workspace_gemm_offset(int32_t M, int32_t N, int32_t K);
 
 const char* status_string(harp_status s);
 

@@ -54,5 +54,12 @@ def zero_f16(w):
 
 
 def workspace(M, N, K) -> torch.Tensor:
+    """Fused-linear workspace, zero-filled (its GEMM counters start at 0)."""
     nbytes = H.harp_linear_workspace_bytes(M, N, K)
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+
+
+def gemm_workspace(M, N, K):
+    """Split-K GEMM workspace (zero-filled), or None when one slice is used."""
+    nbytes = H.harp_deq_gemm_workspace_bytes(M, N, K)
+    return torch.zeros(nbytes, dtype=torch.uint8, device="cuda") if nbytes else None

@@ -105,31 +105,51 @@ def test_rotate_out_checks():
 ])
 def test_qweight_checks(W, expect):
     assert L.lib.harp_deq_gemv(ctypes.byref(W), FAKE, FAKE, 1, None) == expect
-    assert L.lib.harp_deq_gemm(ctypes.byref(W), FAKE, FAKE, 1, None) == expect
+    assert L.lib.harp_deq_gemm(ctypes.byref(W), FAKE, FAKE, 1, FAKE, 1 << 30, None) == expect
     assert L.lib.harp_dequant(ctypes.byref(W), FAKE, 0, None) == expect
 
 
 def test_product_data_checks():
     W = qw()
-    for f in (L.lib.harp_deq_gemv, L.lib.harp_deq_gemm):
-        assert f(None, FAKE, FAKE, 1, None) == L.HARP_ERR_NULL
-        assert f(ctypes.byref(W), 0, FAKE, 1, None) == L.HARP_ERR_NULL
-        assert f(ctypes.byref(W), FAKE, 0, 3, None) == L.HARP_ERR_NULL
-        assert f(ctypes.byref(W), FAKE, MISALIGNED, 3, None) == L.HARP_ERR_ALIGN
-        assert f(ctypes.byref(W), FAKE, FAKE, -2, None) == L.HARP_ERR_SHAPE
-        assert f(ctypes.byref(W), 0, 0, 0, None) == L.HARP_OK
+    gemv = L.lib.harp_deq_gemv
+    gemm = lambda W_, x, y, M: L.lib.harp_deq_gemm(W_, x, y, M, None, 0, None)
+    for f in (lambda W_, x, y, M: gemv(W_, x, y, M, None), gemm):
+        assert f(None, FAKE, FAKE, 1) == L.HARP_ERR_NULL
+        assert f(ctypes.byref(W), 0, FAKE, 1) == L.HARP_ERR_NULL
+        assert f(ctypes.byref(W), FAKE, 0, 3) == L.HARP_ERR_NULL
+        assert f(ctypes.byref(W), FAKE, MISALIGNED, 3) == L.HARP_ERR_ALIGN
+        assert f(ctypes.byref(W), FAKE, FAKE, -2) == L.HARP_ERR_SHAPE
+        assert f(ctypes.byref(W), 0, 0, 0) == L.HARP_OK
+    # split-K workspace: optional, but when given it must be aligned and big
+    W4 = qw(N=4096, K=4096)
+    need = L.harp_deq_gemm_workspace_bytes(512, 4096, 4096)
+    assert need > 0
+    g = L.lib.harp_deq_gemm
+    assert g(ctypes.byref(W4), FAKE, FAKE, 512, FAKE + 16, need, None) == L.HARP_ERR_ALIGN
+    assert g(ctypes.byref(W4), FAKE, FAKE, 512, FAKE, need - 1, None) == L.HARP_ERR_WORKSPACE
+    assert g(ctypes.byref(W4), 0, FAKE, 512, FAKE, need, None) == L.HARP_ERR_NULL
     assert L.lib.harp_dequant(ctypes.byref(W), 0, 0, None) == L.HARP_ERR_NULL
     assert L.lib.harp_dequant(ctypes.byref(W), FAKE, 3, None) == L.HARP_ERR_DTYPE
 
 
 def test_workspace_bytes():
     f = L.harp_linear_workspace_bytes
+    g = L.harp_deq_gemm_workspace_bytes
     assert f(1, 4096, 4096) == 4096 * 4 + 4096 * 4
     assert f(63, 100, 64) == 16128 + 25344      # 63*100*4 = 25200 rounds up to 25344
-    assert f(64, 4096, 4096) == 64 * 4096 * 2 + 64 * 4096 * 4
+    # M=64, 4096x4096: 32 tiles of 128x128 -> 4 K slices (8 groups each at
+    # least); partials 4*32*128*128*4 bytes, then 32 counters (256 B aligned)
+    assert g(64, 4096, 4096) == 4 * 32 * 128 * 128 * 4 + 256
+    assert f(64, 4096, 4096) == 64 * 4096 * 2 + 64 * 4096 * 4 + g(64, 4096, 4096)
+    # M=512, 4096x4096: 128 tiles -> 2 slices; 12288 outputs: 384 tiles -> 1 slice
+    assert g(512, 4096, 4096) == 2 * 128 * 128 * 128 * 4 + 512
+    assert g(512, 12288, 4096) == 0
+    # K of 64 (one group) cannot be split
+    assert g(512, 256, 64) == 0
     assert f(0, 4096, 4096) == 0
     assert f(-1, 4096, 4096) == 0
     assert f(1, 0, 4096) == 0
+    assert g(1, 4096, 32) == 0
 
 
 def fused(V, W, U, x=FAKE, xdt=1, y=FAKE, ydt=0, M=1, ws=FAKE, wsb=1 << 30):
@@ -162,3 +182,13 @@ def test_status_strings():
         assert L.status_string(s).startswith("HARP_")
     assert "unknown" in L.status_string(42)
     assert L.harp_last_hip_error() == 0
+
+
+def test_builder_loads_without_the_package():
+    """build() must work on a tree with no library yet: loading the builder
+    may not import the package (whose import loads the library)."""
+    import subprocess
+    import sys
+    code = ("import sys, __graft_entry__ as g; m = g._builder(); "
+            "assert callable(m.build); assert 'rotated_bit_amd' not in sys.modules")
+    subprocess.run([sys.executable, "-c", code], check=True, cwd=ROOT)

@@ -197,22 +197,39 @@ def test_gemv(N, K, bits, M):
 GEMM_CASES = [
     (100, 320, 2, 64), (300, 256, 3, 65), (257, 128, 4, 1), (128, 64, 2, 200),
     (4096, 4096, 2, 512), (12288, 4096, 4, 512), (4096, 12288, 2, 512),
-    (4096, 4096, 3, 129),
+    (4096, 4096, 3, 129), (1000, 1088, 2, 300), (384, 2048, 4, 64),
 ]
 
 
 @pytest.mark.parametrize("N,K,bits,M", GEMM_CASES)
 def test_gemm(N, K, bits, M):
+    """One K slice (no workspace) and split K (workspace) against the oracle;
+    the split result is bitwise reproducible and its counters return to 0."""
     d = D()
     w = S.qweight(N, K, bits, rng(13, N, K, bits))
     xt = S.activations(M, K, rng(14, K, M), "bf16")
-    yt = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    H().harp_deq_gemm(d.dev_qweight(w), d.dev(xt), yt)
+    Wd, xd = d.dev_qweight(w), d.dev(xt)
     w_hat = O.bf16_round(O.dequant(O.unpack(w.words, bits, K), d.scale_f16(w),
                                    d.zero_f16(w)))
     ref = O.bf16_bits_to_f64(xt) @ w_hat.T
+    yt = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    H().harp_deq_gemm(Wd, xd, yt)
     r = report(f"gemm {N}x{K} b{bits} M={M}", d.host(yt), ref)
     assert r <= CONTRACT_TOL and r <= FP32_PATH_TOL
+    ws = d.gemm_workspace(M, N, K)
+    if ws is not None:
+        y1 = torch.empty_like(yt)
+        y2 = torch.empty_like(yt)
+        H().harp_deq_gemm(Wd, xd, y1, ws)
+        H().harp_deq_gemm(Wd, xd, y2, ws)
+        r = report(f"gemm split-K {N}x{K} b{bits} M={M}", d.host(y1), ref)
+        assert r <= CONTRACT_TOL and r <= FP32_PATH_TOL
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2)
+        nb = ws.numel()
+        tiles = ((M + 127) // 128) * ((N + 127) // 128)
+        counters = ws[nb - ((tiles * 4 + 255) // 256) * 256:].view(torch.int32)[:tiles]
+        assert int(counters.abs().sum().item()) == 0
 
 
 # ---------------------------------------------------------------------------
