@@ -362,14 +362,20 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
           for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
       for (int zz = 0; zz < S; ++zz) {
         const float* p = partials + (static_cast<size_t>(zz) * gridDim.x * gridDim.y + tile) * kTileFloats;
+        // An accumulator's loads first, then its adds: the loads overlap
+        // instead of each waiting for the previous one.
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < 2; ++j) {
+            float part[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-              acc[i][j][v] += __hip_atomic_load(&p[((quad * 4 + i * 2 + j) * 16 + v) * kWave + lane],
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              part[v] = __hip_atomic_load(&p[((quad * 4 + i * 2 + j) * 16 + v) * kWave + lane],
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] += part[v];
+          }
       }
     }
     if (tid == 0)   // ready for the next call
