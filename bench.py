@@ -31,6 +31,16 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+
+# Memory traffic per launch of the decode-chain kernels, from two rocprofv3
+# counter passes (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000, the factors a
+# 256 MiB device copy gives) on the current kernels; set an entry to None
+# when its kernel changes until the counters are taken again.
+TRAFFIC_BYTES = {
+    "rotate_in_b4096": 228557,
+    "deq_gemv_2bit": 5448090,
+    "rotate_out_b4096": 238387,
+}
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores, TFLOP/s
 WORKING_SET_BYTES = 1 << 30
 
@@ -250,7 +260,8 @@ def main():
     achieved = kern[dom]["GB_s"]
     roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": TRAFFIC_BYTES.get(dom)}
 
     # prefill: M = 512, 4096 x 4096 2-bit on the matrix cores
     prefill = None
