@@ -44,6 +44,11 @@ repository's design notes):
   (three words).
 * Rounding points of the batched (bf16 matrix-core) path: the rotated input
   and the dequantized weight are rounded to bf16, round to nearest even.
+* int8 storage of the angles (technical summary §2.4 storage note, §4
+  storage overhead; the pages give no encoding).  Each block's angle
+  perturbation phi = t - pi/4 is stored as one signed 8-bit code c with one
+  float32 step per side: phi = c * step (``decode_angle_codes``).  Code 0 is
+  the Hadamard initialisation.
 
 Every routine is written for clarity, not speed: numpy float64, one library
 matrix product for the contraction, no blocking or fusion.
@@ -88,6 +93,21 @@ def paper_block(phi: float) -> np.ndarray:
 def block(c: float, s: float) -> np.ndarray:
     """2x2 block for the pair (cos t, sin t): [[c, s], [s, -c]]."""
     return np.array([[c, s], [s, -c]], dtype=np.float64)
+
+
+def decode_angle_codes(codes: np.ndarray, step) -> np.ndarray:
+    """(cos t, sin t) pairs of int8-stored angles, t = pi/4 + code * step.
+
+    codes: int8, any shape (the layout of the float32 pair array without its
+    last axis); step: the side's float32 step, taken at its float32 value.
+    Returns float64 (..., 2), ready for ``forward`` and ``transpose``.
+    """
+    c = np.asarray(codes)
+    if c.dtype != np.int8:
+        raise ValueError("angle codes must be int8")
+    phi = c.astype(np.float64) * float(np.float32(step))
+    t = np.pi / 4 + phi
+    return np.stack([np.cos(t), np.sin(t)], axis=-1)
 
 
 # ---------------------------------------------------------------------------

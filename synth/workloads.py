@@ -9,6 +9,9 @@ its boundary format:
 * rotation: per side, float32 (cos t, sin t) with t = pi/4 + N(0, var 0.05)
   per stage and block (pi/4 is the Hadamard initialisation of the page's
   zero-initialised Givens angle), and a random sign bitmask;
+* int8-stored rotation: the same angle spread drawn directly as int8 codes
+  (a normal rounded to integers, clipped to [-127, 127]) with one float32
+  step per side chosen so that +-127 codes span +-4 standard deviations;
 * packed weights: uniformly random uint32 words (so every B-bit code is
   uniform on [0, 2^B - 1]), fp16 group scales with the magnitude a min-max
   grid gives for N(0, 0.02^2) weights, and integer fp16 zeros near the middle
@@ -36,6 +39,7 @@ T_W, T_X, T_THETA_V, T_THETA_U, T_SIGN_V, T_SIGN_U, T_OUTLIER = range(7)
 T_SCALE, T_ZERO = 7, 8
 
 THETA_VAR = 0.05        # angle perturbation variance around pi/4 (rad^2)
+CODE_SPAN_SIGMAS = 4.0  # int8 angle codes: +-127 covers this many std devs
 OUTLIER_FRAC = 0.01
 OUTLIER_GAIN = 20.0
 
@@ -100,9 +104,11 @@ class Rotation:
     """One side's parameters in boundary format."""
     dim: int
     block: int
-    cs: np.ndarray          # float32 [dim/b][log2 b][b/2][2] = (cos t, sin t)
+    cs: np.ndarray          # float32 [dim/b][log2 b][b/2][2] = (cos t, sin t), or None
     sign_bits: np.ndarray   # uint32 [ceil(dim/32)], bit i set -> d_i = -1
     theta: np.ndarray = field(repr=False, default=None)  # float64 angles
+    phi_codes: np.ndarray = None  # int8 [dim/b][log2 b][b/2] when cs is None
+    phi_step: float = 0.0         # float32 step of the codes
 
 
 def rotation(dim: int, block: int, rng, theta_var: float = THETA_VAR,
@@ -119,11 +125,39 @@ def rotation(dim: int, block: int, rng, theta_var: float = THETA_VAR,
                                          size=(dim // block, L, block // 2))
     theta = np.asarray(theta, dtype=np.float64)
     cs = np.stack([np.cos(theta), np.sin(theta)], axis=-1).astype(np.float32)
+    return Rotation(dim, block, np.ascontiguousarray(cs), _sign_bits(dim, rng), theta)
+
+
+def _sign_bits(dim: int, rng) -> np.ndarray:
     nw = (dim + 31) // 32
     bits = rng.integers(0, 2 ** 32, size=nw, dtype=np.uint64).astype(np.uint32)
     if dim % 32:
         bits[-1] &= np.uint32((1 << (dim % 32)) - 1)
-    return Rotation(dim, block, np.ascontiguousarray(cs), bits, theta)
+    return bits
+
+
+def rotation_q8(dim: int, block: int, rng, theta_var: float = THETA_VAR,
+                codes=None, step=None) -> Rotation:
+    """Draw one side with int8-stored angles and a random sign bitmask.
+
+    Codes are integers drawn from N(0, theta_var / step^2), rounded and
+    clipped to [-127, 127]; step = CODE_SPAN_SIGMAS * sqrt(theta_var) / 127
+    in float32.  ``codes`` ([dim/b][L][b/2] int8) and ``step`` override.
+    """
+    if block < 2 or block & (block - 1) or dim % block:
+        raise ValueError("block must be a power of two dividing dim")
+    L = block.bit_length() - 1
+    if step is None:
+        step = CODE_SPAN_SIGMAS * math.sqrt(theta_var) / 127.0
+    step = np.float32(step)
+    if codes is None:
+        z = rng.normal(0.0, math.sqrt(theta_var) / float(step),
+                       size=(dim // block, L, block // 2))
+        codes = np.clip(np.rint(z), -127, 127)
+    codes = np.ascontiguousarray(np.asarray(codes).astype(np.int8))
+    if codes.shape != (dim // block, L, block // 2):
+        raise ValueError("codes must have shape [dim/b][log2 b][b/2]")
+    return Rotation(dim, block, None, _sign_bits(dim, rng), None, codes, float(step))
 
 
 @dataclass
@@ -201,15 +235,19 @@ class LayerInputs:
 
 
 def layer_inputs(cfg: Config, lin_idx: int, bits: int, M: int,
-                 inst: int = 0) -> LayerInputs:
-    """All boundary buffers for one linear of a config, fully seeded."""
+                 inst: int = 0, angles: str = "f32") -> LayerInputs:
+    """All boundary buffers for one linear of a config, fully seeded.
+
+    angles: "f32" for float32 (cos, sin) pairs, "int8" for int8-stored angles.
+    """
     lin = cfg.linears[lin_idx]
     out = outlier_channels(lin.K, rng_for(cfg.cid, T_OUTLIER, lin_idx, inst)) \
         if cfg.outliers else None
     x = activations(M, lin.K, rng_for(cfg.cid, T_X, lin_idx, inst * 1000 + M),
                     cfg.x_dtype, out)
-    V = rotation(lin.K, lin.b_v, rng_for(cfg.cid, T_THETA_V, lin_idx, inst))
-    U = rotation(lin.N, lin.b_u, rng_for(cfg.cid, T_THETA_U, lin_idx, inst))
+    draw = {"f32": rotation, "int8": rotation_q8}[angles]
+    V = draw(lin.K, lin.b_v, rng_for(cfg.cid, T_THETA_V, lin_idx, inst))
+    U = draw(lin.N, lin.b_u, rng_for(cfg.cid, T_THETA_U, lin_idx, inst))
     W = qweight(lin.N, lin.K, bits,
                 rng_for(cfg.cid, T_W, lin_idx, inst * 16 + bits), cfg.w_std)
     return LayerInputs(lin, bits, M, x, cfg.x_dtype, V, U, W)

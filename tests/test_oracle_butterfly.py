@@ -180,3 +180,98 @@ def test_large_init_matches_hadamard_on_vectors():
     H = scipy.linalg.hadamard(b).astype(np.float64)
     ref = (x * signs_pm1(bits, b)) @ H.T / 64.0
     assert np.max(np.abs(got - ref)) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# int8-stored angles: t = pi/4 + code * step (technical summary §2.4 storage
+# note).  Pinned by the page's block definition and by closed forms at the
+# codes that give quarter turns (a swap) and zero turns (a diagonal).
+# ---------------------------------------------------------------------------
+
+QUARTER = np.float32(math.pi / 508)      # 127 * step = pi/4 up to float32
+
+
+def _code_block(d, b, code):
+    L = b.bit_length() - 1
+    return np.full((d // b, L, b // 2), code, dtype=np.int8)
+
+
+def test_angle_codes_match_page_block():
+    """block(decoded pair) equals Q(code * step) G_2 as the page defines it."""
+    r = np.random.default_rng(40)
+    codes = r.integers(-128, 128, size=50).astype(np.int8)
+    step = np.float32(0.0123)
+    cs = O.decode_angle_codes(codes, step)
+    for c, pair in zip(codes, cs):
+        phi = int(c) * float(step)
+        assert np.allclose(O.block(pair[0], pair[1]), O.paper_block(phi),
+                           atol=1e-15, rtol=0)
+
+
+@pytest.mark.parametrize("b", [2, 16, 256])
+def test_angle_code_zero_is_randomized_hadamard(b):
+    """Code 0 is the Hadamard initialisation whatever the step."""
+    r = np.random.default_rng(41 + b)
+    signs = random_signs(2 * b, r)
+    x = r.normal(size=(3, 2 * b))
+    cs = O.decode_angle_codes(_code_block(2 * b, b, 0), np.float32(0.37))
+    Hb = scipy.linalg.hadamard(b) / math.sqrt(b)
+    xd = x * signs_pm1(signs, 2 * b)
+    ref = np.concatenate([xd[:, :b] @ Hb.T, xd[:, b:] @ Hb.T], axis=1)
+    assert np.allclose(O.forward(x, cs, signs, b), ref, atol=1e-13, rtol=0)
+
+
+@pytest.mark.parametrize("b", [4, 32, 512])
+def test_angle_code_quarter_turn_reverses(b):
+    """Code +127 at step pi/508: every stage swaps its pairs, so F x [i] is
+    (D x)[b - 1 - i] (index complement over all L bits)."""
+    r = np.random.default_rng(50 + b)
+    signs = random_signs(b, r)
+    x = r.normal(size=(2, b))
+    cs = O.decode_angle_codes(_code_block(b, b, 127), QUARTER)
+    ref = (x * signs_pm1(signs, b))[:, ::-1]
+    assert np.allclose(O.forward(x, cs, signs, b), ref, atol=1e-6, rtol=0)
+
+
+@pytest.mark.parametrize("b", [4, 32, 512])
+def test_angle_code_negative_quarter_is_parity_sign(b):
+    """Code -127 at step pi/508: t = 0, every stage negates the partner
+    coordinate, so F x [i] = (-1)^popcount(i) (D x)[i]."""
+    r = np.random.default_rng(60 + b)
+    signs = random_signs(b, r)
+    x = r.normal(size=(2, b))
+    cs = O.decode_angle_codes(_code_block(b, b, -127), QUARTER)
+    par = np.array([(-1.0) ** bin(i).count("1") for i in range(b)])
+    ref = x * signs_pm1(signs, b) * par
+    assert np.allclose(O.forward(x, cs, signs, b), ref, atol=1e-6, rtol=0)
+
+
+def test_angle_codes_stage_and_pair_layout():
+    """Codes vary by stage (b = 8) and by pair (b = 4): closed forms.
+
+    b = 8, stages 0 and 2 swap (+127) and stage 1 is diagonal (-127):
+    F x [j] = (-1)^bit1(j) (D x)[j xor 5].
+    b = 4, stage 0 pair 0 swaps, pair 1 is diagonal; stage 1 diagonal:
+    F x = (x1, x0, -x2, x3) after D.
+    """
+    r = np.random.default_rng(70)
+    signs = random_signs(8, r)
+    x = r.normal(size=(2, 8))
+    codes = np.array([[[127] * 4, [-127] * 4, [127] * 4]], dtype=np.int8)
+    got = O.forward(x, O.decode_angle_codes(codes, QUARTER), signs, 8)
+    xd = x * signs_pm1(signs, 8)
+    ref = np.stack([(-1.0) ** ((j >> 1) & 1) * xd[:, j ^ 5] for j in range(8)], axis=1)
+    assert np.allclose(got, ref, atol=1e-6, rtol=0)
+
+    signs4 = random_signs(4, r)
+    x4 = r.normal(size=(2, 4))
+    codes4 = np.array([[[127, -127], [-127, -127]]], dtype=np.int8)
+    got4 = O.forward(x4, O.decode_angle_codes(codes4, QUARTER), signs4, 4)
+    u = x4 * signs_pm1(signs4, 4)
+    ref4 = np.stack([u[:, 1], u[:, 0], -u[:, 2], u[:, 3]], axis=1)
+    assert np.allclose(got4, ref4, atol=1e-6, rtol=0)
+
+
+def test_angle_codes_reject_other_dtypes():
+    with pytest.raises(ValueError):
+        O.decode_angle_codes(np.zeros(4, dtype=np.int16), 0.1)

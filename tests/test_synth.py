@@ -46,3 +46,19 @@ def test_bf16_activations_carry_outliers():
     big = np.abs(v[:, out]).mean()
     small = np.abs(np.delete(v, out, axis=1)).mean()
     assert big > 10 * small
+
+
+def test_int8_angle_codes():
+    cfg = S.CONFIGS["l7b_mlp"]
+    a = S.layer_inputs(cfg, 0, 2, 1, angles="int8")
+    b = S.layer_inputs(cfg, 0, 2, 1, angles="int8")
+    assert a.V.cs is None and a.V.phi_codes.dtype == np.int8
+    assert a.V.phi_codes.shape == (1, 12, 2048) and a.U.phi_codes.shape == (43, 8, 128)
+    assert np.array_equal(a.V.phi_codes, b.V.phi_codes)
+    assert np.array_equal(a.U.sign_bits, b.U.sign_bits)
+    c = a.V.phi_codes.astype(np.float64)
+    assert c.min() >= -127 and c.max() <= 127
+    # spread: std of code * step near sqrt(0.05)
+    std = (c * a.V.phi_step).std()
+    assert abs(std - np.sqrt(S.THETA_VAR)) < 0.02
+    assert np.float32(a.V.phi_step) == a.V.phi_step
