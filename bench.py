@@ -49,9 +49,13 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def alg_bytes(M, N, K, bits, b_v, b_u, x_bytes=2, y_bytes=4):
+def alg_bytes(M, N, K, bits, b_v, b_u, x_bytes=2, y_bytes=4, pair_bytes=8):
+    """pair_bytes: 8 for float32 (cos, sin) pairs, 1 for int8-stored angles
+    (plus the two float32 steps)."""
     Lv, Lu = b_v.bit_length() - 1, b_u.bit_length() - 1
-    return (N * K * bits // 8 + N * (K // 64) * 4 + 8 * (K // 2 * Lv + N // 2 * Lu)
+    steps = 8 if pair_bytes == 1 else 0
+    return (N * K * bits // 8 + N * (K // 64) * 4
+            + pair_bytes * (K // 2 * Lv + N // 2 * Lu) + steps
             + (K + N) // 8 + x_bytes * M * K + y_bytes * M * N)
 
 
@@ -60,9 +64,10 @@ def gemv_bytes(M, N, K, bits):
     return N * K * bits // 8 + N * (K // 64) * 4 + 4 * M * K + 4 * M * N
 
 
-def rotate_bytes(M, d, b, in_bytes, out_bytes):
+def rotate_bytes(M, d, b, in_bytes, out_bytes, pair_bytes=8):
     L = b.bit_length() - 1
-    return 8 * (d // 2) * L + d // 8 + in_bytes * M * d + out_bytes * M * d
+    steps = 4 if pair_bytes == 1 else 0
+    return pair_bytes * (d // 2) * L + steps + d // 8 + in_bytes * M * d + out_bytes * M * d
 
 
 class Instance:
@@ -81,8 +86,14 @@ class Instance:
 
         lin = li.lin
         self.li = li
-        self.V = H.Rotation(dev(li.V.cs), dev(li.V.sign_bits), li.V.dim, li.V.block)
-        self.U = H.Rotation(dev(li.U.cs), dev(li.U.sign_bits), li.U.dim, li.U.block)
+        def rot(r):
+            if r.cs is None:
+                return H.Rotation(None, dev(r.sign_bits), r.dim, r.block,
+                                  phi_codes=dev(r.phi_codes), phi_step=r.phi_step)
+            return H.Rotation(dev(r.cs), dev(r.sign_bits), r.dim, r.block)
+
+        self.V = rot(li.V)
+        self.U = rot(li.U)
         self.W = H.QWeight(dev(li.W.words), dev(li.W.scale), dev(li.W.zero),
                            lin.N, lin.K, li.bits)
         self.x = dev(li.x).view(torch.bfloat16)
@@ -97,10 +108,11 @@ class Instance:
         self.yp = torch.empty((li.M, lin.N), dtype=torch.float32, device="cuda")
 
 
-def make_instances(cfg_name, lin_idx, bits, M, count, torch, H):
+def make_instances(cfg_name, lin_idx, bits, M, count, torch, H, angles="f32"):
     from synth import workloads as S
     cfg = S.CONFIGS[cfg_name]
-    return [Instance(S.layer_inputs(cfg, lin_idx, bits, M, inst=i), torch, H, torch.float32)
+    return [Instance(S.layer_inputs(cfg, lin_idx, bits, M, inst=i, angles=angles),
+                     torch, H, torch.float32)
             for i in range(count)]
 
 
@@ -166,6 +178,8 @@ def main():
     ap.add_argument("--instances", type=int, default=0, help="layer instances (0: >= 1 GiB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=512 figure")
+    ap.add_argument("--no-int8", action="store_true",
+                    help="skip the decode leg with int8-stored angles")
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graph")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (the known-size "
@@ -263,11 +277,38 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": TRAFFIC_BYTES.get(dom)}
 
+    # the same decode workload with int8-stored angles
+    del inst
+    torch.cuda.empty_cache()
+    q8 = None
+    if not args.no_int8:
+        per8 = alg_bytes(M, N, K, bits, bv, bu, pair_bytes=1)
+        count8 = args.instances or -(-WORKING_SET_BYTES // per8)
+        inst8 = make_instances("l7b_decode", 0, bits, M, count8, torch, H, angles="int8")
+        ms8, _ = time_graph(torch, lambda: [H.harp_linear_fused(i.V, i.W, i.U, i.x, i.y, i.ws)
+                                            for i in inst8], max(3, args.steps // 4))
+        ms8_ri, _ = time_graph(torch, lambda: [H.harp_rotate_in(i.V, i.x, i.xt32) for i in inst8], reps)
+        ms8_ro, _ = time_graph(torch, lambda: [H.harp_rotate_out(i.U, i.yp, i.y) for i in inst8], reps)
+        us8 = ms8 * 1e3 / count8
+        q8 = {"workload": "l7b_decode with int8-stored angles (one byte per pair)",
+              "instances_per_step": count8, "bytes_per_call": per8,
+              "us_per_linear": round(us8, 3),
+              "GB_s": round(per8 / (us8 * 1e-6) / 1e9, 2),
+              "speedup_vs_f32_pairs": round((ms * 1e3 / count) / us8, 3),
+              "kernels": {}}
+        for name, msk, nbytes in (
+                ("rotate_in_b4096_int8", ms8_ri, rotate_bytes(M, K, bv, 2, 4, 1)),
+                ("rotate_out_b4096_int8", ms8_ro, rotate_bytes(M, N, bu, 4, 4, 1))):
+            us = msk * 1e3 / count8
+            q8["kernels"][name] = {"us_per_launch": round(us, 3), "alg_bytes": nbytes,
+                                   "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        log("int8 angles: " + json.dumps(q8))
+        del inst8
+        torch.cuda.empty_cache()
+
     # prefill: M = 512, 4096 x 4096 2-bit on the matrix cores
     prefill = None
     if not args.no_prefill:
-        del inst
-        torch.cuda.empty_cache()
         pre = make_instances("q8b_prefill", 0, 2, 512, 8, torch, H)
         flops = 2.0 * 512 * 4096 * 4096
         for it in pre:
@@ -315,6 +356,7 @@ def main():
         "tok_s_equiv_llama2_7b_linears": round(tok_s, 1),
         "roofline": roofline,
         "kernels": kern,
+        "int8_angles": q8,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

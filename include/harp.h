@@ -60,7 +60,7 @@ extern "C" {
 typedef enum harp_status {
   HARP_OK = 0,
   HARP_ERR_NULL = 1,         /* a required pointer is NULL                    */
-  HARP_ERR_SHAPE = 2,        /* inconsistent or out-of-range dimension        */
+  HARP_ERR_SHAPE = 2,        /* inconsistent or out-of-range dimension/value  */
   HARP_ERR_DTYPE = 3,        /* dtype value not in harp_dtype                 */
   HARP_ERR_ALIGN = 4,        /* a data pointer is not 16-byte aligned         */
   HARP_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required       */
@@ -85,14 +85,26 @@ typedef void *harp_stream;   /* hipStream_t */
  *   dim        vector length (K on the input side, N on the output side)
  *   block      b: power of two, 2 <= b <= 8192, dim % b == 0
  *   cs         [dim/b][log2 b][b/2][2] float32: (cos t, sin t) for block j,
- *              stage s, pair index c (i with bit s deleted)
+ *              stage s, pair index c (i with bit s deleted); NULL when the
+ *              angles are given as phi_codes
  *   sign_bits  [ceil(dim/32)] uint32: bit i of word i/32 set means D_ii = -1
+ *   phi_codes  [dim/b][log2 b][b/2] int8, same index order as cs: the angles
+ *              stored in eight bits (technical summary §2.4, storage of the
+ *              HARP parameters), t = pi/4 + phi_codes * phi_step; every int8
+ *              value is valid; NULL when cs is given
+ *   phi_step   float32 step of phi_codes, finite; not read when cs is given
+ * Exactly one of cs and phi_codes is set (neither: HARP_ERR_NULL, both:
+ * HARP_ERR_SHAPE).  With phi_codes the kernels evaluate cos t and sin t in
+ * float32 for the 256 code values.  All pointers are device memory owned by
+ * the caller, 16-byte aligned, and only read.
  */
 typedef struct harp_rotation {
   int32_t dim;
   int32_t block;
   const float *cs;
   const uint32_t *sign_bits;
+  const int8_t *phi_codes;
+  float phi_step;
 } harp_rotation;
 
 /*

@@ -12,7 +12,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import c_int32, c_size_t, c_void_p, c_char_p
+from ctypes import c_char_p, c_float, c_int32, c_size_t, c_void_p
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libharp.so")
@@ -48,7 +48,8 @@ class HarpError(RuntimeError):
 
 class harp_rotation(ctypes.Structure):
     _fields_ = [("dim", c_int32), ("block", c_int32),
-                ("cs", c_void_p), ("sign_bits", c_void_p)]
+                ("cs", c_void_p), ("sign_bits", c_void_p),
+                ("phi_codes", c_void_p), ("phi_step", c_float)]
 
 
 class harp_qweight(ctypes.Structure):
@@ -133,11 +134,18 @@ def _check(status: int, where: str):
 
 
 class Rotation:
-    """One side: cs float32 [dim/b][log2 b][b/2][2], sign_bits int32/uint32 [ceil(dim/32)]."""
+    """One side: sign_bits int32/uint32 [ceil(dim/32)] and the angles, either
+    cs float32 [dim/b][log2 b][b/2][2] (cos t, sin t) or, with cs None,
+    phi_codes int8 [dim/b][log2 b][b/2] and phi_step (t = pi/4 + code*step)."""
 
-    def __init__(self, cs, sign_bits, dim: int, block: int):
+    def __init__(self, cs, sign_bits, dim: int, block: int, phi_codes=None,
+                 phi_step: float = 0.0):
         self.cs, self.sign_bits, self.dim, self.block = cs, sign_bits, dim, block
-        self.c = harp_rotation(dim, block, cs.data_ptr(), sign_bits.data_ptr())
+        self.phi_codes, self.phi_step = phi_codes, phi_step
+        self.c = harp_rotation(dim, block, None if cs is None else cs.data_ptr(),
+                               sign_bits.data_ptr(),
+                               None if phi_codes is None else phi_codes.data_ptr(),
+                               float(phi_step))
 
 
 class QWeight:

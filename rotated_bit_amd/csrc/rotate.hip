@@ -16,6 +16,12 @@
 // it, so b = 4096 needs three LDS exchanges for twelve stages.  All of a
 // thread's (cos, sin) pairs are loaded into registers before the first
 // round, so their memory latency is paid once.
+//
+// Angles stored as int8 codes (technical summary §2.4: the HARP parameters
+// may be kept in eight bits): t = pi/4 + code * step.  Every workgroup
+// evaluates (cos t, sin t) once for all 256 codes into an LDS table while
+// its code loads are in flight, then gathers its pairs from the table, so a
+// block's coefficient fetch is one byte per pair instead of eight.
 #include "launch.hpp"
 #include "device_common.hpp"
 
@@ -89,11 +95,11 @@ __device__ __forceinline__ void store_contig(T* p, const float (&v)[E]) {
   *reinterpret_cast<Pack<T, E>*>(p) = pk;
 }
 
-template <int LOGB, int EL_, bool TRANSPOSE, typename TIn, typename TOut>
+template <int LOGB, int EL_, bool TRANSPOSE, bool Q8, typename TIn, typename TOut>
 __global__ __launch_bounds__((Plan<LOGB, EL_>::THREADS)) void rotate_kernel(
     const TIn* __restrict__ in, TOut* __restrict__ out,
-    const float2* __restrict__ cs, const uint32_t* __restrict__ sign, int dim,
-    int M, int rows_per_slot) {
+    const float2* __restrict__ cs, const int8_t* __restrict__ codes, float step,
+    const uint32_t* __restrict__ sign, int dim, int M, int rows_per_slot) {
   using P = Plan<LOGB, EL_>;
   constexpr int B = P::B;
   constexpr int E = P::E;
@@ -101,6 +107,7 @@ __global__ __launch_bounds__((Plan<LOGB, EL_>::THREADS)) void rotate_kernel(
   constexpr int L = P::L;
   constexpr int NR = P::NR;
   extern __shared__ float lds[];
+  __shared__ float2 table[Q8 ? 256 : 1];   // (cos t, sin t) by code + 128
 
   const int tid = threadIdx.x;
   const int slot = tid / P::TPB;
@@ -108,14 +115,41 @@ __global__ __launch_bounds__((Plan<LOGB, EL_>::THREADS)) void rotate_kernel(
   const int blk = blockIdx.x;
   float* u = lds + slot * B;
 
+  // The first round's input of a row, fetched raw (not converted, not
+  // sign-flipped) so that nothing waits for it before the coefficient
+  // loads are issued; rows past M read as zeros.
+  constexpr int kR0 = TRANSPOSE ? NR - 1 : 0;       // round executed first
+  constexpr int kS00 = kR0 * EL;
+  constexpr int kW0 = round_width(kR0, EL, L);
+  auto fetch = [&](int it, TIn (&raw)[E]) {
+    const int row = (blockIdx.y * rows_per_slot + it) * P::SLOTS + slot;
+    if (row < M) {
+      const TIn* src = in + static_cast<size_t>(row) * dim + static_cast<size_t>(blk) * B;
+      if constexpr (kS00 == 0) {
+        const Pack<TIn, E> pk = *reinterpret_cast<const Pack<TIn, E>*>(src + t * E);
+#pragma unroll
+        for (int j = 0; j < E; ++j) raw[j] = pk.v[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < E; ++j) raw[j] = src[elem_index<E>(t, j, kS00, kW0)];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < E; ++j) raw[j] = TIn(0);
+    }
+  };
+  TIn raw[E];
+  fetch(0, raw);
+
   // (cos, sin) of every pair this thread touches, stage-major.  Rounds are
   // loaded in execution order; when they would not all fit in registers
   // next to the data (b = 8192 at 1024 threads), the last ones are loaded
   // once the first round has released its registers.
   float2 cf[L][E / 2];
-  const float2* csb = cs + static_cast<size_t>(blk) * L * (B / 2);
+  const size_t blk_off = static_cast<size_t>(blk) * L * (B / 2);
   constexpr int kEarly = (L * E) > 96 ? 3 : NR;   // rounds loaded up front
-  auto load_round = [&](int q) {
+  // f(s, p, c): pair p of stage s of this thread has coefficient index c.
+  auto for_round = [&](int q, auto&& f) {
     const int r = TRANSPOSE ? NR - 1 - q : q;
     const int s0 = r * EL;
     const int R = round_width(r, EL, L);
@@ -126,13 +160,43 @@ __global__ __launch_bounds__((Plan<LOGB, EL_>::THREADS)) void rotate_kernel(
 #pragma unroll
         for (int p = 0; p < E / 2; ++p) {
           const int i = elem_index<E>(t, insert_zero_bit(p, k), s0, R);
-          cf[s][p] = csb[s * (B / 2) + delete_bit(i, s)];
+          f(s, p, s * (B / 2) + delete_bit(i, s));
         }
       }
     }
   };
+  // int8 codes: all of them stay in registers (one per pair).  The table
+  // lookups happen once up front when every pair fits in registers, else
+  // round by round just before each round runs.
+  constexpr bool kLookupOnce = kEarly == NR;
+  int qc[Q8 ? L : 1][E / 2];
+  if constexpr (Q8) {
+    const int8_t* qb = codes + blk_off;
 #pragma unroll
-  for (int q = 0; q < kEarly; ++q) load_round(q);
+    for (int q = 0; q < NR; ++q)
+      for_round(q, [&](int s, int p, int c) { qc[s][p] = qb[c]; });
+    for (int i = tid; i < 256; i += P::THREADS) {
+      float sn, cn;
+      sincosf(fmaf(static_cast<float>(i - 128), step, 0.785398163397448310f), &sn, &cn);
+      table[i] = make_float2(cn, sn);
+    }
+    __syncthreads();
+    if constexpr (kLookupOnce) {
+#pragma unroll
+      for (int q = 0; q < NR; ++q)
+        for_round(q, [&](int s, int p, int) { cf[s][p] = table[qc[s][p] + 128]; });
+    }
+  } else {
+    const float2* csb = cs + blk_off;
+#pragma unroll
+    for (int q = 0; q < kEarly; ++q)
+      for_round(q, [&](int s, int p, int c) { cf[s][p] = csb[c]; });
+  }
+  constexpr bool kPrefetchRow = Q8 || kEarly == NR;
+  auto load_round = [&](int q) {
+    const float2* csb = cs + blk_off;
+    for_round(q, [&](int s, int p, int c) { cf[s][p] = csb[c]; });
+  };
   // the E sign bits of this thread's contiguous elements t*E .. t*E+E-1
   const int g0 = blk * B + t * E;
   const uint32_t sbits = sign[g0 >> 5] >> (g0 & 31);
@@ -143,33 +207,29 @@ __global__ __launch_bounds__((Plan<LOGB, EL_>::THREADS)) void rotate_kernel(
     const size_t base = static_cast<size_t>(active ? row : 0) * dim +
                         static_cast<size_t>(blk) * B;
     if (NR > 1 && it > 0) __syncthreads();   // LDS reuse across rows
+    if (!kPrefetchRow && it > 0) fetch(it, raw);
     float v[E];
 #pragma unroll
     for (int q = 0; q < NR; ++q) {
       const int r = TRANSPOSE ? NR - 1 - q : q;
       const int s0 = r * EL;
       const int R = round_width(r, EL, L);
-      if (q == 1 && it == 0) {
+      if constexpr (Q8 && !kLookupOnce) {
+        for_round(q, [&](int s, int p, int) { cf[s][p] = table[qc[s][p] + 128]; });
+      } else if (!Q8 && q == 1 && it == 0) {
 #pragma unroll
         for (int ql = kEarly; ql < NR; ++ql) load_round(ql);
       }
       if (q == 0) {
-        if (s0 == 0) {
-          if (active) {
-            load_contig<TIn, E>(in + base + t * E, v);
-          } else {
 #pragma unroll
-            for (int j = 0; j < E; ++j) v[j] = 0.0f;
-          }
-          if (!TRANSPOSE) {
+        for (int j = 0; j < E; ++j) v[j] = to_f32(raw[j]);
+        if (!TRANSPOSE && s0 == 0) {
 #pragma unroll
-            for (int j = 0; j < E; ++j) v[j] = flip_sign(v[j], (sbits >> j) & 1u);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < E; ++j)
-            v[j] = active ? to_f32(in[base + elem_index<E>(t, j, s0, R)]) : 0.0f;
+          for (int j = 0; j < E; ++j) v[j] = flip_sign(v[j], (sbits >> j) & 1u);
         }
+        // the next row's input is in flight during this row's rounds, unless
+        // the float32 pairs already fill the registers (b = 8192)
+        if (kPrefetchRow && it + 1 < rows_per_slot) fetch(it + 1, raw);
       } else {
 #pragma unroll
         for (int j = 0; j < E; ++j) v[j] = u[elem_index<E>(t, j, s0, R)];
@@ -214,7 +274,7 @@ __global__ __launch_bounds__((Plan<LOGB, EL_>::THREADS)) void rotate_kernel(
   }
 }
 
-template <int LOGB, int EL_, bool TRANSPOSE, typename TIn, typename TOut>
+template <int LOGB, int EL_, bool TRANSPOSE, bool Q8, typename TIn, typename TOut>
 hipError_t launch_typed(const harp_rotation& R, const void* in, void* out, int M,
                         hipStream_t stream) {
   using P = Plan<LOGB, EL_>;
@@ -229,28 +289,38 @@ hipError_t launch_typed(const harp_rotation& R, const void* in, void* out, int M
   if (rps < need) rps = need;
   const dim3 grid(nblk, (ygroups + rps - 1) / rps);
   const size_t shmem = P::NR > 1 ? sizeof(float) * P::SLOTS * P::B : 0;
-  hipLaunchKernelGGL((rotate_kernel<LOGB, EL_, TRANSPOSE, TIn, TOut>), grid,
+  hipLaunchKernelGGL((rotate_kernel<LOGB, EL_, TRANSPOSE, Q8, TIn, TOut>), grid,
                      dim3(P::THREADS), shmem, stream,
                      static_cast<const TIn*>(in), static_cast<TOut*>(out),
-                     reinterpret_cast<const float2*>(R.cs), R.sign_bits, R.dim,
-                     M, rps);
+                     reinterpret_cast<const float2*>(R.cs), R.phi_codes,
+                     R.phi_step, R.sign_bits, R.dim, M, rps);
   return hipGetLastError();
+}
+
+template <int LOGB, int EL_, bool Q8>
+hipError_t launch_q(const harp_rotation& R, const void* in, int in_dt,
+                    void* out, int out_dt, int M, bool transpose,
+                    hipStream_t stream) {
+  const bool ib = in_dt == HARP_BF16;
+  const bool ob = out_dt == HARP_BF16;
+  if (transpose) {   // y' is always float32
+    if (ob) return launch_typed<LOGB, EL_, true, Q8, float, uint16_t>(R, in, out, M, stream);
+    return launch_typed<LOGB, EL_, true, Q8, float, float>(R, in, out, M, stream);
+  }
+  if (ib && ob)
+    return launch_typed<LOGB, EL_, false, Q8, uint16_t, uint16_t>(R, in, out, M, stream);
+  if (ib) return launch_typed<LOGB, EL_, false, Q8, uint16_t, float>(R, in, out, M, stream);
+  if (ob) return launch_typed<LOGB, EL_, false, Q8, float, uint16_t>(R, in, out, M, stream);
+  return launch_typed<LOGB, EL_, false, Q8, float, float>(R, in, out, M, stream);
 }
 
 template <int LOGB, int EL_>
 hipError_t launch_el(const harp_rotation& R, const void* in, int in_dt,
                      void* out, int out_dt, int M, bool transpose,
                      hipStream_t stream) {
-  const bool ib = in_dt == HARP_BF16;
-  const bool ob = out_dt == HARP_BF16;
-  if (transpose) {   // y' is always float32
-    if (ob) return launch_typed<LOGB, EL_, true, float, uint16_t>(R, in, out, M, stream);
-    return launch_typed<LOGB, EL_, true, float, float>(R, in, out, M, stream);
-  }
-  if (ib && ob) return launch_typed<LOGB, EL_, false, uint16_t, uint16_t>(R, in, out, M, stream);
-  if (ib) return launch_typed<LOGB, EL_, false, uint16_t, float>(R, in, out, M, stream);
-  if (ob) return launch_typed<LOGB, EL_, false, float, uint16_t>(R, in, out, M, stream);
-  return launch_typed<LOGB, EL_, false, float, float>(R, in, out, M, stream);
+  if (R.phi_codes != nullptr)
+    return launch_q<LOGB, EL_, true>(R, in, in_dt, out, out_dt, M, transpose, stream);
+  return launch_q<LOGB, EL_, false>(R, in, in_dt, out, out_dt, M, transpose, stream);
 }
 
 template <int LOGB>

@@ -4,6 +4,8 @@
 // batch range, data pointers (NULL when M > 0), alignment, workspace.
 #include "validate.hpp"
 
+#include <cmath>
+
 namespace harp {
 namespace {
 
@@ -34,13 +36,18 @@ harp_status check_data(const void* p, int32_t M) {
 }  // namespace
 
 harp_status check_rotation(const harp_rotation* R) {
-  if (R == nullptr || R->cs == nullptr || R->sign_bits == nullptr)
+  if (R == nullptr || R->sign_bits == nullptr ||
+      (R->cs == nullptr && R->phi_codes == nullptr))
     return HARP_ERR_NULL;
+  if (R->cs != nullptr && R->phi_codes != nullptr) return HARP_ERR_SHAPE;
   if (pow2(R->block) && R->block > HARP_MAX_BLOCK) return HARP_ERR_UNSUPPORTED;
   if (!pow2(R->block) || R->block < 2) return HARP_ERR_SHAPE;
   if (R->dim < 1 || R->dim > HARP_MAX_DIM || R->dim % R->block != 0)
     return HARP_ERR_SHAPE;
-  if (!aligned(R->cs, 16) || !aligned(R->sign_bits, 16)) return HARP_ERR_ALIGN;
+  if (R->phi_codes != nullptr && !std::isfinite(R->phi_step)) return HARP_ERR_SHAPE;
+  const void* angles = R->cs != nullptr ? static_cast<const void*>(R->cs)
+                                        : static_cast<const void*>(R->phi_codes);
+  if (!aligned(angles, 16) || !aligned(R->sign_bits, 16)) return HARP_ERR_ALIGN;
   return HARP_OK;
 }
 

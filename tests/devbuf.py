@@ -19,7 +19,18 @@ def dev(a: np.ndarray) -> torch.Tensor:
 
 
 def dev_rotation(rot) -> "H.Rotation":
+    if rot.cs is None:
+        return H.Rotation(None, dev(rot.sign_bits), rot.dim, rot.block,
+                          phi_codes=dev(rot.phi_codes), phi_step=rot.phi_step)
     return H.Rotation(dev(rot.cs), dev(rot.sign_bits), rot.dim, rot.block)
+
+
+def cs64(rot) -> np.ndarray:
+    """The side's (cos t, sin t) pairs for the oracle: the stored float32
+    pairs, or the oracle's float64 decode of int8-stored angles."""
+    if rot.cs is None:
+        return O.decode_angle_codes(rot.phi_codes, rot.phi_step)
+    return rot.cs
 
 
 def dev_qweight(w) -> "H.QWeight":

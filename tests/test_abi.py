@@ -35,8 +35,12 @@ def test_every_declared_symbol_is_exported():
         assert ctypes.cast(getattr(L.lib, name), ctypes.c_void_p).value
 
 
-def rot(dim=256, block=256, cs=FAKE, sb=FAKE):
-    return L.harp_rotation(dim, block, cs, sb)
+def rot(dim=256, block=256, cs=FAKE, sb=FAKE, codes=0, step=0.0):
+    return L.harp_rotation(dim, block, cs, sb, codes, step)
+
+
+def rot8(codes=FAKE, step=0.01, cs=0, **kw):
+    return rot(cs=cs, codes=codes, step=step, **kw)
 
 
 def qw(N=256, K=256, bits=2, group=64, q=FAKE, s=FAKE, z=FAKE):
@@ -61,9 +65,30 @@ def rot_in(R, x=FAKE, xdt=0, xt=FAKE, xtdt=0, M=1):
     (rot(dim=262144 * 2, block=256), L.HARP_ERR_SHAPE),
     (rot(cs=MISALIGNED), L.HARP_ERR_ALIGN),
     (rot(sb=MISALIGNED), L.HARP_ERR_ALIGN),
+    # int8-stored angles: exactly one angle format, a finite step
+    (rot8(codes=0), L.HARP_ERR_NULL),
+    (rot8(cs=FAKE), L.HARP_ERR_SHAPE),
+    (rot8(step=float("nan")), L.HARP_ERR_SHAPE),
+    (rot8(step=float("inf")), L.HARP_ERR_SHAPE),
+    (rot8(codes=MISALIGNED), L.HARP_ERR_ALIGN),
+    (rot8(sb=0), L.HARP_ERR_NULL),
+    (rot8(block=3), L.HARP_ERR_SHAPE),
 ])
 def test_rotation_checks(R, expect):
     assert rot_in(R) == expect
+
+
+def test_int8_angle_rotation_accepted():
+    # M = 0: passes every check and launches nothing
+    assert rot_in(rot8(), x=0, xt=0, M=0) == L.HARP_OK
+    assert rot_in(rot8(step=0.0), x=0, xt=0, M=0) == L.HARP_OK
+
+
+def test_rotation_struct_layout():
+    f = dict((n, getattr(L.harp_rotation, n)) for n, _ in L.harp_rotation._fields_)
+    assert [f[n].offset for n in ("dim", "block", "cs", "sign_bits", "phi_codes", "phi_step")] \
+        == [0, 4, 8, 16, 24, 32]
+    assert ctypes.sizeof(L.harp_rotation) == 40
 
 
 def test_rotate_in_other_checks():

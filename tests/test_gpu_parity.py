@@ -143,6 +143,55 @@ def test_rotate_in_out(dim, b, M, xdt):
     assert report(f"rotate_out {dim}/{b} M={M}", d.host(y), reft) <= BUTTERFLY_TOL
 
 
+ROT8_CASES = [
+    (2, 2, 5, "f32"), (8, 8, 7, "f32"), (48, 16, 9, "f32"), (256, 256, 4, "f32"),
+    (512, 32, 33, "bf16"), (4096, 4096, 1, "bf16"), (4096, 4096, 17, "bf16"),
+    (8192, 8192, 1, "bf16"), (8192, 8192, 32, "bf16"), (11008, 256, 16, "bf16"),
+    (12288, 256, 512, "bf16"), (4096, 4096, 512, "bf16"),
+]
+
+
+@pytest.mark.parametrize("dim,b,M,xdt", ROT8_CASES)
+def test_rotate_int8_angles(dim, b, M, xdt):
+    """int8-stored angles: the kernel's float32 table against the oracle's
+    float64 decode of the same codes, both directions."""
+    d = D()
+    rot = S.rotation_q8(dim, b, rng(30, dim, b))
+    R = d.dev_rotation(rot)
+    cs = d.cs64(rot)
+    x = S.activations(M, dim, rng(31, dim, M), xdt)
+    xt = torch.empty((M, dim), dtype=torch.float32, device="cuda")
+    H().harp_rotate_in(R, d.dev_x(x, xdt), xt)
+    ref = O.forward(d.x_f64(x, xdt), cs, rot.sign_bits, b)
+    assert report(f"rotate_in int8 {dim}/{b} M={M}", d.host(xt), ref) <= BUTTERFLY_TOL
+    yp = rng(32, dim, M).normal(size=(M, dim)).astype(np.float32)
+    y = torch.empty((M, dim), dtype=torch.float32, device="cuda")
+    H().harp_rotate_out(R, d.dev(yp), y)
+    reft = O.transpose(yp.astype(np.float64), cs, rot.sign_bits, b)
+    assert report(f"rotate_out int8 {dim}/{b} M={M}", d.host(y), reft) <= BUTTERFLY_TOL
+
+
+@pytest.mark.parametrize("b", [16, 4096])
+def test_rotate_int8_extreme_codes(b):
+    """Codes 0 (Hadamard initialisation) and +-127 at step pi/508 (pair swap
+    and pair negation), and the int8 extremes -128 / 127 at a large step."""
+    d = D()
+    L = b.bit_length() - 1
+    x = rng(33, b).normal(size=(2, b)).astype(np.float32)
+    for code, step in ((0, 0.3), (127, math.pi / 508), (-127, math.pi / 508),
+                       (-128, 0.05), (127, 0.05)):
+        rot = S.rotation_q8(b, b, rng(34, b, code + 128),
+                            codes=np.full((1, L, b // 2), code), step=step)
+        xt = torch.empty((2, b), dtype=torch.float32, device="cuda")
+        H().harp_rotate_in(d.dev_rotation(rot), d.dev(x), xt)
+        ref = O.forward(x.astype(np.float64), d.cs64(rot), rot.sign_bits, b)
+        assert report(f"int8 code {code} b={b}", d.host(xt), ref) <= BUTTERFLY_TOL
+        if code == 0:
+            Hm = scipy.linalg.hadamard(b) / math.sqrt(b)
+            rht = (x.astype(np.float64) * O.decode_signs(rot.sign_bits, b)) @ Hm.T
+            assert O.rel_l2(d.host(xt), rht) <= BUTTERFLY_TOL
+
+
 @pytest.mark.parametrize("b", [256, 4096, 8192])
 def test_rotate_in_at_init_is_randomized_hadamard(b):
     """Zero-initialised angles: the kernel computes H D x / sqrt(b) (scipy H)."""
@@ -244,7 +293,7 @@ def oracle_linear_rows(li, x64, mfma, blocks=None, chunk=2048):
     because U is block-diagonal) are produced.  Returns (y, output columns).
     """
     lin, w = li.lin, li.W
-    xt = O.forward(x64, li.V.cs, li.V.sign_bits, lin.b_v)
+    xt = O.forward(x64, D().cs64(li.V), li.V.sign_bits, lin.b_v)
     if mfma:
         xt = O.bf16_round(xt)
     bu = lin.b_u
@@ -259,15 +308,16 @@ def oracle_linear_rows(li, x64, mfma, blocks=None, chunk=2048):
         if mfma:
             wh = O.bf16_round(wh)
         yp[:, c0:c0 + len(rr)] = xt @ wh.T
+    cs_u = D().cs64(li.U)
     if full:
-        return O.transpose(yp, li.U.cs, li.U.sign_bits, bu), rows
+        return O.transpose(yp, cs_u, li.U.sign_bits, bu), rows
     assert bu % 32 == 0
     wpb = bu // 32
     y = np.empty_like(yp)
     for i, j in enumerate(blocks):
         sl = slice(i * bu, (i + 1) * bu)
         sb = li.U.sign_bits[j * wpb:(j + 1) * wpb]
-        y[:, sl] = O.transpose(yp[:, sl], li.U.cs[j:j + 1], sb, bu)
+        y[:, sl] = O.transpose(yp[:, sl], cs_u[j:j + 1], sb, bu)
     return y, rows
 
 
@@ -300,6 +350,20 @@ def test_fused_configs(cfg, lin, bits, M):
 
 
 L70B_CASES = [(0, 2), (0, 3), (0, 4), (1, 2), (1, 3), (1, 4), (2, 2)]
+
+
+FUSED8_CASES = [("tiny", 0, 2, 4), ("l7b_decode", 0, 2, 1), ("l7b_mlp", 1, 2, 16),
+                ("l7b_mlp", 0, 2, 1), ("q8b_prefill", 0, 2, 512), ("q8b_prefill", 2, 4, 512)]
+
+
+@pytest.mark.parametrize("cfg,lin,bits,M", FUSED8_CASES)
+def test_fused_int8_angles(cfg, lin, bits, M):
+    li = S.layer_inputs(S.CONFIGS[cfg], lin, bits, M, angles="int8")
+    y = D().host(run_fused(li))
+    ref, _ = oracle_linear_rows(li, D().x_f64(li.x, li.x_dtype), M >= 64)
+    r = report(f"fused int8 angles {cfg}[{lin}] b{bits} M={M}", y, ref)
+    assert r <= CONTRACT_TOL
+    assert r <= path_tol(M)
 
 
 @pytest.mark.parametrize("lin,bits", L70B_CASES)
