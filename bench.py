@@ -37,9 +37,8 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 # 256 MiB device copy gives) on the current kernels; set an entry to None
 # when its kernel changes until the counters are taken again.
 TRAFFIC_BYTES = {
-    "rotate_in_b4096": 228557,
-    "deq_gemv_2bit": 5448090,
-    "rotate_out_b4096": 238387,
+    "rotate_in_deq_gemv_2bit": None,
+    "rotate_out_b4096": None,
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores, TFLOP/s
 WORKING_SET_BYTES = 1 << 30
@@ -62,6 +61,15 @@ def alg_bytes(M, N, K, bits, b_v, b_u, x_bytes=2, y_bytes=4, pair_bytes=8):
 def gemv_bytes(M, N, K, bits):
     """The product kernel alone: weights, scales/zeros, float32 x~ in, y' out."""
     return N * K * bits // 8 + N * (K // 64) * 4 + 4 * M * K + 4 * M * N
+
+
+def rotgemv_bytes(M, N, K, bits, b, pair_bytes=8):
+    """Input rotation + product in one kernel: weights, scales/zeros, the
+    input side's angles and signs, bf16 x in, float32 y' out."""
+    L = b.bit_length() - 1
+    steps = 4 if pair_bytes == 1 else 0
+    return (N * K * bits // 8 + N * (K // 64) * 4 + pair_bytes * (K // 2) * L + steps
+            + K // 8 + 2 * M * K + 4 * M * N)
 
 
 def rotate_bytes(M, d, b, in_bytes, out_bytes, pair_bytes=8):
@@ -256,21 +264,28 @@ def main():
         log("calibration: 3 x 256 MiB device copies done")
         del src, dst
 
-    # per-kernel launch durations: each kernel alone, graph of `count` launches
+    # Per-kernel launch durations: each kernel alone, a graph of `count`
+    # launches on the capture stream, timed with events around the replays.
+    # The fused decode call launches rotate_in_deq_gemv then rotate_out; the
+    # stand-alone rotate_in and deq_gemv are listed for reference.
     kern = {}
     reps = max(3, args.steps // 10)
+    ms_rg, _ = time_graph(torch, lambda: [H.harp_rotate_in_deq_gemv(i.V, i.W, i.x, i.yp)
+                                          for i in inst], reps)
+    ms_ro, _ = time_graph(torch, lambda: [H.harp_rotate_out(i.U, i.yp, i.y) for i in inst], reps)
     ms_ri, _ = time_graph(torch, lambda: [H.harp_rotate_in(i.V, i.x, i.xt32) for i in inst], reps)
     ms_gv, _ = time_graph(torch, lambda: [H.harp_deq_gemv(i.W, i.xt32, i.yp) for i in inst], reps)
-    ms_ro, _ = time_graph(torch, lambda: [H.harp_rotate_out(i.U, i.yp, i.y) for i in inst], reps)
-    for name, msk, nbytes in (
-            ("rotate_in_b4096", ms_ri, rotate_bytes(M, K, bv, 2, 4)),
-            ("deq_gemv_2bit", ms_gv, gemv_bytes(M, N, K, bits)),
-            ("rotate_out_b4096", ms_ro, rotate_bytes(M, N, bu, 4, 4))):
+    for name, msk, nbytes, in_path in (
+            ("rotate_in_deq_gemv_2bit", ms_rg, rotgemv_bytes(M, N, K, bits, bv), True),
+            ("rotate_out_b4096", ms_ro, rotate_bytes(M, N, bu, 4, 4), True),
+            ("rotate_in_b4096", ms_ri, rotate_bytes(M, K, bv, 2, 4), False),
+            ("deq_gemv_2bit", ms_gv, gemv_bytes(M, N, K, bits), False)):
         us = msk * 1e3 / count
         kern[name] = {"us_per_launch": round(us, 3), "alg_bytes": nbytes,
-                      "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+                      "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1), "in_fused_path": in_path}
     log("kernels: " + json.dumps(kern))
-    dom = max(kern, key=lambda k: kern[k]["us_per_launch"])
+    dom = max((k for k in kern if kern[k]["in_fused_path"]),
+              key=lambda k: kern[k]["us_per_launch"])
     achieved = kern[dom]["GB_s"]
     roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -287,7 +302,8 @@ def main():
         inst8 = make_instances("l7b_decode", 0, bits, M, count8, torch, H, angles="int8")
         ms8, _ = time_graph(torch, lambda: [H.harp_linear_fused(i.V, i.W, i.U, i.x, i.y, i.ws)
                                             for i in inst8], max(3, args.steps // 4))
-        ms8_ri, _ = time_graph(torch, lambda: [H.harp_rotate_in(i.V, i.x, i.xt32) for i in inst8], reps)
+        ms8_rg, _ = time_graph(torch, lambda: [H.harp_rotate_in_deq_gemv(i.V, i.W, i.x, i.yp)
+                                               for i in inst8], reps)
         ms8_ro, _ = time_graph(torch, lambda: [H.harp_rotate_out(i.U, i.yp, i.y) for i in inst8], reps)
         us8 = ms8 * 1e3 / count8
         q8 = {"workload": "l7b_decode with int8-stored angles (one byte per pair)",
@@ -297,7 +313,7 @@ def main():
               "speedup_vs_f32_pairs": round((ms * 1e3 / count) / us8, 3),
               "kernels": {}}
         for name, msk, nbytes in (
-                ("rotate_in_b4096_int8", ms8_ri, rotate_bytes(M, K, bv, 2, 4, 1)),
+                ("rotate_in_deq_gemv_2bit_int8", ms8_rg, rotgemv_bytes(M, N, K, bits, bv, 1)),
                 ("rotate_out_b4096_int8", ms8_ro, rotate_bytes(M, N, bu, 4, 4, 1))):
             us = msk * 1e3 / count8
             q8["kernels"][name] = {"us_per_launch": round(us, 3), "alg_bytes": nbytes,

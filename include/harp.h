@@ -156,6 +156,21 @@ harp_status harp_deq_gemv(const harp_qweight *W, const float *xt, float *yt,
                           int32_t M, harp_stream stream);
 
 /*
+ * y' = w_hat (F_V x) for small batches in one launch: every workgroup applies
+ * the input rotation (technical summary §2.1-2.2, as harp_rotate_in with a
+ * float32 x~) to the whole input row in its local memory while its weights
+ * load, then forms its rows of the float32 product as harp_deq_gemv does.
+ * Supported shapes: 1 <= M <= 4, W->K <= 4096, V->block >= 8; other shapes
+ * return HARP_ERR_UNSUPPORTED (use harp_rotate_in + harp_deq_gemv).
+ * Requires V->dim == W->K.
+ *   x  [M][K] of x_dt;  yt  [M][W->N] float32.
+ */
+harp_status harp_rotate_in_deq_gemv(const harp_rotation *V,
+                                    const harp_qweight *W, const void *x,
+                                    harp_dtype x_dt, float *yt, int32_t M,
+                                    harp_stream stream);
+
+/*
  * y'[m][n] = sum_k bf16(w_hat[n][k]) x~[m][k] on the bf16 matrix cores with
  * float32 accumulation; bf16(w_hat) rounds to nearest even.  Meant for
  * prefill batches (M >= 64); any M is accepted.
@@ -182,9 +197,10 @@ size_t harp_linear_workspace_bytes(int32_t M, int32_t N, int32_t K);
 
 /*
  * y = F_U^T deq(W) F_V x, the whole linear (technical summary §2.4 and §5).
- * M < 64 runs rotate-in (float32 x~), the vector-ALU product and rotate-out;
- * M >= 64 runs rotate-in with a bf16 x~, the matrix-core product and
- * rotate-out.  Requires V->dim == W->K and U->dim == W->N.
+ * M < 64 runs rotate-in (float32 x~), the vector-ALU product and rotate-out,
+ * with the first two in one launch where harp_rotate_in_deq_gemv supports
+ * the shape; M >= 64 runs rotate-in with a bf16 x~, the matrix-core product
+ * and rotate-out.  Requires V->dim == W->K and U->dim == W->N.
  *   x  [M][K] of x_dt;  y  [M][N] of y_dt;
  *   workspace  at least harp_linear_workspace_bytes(M, N, K) bytes, 256-byte
  *              aligned, owned by the caller.  Zero-filled before its first

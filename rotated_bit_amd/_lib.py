@@ -30,7 +30,8 @@ HARP_F32 = 0
 HARP_BF16 = 1
 
 EXPORTED = (
-    "harp_rotate_in", "harp_rotate_out", "harp_deq_gemv", "harp_deq_gemm",
+    "harp_rotate_in", "harp_rotate_out", "harp_deq_gemv", "harp_rotate_in_deq_gemv",
+    "harp_deq_gemm",
     "harp_deq_gemm_workspace_bytes", "harp_linear_workspace_bytes", "harp_linear_fused", "harp_dequant",
     "harp_status_string", "harp_last_hip_error",
 )
@@ -74,6 +75,8 @@ def _load() -> ctypes.CDLL:
         "harp_rotate_in": (c_int32, [R, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p]),
         "harp_rotate_out": (c_int32, [R, c_void_p, c_void_p, c_int32, c_int32, c_void_p]),
         "harp_deq_gemv": (c_int32, [Q, c_void_p, c_void_p, c_int32, c_void_p]),
+        "harp_rotate_in_deq_gemv": (c_int32, [R, Q, c_void_p, c_int32, c_void_p, c_int32,
+                                               c_void_p]),
         "harp_deq_gemm": (c_int32, [Q, c_void_p, c_void_p, c_int32, c_void_p, c_size_t,
                                     c_void_p]),
         "harp_deq_gemm_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
@@ -174,6 +177,14 @@ def harp_deq_gemv(W: QWeight, xt, yt, M: int | None = None, stream=None) -> None
     M = xt.shape[0] if M is None else M
     _check(lib.harp_deq_gemv(ctypes.byref(W.c), _ptr(xt), _ptr(yt), M, _stream(stream)),
            "harp_deq_gemv")
+
+
+def harp_rotate_in_deq_gemv(V: Rotation, W: QWeight, x, yt, M: int | None = None,
+                            stream=None) -> None:
+    M = x.shape[0] if M is None else M
+    _check(lib.harp_rotate_in_deq_gemv(ctypes.byref(V.c), ctypes.byref(W.c), _ptr(x),
+                                       _dtype_code(x), _ptr(yt), M, _stream(stream)),
+           "harp_rotate_in_deq_gemv")
 
 
 def harp_deq_gemm(W: QWeight, xt_bf16, yt, workspace=None, M: int | None = None,

@@ -232,7 +232,353 @@ hipError_t launch_bits(const harp_qweight& W, const float* xt, float* yt, int M,
   return launch_cfg<BITS, 4>(W, xt, yt, M, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Decode batches with the input rotation in the prologue:
+//   y'[m][n] = sum_k w_hat[n][k] (F_V x_m)[k]
+// for M <= 4 and K <= 4096.  Every workgroup computes the whole x~ = F_V x in
+// LDS (HARP technical summary §2.1-2.2: sign flip, then stages 0..L-1), which
+// costs it a few microseconds of VALU and LDS time that overlap the fetch of
+// its own weights, and saves the separate rotation launch.
+//
+// Rotation layout.  Task tid (one per thread, K/8 of them) owns 8 elements of
+// one block of b = 2^L inputs in each round; round r covers stages 3r ..
+// 3r+2 (fewer in the last round), exactly as the stand-alone rotation kernel
+// does with 8 elements per thread.  The rotated rows live in LDS in the
+// padded group layout of the product phase, so the product phase reads them
+// where the rotation left them.
+// ---------------------------------------------------------------------------
+
+constexpr int kRotMaxRounds = 4;            // b <= 4096: L <= 12 stages
+
+// Index inside a block of local element jj (0..7) of task t in a round over
+// stages s0 .. s0+R-1 (R <= 3): the low R bits of jj walk those strides, the
+// rest of the task index and of jj fill the other bits in order.
+__device__ __forceinline__ int round_elem(int t, int jj, int s0, int R) {
+  const int rest = (t << (3 - R)) + (jj >> R);
+  const int jl = jj & ((1 << R) - 1);
+  const int lo = rest & ((1 << s0) - 1);
+  const int hi = rest >> s0;
+  return (hi << (s0 + R)) | (jl << s0) | lo;
+}
+
+__device__ __forceinline__ int pair_of(int i, int s) {   // i with bit s deleted
+  return ((i >> (s + 1)) << s) | (i & ((1 << s) - 1));
+}
+
+__host__ __device__ constexpr int with_zero_bit(int p, int k) {
+  return ((p >> k) << (k + 1)) | (p & ((1 << k) - 1));
+}
+
+__device__ __forceinline__ int padded(int i) { return (i >> 6) * kGStride + (i & 63); }
+
+// LOGB_: log2 of the input-side block size when fixed at compile time (the
+// index arithmetic of the rounds then folds to constants), 0 to take it from
+// logb at run time.
+template <int BITS, int MT, bool Q8, int LOGB_>
+__global__ __launch_bounds__(kThreads) void gemv_rot_kernel(
+    const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
+    const uint16_t* __restrict__ zr, const void* __restrict__ xin, int x_bf16,
+    const float2* __restrict__ cs, const int8_t* __restrict__ codes, float step,
+    const uint32_t* __restrict__ sign, int logb, float* __restrict__ yt, int N,
+    int K, int M) {
+  constexpr int NWG = 2 * BITS;
+  constexpr int SEG = Seg<BITS>::CODES;
+  constexpr int V = RW * MT;
+  __shared__ __attribute__((aligned(16))) float xs[MT][GC * kGStride];
+  __shared__ float sxs[MT][GC];
+  __shared__ float2 table[Q8 ? 256 : 1];
+
+  const int G = K / kGroup;                 // <= 64: one group per lane
+  const size_t WPR = static_cast<size_t>(K) * BITS / 32;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
+  const int rbase = blockIdx.x * kRowsPerWg + wave * RW;
+
+  // 1. This lane's group of each of the wave's rows: in flight during the
+  //    rotation below.
+  const bool gact = lane < G;
+  uint32_t w[RW][NWG];
+  uint16_t s16[RW], z16[RW];
+  if (gact) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int n = min(rbase + r, N - 1);   // rows past N: loaded, never stored
+      load_group<BITS>(qw + static_cast<size_t>(n) * WPR + static_cast<size_t>(lane) * NWG, w[r]);
+      s16[r] = sc[static_cast<size_t>(n) * G + lane];
+      z16[r] = zr[static_cast<size_t>(n) * G + lane];
+    }
+  }
+
+  // 2. Rotation coefficients of this thread's task, every round.
+  const int L = LOGB_ ? LOGB_ : logb;
+  const int B = 1 << L;
+  const int NR = (L + 2) / 3;
+  const bool tact = tid < (K >> 3);
+  const int tl = L - 3;                      // log2 tasks per block
+  const int blk = tid >> tl;
+  const int t = tid & ((1 << tl) - 1);
+  const size_t blk_off = static_cast<size_t>(blk) * L * (B / 2);
+  float2 cf[kRotMaxRounds][3][4];
+  int qc[Q8 ? kRotMaxRounds : 1][3][4];
+  auto for_task = [&](auto&& f) {
+#pragma unroll
+    for (int r = 0; r < kRotMaxRounds; ++r) {
+      if (r < NR) {
+        const int s0 = 3 * r;
+        const int R = min(3, L - s0);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          if (k < R) {
+            const int s = s0 + k;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const int i = round_elem(t, with_zero_bit(p, k), s0, R);
+              f(r, k, p, blk_off + static_cast<size_t>(s) * (B / 2) + pair_of(i, s));
+            }
+          }
+        }
+      }
+    }
+  };
+  if (tact) {
+    if constexpr (Q8) {
+      for_task([&](int r, int k, int p, size_t c) { qc[r][k][p] = codes[c]; });
+    } else {
+      for_task([&](int r, int k, int p, size_t c) { cf[r][k][p] = cs[c]; });
+    }
+  }
+
+  // 3. Eight consecutive inputs per task and row, raw, and their sign bits.
+  u32x4 raw[MT][2];
+  if (tact) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m < M) {
+        if (x_bf16) {
+          raw[m][0] = reinterpret_cast<const u32x4*>(
+              static_cast<const uint16_t*>(xin) + static_cast<size_t>(m) * K)[tid];
+        } else {
+          const u32x4* src = reinterpret_cast<const u32x4*>(
+              static_cast<const float*>(xin) + static_cast<size_t>(m) * K);
+          raw[m][0] = src[2 * tid];
+          raw[m][1] = src[2 * tid + 1];
+        }
+      }
+    }
+  }
+  const uint32_t sbits = tact ? (sign[tid >> 2] >> ((tid & 3) * 8)) : 0u;
+
+  if constexpr (Q8) {
+    for (int i = tid; i < 256; i += kThreads) {
+      float sn, cn;
+      sincosf(fmaf(static_cast<float>(i - 128), step, 0.785398163397448310f), &sn, &cn);
+      table[i] = make_float2(cn, sn);
+    }
+  }
+  // 4. D x into LDS (8 consecutive inputs stay inside one 64-group).
+  if (tact) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      float v[8];
+      if (m >= M) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+      } else if (x_bf16) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          v[j] = bf16_to_f32(static_cast<uint16_t>(raw[m][0][j >> 1] >> (16 * (j & 1))));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = __uint_as_float(raw[m][j >> 2][j & 3]);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = flip_sign(v[j], (sbits >> j) & 1u);
+      float* d = &xs[m][padded(tid * 8)];
+      *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(d + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
+  __syncthreads();
+
+  // 5. Stages in place, three per round, one barrier per round.
+#pragma unroll
+  for (int r = 0; r < kRotMaxRounds; ++r) {
+    if (r < NR) {
+      const int s0 = 3 * r;
+      const int R = min(3, L - s0);
+      if (tact) {
+        if constexpr (Q8) {
+#pragma unroll
+          for (int k = 0; k < 3; ++k)
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+              if (k < R) cf[r][k][p] = table[qc[r][k][p] + 128];
+        }
+        int pos[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pos[j] = padded(blk * B + round_elem(t, j, s0, R));
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          float v[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = xs[m][pos[j]];
+#pragma unroll
+          for (int k = 0; k < 3; ++k) {
+            if (k < R) {
+#pragma unroll
+              for (int p = 0; p < 4; ++p) {
+                const int j1 = with_zero_bit(p, k);
+                const int j2 = j1 | (1 << k);
+                const float a = v[j1];
+                const float b = v[j2];
+                const float c = cf[r][k][p].x;
+                const float sn = cf[r][k][p].y;
+                v[j1] = fmaf(c, a, sn * b);
+                v[j2] = fmaf(sn, a, -(c * b));
+              }
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xs[m][pos[j]] = v[j];
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // 6. Per-group sums of x~ (16 lanes per group, fixed order).
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+#pragma unroll
+    for (int h = 0; h < GC * 16 / kThreads; ++h) {
+      const int f = tid + h * kThreads;
+      const int gi = f >> 4;
+      float part = 0.0f;
+      if (gi < G) {
+        const float4 v = *reinterpret_cast<const float4*>(&xs[m][gi * kGStride + (f & 15) * 4]);
+        part = (v.x + v.y) + (v.z + v.w);
+      }
+      part += shfl_xor(part, 8);
+      part += shfl_xor(part, 4);
+      part += shfl_xor(part, 2);
+      part += shfl_xor(part, 1);
+      if ((f & 15) == 0 && gi < G) sxs[m][gi] = part;
+    }
+  }
+  __syncthreads();
+
+  // 7. The product, as in gemv_kernel.
+  float acc[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[i] = 0.0f;
+  if (gact) {
+    float dot[RW][MT];
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) dot[r][m] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kGroup / SEG; ++i) {
+      float q[RW][SEG];
+#pragma unroll
+      for (int r = 0; r < RW; ++r) seg_codes<BITS>(w[r], i, q[r]);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        float xv[SEG];
+#pragma unroll
+        for (int c = 0; c < SEG / 4; ++c) {
+          const float4 v = *reinterpret_cast<const float4*>(
+              &xs[m][lane * kGStride + i * SEG + 4 * c]);
+          xv[4 * c + 0] = v.x;
+          xv[4 * c + 1] = v.y;
+          xv[4 * c + 2] = v.z;
+          xv[4 * c + 3] = v.w;
+        }
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+#pragma unroll
+          for (int j = 0; j < SEG; ++j) dot[r][m] = fmaf(q[r][j], xv[j], dot[r][m]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const float s = f16_to_f32(s16[r]);
+      const float z = f16_to_f32(z16[r]);
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        acc[r * MT + m] = fmaf(s, fmaf(-z, sxs[m][lane], dot[r][m]), acc[r * MT + m]);
+    }
+  }
+  wave_transpose_reduce<V>(acc, lane);
+#pragma unroll
+  for (int tv = 0; tv < V; ++tv) {
+    if (lane == lane_of_value<V>(tv)) {
+      const int r = tv / MT;
+      const int m = tv - r * MT;
+      const int n = rbase + r;
+      if (n < N && m < M) yt[static_cast<size_t>(m) * N + n] = acc[0];
+    }
+  }
+}
+
+template <int BITS, int MT, bool Q8, int LOGB_>
+hipError_t launch_rot_logb(const harp_rotation& Vr, const harp_qweight& W,
+                           const void* x, int x_dt, float* yt, int M,
+                           hipStream_t stream) {
+  const dim3 grid((W.N + kRowsPerWg - 1) / kRowsPerWg);
+  hipLaunchKernelGGL((gemv_rot_kernel<BITS, MT, Q8, LOGB_>), grid, dim3(kThreads), 0, stream,
+                     W.qweight, W.scale, W.zero, x, x_dt == HARP_BF16 ? 1 : 0,
+                     reinterpret_cast<const float2*>(Vr.cs), Vr.phi_codes, Vr.phi_step,
+                     Vr.sign_bits, __builtin_ctz(static_cast<unsigned>(Vr.block)), yt,
+                     W.N, W.K, M);
+  return hipGetLastError();
+}
+
+template <int BITS, int MT, bool Q8>
+hipError_t launch_rot_cfg(const harp_rotation& Vr, const harp_qweight& W,
+                          const void* x, int x_dt, float* yt, int M,
+                          hipStream_t stream) {
+  if (Vr.block == 4096)
+    return launch_rot_logb<BITS, MT, Q8, 12>(Vr, W, x, x_dt, yt, M, stream);
+  return launch_rot_logb<BITS, MT, Q8, 0>(Vr, W, x, x_dt, yt, M, stream);
+}
+
+template <int BITS, bool Q8>
+hipError_t launch_rot_bits(const harp_rotation& Vr, const harp_qweight& W,
+                           const void* x, int x_dt, float* yt, int M,
+                           hipStream_t stream) {
+  if (M == 1) return launch_rot_cfg<BITS, 1, Q8>(Vr, W, x, x_dt, yt, M, stream);
+  if (M == 2) return launch_rot_cfg<BITS, 2, Q8>(Vr, W, x, x_dt, yt, M, stream);
+  return launch_rot_cfg<BITS, 4, Q8>(Vr, W, x, x_dt, yt, M, stream);
+}
+
+template <bool Q8>
+hipError_t launch_rot_q(const harp_rotation& Vr, const harp_qweight& W,
+                        const void* x, int x_dt, float* yt, int M,
+                        hipStream_t stream) {
+  switch (W.bits) {
+    case 2: return launch_rot_bits<2, Q8>(Vr, W, x, x_dt, yt, M, stream);
+    case 3: return launch_rot_bits<3, Q8>(Vr, W, x, x_dt, yt, M, stream);
+    case 4: return launch_rot_bits<4, Q8>(Vr, W, x, x_dt, yt, M, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
+
+bool gemv_rotated_supported(const harp_rotation& V, const harp_qweight& W, int M) {
+  return M >= 1 && M <= kDecodeRotMaxM && W.K <= kDecodeRotMaxK && V.block >= 8 &&
+         V.dim == W.K;
+}
+
+hipError_t launch_gemv_rotated(const harp_rotation& V, const harp_qweight& W,
+                               const void* x, int x_dt, float* yt, int M,
+                               hipStream_t stream) {
+  if (!gemv_rotated_supported(V, W, M)) return hipErrorInvalidValue;
+  if (V.phi_codes != nullptr) return launch_rot_q<true>(V, W, x, x_dt, yt, M, stream);
+  return launch_rot_q<false>(V, W, x, x_dt, yt, M, stream);
+}
 
 hipError_t launch_gemv(const harp_qweight& W, const float* xt, float* yt, int M,
                        hipStream_t stream) {

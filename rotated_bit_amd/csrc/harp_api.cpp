@@ -46,6 +46,15 @@ harp_status harp_deq_gemv(const harp_qweight* W, const float* xt, float* yt,
   return from_hip(harp::launch_gemv(*W, xt, yt, M, as_stream(stream)));
 }
 
+harp_status harp_rotate_in_deq_gemv(const harp_rotation* V, const harp_qweight* W,
+                                    const void* x, harp_dtype x_dt, float* yt,
+                                    int32_t M, harp_stream stream) {
+  const harp_status st = harp::validate_rotate_gemv(V, W, x, x_dt, yt, M);
+  if (st != HARP_OK || M == 0) return st;
+  if (!harp::gemv_rotated_supported(*V, *W, M)) return HARP_ERR_UNSUPPORTED;
+  return from_hip(harp::launch_gemv_rotated(*V, *W, x, x_dt, yt, M, as_stream(stream)));
+}
+
 harp_status harp_deq_gemm(const harp_qweight* W, const uint16_t* xt_bf16,
                           float* yt, int32_t M, void* workspace, size_t ws_bytes,
                           harp_stream stream) {
@@ -78,7 +87,10 @@ harp_status harp_linear_fused(const harp_rotation* V, const harp_qweight* W,
   const hipStream_t s = as_stream(stream);
   char* ws = static_cast<char*>(workspace);
   float* yp = reinterpret_cast<float*>(ws + harp::workspace_yp_offset(M, W->K));
-  if (M < harp::kGemmMinM) {
+  if (harp::gemv_rotated_supported(*V, *W, M)) {
+    const harp_status r = from_hip(harp::launch_gemv_rotated(*V, *W, x, x_dt, yp, M, s));
+    if (r != HARP_OK) return r;
+  } else if (M < harp::kGemmMinM) {
     float* xt = reinterpret_cast<float*>(ws);
     harp_status r = from_hip(harp::launch_rotate(*V, x, x_dt, xt, HARP_F32, M, false, s));
     if (r != HARP_OK) return r;

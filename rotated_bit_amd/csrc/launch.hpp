@@ -18,6 +18,15 @@ hipError_t launch_rotate(const harp_rotation& R, const void* in, int in_dt,
 hipError_t launch_gemv(const harp_qweight& W, const float* xt, float* yt,
                        int M, hipStream_t stream);
 
+// yt = w_hat (F_V x) in one launch: every workgroup rotates x itself.  For
+// small batches and input sides only (gemv_rotated_supported).
+constexpr int kDecodeRotMaxM = 4;
+constexpr int kDecodeRotMaxK = 4096;
+bool gemv_rotated_supported(const harp_rotation& V, const harp_qweight& W, int M);
+hipError_t launch_gemv_rotated(const harp_rotation& V, const harp_qweight& W,
+                               const void* x, int x_dt, float* yt, int M,
+                               hipStream_t stream);
+
 // yt = bf16(w_hat) xt_bf16 on the matrix cores, float32 accumulation, in
 // `splits` K slices (splits > 1 needs the GEMM workspace, zero-filled
 // before its first use and left zero-filled).

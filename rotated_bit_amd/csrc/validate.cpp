@@ -94,6 +94,18 @@ harp_status validate_gemv(const harp_qweight* W, const void* xt, const void* yt,
   return HARP_OK;
 }
 
+harp_status validate_rotate_gemv(const harp_rotation* V, const harp_qweight* W,
+                                const void* x, int x_dt, const void* yt, int32_t M) {
+  HARP_TRY(check_rotation(V));
+  HARP_TRY(check_qweight(W));
+  if (V->dim != W->K) return HARP_ERR_SHAPE;
+  if (bad_dtype(x_dt)) return HARP_ERR_DTYPE;
+  HARP_TRY(check_m(M));
+  HARP_TRY(check_data(x, M));
+  HARP_TRY(check_data(yt, M));
+  return HARP_OK;
+}
+
 harp_status validate_gemm(const harp_qweight* W, const void* xt, const void* yt,
                           int32_t M, const void* workspace, size_t ws_bytes) {
   HARP_TRY(validate_gemv(W, xt, yt, M));

@@ -19,6 +19,8 @@ harp_status validate_rotate_out(const harp_rotation* U, const void* yt,
                                 const void* y, int y_dt, int32_t M);
 harp_status validate_gemv(const harp_qweight* W, const void* xt, const void* yt,
                           int32_t M);
+harp_status validate_rotate_gemv(const harp_rotation* V, const harp_qweight* W,
+                                const void* x, int x_dt, const void* yt, int32_t M);
 harp_status validate_gemm(const harp_qweight* W, const void* xt, const void* yt,
                           int32_t M, const void* workspace, size_t ws_bytes);
 harp_status validate_fused(const harp_rotation* V, const harp_qweight* W,

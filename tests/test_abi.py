@@ -217,3 +217,25 @@ def test_builder_loads_without_the_package():
     code = ("import sys, __graft_entry__ as g; m = g._builder(); "
             "assert callable(m.build); assert 'rotated_bit_amd' not in sys.modules")
     subprocess.run([sys.executable, "-c", code], check=True, cwd=ROOT)
+
+
+def test_rotate_in_deq_gemv_checks():
+    f = L.lib.harp_rotate_in_deq_gemv
+    V, W = rot(), qw()
+
+    def call(V=V, W=W, x=FAKE, xdt=0, yt=FAKE, M=1):
+        return f(ctypes.byref(V) if V is not None else None,
+                 ctypes.byref(W) if W is not None else None, x, xdt, yt, M, None)
+
+    assert call(V=None) == L.HARP_ERR_NULL
+    assert call(W=None) == L.HARP_ERR_NULL
+    assert call(V=rot(dim=512, block=256)) == L.HARP_ERR_SHAPE      # V.dim != K
+    assert call(xdt=3) == L.HARP_ERR_DTYPE
+    assert call(M=-1) == L.HARP_ERR_SHAPE
+    assert call(x=0) == L.HARP_ERR_NULL
+    assert call(yt=MISALIGNED) == L.HARP_ERR_ALIGN
+    assert call(x=0, yt=0, M=0) == L.HARP_OK
+    # outside the single-launch shapes
+    assert call(M=5) == L.HARP_ERR_UNSUPPORTED
+    assert call(V=rot(dim=256, block=4)) == L.HARP_ERR_UNSUPPORTED
+    assert call(V=rot(dim=8192, block=256), W=qw(K=8192)) == L.HARP_ERR_UNSUPPORTED

@@ -243,6 +243,31 @@ def test_gemv(N, K, bits, M):
     assert r <= CONTRACT_TOL and r <= FP32_PATH_TOL
 
 
+ROTGEMV_CASES = [
+    (256, 256, 8, 2, 1, "f32", "f32"), (300, 256, 16, 3, 3, "int8", "bf16"),
+    (4096, 4096, 4096, 2, 1, "f32", "bf16"), (4096, 4096, 4096, 2, 1, "int8", "bf16"),
+    (11008, 4096, 4096, 4, 2, "int8", "bf16"), (100, 1024, 64, 2, 4, "f32", "f32"),
+    (513, 2048, 2048, 3, 4, "int8", "bf16"), (64, 64, 64, 4, 1, "f32", "bf16"),
+]
+
+
+@pytest.mark.parametrize("N,K,b,bits,M,angles,xdt", ROTGEMV_CASES)
+def test_rotate_in_deq_gemv(N, K, b, bits, M, angles, xdt):
+    """y' = w_hat (F_V x) in one launch against the oracle's two steps."""
+    d = D()
+    draw = S.rotation if angles == "f32" else S.rotation_q8
+    rot = draw(K, b, rng(40, K, b))
+    w = S.qweight(N, K, bits, rng(41, N, K, bits))
+    x = S.activations(M, K, rng(42, K, M), xdt)
+    yt = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    H().harp_rotate_in_deq_gemv(d.dev_rotation(rot), d.dev_qweight(w), d.dev_x(x, xdt), yt)
+    xt = O.forward(d.x_f64(x, xdt), d.cs64(rot), rot.sign_bits, b)
+    w_hat = O.dequant(O.unpack(w.words, bits, K), d.scale_f16(w), d.zero_f16(w))
+    ref = xt @ w_hat.T
+    r = report(f"rotate_in_deq_gemv {N}x{K} b={b} bits={bits} M={M} {angles}", d.host(yt), ref)
+    assert r <= CONTRACT_TOL and r <= FP32_PATH_TOL
+
+
 GEMM_CASES = [
     (100, 320, 2, 64), (300, 256, 3, 65), (257, 128, 4, 1), (128, 64, 2, 200),
     (4096, 4096, 2, 512), (12288, 4096, 4, 512), (4096, 12288, 2, 512),
@@ -390,7 +415,23 @@ def test_fused_l70b_slice(lin, bits):
         m0 += li.M
 
 
-@pytest.mark.parametrize("M", [0, 1, 7, 63, 64, 65, 100])
+@pytest.mark.parametrize("b_v,M,angles,xdt", [
+    (4, 1, "f32", "bf16"), (8, 1, "f32", "bf16"), (8, 3, "int8", "f32"),
+    (64, 2, "int8", "bf16"), (512, 4, "f32", "f32"), (4096, 1, "int8", "bf16"),
+    (4096, 4, "f32", "bf16"), (2048, 2, "f32", "bf16"),
+])
+def test_fused_decode_input_blocks(b_v, M, angles, xdt):
+    """Small batches over the input-side block sizes: b >= 8 takes the
+    single-launch input rotation, b = 4 the separate rotation kernel."""
+    cfg = S.Config(10, "dec", (S.Linear("d", 4096, 768, b_v, 256),), (2,), (M,), x_dtype=xdt)
+    li = S.layer_inputs(cfg, 0, 2, M, angles=angles)
+    ref, _ = oracle_linear_rows(li, D().x_f64(li.x, xdt), False)
+    y = D().host(run_fused(li))
+    r = report(f"decode b_v={b_v} M={M} {angles} {xdt}", y, ref)
+    assert r <= CONTRACT_TOL and r <= FP32_PATH_TOL
+
+
+@pytest.mark.parametrize("M", [0, 1, 2, 3, 4, 5, 7, 63, 64, 65, 100])
 def test_fused_batch_edges_and_bf16_out(M):
     """Ragged batches around the GEMV/GEMM switch, bf16 output, empty input."""
     cfg = S.Config(9, "edge", (S.Linear("e", 256, 512, 16, 256),), (3,), (M,))
