@@ -431,6 +431,32 @@ def test_fused_decode_input_blocks(b_v, M, angles, xdt):
     assert r <= CONTRACT_TOL and r <= FP32_PATH_TOL
 
 
+@pytest.mark.parametrize("M,angles_v,angles_u", [
+    (1, "f32", "f32"), (3, "int8", "int8"), (4, "f32", "f32"),
+    (1, "int8", "f32"), (2, "f32", "int8"),
+])
+def test_fused_decode_mixed_angle_formats(M, angles_v, angles_u):
+    """Decode linear with each side's angles in either format: oracle parity
+    and two calls on one workspace bitwise equal."""
+    cfg = S.Config(11, "mix", (S.Linear("t", 2048, 4096, 2048, 4096),), (2,), (M,))
+    base = S.layer_inputs(cfg, 0, 2, M, angles=angles_v)
+    other = S.layer_inputs(cfg, 0, 2, M, angles=angles_u)
+    li = S.LayerInputs(base.lin, 2, M, base.x, base.x_dtype, base.V, other.U, base.W)
+    d = D()
+    V, U, W = d.dev_rotation(li.V), d.dev_rotation(li.U), d.dev_qweight(li.W)
+    x = d.dev_x(li.x, li.x_dtype)
+    ws = d.workspace(M, 4096, 2048)
+    y1 = torch.empty((M, 4096), dtype=torch.float32, device="cuda")
+    y2 = torch.empty_like(y1)
+    H().harp_linear_fused(V, W, U, x, y1, ws)
+    H().harp_linear_fused(V, W, U, x, y2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    ref, _ = oracle_linear_rows(li, d.x_f64(li.x, li.x_dtype), False)
+    r = report(f"decode M={M} V {angles_v} U {angles_u}", d.host(y1), ref)
+    assert r <= CONTRACT_TOL and r <= FP32_PATH_TOL
+
+
 @pytest.mark.parametrize("M", [0, 1, 2, 3, 4, 5, 7, 63, 64, 65, 100])
 def test_fused_batch_edges_and_bf16_out(M):
     """Ragged batches around the GEMV/GEMM switch, bf16 output, empty input."""
