@@ -43,7 +43,9 @@ repository's design notes):
   word; 3-bit codes as a 96-bit little-endian bit stream per 32 weights
   (three words).
 * Rounding points of the batched (bf16 matrix-core) path: the rotated input
-  and the dequantized weight are rounded to bf16, round to nearest even.
+  and the dequantized weight are rounded to bf16, round to nearest even; a
+  matrix-core product that multiplies the integer codes and applies scale
+  and zero per group afterwards rounds only the rotated input.
 * int8 storage of the angles (technical summary §2.4 storage note, §4
   storage overhead; the pages give no encoding).  Each block's angle
   perturbation phi = t - pi/4 is stored as one signed 8-bit code c with one
@@ -340,13 +342,16 @@ def dequant(q: np.ndarray, scale: np.ndarray, zero: np.ndarray,
 
 def linear(x: np.ndarray, words: np.ndarray, scale: np.ndarray,
            zero: np.ndarray, bits: int, cs_v, signs_v, b_v, cs_u, signs_u,
-           b_u, mfma_contract: bool = False) -> np.ndarray:
+           b_u, mfma_contract: bool = False, weights_exact: bool = False) -> np.ndarray:
     """y = F_U^T (W_hat (F_V x)) for x of shape (M, K); returns (M, N).
 
     x holds the values the device received (decoded to float64).  With
-    ``mfma_contract`` the two rounding points of the bf16 matrix-core path are
-    modelled: x~ and w_hat are rounded to bf16 (round to nearest even) before
-    the float64 contraction.  Everything else is float64.
+    ``mfma_contract`` the rounding points of a bf16 matrix-core product are
+    modelled: x~ is rounded to bf16 (round to nearest even) and, unless
+    ``weights_exact``, so is w_hat, before the float64 contraction.  (A
+    product that feeds the integer codes to the matrix cores and applies
+    scale and zero afterwards uses w_hat exactly: ``weights_exact``.)
+    Everything else is float64.
     """
     x = np.asarray(x, dtype=np.float64)
     K = x.shape[-1]
@@ -354,7 +359,8 @@ def linear(x: np.ndarray, words: np.ndarray, scale: np.ndarray,
     xt = forward(x, cs_v, signs_v, b_v)
     if mfma_contract:
         xt = bf16_round(xt)
-        w_hat = bf16_round(w_hat)
+        if not weights_exact:
+            w_hat = bf16_round(w_hat)
     yp = xt @ w_hat.T
     return transpose(yp, cs_u, signs_u, b_u)
 

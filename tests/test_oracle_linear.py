@@ -91,6 +91,26 @@ def test_mfma_contract_rounds_both_operands():
     assert 1e-4 < r < 5e-3
 
 
+def test_mfma_contract_with_exact_weights_rounds_only_x():
+    """weights_exact: the dense composition with only x~ rounded to bf16."""
+    li = S.layer_inputs(S.CONFIGS["tiny"], 0, 2, 4)
+    x = li.x.astype(np.float64)
+    s16, z16 = li.W.scale.view(np.float16), li.W.zero.view(np.float16)
+    args = (li.W.words, s16, z16, 2, li.V.cs, li.V.sign_bits, 256, li.U.cs,
+            li.U.sign_bits, 256)
+    y = O.linear(x, *args, mfma_contract=True, weights_exact=True)
+    FV = O.rotation_matrix(li.V.cs, li.V.sign_bits, 256, 256)
+    FU = O.rotation_matrix(li.U.cs, li.U.sign_bits, 256, 256)
+    w_hat = O.dequant(O.unpack(li.W.words, 2, 256), s16, z16)
+    xt = O.bf16_round((FV @ x.T).T)
+    ref = (FU.T @ (w_hat @ xt.T)).T
+    assert np.max(np.abs(y - ref)) < 1e-12 * np.max(np.abs(ref))
+    # one rounding point instead of two: closer to the float64 linear
+    y0 = O.linear(x, *args)
+    y2 = O.linear(x, *args, mfma_contract=True)
+    assert 0 < O.rel_l2(y, y0) < O.rel_l2(y2, y0)
+
+
 def test_offline_pipeline_and_incoherence():
     """Rotate -> quantize -> pack, then the online linear approximates W x;
     with outlier channels, rotation lowers the 2-bit output error."""
