@@ -149,7 +149,7 @@ harp_status harp_rotate_out(const harp_rotation *U, const float *yt, void *y,
 /*
  * y'[m][n] = sum_k w_hat[n][k] x~[m][k] on the vector ALUs, float32
  * throughout: w_hat is exact in float32 and x~ is not rounded.  Meant for
- * decode batches (M < 64); any M is accepted.
+ * decode batches (M < 16); any M is accepted.
  *   xt  [M][W->K] float32;  yt  [M][W->N] float32.
  */
 harp_status harp_deq_gemv(const harp_qweight *W, const float *xt, float *yt,
@@ -172,10 +172,12 @@ harp_status harp_rotate_in_deq_gemv(const harp_rotation *V,
 
 /*
  * y'[m][n] = sum_k bf16(w_hat[n][k]) x~[m][k] on the bf16 matrix cores with
- * float32 accumulation; bf16(w_hat) rounds to nearest even.  Meant for
- * prefill batches (M >= 64); any M is accepted.
+ * float32 accumulation; bf16(w_hat) rounds to nearest even.  Any M >= 0.
+ * M <= 64: one workgroup per 16 output features, each weight fetched and
+ * dequantized once, no workspace (a given workspace is not used).  M > 64:
+ * 128 x 128 output tiles.
  *   xt_bf16    [M][W->K] bf16;  yt  [M][W->N] float32.
- *   workspace  optional.  NULL runs the product as one K slice.  Otherwise
+ *   workspace  optional (M > 64).  NULL runs the product as one K slice.  Otherwise
  *              at least harp_deq_gemm_workspace_bytes(M, N, K) bytes,
  *              256-byte aligned: the K dimension is split into slices that
  *              run concurrently and are summed in a fixed slice order
@@ -188,7 +190,7 @@ harp_status harp_deq_gemm(const harp_qweight *W, const uint16_t *xt_bf16,
                           size_t ws_bytes, harp_stream stream);
 
 /* Workspace bytes harp_deq_gemm uses for M rows of a K -> N product (0: the
- * product runs as one K slice and needs none); 0 for out-of-range sizes. */
+ * product needs none: M <= 64, or one K slice); 0 for out-of-range sizes. */
 size_t harp_deq_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
 
 /* Workspace bytes harp_linear_fused needs for M rows of a K -> N linear;
@@ -197,10 +199,11 @@ size_t harp_linear_workspace_bytes(int32_t M, int32_t N, int32_t K);
 
 /*
  * y = F_U^T deq(W) F_V x, the whole linear (technical summary §2.4 and §5).
- * M < 64 runs rotate-in (float32 x~), the vector-ALU product and rotate-out,
+ * M < 16 runs rotate-in (float32 x~), the vector-ALU product and rotate-out,
  * with the first two in one launch where harp_rotate_in_deq_gemv supports
- * the shape; M >= 64 runs rotate-in with a bf16 x~, the matrix-core product
- * and rotate-out.  Requires V->dim == W->K and U->dim == W->N.
+ * the shape; M >= 16 runs rotate-in with a bf16 x~, the matrix-core product
+ * of harp_deq_gemm and rotate-out.  Requires V->dim == W->K and
+ * U->dim == W->N.
  *   x  [M][K] of x_dt;  y  [M][N] of y_dt;
  *   workspace  at least harp_linear_workspace_bytes(M, N, K) bytes, 256-byte
  *              aligned, owned by the caller.  Zero-filled before its first

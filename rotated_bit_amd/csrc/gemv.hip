@@ -31,29 +31,6 @@ constexpr int KC = 4096;                   // inputs per staged chunk
 constexpr int GC = KC / kGroup;            // groups per chunk: one per lane
 constexpr int kGStride = kGroup + 4;       // LDS floats per staged group
 
-// One group (64 codes) of one row occupies 2*BITS words.
-template <int BITS>
-__device__ __forceinline__ void load_group(const uint32_t* __restrict__ p,
-                                           uint32_t (&w)[2 * BITS]) {
-  if constexpr (BITS == 2) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
-    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
-  } else if constexpr (BITS == 4) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(p);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(p + 4);
-    w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
-    w[4] = b[0]; w[5] = b[1]; w[6] = b[2]; w[7] = b[3];
-  } else {
-    // 24 bytes per group: 8-byte aligned (the row stride is 24*G bytes).
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const uint2 v = *reinterpret_cast<const uint2*>(p + 2 * i);
-      w[2 * i] = v.x;
-      w[2 * i + 1] = v.y;
-    }
-  }
-}
-
 // Codes per segment of the inner loop: one word for 2- and 4-bit codes,
 // 8 codes (24 bits) for 3-bit codes.
 template <int BITS> struct Seg { static constexpr int CODES = BITS == 2 ? 16 : 8; };

@@ -60,6 +60,8 @@ harp_status harp_deq_gemm(const harp_qweight* W, const uint16_t* xt_bf16,
                           harp_stream stream) {
   const harp_status st = harp::validate_gemm(W, xt_bf16, yt, M, workspace, ws_bytes);
   if (st != HARP_OK || M == 0) return st;
+  if (M <= harp::kSkinnyMaxM)
+    return from_hip(harp::launch_gemm_skinny(*W, xt_bf16, yt, M, as_stream(stream)));
   const int splits = workspace ? harp::gemm_splits(M, W->N, W->K) : 1;
   return from_hip(harp::launch_gemm(*W, xt_bf16, yt, M, splits, workspace,
                                     as_stream(stream)));
@@ -90,7 +92,7 @@ harp_status harp_linear_fused(const harp_rotation* V, const harp_qweight* W,
   if (harp::gemv_rotated_supported(*V, *W, M)) {
     const harp_status r = from_hip(harp::launch_gemv_rotated(*V, *W, x, x_dt, yp, M, s));
     if (r != HARP_OK) return r;
-  } else if (M < harp::kGemmMinM) {
+  } else if (M < harp::kMfmaMinM) {
     float* xt = reinterpret_cast<float*>(ws);
     harp_status r = from_hip(harp::launch_rotate(*V, x, x_dt, xt, HARP_F32, M, false, s));
     if (r != HARP_OK) return r;
@@ -100,8 +102,11 @@ harp_status harp_linear_fused(const harp_rotation* V, const harp_qweight* W,
     uint16_t* xt = reinterpret_cast<uint16_t*>(ws);
     harp_status r = from_hip(harp::launch_rotate(*V, x, x_dt, xt, HARP_BF16, M, false, s));
     if (r != HARP_OK) return r;
-    r = from_hip(harp::launch_gemm(*W, xt, yp, M, harp::gemm_splits(M, W->N, W->K),
-                                   ws + harp::workspace_gemm_offset(M, W->N, W->K), s));
+    if (M <= harp::kSkinnyMaxM)
+      r = from_hip(harp::launch_gemm_skinny(*W, xt, yp, M, s));
+    else
+      r = from_hip(harp::launch_gemm(*W, xt, yp, M, harp::gemm_splits(M, W->N, W->K),
+                                     ws + harp::workspace_gemm_offset(M, W->N, W->K), s));
     if (r != HARP_OK) return r;
   }
   return from_hip(harp::launch_rotate(*U, yp, HARP_F32, y, y_dt, M, true, s));

@@ -33,6 +33,11 @@ hipError_t launch_gemv_rotated(const harp_rotation& V, const harp_qweight& W,
 hipError_t launch_gemm(const harp_qweight& W, const uint16_t* xt, float* yt,
                        int M, int splits, void* workspace, hipStream_t stream);
 
+// The same product for 1 <= M <= 64 with one workgroup per 16 output
+// features (no workspace, no tiles).
+hipError_t launch_gemm_skinny(const harp_qweight& W, const uint16_t* xt, float* yt,
+                              int M, hipStream_t stream);
+
 // Dense w_hat [N][K], float32 or bf16.
 hipError_t launch_dequant(const harp_qweight& W, void* out, int out_dt,
                           hipStream_t stream);

@@ -111,6 +111,111 @@ __device__ __forceinline__ void codes_16(const uint32_t* w, float (&q)[16]) {
   }
 }
 
+// One group (64 codes) of one row occupies 2*BITS words, loaded as
+// 16-byte (2 and 4 bits) or 8-byte (3 bits: the row stride is 24*G bytes)
+// vector loads.
+template <int BITS>
+__device__ __forceinline__ void load_group(const uint32_t* __restrict__ p,
+                                           uint32_t (&w)[2 * BITS]) {
+  if constexpr (BITS == 2) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+  } else if constexpr (BITS == 4) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(p + 4);
+    w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
+    w[4] = b[0]; w[5] = b[1]; w[6] = b[2]; w[7] = b[3];
+  } else {
+    // 24 bytes per group: 8-byte aligned (the row stride is 24*G bytes).
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p + 2 * i);
+      w[2 * i] = v.x;
+      w[2 * i + 1] = v.y;
+    }
+  }
+}
+
+// Eight consecutive codes 8c .. 8c+7 (c = 0..3) of 32-code run h of a
+// group, packed in the low 8*BITS bits of the result.  h must be a
+// compile-time constant after unrolling; c may vary per lane, so the words
+// are chosen with selects (an array indexed by c would live in scratch
+// memory).
+template <int BITS>
+__device__ __forceinline__ uint32_t chunk8(const uint32_t (&w)[2 * BITS], int h, int c) {
+  // The words pass through opaque() so that the selects below stay selects
+  // between registers (the optimizer would otherwise turn them back into an
+  // indexed access).
+  uint32_t r[BITS];
+#pragma unroll
+  for (int i = 0; i < BITS; ++i) r[i] = opaque(w[h * BITS + i]);
+  if constexpr (BITS == 2) {
+    const uint32_t x = (c & 2) ? r[1] : r[0];
+    return x >> (16 * (c & 1));
+  } else if constexpr (BITS == 4) {
+    const uint32_t lo = (c & 1) ? r[1] : r[0];
+    const uint32_t hi = (c & 1) ? r[3] : r[2];
+    return (c & 2) ? hi : lo;
+  } else {
+    // 3 bits: 24 bits at bit 24c of the run's 96-bit integer, i.e. word
+    // (24c)/32 from bit (24c)%32 on, continued in the next word.
+    const uint32_t lo = c == 3 ? r[2] : (c == 2 ? r[1] : r[0]);
+    const uint32_t hi = c >= 2 ? r[2] : r[1];
+    return __builtin_amdgcn_alignbit(hi, lo, (24 * c) & 31);
+  }
+}
+
+// The eight codes of a chunk as floats (2 and 4 bits: masked into byte
+// lanes, one byte-to-float convert each).
+template <int BITS>
+__device__ __forceinline__ void chunk8_codes(uint32_t v, float (&q)[8]) {
+  if constexpr (BITS == 2) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t m = opaque((v >> (2 * t)) & 0x0303u);   // codes t, t+4
+      q[t] = static_cast<float>(m & 0xffu);
+      q[t + 4] = static_cast<float>((m >> 8) & 0xffu);
+    }
+  } else if constexpr (BITS == 4) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t m = opaque((v >> (4 * t)) & 0x0f0f0f0fu);  // codes t, t+2, t+4, t+6
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[t + 2 * i] = static_cast<float>((m >> (8 * i)) & 0xffu);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = static_cast<float>((v >> (3 * j)) & 7u);
+  }
+}
+
+// The eight codes of a chunk as bf16 values 128 + q (exact: 128..143 are
+// integers of 8 significant bits), two per word, code 2i in the low half of
+// word i.  bf16 128 is 0x4300 and q fills the low mantissa bits, so each word
+// is an AND-OR of the shifted chunk.
+template <int BITS>
+__device__ __forceinline__ u32x4 chunk8_bf16_offset(uint32_t v) {
+  constexpr uint32_t kBase = 0x43004300u;
+  u32x4 out;
+  if constexpr (BITS == 2) {
+    const uint32_t v16 = v & 0xffffu;          // the chunk; higher bits are other codes
+    const uint32_t u = v16 | (v16 << 14);      // code 2i+1 moves to bit 4i + 16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = ((u >> (4 * i)) & 0x00030003u) | kBase;
+  } else if constexpr (BITS == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t x = v >> (8 * i);
+      out[i] = (x & 0x0000000fu) | ((x & 0x000000f0u) << 12) | kBase;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      out[i] = ((v >> (6 * i)) & 7u) | (((v >> (6 * i + 3)) & 7u) << 16) | kBase;
+  }
+  return out;
+}
+
 // Dequantize one 32-code run to float32, exactly: q*s and z*s are exact
 // (at most 4 + 11 significant bits) and so is their difference, so the
 // fused multiply-add q*s - z*s equals (q - z)*s in every evaluation order.

@@ -142,7 +142,7 @@ harp_status validate_dequant(const harp_qweight* W, const void* out, int out_dt)
 }
 
 int32_t gemm_splits(int32_t M, int32_t N, int32_t K) {
-  if (M < 1 || N < 1 || K < 64) return 1;
+  if (M <= kSkinnyMaxM || N < 1 || K < 64) return 1;
   const int64_t tiles = static_cast<int64_t>((M + kGemmTile - 1) / kGemmTile) *
                         ((N + kGemmTile - 1) / kGemmTile);
   int32_t s = static_cast<int32_t>((256 + tiles / 2) / tiles);
@@ -162,7 +162,7 @@ size_t gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) {
 }
 
 size_t workspace_yp_offset(int32_t M, int32_t K) {
-  const size_t xt_elem = M < kGemmMinM ? 4 : 2;
+  const size_t xt_elem = M < kMfmaMinM ? 4 : 2;
   return align256(static_cast<size_t>(M) * K * xt_elem);
 }
 
@@ -174,7 +174,7 @@ size_t workspace_bytes(int32_t M, int32_t N, int32_t K) {
   if (M < 0 || M > HARP_MAX_M || N < 1 || N > HARP_MAX_DIM || K < 1 ||
       K > HARP_MAX_DIM)
     return 0;
-  const size_t gemm = M >= kGemmMinM ? gemm_workspace_bytes(M, N, K) : 0;
+  const size_t gemm = M > kSkinnyMaxM ? gemm_workspace_bytes(M, N, K) : 0;
   return workspace_gemm_offset(M, N, K) + gemm;
 }
 

@@ -38,10 +38,16 @@ constexpr int32_t kGemmTile = 128;
 int32_t gemm_splits(int32_t M, int32_t N, int32_t K);
 size_t gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
 
-// Workspace layout of the fused linear: x~, then y', then (M >= kGemmMinM)
-// the GEMM workspace, each 256-byte aligned.  x~ is float32 below kGemmMinM
-// rows and bf16 from there on.
-constexpr int32_t kGemmMinM = 64;
+// Batch ranges of the products: harp_deq_gemm runs the small-batch
+// matrix-core kernel (no workspace) up to kSkinnyMaxM rows and the tiled
+// kernel above; the fused linear takes the float32 vector-ALU product below
+// kMfmaMinM rows and the bf16 matrix-core product from there on.
+constexpr int32_t kSkinnyMaxM = 64;
+constexpr int32_t kMfmaMinM = 16;
+
+// Workspace layout of the fused linear: x~, then y', then (M > kSkinnyMaxM)
+// the tiled GEMM's workspace, each 256-byte aligned.  x~ is float32 below
+// kMfmaMinM rows and bf16 from there on.
 size_t workspace_bytes(int32_t M, int32_t N, int32_t K);
 size_t workspace_yp_offset(int32_t M, int32_t K);
 size_t workspace_gemm_offset(int32_t M, int32_t N, int32_t K);

@@ -160,12 +160,18 @@ def test_product_data_checks():
 def test_workspace_bytes():
     f = L.harp_linear_workspace_bytes
     g = L.harp_deq_gemm_workspace_bytes
+    # M < 16: float32 x~, then y'
     assert f(1, 4096, 4096) == 4096 * 4 + 4096 * 4
-    assert f(63, 100, 64) == 16128 + 25344      # 63*100*4 = 25200 rounds up to 25344
-    # M=64, 4096x4096: 32 tiles of 128x128 -> 4 K slices (8 groups each at
+    assert f(15, 100, 64) == 3840 + 6144         # 15*100*4 = 6000 rounds up to 6144
+    # 16 <= M <= 64: bf16 x~, y', and the small-batch product needs no workspace
+    assert f(63, 100, 64) == 8192 + 25344        # 63*64*2 = 8064 -> 8192; 25200 -> 25344
+    assert g(64, 4096, 4096) == 0 and g(16, 4096, 4096) == 0
+    assert f(64, 4096, 4096) == 64 * 4096 * 2 + 64 * 4096 * 4
+    # M=65, 4096x4096: 32 tiles of 128x128 -> 4 K slices (8 groups each at
     # least); partials 4*32*128*128*4 bytes, then 32 counters (256 B aligned)
-    assert g(64, 4096, 4096) == 4 * 32 * 128 * 128 * 4 + 256
-    assert f(64, 4096, 4096) == 64 * 4096 * 2 + 64 * 4096 * 4 + g(64, 4096, 4096)
+    assert g(65, 4096, 4096) == 4 * 32 * 128 * 128 * 4 + 256
+    assert f(65, 4096, 4096) == (65 * 4096 * 2 + 255) // 256 * 256 + 65 * 4096 * 4 \
+        + g(65, 4096, 4096)
     # M=512, 4096x4096: 128 tiles -> 2 slices; 12288 outputs: 384 tiles -> 1 slice
     assert g(512, 4096, 4096) == 2 * 128 * 128 * 128 * 4 + 512
     assert g(512, 12288, 4096) == 0

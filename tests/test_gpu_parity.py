@@ -32,10 +32,24 @@ FP32_PATH_TOL = 2e-5
 # p <= 2e-5 / 2^-8 ~ 5e-3, each flip one ulp (2^-8 relative), so the
 # output error is <= sqrt(p) 2^-8 ~ 2.8e-4.
 MFMA_PATH_TOL = 3e-4
+# The fused linear uses the float32 vector-ALU product below this batch and
+# the bf16 matrix-core product from it on; up to SKINNY_MAX_M rows that
+# product feeds the integer codes to the matrix cores and applies scale and
+# zero per group (w_hat exact, only x~ rounded), above it rounds both x~ and
+# w_hat to bf16.
+MFMA_MIN_M = 16
+SKINNY_MAX_M = 64
 
 
 def path_tol(M):
-    return FP32_PATH_TOL if M < 64 else MFMA_PATH_TOL
+    return FP32_PATH_TOL if M < MFMA_MIN_M else MFMA_PATH_TOL
+
+
+def mode_for(M):
+    """Rounding points of the product the fused linear runs at batch M."""
+    if M < MFMA_MIN_M:
+        return "f32"
+    return "mfma_exact_w" if M <= SKINNY_MAX_M else "mfma"
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -269,7 +283,12 @@ def test_rotate_in_deq_gemv(N, K, b, bits, M, angles, xdt):
 
 
 GEMM_CASES = [
-    (100, 320, 2, 64), (300, 256, 3, 65), (257, 128, 4, 1), (128, 64, 2, 200),
+    # M <= 64: the small-batch kernel (16 features per workgroup)
+    (100, 320, 2, 16), (300, 256, 3, 33), (257, 128, 4, 1), (4096, 4096, 2, 16),
+    (4096, 4096, 2, 32), (11008, 4096, 2, 16), (4096, 11008, 4, 48),
+    (1024, 28672, 3, 32), (2000, 8192, 2, 5), (1000, 1088, 4, 64), (64, 64, 2, 17),
+    # M > 64: 128 x 128 tiles, optionally split K
+    (300, 256, 3, 65), (128, 64, 2, 200),
     (4096, 4096, 2, 512), (12288, 4096, 4, 512), (4096, 12288, 2, 512),
     (4096, 4096, 3, 129), (1000, 1088, 2, 300), (384, 2048, 4, 64),
 ]
@@ -283,11 +302,16 @@ def test_gemm(N, K, bits, M):
     w = S.qweight(N, K, bits, rng(13, N, K, bits))
     xt = S.activations(M, K, rng(14, K, M), "bf16")
     Wd, xd = d.dev_qweight(w), d.dev(xt)
-    w_hat = O.bf16_round(O.dequant(O.unpack(w.words, bits, K), d.scale_f16(w),
-                                   d.zero_f16(w)))
+    w_hat = O.dequant(O.unpack(w.words, bits, K), d.scale_f16(w), d.zero_f16(w))
+    if M > SKINNY_MAX_M:      # the tiled product rounds w_hat to bf16
+        w_hat = O.bf16_round(w_hat)
     ref = O.bf16_bits_to_f64(xt) @ w_hat.T
     yt = torch.empty((M, N), dtype=torch.float32, device="cuda")
     H().harp_deq_gemm(Wd, xd, yt)
+    y_again = torch.empty_like(yt)
+    H().harp_deq_gemm(Wd, xd, y_again)
+    torch.cuda.synchronize()
+    assert torch.equal(yt, y_again)
     r = report(f"gemm {N}x{K} b{bits} M={M}", d.host(yt), ref)
     assert r <= CONTRACT_TOL and r <= FP32_PATH_TOL
     ws = d.gemm_workspace(M, N, K)
@@ -310,16 +334,19 @@ def test_gemm(N, K, bits, M):
 # a6: the whole linear
 # ---------------------------------------------------------------------------
 
-def oracle_linear_rows(li, x64, mfma, blocks=None, chunk=2048):
+def oracle_linear_rows(li, x64, mode, blocks=None, chunk=2048):
     """Oracle linear composed from oracle steps; output-side blocks optional.
 
-    y' rows are produced in chunks so that large layers fit in memory.  When
-    ``blocks`` is given, only those output blocks (of size b_U; independent
-    because U is block-diagonal) are produced.  Returns (y, output columns).
+    mode: "f32" (no rounding), "mfma" (x~ and w_hat rounded to bf16) or
+    "mfma_exact_w" (only x~ rounded).  y' rows are produced in chunks so that
+    large layers fit in memory.  When ``blocks`` is given, only those output
+    blocks (of size b_U; independent because U is block-diagonal) are
+    produced.  Returns (y, output columns).
     """
+    assert mode in ("f32", "mfma", "mfma_exact_w")
     lin, w = li.lin, li.W
     xt = O.forward(x64, D().cs64(li.V), li.V.sign_bits, lin.b_v)
-    if mfma:
+    if mode != "f32":
         xt = O.bf16_round(xt)
     bu = lin.b_u
     full = blocks is None
@@ -330,7 +357,7 @@ def oracle_linear_rows(li, x64, mfma, blocks=None, chunk=2048):
     for c0 in range(0, len(rows), chunk):
         rr = rows[c0:c0 + chunk]
         wh = O.dequant(O.unpack(w.words[rr], w.bits, lin.K), s16[rr], z16[rr])
-        if mfma:
+        if mode == "mfma":
             wh = O.bf16_round(wh)
         yp[:, c0:c0 + len(rr)] = xt @ wh.T
     cs_u = D().cs64(li.U)
@@ -367,8 +394,7 @@ def test_fused_configs(cfg, lin, bits, M):
     c = S.CONFIGS[cfg]
     li = S.layer_inputs(c, lin, bits, M)
     y = D().host(run_fused(li))
-    mfma = M >= 64
-    ref, _ = oracle_linear_rows(li, D().x_f64(li.x, li.x_dtype), mfma)
+    ref, _ = oracle_linear_rows(li, D().x_f64(li.x, li.x_dtype), mode_for(M))
     r = report(f"fused {cfg}[{lin}] b{bits} M={M}", y, ref)
     assert r <= CONTRACT_TOL
     assert r <= path_tol(M)
@@ -385,7 +411,7 @@ FUSED8_CASES = [("tiny", 0, 2, 4), ("l7b_decode", 0, 2, 1), ("l7b_mlp", 1, 2, 16
 def test_fused_int8_angles(cfg, lin, bits, M):
     li = S.layer_inputs(S.CONFIGS[cfg], lin, bits, M, angles="int8")
     y = D().host(run_fused(li))
-    ref, _ = oracle_linear_rows(li, D().x_f64(li.x, li.x_dtype), M >= 64)
+    ref, _ = oracle_linear_rows(li, D().x_f64(li.x, li.x_dtype), mode_for(M))
     r = report(f"fused int8 angles {cfg}[{lin}] b{bits} M={M}", y, ref)
     assert r <= CONTRACT_TOL
     assert r <= path_tol(M)
@@ -405,14 +431,13 @@ def test_fused_l70b_slice(lin, bits):
     if L0.N // L0.b_u > 16:
         nb = L0.N // L0.b_u
         blocks = sorted(set(rng(20, lin, bits).integers(0, nb, 12).tolist()) | {nb - 1})
-    # one oracle pass over both batches (same weights and rotations)
-    x64 = np.concatenate([D().x_f64(li.x, li.x_dtype) for li in lis])
-    ref, rows = oracle_linear_rows(lis[0], x64, False, blocks)
-    m0 = 0
+    # one oracle pass per batch: M = 1 takes the float32 product, M = 32 the
+    # bf16 matrix-core product, whose rounding points the oracle models
     for li, y in zip(lis, ys):
-        r = report(f"fused l70b[{lin}] b{bits} M={li.M}", y[:, rows], ref[m0:m0 + li.M])
-        assert r <= CONTRACT_TOL and r <= FP32_PATH_TOL
-        m0 += li.M
+        ref, rows = oracle_linear_rows(li, D().x_f64(li.x, li.x_dtype), mode_for(li.M),
+                                       blocks)
+        r = report(f"fused l70b[{lin}] b{bits} M={li.M}", y[:, rows], ref)
+        assert r <= CONTRACT_TOL and r <= path_tol(li.M)
 
 
 @pytest.mark.parametrize("b_v,M,angles,xdt", [
@@ -425,7 +450,7 @@ def test_fused_decode_input_blocks(b_v, M, angles, xdt):
     single-launch input rotation, b = 4 the separate rotation kernel."""
     cfg = S.Config(10, "dec", (S.Linear("d", 4096, 768, b_v, 256),), (2,), (M,), x_dtype=xdt)
     li = S.layer_inputs(cfg, 0, 2, M, angles=angles)
-    ref, _ = oracle_linear_rows(li, D().x_f64(li.x, xdt), False)
+    ref, _ = oracle_linear_rows(li, D().x_f64(li.x, xdt), "f32")
     y = D().host(run_fused(li))
     r = report(f"decode b_v={b_v} M={M} {angles} {xdt}", y, ref)
     assert r <= CONTRACT_TOL and r <= FP32_PATH_TOL
@@ -452,7 +477,7 @@ def test_fused_decode_mixed_angle_formats(M, angles_v, angles_u):
     H().harp_linear_fused(V, W, U, x, y2, ws)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
-    ref, _ = oracle_linear_rows(li, d.x_f64(li.x, li.x_dtype), False)
+    ref, _ = oracle_linear_rows(li, d.x_f64(li.x, li.x_dtype), "f32")
     r = report(f"decode M={M} V {angles_v} U {angles_u}", d.host(y1), ref)
     assert r <= CONTRACT_TOL and r <= FP32_PATH_TOL
 
@@ -470,7 +495,7 @@ def test_fused_batch_edges_and_bf16_out(M):
                               d.workspace(1, 512, 256), M=0)
         assert torch.all(y == 7.0)
         return
-    ref, _ = oracle_linear_rows(li, D().x_f64(li.x, "bf16"), M >= 64)
+    ref, _ = oracle_linear_rows(li, D().x_f64(li.x, "bf16"), mode_for(M))
     y = D().host(run_fused(li))
     r = report(f"edge M={M}", y, ref)
     assert r <= CONTRACT_TOL and r <= path_tol(M)
