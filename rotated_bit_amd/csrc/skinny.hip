@@ -32,28 +32,36 @@ constexpr int kStrip = 16;                   // output features per workgroup
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kXsRow = kGroup + 8;        // bf16 per padded LDS row of x~
+constexpr int kBlk = 4;                   // groups per coalesced code block
 
-// Operands of one quantization group for one lane.  x~ is loaded coalesced
-// (eight lanes per 128-byte row segment: lane l holds row 8i + l/8, inputs
-// 8 (l % 8) .. +7 of the group, i = 0, 1) and re-laid out through LDS into
-// the matrix-core operand order, where neighbouring lanes read different
-// rows.
-template <int BITS, int MB>
-struct GroupRegs {
-  uint32_t w[2 * BITS];      // the feature's 64 codes
-  uint16_t s16, z16;         // its fp16 scale and zero
-  u32x4 a[MB][2];            // x~ rows 16 mb + 8 i + l/8, inputs 8 (l % 8) .. +7
+// x~ of one quantization group for one lane, loaded coalesced (eight lanes
+// per 128-byte row segment: lane l holds row 16 mb + 8 i + l/8, inputs
+// 8 (l % 8) .. +7 of the group) and re-laid out through LDS into the
+// matrix-core operand order, where neighbouring lanes read different rows.
+template <int MB>
+struct ARegs {
+  u32x4 a[MB][2];
 };
 
-template <int BITS, int MB>
-__device__ __forceinline__ void load_group_regs(GroupRegs<BITS, MB>& r, int g,
-                                                const uint32_t* __restrict__ wrow,
-                                                const uint16_t* __restrict__ srow,
-                                                const uint16_t* __restrict__ zrow,
-                                                const uint16_t* const (&arow)[MB][2], int lane) {
-  load_group<BITS>(wrow + static_cast<size_t>(g) * 2 * BITS, r.w);
-  r.s16 = srow[g];
-  r.z16 = zrow[g];
+// One lane's share of a code block: feature row l/4 of the strip, group
+// g0 + l % 4, so neighbouring lanes read neighbouring groups of a row.
+template <int BITS>
+struct CodeRegs {
+  uint32_t w[2 * BITS];
+  uint16_t s16, z16;
+};
+
+// Per-wave LDS of a code block: [buffer][feature][group slot][words], rows
+// padded by 16 bytes so that the operand-order reads (feature per lane)
+// spread over the banks; scale and zero packed in one word per slot.
+template <int BITS>
+struct CodeLds {
+  static constexpr int ROW = kBlk * 2 * BITS + 4;
+};
+
+template <int MB>
+__device__ __forceinline__ void load_a(ARegs<MB>& r, int g, const uint16_t* const (&arow)[MB][2],
+                                       int lane) {
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -61,9 +69,11 @@ __device__ __forceinline__ void load_group_regs(GroupRegs<BITS, MB>& r, int g,
       r.a[mb][i] = *reinterpret_cast<const u32x4*>(arow[mb][i] + g * kGroup + 8 * (lane & 7));
 }
 
+// One group: the lane's feature codes (w) and packed scale/zero (sz) from
+// the code block in LDS, x~ from registers via the wave's LDS rows.
 template <int BITS, int MB>
-__device__ __forceinline__ void mma_group(const GroupRegs<BITS, MB>& r, int lane,
-                                          uint16_t (*xs)[16][kXsRow],
+__device__ __forceinline__ void mma_group(const ARegs<MB>& r, const uint32_t (&w)[2 * BITS],
+                                          uint32_t sz, int lane, uint16_t (*xs)[16][kXsRow],
                                           floatx4_t (&acc)[MB]) {
   const int c = lane >> 4;
   // This wave's x~ block of the group into its own LDS rows (no other wave
@@ -83,7 +93,7 @@ __device__ __forceinline__ void mma_group(const GroupRegs<BITS, MB>& r, int lane
   }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const bf16x8 b = __builtin_bit_cast(bf16x8, chunk8_bf16_offset<BITS>(chunk8<BITS>(r.w, h, c)));
+    const bf16x8 b = __builtin_bit_cast(bf16x8, chunk8_bf16_offset<BITS>(chunk8<BITS>(w, h, c)));
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(&xs[mb][lane & 15][32 * h + 8 * c]);
@@ -93,8 +103,8 @@ __device__ __forceinline__ void mma_group(const GroupRegs<BITS, MB>& r, int lane
   }
   // Accumulator layout of a 16x16 block: lane l holds column (feature)
   // l % 16, so one scale and zero per lane.
-  const float s = f16_to_f32(r.s16);
-  const float zo = f16_to_f32(r.z16) + 128.0f;   // exact
+  const float s = f16_to_f32(static_cast<uint16_t>(sz & 0xffffu));
+  const float zo = f16_to_f32(static_cast<uint16_t>(sz >> 16)) + 128.0f;   // exact
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -106,19 +116,24 @@ __global__ __launch_bounds__(kThreadsS) void skinny_kernel(
     const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
     const uint16_t* __restrict__ zr, const uint16_t* __restrict__ xt,
     float* __restrict__ yt, int N, int K, int M) {
+  constexpr int NW = 2 * BITS;
+  constexpr int CROW = CodeLds<BITS>::ROW;
   __shared__ floatx4_t red[kWavesS][MB][kWave];
   __shared__ __attribute__((aligned(16))) uint16_t xsw[kWavesS][MB][16][kXsRow];
+  __shared__ __attribute__((aligned(16))) uint32_t cw[kWavesS][2][16][CROW];
+  __shared__ uint32_t szw[kWavesS][2][16][kBlk];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid >> 6;
   const int G = K / kGroup;
   const size_t WPR = static_cast<size_t>(K) * BITS / 32;
-  const int fl = lane & 15;          // feature within the strip (B column)
-  const int n = min(blockIdx.x * kStrip + fl, N - 1);   // rows past N: never stored
-  const uint32_t* wrow = qw + static_cast<size_t>(n) * WPR;
-  const uint16_t* srow = sc + static_cast<size_t>(n) * G;
-  const uint16_t* zrow = zr + static_cast<size_t>(n) * G;
+  const int n0 = blockIdx.x * kStrip;
+  // code-block role: row n0 + l/4 (rows past N: loaded, never stored)
+  const int crow = min(n0 + (lane >> 2), N - 1);
+  const uint32_t* wrow = qw + static_cast<size_t>(crow) * WPR;
+  const uint16_t* srow = sc + static_cast<size_t>(crow) * G;
+  const uint16_t* zrow = zr + static_cast<size_t>(crow) * G;
   const uint16_t* arow[MB][2];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)   // rows past M: read, never stored
@@ -126,56 +141,101 @@ __global__ __launch_bounds__(kThreadsS) void skinny_kernel(
     for (int i = 0; i < 2; ++i)
       arow[mb][i] = xt + static_cast<size_t>(min(16 * mb + 8 * i + (lane >> 3), M - 1)) * K;
   uint16_t (*xs)[16][kXsRow] = xsw[wave];
+  uint32_t (*cl)[16][CROW] = cw[wave];
+  uint32_t (*szl)[16][kBlk] = szw[wave];
 
   floatx4_t acc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // This wave's groups [gb, ge) through a ring of register sets (four, or
-  // two for the widest batch block, whose x~ fragments fill the registers):
-  // the loads of the next groups are in flight while a group is multiplied
-  // (memory latency, not bandwidth, bounds a wave's progress here).  Loads
-  // past ge re-read group ge-1 (valid memory, never multiplied).  Named sets,
-  // not an array, keep the ring in registers.
+  // This wave's groups [gb, ge), in blocks of kBlk.  The codes and scales of
+  // block b+1 are in flight while block b is multiplied; the x~ of the next
+  // groups rides in a ring of register sets (four, or two for the widest
+  // batch block, whose fragments fill the registers).  Loads past ge re-read
+  // group ge-1 (valid memory, never multiplied).  Named sets, not arrays,
+  // keep the rings in registers.
   const int gb = wave * G / kWavesS;
   const int ge = (wave + 1) * G / kWavesS;
   if (gb < ge) {
-    auto load = [&](GroupRegs<BITS, MB>& r, int g) {
-      load_group_regs<BITS, MB>(r, min(g, ge - 1), wrow, srow, zrow, arow, lane);
+    const int cnt = ge - gb;
+    CodeRegs<BITS> cr;
+    auto load_codes = [&](int blk) {
+      const int g = min(gb + kBlk * blk + (lane & 3), ge - 1);
+      load_group<BITS>(wrow + static_cast<size_t>(g) * NW, cr.w);
+      cr.s16 = srow[g];
+      cr.z16 = zrow[g];
     };
+    auto store_codes = [&](int buf) {
+      uint32_t* d = &cl[buf][lane >> 2][(lane & 3) * NW];
+#pragma unroll
+      for (int i = 0; i < NW; ++i) d[i] = cr.w[i];
+      szl[buf][lane >> 2][lane & 3] = static_cast<uint32_t>(cr.s16) |
+                                      (static_cast<uint32_t>(cr.z16) << 16);
+    };
+    // group j of the block in buffer buf, for this lane's feature
+    auto group = [&](const ARegs<MB>& r, int buf, int j) {
+      uint32_t w[NW];
+      const uint32_t* src = &cl[buf][lane & 15][j * NW];
+#pragma unroll
+      for (int i = 0; i < NW; ++i) w[i] = src[i];
+      mma_group<BITS, MB>(r, w, szl[buf][lane & 15][j], lane, xs, acc);
+    };
+    auto load = [&](ARegs<MB>& r, int g) { load_a<MB>(r, min(g, ge - 1), arow, lane); };
+
+    load_codes(0);
+    store_codes(0);
+    load_codes(1);
+    int g = gb;
+    int blk = 0;
     if constexpr (MB <= 3) {
-      GroupRegs<BITS, MB> r0, r1, r2, r3;
+      ARegs<MB> r0, r1, r2, r3;
       load(r0, gb);
       load(r1, gb + 1);
       load(r2, gb + 2);
       load(r3, gb + 3);
-      int g = gb;
-      for (; g + 4 <= ge; g += 4) {
-        mma_group<BITS, MB>(r0, lane, xs, acc);
+      for (; g + kBlk <= ge; g += kBlk, ++blk) {
+        const int buf = blk & 1;
+        group(r0, buf, 0);
         load(r0, g + 4);
-        mma_group<BITS, MB>(r1, lane, xs, acc);
+        group(r1, buf, 1);
         load(r1, g + 5);
-        mma_group<BITS, MB>(r2, lane, xs, acc);
+        group(r2, buf, 2);
         load(r2, g + 6);
-        mma_group<BITS, MB>(r3, lane, xs, acc);
+        group(r3, buf, 3);
         load(r3, g + 7);
+        store_codes(buf ^ 1);          // block blk+1, loaded during this block
+        load_codes(blk + 2);
       }
-      if (g < ge) mma_group<BITS, MB>(r0, lane, xs, acc);
-      if (g + 1 < ge) mma_group<BITS, MB>(r1, lane, xs, acc);
-      if (g + 2 < ge) mma_group<BITS, MB>(r2, lane, xs, acc);
+      const int buf = blk & 1;
+      if (g < ge) group(r0, buf, 0);
+      if (g + 1 < ge) group(r1, buf, 1);
+      if (g + 2 < ge) group(r2, buf, 2);
     } else {
-      GroupRegs<BITS, MB> r0, r1;
+      ARegs<MB> r0, r1;
       load(r0, gb);
       load(r1, gb + 1);
-      int g = gb;
-      for (; g + 2 <= ge; g += 2) {
-        mma_group<BITS, MB>(r0, lane, xs, acc);
+      for (; g + kBlk <= ge; g += kBlk, ++blk) {
+        const int buf = blk & 1;
+        group(r0, buf, 0);
         load(r0, g + 2);
-        mma_group<BITS, MB>(r1, lane, xs, acc);
+        group(r1, buf, 1);
         load(r1, g + 3);
+        group(r0, buf, 2);
+        load(r0, g + 4);
+        group(r1, buf, 3);
+        load(r1, g + 5);
+        store_codes(buf ^ 1);
+        load_codes(blk + 2);
       }
-      if (g < ge) mma_group<BITS, MB>(r0, lane, xs, acc);
+      const int buf = blk & 1;
+      if (g < ge) group(r0, buf, 0);
+      if (g + 1 < ge) group(r1, buf, 1);
+      if (g + 2 < ge) {
+        load(r0, g + 2);
+        group(r0, buf, 2);
+      }
     }
+    (void)cnt;
   }
 
   // Combine the eight K ranges in wave order.  Accumulator layout of the
@@ -192,7 +252,7 @@ __global__ __launch_bounds__(kThreadsS) void skinny_kernel(
 #pragma unroll
     for (int w = 0; w < kWavesS; ++w) sum += red[w][mb][l][v];
     const int m = 16 * mb + 4 * (l >> 4) + v;
-    const int nn = blockIdx.x * kStrip + (l & 15);
+    const int nn = n0 + (l & 15);
     if (m < M && nn < N) yt[static_cast<size_t>(m) * N + nn] = sum;
   }
 }
