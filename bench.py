@@ -188,6 +188,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=512 figure")
     ap.add_argument("--no-int8", action="store_true",
                     help="skip the decode leg with int8-stored angles")
+    ap.add_argument("--no-batched", action="store_true",
+                    help="skip the M=16 batched-decode leg")
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graph")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (the known-size "
@@ -322,6 +324,32 @@ def main():
         del inst8
         torch.cuda.empty_cache()
 
+    # batched decode: the Llama-2-7B MLP pair at M = 16 (small-batch
+    # matrix-core product)
+    batched = None
+    if not args.no_batched:
+        batched = {"workload": "l7b_mlp: 4096->11008 (b_U=256) and 11008->4096 (b_V=256), "
+                               "2-bit, M=16, harp_linear_fused", "linears": {}}
+        for li_idx, name in ((0, "up_4096x11008"), (1, "down_11008x4096")):
+            bi = make_instances("l7b_mlp", li_idx, 2, 16, 16, torch, H)
+            lin = bi[0].li.lin
+            for it in bi:
+                H.harp_rotate_in(it.V, it.x, it.xt16)
+            msf, _ = time_graph(torch, lambda: [H.harp_linear_fused(i.V, i.W, i.U, i.x, i.y, i.ws)
+                                                for i in bi], 10)
+            msg, _ = time_graph(torch, lambda: [H.harp_deq_gemm(i.W, i.xt16, i.yp) for i in bi], 10)
+            usf, usg = msf * 1e3 / len(bi), msg * 1e3 / len(bi)
+            nb = alg_bytes(16, lin.N, lin.K, 2, lin.b_v, lin.b_u)
+            wb = lin.N * lin.K * 2 // 8 + lin.N * (lin.K // 64) * 4
+            batched["linears"][name] = {
+                "fused_us": round(usf, 2), "fused_GB_s": round(nb / (usf * 1e-6) / 1e9, 1),
+                "deq_gemm_us": round(usg, 2),
+                "deq_gemm_TFLOPs": round(2.0 * 16 * lin.N * lin.K / (usg * 1e-6) / 1e12, 1),
+                "deq_gemm_weight_GB_s": round(wb / (usg * 1e-6) / 1e9, 1)}
+            del bi
+            torch.cuda.empty_cache()
+        log("batched decode: " + json.dumps(batched))
+
     # prefill: M = 512, 4096 x 4096 2-bit on the matrix cores
     prefill = None
     if not args.no_prefill:
@@ -373,6 +401,7 @@ def main():
         "roofline": roofline,
         "kernels": kern,
         "int8_angles": q8,
+        "batched_decode": batched,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }
