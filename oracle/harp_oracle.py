@@ -236,7 +236,7 @@ def rotate_weight(W: np.ndarray, cs_u, signs_u, b_u, cs_v, signs_v,
     return forward(rows.T, cs_u, signs_u, b_u).T   # each column: F_U
 
 
-def quantize(Wp: np.ndarray, bits: int, group: int = GROUP):
+def quantize(Wp: np.ndarray, bits: int, group: int = GROUP, arith: str = "f64"):
     """Per-row, per-group uniform asymmetric quantizer (stand-in reading).
 
     Returns (q uint8 [N][K], scale fp16 [N][K/group], zero fp16 [N][K/group]).
@@ -244,22 +244,33 @@ def quantize(Wp: np.ndarray, bits: int, group: int = GROUP):
     when both are 0); s = fp16((hi - lo) / (2^B - 1)), at least 2^-14;
     z = clamp(rint(-lo / s), 0, 2^B - 1); q = clamp(rint(w / s) + z, 0, 2^B - 1).
     rint rounds half to even.
+
+    arith: the precision each step is evaluated in.  "f64" evaluates in
+    float64 (the offline reference).  "f32" takes every step as one IEEE
+    float32 operation rounded to nearest even (hi - lo, the division by
+    2^B - 1, each w / s and -lo / s), as a float32 implementation does;
+    float decides the integer codes, so a check of such an implementation
+    takes the decisions in its precision.  The input is then float32.
     """
-    Wp = np.asarray(Wp, dtype=np.float64)
+    if arith not in ("f64", "f32"):
+        raise ValueError("arith must be 'f64' or 'f32'")
+    ft = np.float64 if arith == "f64" else np.float32
+    Wp = np.asarray(Wp, dtype=ft)
     n, k = Wp.shape
     if k % group:
         raise ValueError("K must be a multiple of the group size")
     qmax = (1 << bits) - 1
     g = Wp.reshape(n, k // group, group)
-    lo = np.minimum(g.min(axis=2), 0.0)
-    hi = np.maximum(g.max(axis=2), 0.0)
+    zero = ft(0.0)
+    lo = np.minimum(g.min(axis=2), zero)
+    hi = np.maximum(g.max(axis=2), zero)
     flat = hi == lo
-    lo = np.where(flat, -1.0, lo)
-    hi = np.where(flat, 1.0, hi)
-    s16 = ((hi - lo) / qmax).astype(np.float16)
+    lo = np.where(flat, ft(-1.0), lo).astype(ft)
+    hi = np.where(flat, ft(1.0), hi).astype(ft)
+    s16 = ((hi - lo) / ft(qmax)).astype(np.float16)
     s16 = np.maximum(s16, np.float16(2.0 ** -14))
-    s = s16.astype(np.float64)
-    z = np.clip(np.rint(-lo / s), 0, qmax)
+    s = s16.astype(ft)
+    z = np.clip(np.rint(-lo / s), 0, qmax).astype(ft)
     q = np.clip(np.rint(g / s[..., None]) + z[..., None], 0, qmax)
     return (q.reshape(n, k).astype(np.uint8), s16,
             z.astype(np.float16))

@@ -66,12 +66,15 @@ def test_unpack_random_words_in_range(bits):
     assert np.array_equal(O.pack(q, bits), w)
 
 
+@pytest.mark.parametrize("arith", ["f64", "f32"])
 @pytest.mark.parametrize("bits", [2, 3, 4])
-def test_quantizer_bounds(bits):
+def test_quantizer_bounds(bits, arith):
     qmax = (1 << bits) - 1
     W = rng0.normal(0, 0.02, size=(16, 512))
     W[:, 7] *= 20
-    q, s16, z16 = O.quantize(W, bits)
+    if arith == "f32":
+        W = W.astype(np.float32).astype(np.float64)
+    q, s16, z16 = O.quantize(W, bits, arith=arith)
     assert q.max() <= qmax
     s = s16.astype(np.float64)
     z = z16.astype(np.float64)
@@ -83,7 +86,8 @@ def test_quantizer_bounds(bits):
     hi_grid = (qmax - zr) * sr
     inside = (W >= lo_grid) & (W <= hi_grid)
     err = np.abs(W - w_hat)
-    assert np.all(err[inside] <= sr[inside] / 2 * (1 + 1e-12))
+    rel = 1e-12 if arith == "f64" else 1e-6     # w / s rounded to float32
+    assert np.all(err[inside] <= sr[inside] / 2 * (1 + rel))
     # outside the grid, the clamp costs at most one more half step
     # (z rounding) plus fp16 rounding of s over qmax steps
     assert np.all(err <= sr * (1.0 + qmax * 2.0 ** -11) + 1e-15)
@@ -91,8 +95,9 @@ def test_quantizer_bounds(bits):
     assert np.all(w_hat[q == zr] == 0.0)
 
 
+@pytest.mark.parametrize("arith", ["f64", "f32"])
 @pytest.mark.parametrize("bits", [2, 3, 4])
-def test_quantizer_exact_recovery(bits):
+def test_quantizer_exact_recovery(bits, arith):
     """A group that lies on a grid spanning its own min and max is recovered."""
     qmax = (1 << bits) - 1
     n, G = 6, 4
@@ -101,27 +106,49 @@ def test_quantizer_exact_recovery(bits):
     q0 = rng0.integers(0, qmax + 1, size=(n, G, 64))
     q0[..., 0] = 0
     q0[..., 1] = qmax
-    W = (q0 - z0[..., None]) * s0[..., None]
-    q, s16, z16 = O.quantize(W.reshape(n, G * 64), bits)
+    W = (q0 - z0[..., None]) * s0[..., None]      # exact in float32 too
+    q, s16, z16 = O.quantize(W.reshape(n, G * 64), bits, arith=arith)
     assert np.array_equal(s16.astype(np.float64), s0)
     assert np.array_equal(z16.astype(np.float64), z0)
     assert np.array_equal(q, q0.reshape(n, G * 64))
 
 
-def test_quantizer_degenerate_group():
+@pytest.mark.parametrize("arith", ["f64", "f32"])
+def test_quantizer_degenerate_group(arith):
     W = np.zeros((2, 128))
     W[1, 64:] = 0.5
-    q, s16, z16 = O.quantize(W, 2)
+    q, s16, z16 = O.quantize(W, 2, arith=arith)
     assert float(s16[0, 0]) == float(np.float16(2.0 / 3.0))
     assert np.all(O.dequant(q, s16, z16)[0] == 0.0)
     # all-positive group: lo forced to 0 -> z = 0, top code hits max exactly
     assert float(z16[1, 1]) == 0.0 and np.all(q[1, 64:] == 3)
 
 
-def test_quantizer_scale_floor():
+@pytest.mark.parametrize("arith", ["f64", "f32"])
+def test_quantizer_scale_floor(arith):
     W = np.full((1, 64), 1e-9)
-    _, s16, _ = O.quantize(W, 2)
+    _, s16, _ = O.quantize(W, 2, arith=arith)
     assert float(s16[0, 0]) == 2.0 ** -14
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_quantizer_f32_decisions_differ_only_at_boundaries(bits):
+    """The float32 mode takes the float64 decisions except where a value
+    lies within float32 rounding of a decision boundary: rarely, and then
+    by one code."""
+    W = (rng0.normal(0, 0.02, size=(256, 1024))).astype(np.float32).astype(np.float64)
+    q64, s64, z64 = O.quantize(W, bits)
+    q32, s32, z32 = O.quantize(W, bits, arith="f32")
+    same_s = s64 == s32
+    assert same_s.mean() > 0.99
+    rows = np.repeat(same_s & (z64 == z32), 64, axis=1)
+    d = np.abs(q64.astype(int) - q32.astype(int))[rows]
+    assert d.max() <= 1 and (d > 0).mean() < 1e-3
+
+
+def test_quantizer_rejects_unknown_arith():
+    with pytest.raises(ValueError):
+        O.quantize(np.zeros((1, 64)), 2, arith="f16")
 
 
 def test_dequant_exact_in_float32():
