@@ -242,8 +242,8 @@ def quantize(Wp: np.ndarray, bits: int, group: int = GROUP, arith: str = "f64"):
     Returns (q uint8 [N][K], scale fp16 [N][K/group], zero fp16 [N][K/group]).
     For one group w: lo = min(min w, 0), hi = max(max w, 0) (lo = -1, hi = 1
     when both are 0); s = fp16((hi - lo) / (2^B - 1)), at least 2^-14;
-    z = clamp(rint(-lo / s), 0, 2^B - 1); q = clamp(rint(w / s) + z, 0, 2^B - 1).
-    rint rounds half to even.
+    z = clamp(rint(-lo / s), 0, 2^B - 1) (a zero-point of 0 stored as +0);
+    q = clamp(rint(w / s) + z, 0, 2^B - 1).  rint rounds half to even.
 
     arith: the precision each step is evaluated in.  "f64" evaluates in
     float64 (the offline reference).  "f32" takes every step as one IEEE
@@ -270,7 +270,9 @@ def quantize(Wp: np.ndarray, bits: int, group: int = GROUP, arith: str = "f64"):
     s16 = ((hi - lo) / ft(qmax)).astype(np.float16)
     s16 = np.maximum(s16, np.float16(2.0 ** -14))
     s = s16.astype(ft)
-    z = np.clip(np.rint(-lo / s), 0, qmax).astype(ft)
+    # + 0: a zero-point of 0 is stored as +0 (a group whose minimum is -0.0
+    # would otherwise give -0)
+    z = (np.clip(np.rint(-lo / s), 0, qmax) + ft(0.0)).astype(ft)
     q = np.clip(np.rint(g / s[..., None]) + z[..., None], 0, qmax)
     return (q.reshape(n, k).astype(np.uint8), s16,
             z.astype(np.float16))

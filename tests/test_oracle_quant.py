@@ -146,6 +146,15 @@ def test_quantizer_f32_decisions_differ_only_at_boundaries(bits):
     assert d.max() <= 1 and (d > 0).mean() < 1e-3
 
 
+@pytest.mark.parametrize("arith", ["f64", "f32"])
+def test_quantizer_zero_point_is_positive_zero(arith):
+    W = np.full((2, 64), 0.3)
+    W[0, 0] = -0.0               # minimum -0.0: lo = -0.0, z = +0
+    W[1, :] = -0.0               # all -0.0: the flat-group case
+    _, _, z16 = O.quantize(W, 2, arith=arith)
+    assert not np.any(z16.view(np.uint16) & 0x8000)
+
+
 def test_quantizer_rejects_unknown_arith():
     with pytest.raises(ValueError):
         O.quantize(np.zeros((1, 64)), 2, arith="f16")
