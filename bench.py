@@ -190,6 +190,8 @@ def main():
                     help="skip the decode leg with int8-stored angles")
     ap.add_argument("--no-batched", action="store_true",
                     help="skip the M=16 batched-decode leg")
+    ap.add_argument("--no-prep", action="store_true",
+                    help="skip the offline-preparation leg")
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graph")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (the known-size "
@@ -350,6 +352,39 @@ def main():
             torch.cuda.empty_cache()
         log("batched decode: " + json.dumps(batched))
 
+    # offline preparation: W' = F_U W F_V^T, then quantize and pack (2-bit)
+    prep = None
+    if not args.no_prep:
+        import numpy as np
+        from synth import workloads as S
+        prep = {"workload": "dense float32 W 4096x4096 (b=4096 both sides) and 8192x28672 "
+                            "(b_V=256, b_U=8192): harp_rotate_weight, harp_quantize_pack 2-bit"}
+        for (N, K, bu, bv) in ((4096, 4096, 4096, 4096), (8192, 28672, 8192, 256)):
+            rV = S.rotation(K, bv, np.random.default_rng(1))
+            rU = S.rotation(N, bu, np.random.default_rng(2))
+            dv = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int32) if a.dtype == np.uint32 else a)).cuda()
+            V = H.Rotation(dv(rV.cs), dv(rV.sign_bits), K, bv)
+            U = H.Rotation(dv(rU.cs), dv(rU.sign_bits), N, bu)
+            W = torch.randn((N, K), device="cuda") * 0.02
+            Wp = torch.empty_like(W)
+            ws = torch.empty(H.harp_rotate_weight_workspace_bytes(N, K), dtype=torch.uint8,
+                             device="cuda")
+            qw = torch.empty((N, K * 2 // 32), dtype=torch.int32, device="cuda")
+            sc = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
+            zr = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
+            ms_r, _ = time_graph(torch, lambda: H.harp_rotate_weight(V, U, W, Wp, ws), 5)
+            ms_q, _ = time_graph(torch, lambda: H.harp_quantize_pack(Wp, 2, qw, sc, zr), 5)
+            nrot = 8 * N * K + 8 * (K // 2 * (bv.bit_length() - 1) + N // 2 * (bu.bit_length() - 1))
+            nq = 4 * N * K + N * K // 4 + N * (K // 64) * 4
+            prep[f"{N}x{K}"] = {
+                "rotate_weight_us": round(ms_r * 1e3, 1),
+                "rotate_weight_GB_s": round(nrot / (ms_r * 1e-3) / 1e9, 1),
+                "quantize_pack_us": round(ms_q * 1e3, 1),
+                "quantize_pack_GB_s": round(nq / (ms_q * 1e-3) / 1e9, 1)}
+            del W, Wp, ws, qw, sc, zr
+            torch.cuda.empty_cache()
+        log("offline prep: " + json.dumps(prep))
+
     # prefill: M = 512, 4096 x 4096 2-bit on the matrix cores
     prefill = None
     if not args.no_prefill:
@@ -402,6 +437,7 @@ def main():
         "kernels": kern,
         "int8_angles": q8,
         "batched_decode": batched,
+        "offline_prep": prep,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

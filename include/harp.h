@@ -222,6 +222,38 @@ harp_status harp_linear_fused(const harp_rotation *V, const harp_qweight *W,
  * (exact) or bf16 (nearest even), through the same device unpack and
  * dequant code the products use.
  */
+/*
+ * Offline preparation (technical summary §2.4: the processor rotates the
+ * weight before the quantization backend; §5: an exact change of basis).
+ *
+ * W' = F_U W F_V^T for a dense float32 weight W [N][K] (out x in): each row
+ * w_n becomes F_V w_n (the input-side rotation of harp_rotate_in, rows as
+ * the batch), then each column is rotated by F_U (the rows of the
+ * transpose).  float32 throughout.  Requires V->dim == K, U->dim == N,
+ * N, K <= HARP_MAX_M.
+ *   W, Wp      [N][K] float32, device, 16-byte aligned; Wp may not alias W.
+ *   workspace  at least harp_rotate_weight_workspace_bytes(N, K) bytes,
+ *              256-byte aligned, clobbered.
+ */
+harp_status harp_rotate_weight(const harp_rotation *V, const harp_rotation *U,
+                               const float *W, float *Wp, int32_t N, int32_t K,
+                               void *workspace, size_t ws_bytes, harp_stream stream);
+size_t harp_rotate_weight_workspace_bytes(int32_t N, int32_t K);
+
+/*
+ * Quantize and pack a float32 weight Wp [N][K] into the harp_qweight layout
+ * (qweight [N][K*bits/32], scale and zero [N][K/64] fp16 bit patterns):
+ * per row and group of 64 inputs, lo = min(min w, 0), hi = max(max w, 0)
+ * (-1 and 1 when both are 0), s = fp16((hi - lo) / (2^bits - 1)) at least
+ * 2^-14, z = clamp(rint(-lo / s), 0, 2^bits - 1) (+0 when 0),
+ * q = clamp(rint(w / s) + z, 0, 2^bits - 1); rint rounds half to even and
+ * every step is one IEEE float32 operation, so the result is reproducible
+ * bit for bit.  Wp finite.  bits 2, 3 or 4; K % 64 == 0.
+ */
+harp_status harp_quantize_pack(const float *Wp, int32_t N, int32_t K, int32_t bits,
+                               uint32_t *qweight, uint16_t *scale, uint16_t *zero,
+                               harp_stream stream);
+
 harp_status harp_dequant(const harp_qweight *W, void *out, harp_dtype out_dt,
                          harp_stream stream);
 

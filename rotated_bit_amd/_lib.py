@@ -33,6 +33,7 @@ EXPORTED = (
     "harp_rotate_in", "harp_rotate_out", "harp_deq_gemv", "harp_rotate_in_deq_gemv",
     "harp_deq_gemm",
     "harp_deq_gemm_workspace_bytes", "harp_linear_workspace_bytes", "harp_linear_fused", "harp_dequant",
+    "harp_rotate_weight", "harp_rotate_weight_workspace_bytes", "harp_quantize_pack",
     "harp_status_string", "harp_last_hip_error",
 )
 
@@ -84,6 +85,11 @@ def _load() -> ctypes.CDLL:
         "harp_linear_fused": (c_int32, [R, Q, R, c_void_p, c_int32, c_void_p, c_int32,
                                         c_int32, c_void_p, c_size_t, c_void_p]),
         "harp_dequant": (c_int32, [Q, c_void_p, c_int32, c_void_p]),
+        "harp_rotate_weight": (c_int32, [R, R, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
+                                          c_size_t, c_void_p]),
+        "harp_rotate_weight_workspace_bytes": (c_size_t, [c_int32, c_int32]),
+        "harp_quantize_pack": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                                          c_void_p, c_void_p]),
         "harp_status_string": (c_char_p, [c_int32]),
         "harp_last_hip_error": (c_int32, []),
     }
@@ -216,6 +222,27 @@ def harp_linear_fused(V: Rotation, W: QWeight, U: Rotation, x, y, workspace,
 def harp_dequant(W: QWeight, out, stream=None) -> None:
     _check(lib.harp_dequant(ctypes.byref(W.c), _ptr(out), _dtype_code(out), _stream(stream)),
            "harp_dequant")
+
+
+def harp_rotate_weight_workspace_bytes(N: int, K: int) -> int:
+    return int(lib.harp_rotate_weight_workspace_bytes(N, K))
+
+
+def harp_rotate_weight(V: Rotation, U: Rotation, W, Wp, workspace, stream=None) -> None:
+    """Wp = F_U W F_V^T for W, Wp float32 [N][K]."""
+    N, K = W.shape
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.harp_rotate_weight(ctypes.byref(V.c), ctypes.byref(U.c), _ptr(W), _ptr(Wp), N, K,
+                                  _ptr(workspace), ws_bytes, _stream(stream)),
+           "harp_rotate_weight")
+
+
+def harp_quantize_pack(Wp, bits: int, qweight, scale, zero, stream=None) -> None:
+    """Quantize float32 Wp [N][K] into qweight [N][K*bits/32] and fp16-bit
+    scale / zero [N][K/64] (int32 / int16 tensors)."""
+    N, K = Wp.shape
+    _check(lib.harp_quantize_pack(_ptr(Wp), N, K, bits, _ptr(qweight), _ptr(scale), _ptr(zero),
+                                  _stream(stream)), "harp_quantize_pack")
 
 
 def harp_last_hip_error() -> int:

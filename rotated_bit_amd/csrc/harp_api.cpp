@@ -119,6 +119,37 @@ harp_status harp_dequant(const harp_qweight* W, void* out, harp_dtype out_dt,
   return from_hip(harp::launch_dequant(*W, out, out_dt, as_stream(stream)));
 }
 
+size_t harp_rotate_weight_workspace_bytes(int32_t N, int32_t K) {
+  return harp::rotate_weight_workspace_bytes(N, K);
+}
+
+harp_status harp_rotate_weight(const harp_rotation* V, const harp_rotation* U,
+                               const float* W, float* Wp, int32_t N, int32_t K,
+                               void* workspace, size_t ws_bytes, harp_stream stream) {
+  const harp_status st = harp::validate_rotate_weight(V, U, W, Wp, N, K, workspace, ws_bytes);
+  if (st != HARP_OK) return st;
+  const hipStream_t s = as_stream(stream);
+  float* t = static_cast<float*>(workspace);
+  // rows: W F_V^T (each row w_n -> F_V w_n), then columns: F_U (.) by
+  // rotating the rows of the transpose
+  harp_status r = from_hip(harp::launch_rotate(*V, W, HARP_F32, t, HARP_F32, N, false, s));
+  if (r != HARP_OK) return r;
+  r = from_hip(harp::launch_transpose(t, Wp, N, K, s));          // Wp holds [K][N]
+  if (r != HARP_OK) return r;
+  r = from_hip(harp::launch_rotate(*U, Wp, HARP_F32, t, HARP_F32, K, false, s));
+  if (r != HARP_OK) return r;
+  return from_hip(harp::launch_transpose(t, Wp, K, N, s));
+}
+
+harp_status harp_quantize_pack(const float* Wp, int32_t N, int32_t K, int32_t bits,
+                               uint32_t* qweight, uint16_t* scale, uint16_t* zero,
+                               harp_stream stream) {
+  const harp_status st = harp::validate_quantize_pack(Wp, N, K, bits, qweight, scale, zero);
+  if (st != HARP_OK) return st;
+  return from_hip(harp::launch_quantize_pack(Wp, N, K, bits, qweight, scale, zero,
+                                             as_stream(stream)));
+}
+
 const char* harp_status_string(harp_status status) {
   return harp::status_string(status);
 }

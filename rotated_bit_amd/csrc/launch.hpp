@@ -38,6 +38,13 @@ hipError_t launch_gemm(const harp_qweight& W, const uint16_t* xt, float* yt,
 hipError_t launch_gemm_skinny(const harp_qweight& W, const uint16_t* xt, float* yt,
                               int M, hipStream_t stream);
 
+// Offline preparation: out [C][R] = in [R][C]^T (float32), and the packed
+// uniform grid of a float32 weight [N][K] (qweight, scale, zero in the
+// harp_qweight layout).
+hipError_t launch_transpose(const float* in, float* out, int R, int C, hipStream_t stream);
+hipError_t launch_quantize_pack(const float* wp, int N, int K, int bits, uint32_t* qw,
+                                uint16_t* sc, uint16_t* zr, hipStream_t stream);
+
 // Dense w_hat [N][K], float32 or bf16.
 hipError_t launch_dequant(const harp_qweight& W, void* out, int out_dt,
                           hipStream_t stream);

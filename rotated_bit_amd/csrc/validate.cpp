@@ -134,6 +134,37 @@ harp_status validate_fused(const harp_rotation* V, const harp_qweight* W,
   return HARP_OK;
 }
 
+harp_status validate_rotate_weight(const harp_rotation* V, const harp_rotation* U,
+                                   const float* W, const float* Wp, int32_t N, int32_t K,
+                                   const void* workspace, size_t ws_bytes) {
+  HARP_TRY(check_rotation(V));
+  HARP_TRY(check_rotation(U));
+  // weight rows (N) and columns (K) are the batches of the two rotations
+  if (N < 1 || K < 1 || N > HARP_MAX_M || K > HARP_MAX_M) return HARP_ERR_SHAPE;
+  if (V->dim != K || U->dim != N) return HARP_ERR_SHAPE;
+  if (W == nullptr || Wp == nullptr || workspace == nullptr) return HARP_ERR_NULL;
+  if (!aligned(W, 16) || !aligned(Wp, 16) || !aligned(workspace, 256)) return HARP_ERR_ALIGN;
+  if (ws_bytes < rotate_weight_workspace_bytes(N, K)) return HARP_ERR_WORKSPACE;
+  return HARP_OK;
+}
+
+harp_status validate_quantize_pack(const float* Wp, int32_t N, int32_t K, int32_t bits,
+                                   const void* qweight, const void* scale, const void* zero) {
+  if (bits != 2 && bits != 3 && bits != 4) return HARP_ERR_UNSUPPORTED;
+  if (N < 1 || N > HARP_MAX_DIM || K < 64 || K > HARP_MAX_DIM || K % 64 != 0)
+    return HARP_ERR_SHAPE;
+  if (Wp == nullptr || qweight == nullptr || scale == nullptr || zero == nullptr)
+    return HARP_ERR_NULL;
+  if (!aligned(Wp, 16) || !aligned(qweight, 16) || !aligned(scale, 16) || !aligned(zero, 16))
+    return HARP_ERR_ALIGN;
+  return HARP_OK;
+}
+
+size_t rotate_weight_workspace_bytes(int32_t N, int32_t K) {
+  if (N < 1 || K < 1 || N > HARP_MAX_M || K > HARP_MAX_M) return 0;
+  return align256(static_cast<size_t>(N) * K * 4);
+}
+
 harp_status validate_dequant(const harp_qweight* W, const void* out, int out_dt) {
   HARP_TRY(check_qweight(W));
   if (bad_dtype(out_dt)) return HARP_ERR_DTYPE;

@@ -28,6 +28,12 @@ harp_status validate_fused(const harp_rotation* V, const harp_qweight* W,
                            const void* y, int y_dt, int32_t M,
                            const void* workspace, size_t ws_bytes);
 harp_status validate_dequant(const harp_qweight* W, const void* out, int out_dt);
+harp_status validate_rotate_weight(const harp_rotation* V, const harp_rotation* U,
+                                   const float* W, const float* Wp, int32_t N, int32_t K,
+                                   const void* workspace, size_t ws_bytes);
+harp_status validate_quantize_pack(const float* Wp, int32_t N, int32_t K, int32_t bits,
+                                   const void* qweight, const void* scale, const void* zero);
+size_t rotate_weight_workspace_bytes(int32_t N, int32_t K);
 
 // Matrix-core GEMM tiling and its split over K: the number of K slices is
 // chosen so that about one 128 x 128 output tile slice runs per CU (256 on

@@ -245,3 +245,43 @@ def test_rotate_in_deq_gemv_checks():
     assert call(M=5) == L.HARP_ERR_UNSUPPORTED
     assert call(V=rot(dim=256, block=4)) == L.HARP_ERR_UNSUPPORTED
     assert call(V=rot(dim=8192, block=256), W=qw(K=8192)) == L.HARP_ERR_UNSUPPORTED
+
+
+def test_rotate_weight_checks():
+    f = L.lib.harp_rotate_weight
+    V, U = rot(dim=256), rot(dim=512, block=256)
+    need = L.harp_rotate_weight_workspace_bytes(512, 256)
+    assert need == 512 * 256 * 4
+    b = lambda s: ctypes.byref(s) if s is not None else None
+
+    def call(V=V, U=U, W=FAKE, Wp=FAKE, N=512, K=256, ws=FAKE, wsb=need):
+        return f(b(V), b(U), W, Wp, N, K, ws, wsb, None)
+
+    assert call(V=None) == L.HARP_ERR_NULL
+    assert call(U=None) == L.HARP_ERR_NULL
+    assert call(K=512) == L.HARP_ERR_SHAPE                 # V.dim != K
+    assert call(N=256) == L.HARP_ERR_SHAPE                 # U.dim != N
+    assert call(N=0) == L.HARP_ERR_SHAPE
+    assert call(W=0) == L.HARP_ERR_NULL
+    assert call(ws=0) == L.HARP_ERR_NULL
+    assert call(Wp=MISALIGNED) == L.HARP_ERR_ALIGN
+    assert call(ws=FAKE + 16) == L.HARP_ERR_ALIGN
+    assert call(wsb=need - 1) == L.HARP_ERR_WORKSPACE
+    assert L.harp_rotate_weight_workspace_bytes(0, 256) == 0
+    assert L.harp_rotate_weight_workspace_bytes(70000, 256) == 0
+
+
+def test_quantize_pack_checks():
+    f = L.lib.harp_quantize_pack
+
+    def call(Wp=FAKE, N=4, K=128, bits=2, q=FAKE, s=FAKE, z=FAKE):
+        return f(Wp, N, K, bits, q, s, z, None)
+
+    assert call(bits=5) == L.HARP_ERR_UNSUPPORTED
+    assert call(bits=1) == L.HARP_ERR_UNSUPPORTED
+    assert call(K=100) == L.HARP_ERR_SHAPE
+    assert call(K=0) == L.HARP_ERR_SHAPE
+    assert call(N=0) == L.HARP_ERR_SHAPE
+    assert call(Wp=0) == L.HARP_ERR_NULL
+    assert call(z=0) == L.HARP_ERR_NULL
+    assert call(q=MISALIGNED) == L.HARP_ERR_ALIGN
