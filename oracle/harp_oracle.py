@@ -46,6 +46,11 @@ repository's design notes):
   and the dequantized weight are rounded to bf16, round to nearest even; a
   matrix-core product that multiplies the integer codes and applies scale
   and zero per group afterwards rounds only the rotated input.
+* Mixed radix (technical summary §2.1-2.2, ``mixed_forward``): stage t acts
+  on mixed-radix digit t (stride prod_{s<t} b_s); blocks Q(theta) G_b with
+  Q the Cayley map (I - A)(I + A)^-1 for b > 2 and the QR factor of a fixed
+  Gaussian (positive R diagonal, numpy seed mixer_seed + b) as G_b for radices
+  that are not powers of two.
 * int8 storage of the angles (technical summary §2.4 storage note, §4
   storage overhead; the pages give no encoding).  Each block's angle
   perturbation phi = t - pi/4 is stored as one signed 8-bit code c with one
@@ -222,6 +227,133 @@ def rotation_matrix(cs: np.ndarray, sign_bits: np.ndarray, d: int,
                     b: int) -> np.ndarray:
     """Dense F (d x d): column j is F e_j."""
     return forward(np.eye(d), cs, sign_bits, b).T
+
+
+# ---------------------------------------------------------------------------
+# Mixed-radix stages (technical summary §2.1-2.2)
+# ---------------------------------------------------------------------------
+# Schedule b = (b_0, ..., b_{m-1}) with prod b_t = d.  Index i is written in
+# mixed-radix digits, i = sum_t i_t * stride_t with stride_t = prod_{s<t} b_s
+# and 0 <= i_t < b_t.  Stage t applies one b_t x b_t block to each group of
+# coordinates that differ only in digit t; the group index c is i with digit
+# t deleted: c = (i mod stride_t) + stride_t * (i div (stride_t * b_t)).
+# Each block is B_{t,c} = Q_{t,c}(theta) G_{b_t}: G the fixed base mixer
+# (normalised Sylvester Hadamard for powers of two, else the Q factor of a
+# fixed Gaussian matrix), Q the Givens rotation for b_t = 2 and the Cayley
+# map of a skew-symmetric parameter for b_t > 2, so theta = 0 gives B = G.
+# F = B_{m-1} ... B_0 D, and the all-2 schedule is the radix-2 butterfly
+# above.  Blocks are stored row-major: output r = sum_j B[r][j] input j.
+
+
+def strides(radices) -> list:
+    out, acc = [], 1
+    for b in radices:
+        out.append(acc)
+        acc *= b
+    return out
+
+
+def cayley(A: np.ndarray) -> np.ndarray:
+    """Q = (I - A)(I + A)^-1 for a skew-symmetric A (orthogonal, Q(0) = I)."""
+    A = np.asarray(A, dtype=np.float64)
+    if not np.allclose(A, -A.T, atol=0, rtol=0):
+        raise ValueError("A must be skew-symmetric")
+    I = np.eye(A.shape[0])
+    return (I - A) @ np.linalg.inv(I + A)
+
+
+def skew_from_params(p: np.ndarray, b: int) -> np.ndarray:
+    """Skew-symmetric b x b matrix from its b(b-1)/2 upper-triangle entries
+    (row-major order): A[r][c] = p_k for r < c, A[c][r] = -p_k."""
+    p = np.asarray(p, dtype=np.float64)
+    if p.shape != (b * (b - 1) // 2,):
+        raise ValueError("need b(b-1)/2 parameters")
+    A = np.zeros((b, b))
+    iu = np.triu_indices(b, 1)
+    A[iu] = p
+    return A - A.T
+
+
+def qr_mixer(b: int, seed: int) -> np.ndarray:
+    """Q factor of a fixed b x b Gaussian (numpy default_rng(seed)), with the
+    sign of each column chosen so that R has a positive diagonal (the unique
+    QR factorisation)."""
+    g = np.random.default_rng(seed).normal(size=(b, b))
+    q, r = np.linalg.qr(g)
+    return q * np.sign(np.diag(r))[None, :]
+
+
+def base_mixer(b: int, seed: int) -> np.ndarray:
+    """G_b: normalised Sylvester Hadamard for powers of two, else qr_mixer."""
+    if b & (b - 1) == 0:
+        return sylvester_hadamard(b) / np.sqrt(b)
+    return qr_mixer(b, seed)
+
+
+def mixed_blocks(radices, params, mixer_seed: int = 0) -> list:
+    """Expand the learnable parameters into blocks, one array per stage.
+
+    params[t]: shape (d / b_t, b_t (b_t - 1) / 2): per group, the Givens
+    angle phi (b_t = 2) or the upper triangle of the Cayley parameter
+    (b_t > 2).  Returns [t] -> (d / b_t, b_t, b_t) float64 blocks
+    B = Q(theta) G_{b_t}; the QR mixer of radix b uses seed mixer_seed + b.
+    """
+    d = int(np.prod(radices))
+    out = []
+    for t, b in enumerate(radices):
+        G = base_mixer(b, mixer_seed + b)
+        P = np.asarray(params[t], dtype=np.float64)
+        if P.shape != (d // b, b * (b - 1) // 2):
+            raise ValueError(f"stage {t}: params must have shape {(d // b, b * (b - 1) // 2)}")
+        blocks = np.empty((d // b, b, b))
+        for c in range(d // b):
+            if b == 2:
+                phi = P[c, 0]
+                Q = np.array([[np.cos(phi), -np.sin(phi)], [np.sin(phi), np.cos(phi)]])
+            else:
+                Q = cayley(skew_from_params(P[c], b))
+            blocks[c] = Q @ G
+        out.append(blocks)
+    return out
+
+
+def _mixed_stage(u: np.ndarray, blocks: np.ndarray, stride: int, b: int,
+                 transpose: bool) -> np.ndarray:
+    """Apply stage blocks (d/b, b, b) along the digit of stride `stride`."""
+    d = u.shape[-1]
+    lead = u.shape[:-1]
+    # view: [hi][digit][lo] with lo < stride; group c = lo + stride * hi
+    v = u.reshape(lead + (d // (stride * b), b, stride))
+    Bm = blocks.reshape(d // (stride * b), stride, b, b)     # [hi][lo][r][j]
+    if transpose:
+        Bm = np.swapaxes(Bm, -1, -2)
+    out = np.einsum("hlrj,...hjl->...hrl", Bm, v)
+    return out.reshape(u.shape)
+
+
+def mixed_forward(x: np.ndarray, radices, blocks, sign_bits) -> np.ndarray:
+    """F x = B_{m-1} ... B_0 D x on the last axis (length prod radices)."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    if int(np.prod(radices)) != d:
+        raise ValueError("radices must multiply to the dimension")
+    u = x * decode_signs(sign_bits, d)
+    for t, (b, st) in enumerate(zip(radices, strides(radices))):
+        u = _mixed_stage(u, np.asarray(blocks[t], dtype=np.float64), st, b, False)
+    return u
+
+
+def mixed_transpose(y: np.ndarray, radices, blocks, sign_bits) -> np.ndarray:
+    """F^T y = D B_0^T ... B_{m-1}^T y (blocks transposed, stages reversed)."""
+    y = np.asarray(y, dtype=np.float64)
+    d = y.shape[-1]
+    if int(np.prod(radices)) != d:
+        raise ValueError("radices must multiply to the dimension")
+    u = y
+    for t in reversed(range(len(radices))):
+        u = _mixed_stage(u, np.asarray(blocks[t], dtype=np.float64),
+                         strides(radices)[t], radices[t], True)
+    return u * decode_signs(sign_bits, d)
 
 
 # ---------------------------------------------------------------------------

@@ -9,6 +9,10 @@ its boundary format:
 * rotation: per side, float32 (cos t, sin t) with t = pi/4 + N(0, var 0.05)
   per stage and block (pi/4 is the Hadamard initialisation of the page's
   zero-initialised Givens angle), and a random sign bitmask;
+* mixed-radix rotation: per stage and group the learnable parameters
+  (Givens angle or Cayley upper triangle) drawn as N(0, 0.1^2) around the
+  zero initialisation, and a random sign bitmask (the blocks themselves are
+  an offline expansion of these parameters);
 * int8-stored rotation: the same angle spread drawn directly as int8 codes
   (a normal rounded to integers, clipped to [-127, 127]) with one float32
   step per side chosen so that +-127 codes span +-4 standard deviations;
@@ -158,6 +162,25 @@ def rotation_q8(dim: int, block: int, rng, theta_var: float = THETA_VAR,
     if codes.shape != (dim // block, L, block // 2):
         raise ValueError("codes must have shape [dim/b][log2 b][b/2]")
     return Rotation(dim, block, None, _sign_bits(dim, rng), None, codes, float(step))
+
+
+@dataclass
+class MixedRotation:
+    """One side with a mixed-radix schedule: learnable parameters per stage
+    and group (Givens angle for radix 2, the b(b-1)/2 upper-triangle entries
+    of the Cayley parameter otherwise) and a random sign bitmask."""
+    dim: int
+    radices: tuple
+    params: list            # [t] -> float64 (dim / b_t, b_t (b_t - 1) / 2)
+    sign_bits: np.ndarray
+
+
+def mixed_rotation(radices, rng, scale: float = 0.1) -> MixedRotation:
+    """Draw the parameters as N(0, scale^2) around the zero initialisation."""
+    radices = tuple(int(b) for b in radices)
+    dim = int(np.prod(radices))
+    params = [rng.normal(0.0, scale, size=(dim // b, b * (b - 1) // 2)) for b in radices]
+    return MixedRotation(dim, radices, params, _sign_bits(dim, rng))
 
 
 @dataclass

@@ -62,3 +62,13 @@ def test_int8_angle_codes():
     std = (c * a.V.phi_step).std()
     assert abs(std - np.sqrt(S.THETA_VAR)) < 0.02
     assert np.float32(a.V.phi_step) == a.V.phi_step
+
+
+def test_mixed_rotation_parameters():
+    a = S.mixed_rotation((8, 8, 8, 5, 2), np.random.default_rng(5))
+    b = S.mixed_rotation((8, 8, 8, 5, 2), np.random.default_rng(5))
+    assert a.dim == 5120 and len(a.params) == 5
+    assert a.params[0].shape == (640, 28) and a.params[3].shape == (1024, 10)
+    assert a.params[4].shape == (2560, 1)
+    assert all(np.array_equal(p, q) for p, q in zip(a.params, b.params))
+    assert a.sign_bits.shape == (160,)
