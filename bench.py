@@ -192,6 +192,8 @@ def main():
                     help="skip the M=16 batched-decode leg")
     ap.add_argument("--no-prep", action="store_true",
                     help="skip the offline-preparation leg")
+    ap.add_argument("--no-mixed", action="store_true",
+                    help="skip the mixed-radix rotation leg")
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graph")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (the known-size "
@@ -352,6 +354,34 @@ def main():
             torch.cuda.empty_cache()
         log("batched decode: " + json.dumps(batched))
 
+    # mixed-radix rotation (full-width schedules instead of block-diagonal 256)
+    mixed = None
+    if not args.no_mixed:
+        import numpy as np
+        mixed = {"workload": "harp_rotate_in_mixed, bf16 x -> float32 x~, random orthogonal "
+                             "blocks (float32) per stage and group"}
+        for radices in ((8, 8, 8, 5, 2), (8, 8, 4, 43), (8, 8, 8, 8, 3), (8, 8, 8, 8, 7)):
+            dim = int(np.prod(radices))
+            nblk = sum(dim * b for b in radices)
+            R = H.MixedRotation(torch.randn(nblk, device="cuda") * 0.1,
+                                torch.zeros((dim + 31) // 32, dtype=torch.int32, device="cuda"),
+                                radices)
+            entry = {}
+            for M in (1, 512):
+                xs = [torch.randn((M, dim), device="cuda").to(torch.bfloat16) for _ in range(8)]
+                outs = [torch.empty((M, dim), device="cuda") for _ in range(8)]
+                ms, _ = time_graph(torch, lambda: [H.harp_rotate_in_mixed(R, a, o)
+                                                   for a, o in zip(xs, outs)], 5)
+                us = ms * 1e3 / 8
+                nb = 4 * nblk + dim // 8 + 6 * M * dim
+                entry[f"M{M}_us"] = round(us, 2)
+                entry[f"M{M}_GB_s"] = round(nb / (us * 1e-6) / 1e9, 1)
+                del xs, outs
+            mixed["x".join(str(b) for b in radices)] = entry
+            del R
+            torch.cuda.empty_cache()
+        log("mixed radix: " + json.dumps(mixed))
+
     # offline preparation: W' = F_U W F_V^T, then quantize and pack (2-bit)
     prep = None
     if not args.no_prep:
@@ -437,6 +467,7 @@ def main():
         "kernels": kern,
         "int8_angles": q8,
         "batched_decode": batched,
+        "mixed_radix": mixed,
         "offline_prep": prep,
         "prefill": prefill,
         "cpu_baseline": cpu,

@@ -108,6 +108,35 @@ typedef struct harp_rotation {
 } harp_rotation;
 
 /*
+ * One side with a mixed-radix schedule (technical summary §2.1: stage t
+ * applies a block-diagonal orthogonal matrix to groups of coordinates a
+ * stride apart; radices need not be powers of two, e.g. 5120 = 8*8*8*5*2).
+ *   dim        prod radix[0 .. n_stages-1], at most HARP_MAX_MIXED_DIM
+ *   n_stages   1 .. HARP_MAX_STAGES;  radix[t] in 2 .. HARP_MAX_RADIX
+ *   blocks     float32, the stages one after the other; stage t holds
+ *              [dim / b_t][b_t][b_t] row-major blocks B (output r =
+ *              sum_j B[r][j] input j) for the groups c = (i mod s_t) +
+ *              s_t (i div (s_t b_t)) of the coordinates i that differ only in
+ *              mixed-radix digit t, s_t = b_0 ... b_{t-1}.  The blocks are
+ *              the expanded learnable blocks Q(theta) G_{b_t} (technical
+ *              summary §2.2: Cayley map times the fixed mixer, or the QR
+ *              factor of a fixed Gaussian for radices that are not powers of
+ *              two); the library only applies them.
+ *   sign_bits  [ceil(dim/32)] uint32: bit i set means D_ii = -1
+ * Device pointers owned by the caller, 16-byte aligned, only read.
+ */
+#define HARP_MAX_STAGES 16
+#define HARP_MAX_RADIX 64
+#define HARP_MAX_MIXED_DIM 32768
+typedef struct harp_mixed_rotation {
+  int32_t dim;
+  int32_t n_stages;
+  int32_t radix[HARP_MAX_STAGES];
+  const float *blocks;
+  const uint32_t *sign_bits;
+} harp_mixed_rotation;
+
+/*
  * Packed low-bit weight W_hat [N][K] (out x in).
  *   bits     2, 3 or 4;  group must be 64;  K % 64 == 0
  *   qweight  [N][K*bits/32] uint32.  bits 2 and 4: code k in word k/(32/bits)
@@ -145,6 +174,20 @@ harp_status harp_rotate_in(const harp_rotation *V, const void *x,
  */
 harp_status harp_rotate_out(const harp_rotation *U, const float *yt, void *y,
                             harp_dtype y_dt, int32_t M, harp_stream stream);
+
+/*
+ * x~ = F x (stages 0 .. m-1 after the sign flip) and y = F^T y' (transposed
+ * blocks, stages m-1 .. 0, then the sign flip) for M rows of a mixed-radix
+ * side; float32 arithmetic, a bf16 output rounds to nearest even.
+ *   x  [M][dim] of x_dt;  xt [M][dim] of xt_dt;  yt [M][dim] float32;
+ *   y  [M][dim] of y_dt.
+ */
+harp_status harp_rotate_in_mixed(const harp_mixed_rotation *R, const void *x,
+                                 harp_dtype x_dt, void *xt, harp_dtype xt_dt,
+                                 int32_t M, harp_stream stream);
+harp_status harp_rotate_out_mixed(const harp_mixed_rotation *R, const float *yt,
+                                  void *y, harp_dtype y_dt, int32_t M,
+                                  harp_stream stream);
 
 /*
  * y'[m][n] = sum_k w_hat[n][k] x~[m][k] on the vector ALUs, float32

@@ -34,6 +34,7 @@ EXPORTED = (
     "harp_deq_gemm",
     "harp_deq_gemm_workspace_bytes", "harp_linear_workspace_bytes", "harp_linear_fused", "harp_dequant",
     "harp_rotate_weight", "harp_rotate_weight_workspace_bytes", "harp_quantize_pack",
+    "harp_rotate_in_mixed", "harp_rotate_out_mixed",
     "harp_status_string", "harp_last_hip_error",
 )
 
@@ -54,6 +55,14 @@ class harp_rotation(ctypes.Structure):
                 ("phi_codes", c_void_p), ("phi_step", c_float)]
 
 
+HARP_MAX_STAGES = 16
+
+
+class harp_mixed_rotation(ctypes.Structure):
+    _fields_ = [("dim", c_int32), ("n_stages", c_int32), ("radix", c_int32 * HARP_MAX_STAGES),
+                ("blocks", c_void_p), ("sign_bits", c_void_p)]
+
+
 class harp_qweight(ctypes.Structure):
     _fields_ = [("N", c_int32), ("K", c_int32), ("bits", c_int32),
                 ("group", c_int32), ("qweight", c_void_p), ("scale", c_void_p),
@@ -72,6 +81,7 @@ def _load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     R = ctypes.POINTER(harp_rotation)
     Q = ctypes.POINTER(harp_qweight)
+    MR = ctypes.POINTER(harp_mixed_rotation)
     sig = {
         "harp_rotate_in": (c_int32, [R, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p]),
         "harp_rotate_out": (c_int32, [R, c_void_p, c_void_p, c_int32, c_int32, c_void_p]),
@@ -88,6 +98,9 @@ def _load() -> ctypes.CDLL:
         "harp_rotate_weight": (c_int32, [R, R, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
                                           c_size_t, c_void_p]),
         "harp_rotate_weight_workspace_bytes": (c_size_t, [c_int32, c_int32]),
+        "harp_rotate_in_mixed": (c_int32, [MR, c_void_p, c_int32, c_void_p, c_int32, c_int32,
+                                            c_void_p]),
+        "harp_rotate_out_mixed": (c_int32, [MR, c_void_p, c_void_p, c_int32, c_int32, c_void_p]),
         "harp_quantize_pack": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p,
                                           c_void_p, c_void_p]),
         "harp_status_string": (c_char_p, [c_int32]),
@@ -157,6 +170,23 @@ class Rotation:
                                float(phi_step))
 
 
+class MixedRotation:
+    """A mixed-radix side: blocks float32 (stages concatenated, stage t
+    [dim/b_t][b_t][b_t] row-major), sign_bits int32/uint32 [ceil(dim/32)]."""
+
+    def __init__(self, blocks, sign_bits, radices):
+        radices = [int(b) for b in radices]
+        if len(radices) > HARP_MAX_STAGES:
+            raise ValueError("too many stages")
+        self.blocks, self.sign_bits, self.radices = blocks, sign_bits, radices
+        self.dim = 1
+        for b in radices:
+            self.dim *= b
+        arr = (c_int32 * HARP_MAX_STAGES)(*(radices + [0] * (HARP_MAX_STAGES - len(radices))))
+        self.c = harp_mixed_rotation(self.dim, len(radices), arr, blocks.data_ptr(),
+                                     sign_bits.data_ptr())
+
+
 class QWeight:
     """Packed weight: qweight int32 [N][K*bits/32], scale/zero int16 or fp16 [N][K/64]."""
 
@@ -222,6 +252,18 @@ def harp_linear_fused(V: Rotation, W: QWeight, U: Rotation, x, y, workspace,
 def harp_dequant(W: QWeight, out, stream=None) -> None:
     _check(lib.harp_dequant(ctypes.byref(W.c), _ptr(out), _dtype_code(out), _stream(stream)),
            "harp_dequant")
+
+
+def harp_rotate_in_mixed(R: MixedRotation, x, xt, M: int | None = None, stream=None) -> None:
+    M = x.shape[0] if M is None else M
+    _check(lib.harp_rotate_in_mixed(ctypes.byref(R.c), _ptr(x), _dtype_code(x), _ptr(xt),
+                                    _dtype_code(xt), M, _stream(stream)), "harp_rotate_in_mixed")
+
+
+def harp_rotate_out_mixed(R: MixedRotation, yt, y, M: int | None = None, stream=None) -> None:
+    M = yt.shape[0] if M is None else M
+    _check(lib.harp_rotate_out_mixed(ctypes.byref(R.c), _ptr(yt), _ptr(y), _dtype_code(y), M,
+                                     _stream(stream)), "harp_rotate_out_mixed")
 
 
 def harp_rotate_weight_workspace_bytes(N: int, K: int) -> int:

@@ -4,6 +4,7 @@
 // batch range, data pointers (NULL when M > 0), alignment, workspace.
 #include "validate.hpp"
 
+#include <algorithm>
 #include <cmath>
 
 namespace harp {
@@ -163,6 +164,26 @@ harp_status validate_quantize_pack(const float* Wp, int32_t N, int32_t K, int32_
 size_t rotate_weight_workspace_bytes(int32_t N, int32_t K) {
   if (N < 1 || K < 1 || N > HARP_MAX_M || K > HARP_MAX_M) return 0;
   return align256(static_cast<size_t>(N) * K * 4);
+}
+
+harp_status validate_rotate_mixed(const harp_mixed_rotation* R, const void* in, int in_dt,
+                                  const void* out, int out_dt, int32_t M) {
+  if (R == nullptr || R->blocks == nullptr || R->sign_bits == nullptr) return HARP_ERR_NULL;
+  if (R->n_stages < 1 || R->n_stages > HARP_MAX_STAGES) return HARP_ERR_SHAPE;
+  int64_t prod = 1;                 // capped: 16 radices of 64 would overflow
+  for (int t = 0; t < R->n_stages; ++t) {
+    if (R->radix[t] > HARP_MAX_RADIX) return HARP_ERR_UNSUPPORTED;
+    if (R->radix[t] < 2) return HARP_ERR_SHAPE;
+    prod = std::min<int64_t>(prod * R->radix[t], int64_t{HARP_MAX_MIXED_DIM} + 1);
+  }
+  if (R->dim > HARP_MAX_MIXED_DIM) return HARP_ERR_UNSUPPORTED;
+  if (R->dim < 2 || prod != R->dim) return HARP_ERR_SHAPE;
+  if (!aligned(R->blocks, 16) || !aligned(R->sign_bits, 16)) return HARP_ERR_ALIGN;
+  if (bad_dtype(in_dt) || bad_dtype(out_dt)) return HARP_ERR_DTYPE;
+  HARP_TRY(check_m(M));
+  HARP_TRY(check_data(in, M));
+  HARP_TRY(check_data(out, M));
+  return HARP_OK;
 }
 
 harp_status validate_dequant(const harp_qweight* W, const void* out, int out_dt) {

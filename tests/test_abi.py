@@ -285,3 +285,36 @@ def test_quantize_pack_checks():
     assert call(Wp=0) == L.HARP_ERR_NULL
     assert call(z=0) == L.HARP_ERR_NULL
     assert call(q=MISALIGNED) == L.HARP_ERR_ALIGN
+
+
+def mixed(dim=40, radices=(8, 5), blocks=FAKE, sb=FAKE, n=None):
+    arr = (ctypes.c_int32 * L.HARP_MAX_STAGES)(*(list(radices) + [0] * (16 - len(radices))))
+    return L.harp_mixed_rotation(dim, len(radices) if n is None else n, arr, blocks, sb)
+
+
+@pytest.mark.parametrize("R,expect", [
+    (mixed(blocks=0), L.HARP_ERR_NULL),
+    (mixed(sb=0), L.HARP_ERR_NULL),
+    (mixed(n=0), L.HARP_ERR_SHAPE),
+    (mixed(n=17), L.HARP_ERR_SHAPE),
+    (mixed(dim=40, radices=(8, 1, 5)), L.HARP_ERR_SHAPE),
+    (mixed(dim=65 * 2, radices=(65, 2)), L.HARP_ERR_UNSUPPORTED),
+    (mixed(dim=41), L.HARP_ERR_SHAPE),                       # product 40
+    (mixed(dim=65536, radices=(64, 64, 16)), L.HARP_ERR_UNSUPPORTED),
+    (mixed(blocks=MISALIGNED), L.HARP_ERR_ALIGN),
+])
+def test_mixed_rotation_checks(R, expect):
+    assert L.lib.harp_rotate_in_mixed(ctypes.byref(R), FAKE, 0, FAKE, 0, 1, None) == expect
+
+
+def test_mixed_rotation_other_checks():
+    R = mixed()
+    f_in, f_out = L.lib.harp_rotate_in_mixed, L.lib.harp_rotate_out_mixed
+    assert f_in(None, FAKE, 0, FAKE, 0, 1, None) == L.HARP_ERR_NULL
+    assert f_in(ctypes.byref(R), FAKE, 7, FAKE, 0, 1, None) == L.HARP_ERR_DTYPE
+    assert f_in(ctypes.byref(R), FAKE, 0, FAKE, 0, -2, None) == L.HARP_ERR_SHAPE
+    assert f_in(ctypes.byref(R), 0, 0, FAKE, 0, 1, None) == L.HARP_ERR_NULL
+    assert f_in(ctypes.byref(R), 0, 0, 0, 0, 0, None) == L.HARP_OK
+    assert f_out(ctypes.byref(R), FAKE, FAKE, 9, 1, None) == L.HARP_ERR_DTYPE
+    assert f_out(ctypes.byref(R), FAKE, MISALIGNED, 0, 1, None) == L.HARP_ERR_ALIGN
+    assert f_out(ctypes.byref(R), 0, 0, 0, 0, None) == L.HARP_OK

@@ -1,0 +1,101 @@
+"""GPU parity of the mixed-radix rotation (HARP technical summary §2.1-2.2)
+against the float64 oracle: the pages' 5120 = 8*8*8*5*2 schedule, the
+layer dimensions of the workloads as mixed-radix products (11008, 12288,
+28672), power-of-two and tiny odd schedules, both directions, float32 and
+bf16.  The blocks are the oracle's offline expansion of seeded parameters
+(Cayley map, QR mixers), rounded to float32 for the device; the oracle
+applies the same float32 blocks.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+from oracle import harp_oracle as O
+from synth import workloads as S
+
+pytestmark = pytest.mark.gpu
+
+BUTTERFLY_TOL = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rotated_bit_amd  # noqa: F401
+    yield
+
+
+def H():
+    import rotated_bit_amd
+    return rotated_bit_amd
+
+
+def D():
+    import devbuf
+    return devbuf
+
+
+def rng(*k):
+    return np.random.default_rng(np.random.SeedSequence([3131, *k]))
+
+
+def device_side(radices, seed, zero=False):
+    side = S.mixed_rotation(radices, rng(1, seed))
+    params = [np.zeros_like(p) for p in side.params] if zero else side.params
+    blocks32 = [b.astype(np.float32) for b in O.mixed_blocks(radices, params, mixer_seed=seed)]
+    flat = np.concatenate([b.ravel() for b in blocks32])
+    R = H().MixedRotation(D().dev(flat), D().dev(side.sign_bits), radices)
+    return R, blocks32, side.sign_bits
+
+
+CASES = [
+    ((8, 8, 8, 5, 2), 1, "bf16"), ((8, 8, 8, 5, 2), 17, "f32"), ((8, 8, 4, 43), 2, "bf16"),
+    ((16, 16, 16, 3), 3, "bf16"), ((64, 64, 7), 2, "bf16"), ((2,) * 12, 5, "f32"),
+    ((5, 3), 9, "f32"), ((3,), 4, "f32"), ((7, 2, 5, 3), 64, "bf16"), ((43, 4, 64), 1, "bf16"),
+]
+
+
+@pytest.mark.parametrize("radices,M,xdt", CASES)
+def test_rotate_mixed_in_out(radices, M, xdt):
+    d = D()
+    R, blocks, signs = device_side(radices, 7)
+    dim = R.dim
+    x = S.activations(M, dim, rng(2, dim, M), xdt)
+    xt = torch.empty((M, dim), dtype=torch.float32, device="cuda")
+    H().harp_rotate_in_mixed(R, d.dev_x(x, xdt), xt)
+    ref = O.mixed_forward(d.x_f64(x, xdt), radices, blocks, signs)
+    r = O.rel_l2(d.host(xt), ref)
+    print(f"[mixed in {radices} M={M}] rel_l2={r:.3e}", flush=True)
+    assert r <= BUTTERFLY_TOL
+    yp = rng(3, dim, M).normal(size=(M, dim)).astype(np.float32)
+    y = torch.empty((M, dim), dtype=torch.float32, device="cuda")
+    H().harp_rotate_out_mixed(R, d.dev(yp), y)
+    reft = O.mixed_transpose(yp.astype(np.float64), radices, blocks, signs)
+    r = O.rel_l2(d.host(y), reft)
+    print(f"[mixed out {radices} M={M}] rel_l2={r:.3e}", flush=True)
+    assert r <= BUTTERFLY_TOL
+    # bf16 output rounds the float32 result
+    yb = torch.empty((M, dim), dtype=torch.bfloat16, device="cuda")
+    H().harp_rotate_out_mixed(R, d.dev(yp), yb)
+    refb = O.bf16_round(reft)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(refb))[1] - 8)
+    delta = BUTTERFLY_TOL * np.sqrt(np.mean(reft ** 2))
+    assert np.all(np.abs(d.host(yb) - refb) <= ulp + delta)
+
+
+@pytest.mark.parametrize("radices", [(4, 4, 4, 4, 4, 4), (16, 8, 32)])
+def test_rotate_mixed_zero_parameters_is_hadamard(radices):
+    """theta = 0 with power-of-two radices: F x = H_d D x / sqrt(d) (scipy)."""
+    d = D()
+    R, _, signs = device_side(radices, 11, zero=True)
+    dim = R.dim
+    x = rng(4, dim).normal(size=(2, dim)).astype(np.float32)
+    xt = torch.empty((2, dim), dtype=torch.float32, device="cuda")
+    H().harp_rotate_in_mixed(R, d.dev(x), xt)
+    Hd = scipy.linalg.hadamard(dim) / math.sqrt(dim)
+    ref = (x.astype(np.float64) * O.decode_signs(signs, dim)) @ Hd.T
+    assert O.rel_l2(d.host(xt), ref) <= BUTTERFLY_TOL
