@@ -6,20 +6,27 @@
 // F = B_{m-1} ... B_0 D; F^T = D B_0^T ... B_{m-1}^T.  Blocks arrive expanded
 // (Q(theta) G_{b_t}, row-major: output r = sum_j B[r][j] input j).
 //
-// gfx950 mapping.  One workgroup of 512 threads owns one row, held in LDS as
-// float32 (d <= 32768: at most 128 KB).  A stage gives each thread whole
-// groups: it reads the group's b_t coordinates into registers, forms the
-// b_t outputs from the group's block (read from global memory, where the
-// L2 keeps it for the other rows), and writes them back in place; one
-// barrier per stage.  The register arrays are sized by the next power of two
-// of the radix, a compile-time bound chosen per stage.
+// gfx950 mapping.  Batches: one workgroup of 512 threads owns one row, held
+// in LDS as float32 (d <= 32768: at most 128 KB), one barrier per stage.  A
+// group of radix b takes the next power of two of b lanes of one wave, lane
+// r forming output r from the group's inputs and row (or column) r of its
+// block, so that a wave's coefficient loads are contiguous.  The blocks
+// stream from global memory, where the L2 keeps them for the other rows.  Small batches with a float32 output run one launch per stage
+// instead, spread over the whole chip, in place in the output (a group's
+// inputs and outputs are the same coordinates, and groups are disjoint),
+// so that the blocks of a single row are not fetched by one CU.  Register
+// arrays are sized by the next power of two of the radix, a compile-time
+// bound chosen per stage.
 #include "launch.hpp"
 #include "device_common.hpp"
+
+#include <type_traits>
 
 namespace harp {
 namespace {
 
 constexpr int kMixedThreads = 512;
+constexpr int kByStageMaxM = 16;   // batches up to this size run stage by stage
 
 struct MixedPlan {
   int dim;
@@ -34,29 +41,56 @@ __device__ __forceinline__ float load_elem(const uint16_t* p, size_t i) { return
 __device__ __forceinline__ void store_elem(float* p, size_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void store_elem(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
 
-// One stage on the LDS row u: groups c = tid, tid + T, ...  BMAX >= b.
+// Lane mapping of a stage: BMAX lanes per group (BMAX the next power of two
+// of the radix b, at most one wave), lane r of a group forming output r from
+// all b inputs of the group and row r of its block (column r for F^T).
+// Neighbouring lanes then read neighbouring block rows (or columns), so the
+// coefficient loads of a wave are contiguous.
+template <int BMAX>
+struct StageLanes {
+  static constexpr int PER_WAVE = kWave / BMAX;   // groups per wave
+  int sub, r;                                     // group slot in the wave, output row
+  __device__ explicit StageLanes(int lane) : sub(lane / BMAX), r(lane % BMAX) {}
+};
+
+template <int BMAX, bool TRANSPOSE>
+__device__ __forceinline__ float block_dot(const float* __restrict__ B, int b, int r,
+                                           const float (&xin)[BMAX]) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int j = 0; j < BMAX; ++j) {
+    if (j < b) {
+      const float coef = TRANSPOSE ? B[j * b + r] : B[r * b + j];
+      acc = fmaf(coef, xin[j], acc);
+    }
+  }
+  return acc;
+}
+
+// One stage on the LDS row u (one workgroup per row).
 template <int BMAX, bool TRANSPOSE>
 __device__ __forceinline__ void mixed_stage(float* u, const float* __restrict__ blk, int dim,
                                             int b, int stride) {
+  const StageLanes<BMAX> ln(threadIdx.x & (kWave - 1));
+  const int wave = threadIdx.x >> 6;
   const int groups = dim / b;
-  for (int c = threadIdx.x; c < groups; c += kMixedThreads) {
-    const int lo = c % stride;
-    const int hi = c / stride;
+  constexpr int kUnits = (kMixedThreads / kWave) * StageLanes<BMAX>::PER_WAVE;
+  // every group of a wave is read before any is written (one wave, program
+  // order; the groups of a wave are disjoint from other waves' groups)
+  for (int c0 = wave * StageLanes<BMAX>::PER_WAVE; c0 < groups; c0 += kUnits) {
+    const int c = c0 + ln.sub;
+    const bool act = c < groups && ln.r < b;
+    const int cc = min(c, groups - 1);
+    const int lo = cc % stride;
+    const int hi = cc / stride;
     const int base = lo + hi * stride * b;
     float xin[BMAX];
 #pragma unroll
     for (int j = 0; j < BMAX; ++j) xin[j] = j < b ? u[base + j * stride] : 0.0f;
-    const float* B = blk + static_cast<size_t>(c) * b * b;
-    for (int r = 0; r < b; ++r) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int j = 0; j < BMAX; ++j) {
-        if (j < b) {
-          const float coef = TRANSPOSE ? B[j * b + r] : B[r * b + j];
-          acc = fmaf(coef, xin[j], acc);
-        }
-      }
-      u[base + r * stride] = acc;
+    if (act) {
+      const float acc = block_dot<BMAX, TRANSPOSE>(blk + static_cast<size_t>(c) * b * b, b,
+                                                   ln.r, xin);
+      u[base + ln.r * stride] = acc;
     }
   }
 }
@@ -69,6 +103,47 @@ __device__ __forceinline__ void run_stage(float* u, const float* blk, int dim, i
   else if (b <= 16) mixed_stage<16, TRANSPOSE>(u, blk, dim, b, stride);
   else if (b <= 32) mixed_stage<32, TRANSPOSE>(u, blk, dim, b, stride);
   else mixed_stage<64, TRANSPOSE>(u, blk, dim, b, stride);
+}
+
+// One stage over global memory for small batches: row blockIdx.y, groups
+// spread over blockIdx.x.  src is the input of the first stage (sign flip
+// on read for the forward map) or dst itself; the last stage of the
+// transposed map flips signs on write.
+template <int BMAX, bool TRANSPOSE, typename TIn>
+__global__ __launch_bounds__(kMixedThreads) void mixed_stage_kernel(
+    const TIn* src, float* dst, const float* __restrict__ blk,
+    const uint32_t* __restrict__ sign, int dim, int b, int stride, int sign_in, int sign_out) {
+  const size_t row = blockIdx.y;
+  const TIn* s = src + row * dim;
+  float* d = dst + row * dim;
+  const int groups = dim / b;
+  const StageLanes<BMAX> ln(threadIdx.x & (kWave - 1));
+  const int c = (blockIdx.x * (kMixedThreads / kWave) + (threadIdx.x >> 6)) *
+                    StageLanes<BMAX>::PER_WAVE + ln.sub;
+  const bool act = c < groups && ln.r < b;
+  const int cc = min(c, groups - 1);
+  const int lo = cc % stride;
+  const int hi = cc / stride;
+  const int base = lo + hi * stride * b;
+  float xin[BMAX];
+#pragma unroll
+  for (int j = 0; j < BMAX; ++j) {
+    float v = 0.0f;
+    if (j < b) {
+      const int i = base + j * stride;
+      v = load_elem(s, i);
+      if (sign_in) v = flip_sign(v, (sign[i >> 5] >> (i & 31)) & 1u);
+    }
+    xin[j] = v;
+  }
+  // in place (src == dst) is safe: a wave reads all of its groups before
+  // writing, and groups are disjoint
+  if (act) {
+    const float acc = block_dot<BMAX, TRANSPOSE>(blk + static_cast<size_t>(c) * b * b, b,
+                                                 ln.r, xin);
+    const int o = base + ln.r * stride;
+    d[o] = sign_out ? flip_sign(acc, (sign[o >> 5] >> (o & 31)) & 1u) : acc;
+  }
 }
 
 template <bool TRANSPOSE, typename TIn, typename TOut>
@@ -114,9 +189,65 @@ MixedPlan make_plan(const harp_mixed_rotation& R) {
   return p;
 }
 
+template <int BMAX, bool TRANSPOSE, typename TIn>
+hipError_t launch_stage_bmax(const TIn* src, float* dst, const float* blk, const uint32_t* sign,
+                             int dim, int b, int stride, int M, bool sign_in, bool sign_out,
+                             hipStream_t stream) {
+  const int groups = dim / b;
+  const int per_wg = (kMixedThreads / kWave) * StageLanes<BMAX>::PER_WAVE;
+  const dim3 grid((groups + per_wg - 1) / per_wg, M);
+  hipLaunchKernelGGL((mixed_stage_kernel<BMAX, TRANSPOSE, TIn>), grid, dim3(kMixedThreads), 0,
+                     stream, src, dst, blk, sign, dim, b, stride, sign_in ? 1 : 0,
+                     sign_out ? 1 : 0);
+  return hipGetLastError();
+}
+
+template <bool TRANSPOSE, typename TIn>
+hipError_t launch_stage(const TIn* src, float* dst, const float* blk, const uint32_t* sign,
+                        int dim, int b, int stride, int M, bool sign_in, bool sign_out,
+                        hipStream_t stream) {
+#define HARP_STAGE(BM) \
+  launch_stage_bmax<BM, TRANSPOSE, TIn>(src, dst, blk, sign, dim, b, stride, M, sign_in, \
+                                        sign_out, stream)
+  if (b <= 2) return HARP_STAGE(2);
+  if (b <= 4) return HARP_STAGE(4);
+  if (b <= 8) return HARP_STAGE(8);
+  if (b <= 16) return HARP_STAGE(16);
+  if (b <= 32) return HARP_STAGE(32);
+  return HARP_STAGE(64);
+#undef HARP_STAGE
+}
+
+// Small batch, float32 output: one launch per stage.
+template <bool TRANSPOSE, typename TIn>
+hipError_t launch_by_stage(const harp_mixed_rotation& R, const void* in, float* out, int M,
+                           hipStream_t stream) {
+  const MixedPlan plan = make_plan(R);
+  for (int q = 0; q < plan.n; ++q) {
+    const int t = TRANSPOSE ? plan.n - 1 - q : q;
+    const float* blk = R.blocks + plan.offset[t];
+    hipError_t e;
+    if (q == 0) {
+      e = launch_stage<TRANSPOSE, TIn>(static_cast<const TIn*>(in), out, blk, R.sign_bits,
+                                       plan.dim, plan.radix[t], plan.stride[t], M, !TRANSPOSE,
+                                       TRANSPOSE && plan.n == 1, stream);
+    } else {
+      e = launch_stage<TRANSPOSE, float>(out, out, blk, R.sign_bits, plan.dim, plan.radix[t],
+                                         plan.stride[t], M, false,
+                                         TRANSPOSE && q == plan.n - 1, stream);
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <bool TRANSPOSE, typename TIn, typename TOut>
 hipError_t launch_typed(const harp_mixed_rotation& R, const void* in, void* out, int M,
                         hipStream_t stream) {
+  if constexpr (std::is_same<TOut, float>::value) {
+    if (M <= kByStageMaxM)
+      return launch_by_stage<TRANSPOSE, TIn>(R, in, static_cast<float*>(out), M, stream);
+  }
   const MixedPlan plan = make_plan(R);
   const size_t shmem = sizeof(float) * static_cast<size_t>(R.dim);
   if (shmem > 65536) {   // rows above 16384 floats: raise the dynamic LDS limit
