@@ -6,27 +6,31 @@
 // F = B_{m-1} ... B_0 D; F^T = D B_0^T ... B_{m-1}^T.  Blocks arrive expanded
 // (Q(theta) G_{b_t}, row-major: output r = sum_j B[r][j] input j).
 //
-// gfx950 mapping.  Batches: one workgroup of 512 threads owns one row, held
-// in LDS as float32 (d <= 32768: at most 128 KB), one barrier per stage.  A
-// group of radix b takes the next power of two of b lanes of one wave, lane
-// r forming output r from the group's inputs and row (or column) r of its
-// block, so that a wave's coefficient loads are contiguous.  The blocks
-// stream from global memory, where the L2 keeps them for the other rows.  Small batches with a float32 output run one launch per stage
-// instead, spread over the whole chip, in place in the output (a group's
-// inputs and outputs are the same coordinates, and groups are disjoint),
-// so that the blocks of a single row are not fetched by one CU.  Register
-// arrays are sized by the next power of two of the radix, a compile-time
-// bound chosen per stage.
+// gfx950 mapping.  A group of radix b takes the next power of two of b
+// lanes of one wave, lane r forming output r from the group's inputs and
+// row (or column) r of its block, so that a wave's coefficient loads are
+// contiguous.  Float32 outputs run one launch per stage, in place in the
+// output (a group's inputs and outputs are the same coordinates, and groups
+// are disjoint), spread over the whole chip; each lane keeps its block row
+// in registers for a tile of rows.  bf16 outputs have no float32 buffer to
+// pass between stages: one workgroup of 512 threads owns one row, held in
+// LDS as float32 (d <= 32768: at most 128 KB), one barrier per stage, the
+// blocks streaming from global memory where the L2 keeps them for the other
+// rows.  Register arrays are sized by the next power of two of the radix, a
+// compile-time bound chosen per stage.
 #include "launch.hpp"
 #include "device_common.hpp"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace harp {
 namespace {
 
 constexpr int kMixedThreads = 512;
-constexpr int kByStageMaxM = 16;   // batches up to this size run stage by stage
+constexpr int kStageMaxRows = 32;     // rows per workgroup of a stage launch
+constexpr int kStageTargetWaves = 8192;  // waves a stage launch aims for
+constexpr int kStageWideM = 64;         // batches from this size use 8-wave workgroups
 
 struct MixedPlan {
   int dim;
@@ -53,18 +57,35 @@ struct StageLanes {
   __device__ explicit StageLanes(int lane) : sub(lane / BMAX), r(lane % BMAX) {}
 };
 
+// Lane r's coefficients: row r of the block B (b x b, row-major), or
+// column r for F^T; zero beyond b.  Neighbouring lanes of a column read
+// neighbouring floats.  A row is read as 16-byte vectors, which gfx950
+// loads from any 4-byte boundary, and a scalar tail of b mod 4 floats, so
+// that no load leaves the row.
 template <int BMAX, bool TRANSPOSE>
-__device__ __forceinline__ float block_dot(const float* __restrict__ B, int b, int r,
-                                           const float (&xin)[BMAX]) {
-  float acc = 0.0f;
+__device__ __forceinline__ void load_coef(const float* __restrict__ B, int b, int r,
+                                          float (&coef)[BMAX]) {
+  if constexpr (!TRANSPOSE && BMAX >= 4) {
+    const float* row = B + r * b;
 #pragma unroll
-  for (int j = 0; j < BMAX; ++j) {
-    if (j < b) {
-      const float coef = TRANSPOSE ? B[j * b + r] : B[r * b + j];
-      acc = fmaf(coef, xin[j], acc);
+    for (int j = 0; j < BMAX; j += 4) {
+      if (j + 4 <= b) {
+        float4 v;
+        __builtin_memcpy(&v, row + j, sizeof(v));
+        coef[j] = v.x;
+        coef[j + 1] = v.y;
+        coef[j + 2] = v.z;
+        coef[j + 3] = v.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) coef[j + i] = j + i < b ? row[j + i] : 0.0f;
+      }
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < BMAX; ++j)
+      coef[j] = j < b ? (TRANSPOSE ? B[j * b + r] : B[r * b + j]) : 0.0f;
   }
-  return acc;
 }
 
 // One stage on the LDS row u (one workgroup per row).
@@ -87,11 +108,20 @@ __device__ __forceinline__ void mixed_stage(float* u, const float* __restrict__ 
     float xin[BMAX];
 #pragma unroll
     for (int j = 0; j < BMAX; ++j) xin[j] = j < b ? u[base + j * stride] : 0.0f;
-    if (act) {
-      const float acc = block_dot<BMAX, TRANSPOSE>(blk + static_cast<size_t>(c) * b * b, b,
-                                                   ln.r, xin);
-      u[base + ln.r * stride] = acc;
+    const float* B = blk + static_cast<size_t>(cc) * b * b;
+    const int rr = min(ln.r, b - 1);
+    float acc = 0.0f;
+    if (!TRANSPOSE && b == BMAX) {   // whole aligned rows as vectors
+      float coef[BMAX];
+      load_coef<BMAX, TRANSPOSE>(B, b, rr, coef);
+#pragma unroll
+      for (int j = 0; j < BMAX; ++j) acc = fmaf(coef[j], xin[j], acc);
+    } else {
+#pragma unroll
+      for (int j = 0; j < BMAX; ++j)
+        if (j < b) acc = fmaf(TRANSPOSE ? B[j * b + rr] : B[rr * b + j], xin[j], acc);
     }
+    if (act) u[base + ln.r * stride] = acc;
   }
 }
 
@@ -105,44 +135,82 @@ __device__ __forceinline__ void run_stage(float* u, const float* blk, int dim, i
   else mixed_stage<64, TRANSPOSE>(u, blk, dim, b, stride);
 }
 
-// One stage over global memory for small batches: row blockIdx.y, groups
-// spread over blockIdx.x.  src is the input of the first stage (sign flip
-// on read for the forward map) or dst itself; the last stage of the
-// transposed map flips signs on write.
-template <int BMAX, bool TRANSPOSE, typename TIn>
-__global__ __launch_bounds__(kMixedThreads) void mixed_stage_kernel(
+// One stage over global memory: groups spread over blockIdx.x (WAVES waves
+// per workgroup), a tile of `rows` rows over blockIdx.y.  Lane (group slot, r) loads coordinate
+// o = base + r stride of each row, which is also the coordinate it writes,
+// so running in place needs no ordering between lanes.  The wave passes the
+// group's inputs through its own LDS slot (one wave: in-order LDS), and each
+// lane reads its group's b inputs back as vectors; its block row (column for
+// F^T) stays in registers for the whole tile.  src is the input of the first
+// stage (sign flip on read for the forward map) or dst itself; the last
+// stage of the transposed map flips signs on write.
+constexpr int kStageRB = 8;   // rows per load batch
+
+template <int BMAX>
+__device__ __forceinline__ void read_group(const float* p, float (&xin)[BMAX]) {
+  if constexpr (BMAX == 2) {
+    const float2 v = *reinterpret_cast<const float2*>(p);
+    xin[0] = v.x;
+    xin[1] = v.y;
+  } else {
+#pragma unroll
+    for (int j = 0; j < BMAX; j += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(p + j);
+      xin[j] = v.x;
+      xin[j + 1] = v.y;
+      xin[j + 2] = v.z;
+      xin[j + 3] = v.w;
+    }
+  }
+}
+
+template <int BMAX, int WAVES, bool TRANSPOSE, typename TIn>
+__global__ __launch_bounds__(WAVES * kWave) void mixed_stage_kernel(
     const TIn* src, float* dst, const float* __restrict__ blk,
-    const uint32_t* __restrict__ sign, int dim, int b, int stride, int sign_in, int sign_out) {
-  const size_t row = blockIdx.y;
-  const TIn* s = src + row * dim;
-  float* d = dst + row * dim;
+    const uint32_t* __restrict__ sign, int dim, int b, int stride, int M, int rows,
+    int sign_in, int sign_out) {
+  __shared__ __attribute__((aligned(16))) float xsw[WAVES][kStageRB][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  float (*xs)[kWave] = xsw[wave];
   const int groups = dim / b;
-  const StageLanes<BMAX> ln(threadIdx.x & (kWave - 1));
-  const int c = (blockIdx.x * (kMixedThreads / kWave) + (threadIdx.x >> 6)) *
-                    StageLanes<BMAX>::PER_WAVE + ln.sub;
+  const StageLanes<BMAX> ln(lane);
+  const int c = (blockIdx.x * WAVES + wave) * StageLanes<BMAX>::PER_WAVE + ln.sub;
   const bool act = c < groups && ln.r < b;
   const int cc = min(c, groups - 1);
+  const int rr = min(ln.r, b - 1);
   const int lo = cc % stride;
   const int hi = cc / stride;
-  const int base = lo + hi * stride * b;
-  float xin[BMAX];
+  const int o = lo + hi * stride * b + rr * stride;
+  const float* B = blk + static_cast<size_t>(cc) * b * b;
+  float coef[BMAX];
+  load_coef<BMAX, TRANSPOSE>(B, b, rr, coef);
+  const uint32_t sgn = (sign[o >> 5] >> (o & 31)) & 1u;
+  const uint32_t sgn_in = sign_in ? sgn : 0u;
+  const uint32_t sgn_out = sign_out ? sgn : 0u;
+  const float* grp = &xs[0][ln.sub * BMAX];
+
+  const int m0 = blockIdx.y * rows;
+  const int m1 = min(M, m0 + rows);
+  for (int mb = m0; mb < m1; mb += kStageRB) {
+    float v[kStageRB];
 #pragma unroll
-  for (int j = 0; j < BMAX; ++j) {
-    float v = 0.0f;
-    if (j < b) {
-      const int i = base + j * stride;
-      v = load_elem(s, i);
-      if (sign_in) v = flip_sign(v, (sign[i >> 5] >> (i & 31)) & 1u);
+    for (int k = 0; k < kStageRB; ++k) {
+      const int m = min(mb + k, m1 - 1);
+      v[k] = act ? flip_sign(load_elem(src + static_cast<size_t>(m) * dim, o), sgn_in) : 0.0f;
     }
-    xin[j] = v;
-  }
-  // in place (src == dst) is safe: a wave reads all of its groups before
-  // writing, and groups are disjoint
-  if (act) {
-    const float acc = block_dot<BMAX, TRANSPOSE>(blk + static_cast<size_t>(c) * b * b, b,
-                                                 ln.r, xin);
-    const int o = base + ln.r * stride;
-    d[o] = sign_out ? flip_sign(acc, (sign[o >> 5] >> (o & 31)) & 1u) : acc;
+#pragma unroll
+    for (int k = 0; k < kStageRB; ++k) xs[k][lane] = v[k];
+#pragma unroll
+    for (int k = 0; k < kStageRB; ++k) {
+      float xin[BMAX];
+      read_group<BMAX>(grp + k * kWave, xin);
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < BMAX; ++j) acc = fmaf(coef[j], xin[j], acc);
+      if (act && mb + k < m1)
+        dst[static_cast<size_t>(mb + k) * dim + o] = flip_sign(acc, sgn_out);
+    }
   }
 }
 
@@ -189,17 +257,36 @@ MixedPlan make_plan(const harp_mixed_rotation& R) {
   return p;
 }
 
+template <int BMAX, int WAVES, bool TRANSPOSE, typename TIn>
+hipError_t launch_stage_waves(const TIn* src, float* dst, const float* blk, const uint32_t* sign,
+                              int dim, int b, int stride, int M, bool sign_in, bool sign_out,
+                              hipStream_t stream) {
+  const int groups = dim / b;
+  const int per_wg = WAVES * StageLanes<BMAX>::PER_WAVE;
+  const int gtiles = (groups + per_wg - 1) / per_wg;
+  // rows per workgroup: enough workgroups to fill the chip, block rows
+  // reused over as many rows as that allows
+  const int rows =
+      std::max(1, std::min(kStageMaxRows, M * gtiles * WAVES / kStageTargetWaves));
+  const dim3 grid(gtiles, (M + rows - 1) / rows);
+  hipLaunchKernelGGL((mixed_stage_kernel<BMAX, WAVES, TRANSPOSE, TIn>), grid,
+                     dim3(WAVES * kWave), 0, stream, src, dst, blk, sign, dim, b, stride, M,
+                     rows, sign_in ? 1 : 0, sign_out ? 1 : 0);
+  return hipGetLastError();
+}
+
+// Small batches: one-wave workgroups, spread over as many compute units as
+// there are groups.  Larger batches: eight waves on neighbouring groups
+// share a compute unit, so that their strided rows share cache lines.
 template <int BMAX, bool TRANSPOSE, typename TIn>
 hipError_t launch_stage_bmax(const TIn* src, float* dst, const float* blk, const uint32_t* sign,
                              int dim, int b, int stride, int M, bool sign_in, bool sign_out,
                              hipStream_t stream) {
-  const int groups = dim / b;
-  const int per_wg = (kMixedThreads / kWave) * StageLanes<BMAX>::PER_WAVE;
-  const dim3 grid((groups + per_wg - 1) / per_wg, M);
-  hipLaunchKernelGGL((mixed_stage_kernel<BMAX, TRANSPOSE, TIn>), grid, dim3(kMixedThreads), 0,
-                     stream, src, dst, blk, sign, dim, b, stride, sign_in ? 1 : 0,
-                     sign_out ? 1 : 0);
-  return hipGetLastError();
+  if (M < kStageWideM)
+    return launch_stage_waves<BMAX, 1, TRANSPOSE, TIn>(src, dst, blk, sign, dim, b, stride, M,
+                                                       sign_in, sign_out, stream);
+  return launch_stage_waves<BMAX, 8, TRANSPOSE, TIn>(src, dst, blk, sign, dim, b, stride, M,
+                                                     sign_in, sign_out, stream);
 }
 
 template <bool TRANSPOSE, typename TIn>
@@ -218,7 +305,7 @@ hipError_t launch_stage(const TIn* src, float* dst, const float* blk, const uint
 #undef HARP_STAGE
 }
 
-// Small batch, float32 output: one launch per stage.
+// Float32 output: one launch per stage, in place in the output.
 template <bool TRANSPOSE, typename TIn>
 hipError_t launch_by_stage(const harp_mixed_rotation& R, const void* in, float* out, int M,
                            hipStream_t stream) {
@@ -245,21 +332,21 @@ template <bool TRANSPOSE, typename TIn, typename TOut>
 hipError_t launch_typed(const harp_mixed_rotation& R, const void* in, void* out, int M,
                         hipStream_t stream) {
   if constexpr (std::is_same<TOut, float>::value) {
-    if (M <= kByStageMaxM)
-      return launch_by_stage<TRANSPOSE, TIn>(R, in, static_cast<float*>(out), M, stream);
+    return launch_by_stage<TRANSPOSE, TIn>(R, in, static_cast<float*>(out), M, stream);
+  } else {
+    const MixedPlan plan = make_plan(R);
+    const size_t shmem = sizeof(float) * static_cast<size_t>(R.dim);
+    if (shmem > 65536) {   // rows above 16384 floats: raise the dynamic LDS limit
+      const hipError_t e = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(&mixed_kernel<TRANSPOSE, TIn, TOut>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shmem));
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((mixed_kernel<TRANSPOSE, TIn, TOut>), dim3(M), dim3(kMixedThreads), shmem,
+                       stream, static_cast<const TIn*>(in), static_cast<TOut*>(out), R.blocks,
+                       R.sign_bits, plan);
+    return hipGetLastError();
   }
-  const MixedPlan plan = make_plan(R);
-  const size_t shmem = sizeof(float) * static_cast<size_t>(R.dim);
-  if (shmem > 65536) {   // rows above 16384 floats: raise the dynamic LDS limit
-    const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&mixed_kernel<TRANSPOSE, TIn, TOut>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shmem));
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL((mixed_kernel<TRANSPOSE, TIn, TOut>), dim3(M), dim3(kMixedThreads), shmem,
-                     stream, static_cast<const TIn*>(in), static_cast<TOut*>(out), R.blocks,
-                     R.sign_bits, plan);
-  return hipGetLastError();
 }
 
 }  // namespace
