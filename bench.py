@@ -358,8 +358,9 @@ def main():
     mixed = None
     if not args.no_mixed:
         import numpy as np
-        mixed = {"workload": "harp_rotate_in_mixed, bf16 x -> float32 x~, random orthogonal "
-                             "blocks (float32) per stage and group"}
+        mixed = {"workload": "harp_rotate_in_mixed (bf16 x -> float32 x~, or bf16 x~ for the "
+                             "matrix-core product) and harp_rotate_out_mixed (float32 -> float32), "
+                             "random orthogonal blocks (float32) per stage and group"}
         for radices in ((8, 8, 8, 5, 2), (8, 8, 4, 43), (8, 8, 8, 8, 3), (8, 8, 8, 8, 7)):
             dim = int(np.prod(radices))
             nblk = sum(dim * b for b in radices)
@@ -367,15 +368,21 @@ def main():
                                 torch.zeros((dim + 31) // 32, dtype=torch.int32, device="cuda"),
                                 radices)
             entry = {}
-            for M in (1, 512):
-                xs = [torch.randn((M, dim), device="cuda").to(torch.bfloat16) for _ in range(8)]
-                outs = [torch.empty((M, dim), device="cuda") for _ in range(8)]
-                ms, _ = time_graph(torch, lambda: [H.harp_rotate_in_mixed(R, a, o)
-                                                   for a, o in zip(xs, outs)], 5)
+            legs = [("in", 1, torch.bfloat16, torch.float32),
+                    ("in", 512, torch.bfloat16, torch.float32),
+                    ("in", 512, torch.bfloat16, torch.bfloat16),
+                    ("out", 1, torch.float32, torch.float32),
+                    ("out", 512, torch.float32, torch.float32)]
+            for side, M, idt, odt in legs:
+                xs = [torch.randn((M, dim), device="cuda").to(idt) for _ in range(8)]
+                outs = [torch.empty((M, dim), device="cuda", dtype=odt) for _ in range(8)]
+                fn = H.harp_rotate_in_mixed if side == "in" else H.harp_rotate_out_mixed
+                ms, _ = time_graph(torch, lambda: [fn(R, a, o) for a, o in zip(xs, outs)], 5)
                 us = ms * 1e3 / 8
-                nb = 4 * nblk + dim // 8 + 6 * M * dim
-                entry[f"M{M}_us"] = round(us, 2)
-                entry[f"M{M}_GB_s"] = round(nb / (us * 1e-6) / 1e9, 1)
+                nb = 4 * nblk + dim // 8 + (xs[0].element_size() + outs[0].element_size()) * M * dim
+                key = f"{side}_M{M}" + ("_bf16" if odt == torch.bfloat16 else "")
+                entry[f"{key}_us"] = round(us, 2)
+                entry[f"{key}_GB_s"] = round(nb / (us * 1e-6) / 1e9, 1)
                 del xs, outs
             mixed["x".join(str(b) for b in radices)] = entry
             del R
