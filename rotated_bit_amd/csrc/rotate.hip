@@ -274,6 +274,157 @@ __global__ __launch_bounds__((Plan<LOGB, EL_>::THREADS)) void rotate_kernel(
   }
 }
 
+// Output rotation of a few rows with the block split over eight
+// workgroups.  F^T applies the stages in descending order: the first three
+// (strides B/2, B/4, B/8) mix the eight elements q + j B/8 (j = 0..7) of
+// each residue q < B/8, and every later stage stays inside one of the eight
+// sub-blocks [w B/8, (w + 1) B/8).  Workgroup w therefore applies the first
+// three stages to every residue (the whole row, which its sub-block depends
+// on), keeps element j = w of each, and finishes its sub-block alone with
+// the register rounds of rotate_kernel.  Its coefficient reads are the
+// first three stages and its own sub-block's share of the others, about a
+// third of the block's; the eight workgroups run on eight CUs instead of
+// one CU reading all of them.
+constexpr int kSplitParts = 8;
+constexpr int kSplitThreads = 512;
+constexpr int kSplitMaxM = 8;   // rows up to this count take the split form
+
+template <int LOGB, typename TOut>
+__global__ __launch_bounds__(kSplitThreads) void rotate_out_split_kernel(
+    const float* __restrict__ in, TOut* __restrict__ out, const float2* __restrict__ cs,
+    const uint32_t* __restrict__ sign, int dim) {
+  constexpr int B = 1 << LOGB;
+  constexpr int BB = B / kSplitParts;           // sub-block
+  constexpr int LB = LOGB - 3;                  // stages inside a sub-block
+  constexpr int QPT = BB / kSplitThreads;       // residues per thread
+  constexpr int E = 8;
+  constexpr int TB = BB / E;                    // threads of the sub-block rounds
+  constexpr int NRB = (LB + 2) / 3;             // their register rounds
+  static_assert(QPT >= 1 && BB % kSplitThreads == 0, "sub-blocks of 512 or more");
+  __shared__ float u[BB];
+
+  const int tid = threadIdx.x;
+  const int w = blockIdx.x % kSplitParts;
+  const int blk = blockIdx.x / kSplitParts;
+  const size_t row = blockIdx.y;
+  const float* src = in + row * dim + static_cast<size_t>(blk) * B;
+  const float2* csb = cs + static_cast<size_t>(blk) * LOGB * (B / 2);
+
+  // sub-block rounds: the coefficients this thread will need, issued first
+  float2 cfb[LB][E / 2];
+  if (tid < TB) {
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) {
+      const int s0 = 3 * r;
+      const int R = round_width(r, 3, LB);
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        if (k < R) {
+          const int sg = s0 + k;
+#pragma unroll
+          for (int p = 0; p < E / 2; ++p) {
+            const int il = elem_index<E>(tid, insert_zero_bit(p, k), s0, R);
+            const int i = w * BB + il;
+            cfb[sg][p] = csb[sg * (B / 2) + delete_bit(i, sg)];
+          }
+        }
+      }
+    }
+  }
+
+  // first three stages on every residue, then keep element j = w
+#pragma unroll
+  for (int qi = 0; qi < QPT; ++qi) {
+    const int q = tid + qi * kSplitThreads;
+    float x[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) x[j] = src[q + BB * j];
+    float2 c3[3][E / 2];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int sg = LB + k;
+#pragma unroll
+      for (int p = 0; p < E / 2; ++p) {
+        const int i = q + BB * insert_zero_bit(p, k);
+        c3[k][p] = csb[sg * (B / 2) + delete_bit(i, sg)];
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 3; ++kk) {
+      const int k = 2 - kk;                     // descending stages
+#pragma unroll
+      for (int p = 0; p < E / 2; ++p) {
+        const int j = insert_zero_bit(p, k);
+        const int j2 = j | (1 << k);
+        const float a = x[j];
+        const float b = x[j2];
+        const float c = c3[k][p].x;
+        const float sn = c3[k][p].y;
+        x[j] = fmaf(c, a, sn * b);
+        x[j2] = fmaf(sn, a, -(c * b));
+      }
+    }
+    float keep = x[0];
+#pragma unroll
+    for (int j = 1; j < E; ++j) keep = (j == w) ? x[j] : keep;
+    u[q] = keep;
+  }
+  __syncthreads();
+
+  // the sub-block's stages LB-1 .. 0
+#pragma unroll
+  for (int qq = 0; qq < NRB; ++qq) {
+    const int r = NRB - 1 - qq;
+    const int s0 = 3 * r;
+    const int R = round_width(r, 3, LB);
+    if (tid < TB) {
+      float v[E];
+#pragma unroll
+      for (int j = 0; j < E; ++j) v[j] = u[elem_index<E>(tid, j, s0, R)];
+#pragma unroll
+      for (int kk = 0; kk < 3; ++kk) {
+        const int k = 2 - kk;
+        if (k < R) {
+          const int sg = s0 + k;
+#pragma unroll
+          for (int p = 0; p < E / 2; ++p) {
+            const int j = insert_zero_bit(p, k);
+            const int j2 = j | (1 << k);
+            const float a = v[j];
+            const float b = v[j2];
+            const float c = cfb[sg][p].x;
+            const float sn = cfb[sg][p].y;
+            v[j] = fmaf(c, a, sn * b);
+            v[j2] = fmaf(sn, a, -(c * b));
+          }
+        }
+      }
+      if (r == 0) {   // contiguous elements 8 tid .. 8 tid + 7: signs, store
+        const int g = blk * B + w * BB + tid * E;
+        const uint32_t sbits = sign[g >> 5] >> (g & 31);
+#pragma unroll
+        for (int j = 0; j < E; ++j) v[j] = flip_sign(v[j], (sbits >> j) & 1u);
+        store_contig<TOut, E>(out + row * dim + static_cast<size_t>(g), v);
+      } else {
+#pragma unroll
+        for (int j = 0; j < E; ++j) u[elem_index<E>(tid, j, s0, R)] = v[j];
+      }
+    }
+    if (r > 0) __syncthreads();
+  }
+}
+
+template <int LOGB, typename TOut>
+hipError_t launch_split(const harp_rotation& R, const void* in, void* out, int M,
+                        hipStream_t stream) {
+  const int nblk = R.dim >> LOGB;
+  const dim3 grid(nblk * kSplitParts, M);
+  hipLaunchKernelGGL((rotate_out_split_kernel<LOGB, TOut>), grid, dim3(kSplitThreads), 0,
+                     stream, static_cast<const float*>(in), static_cast<TOut*>(out),
+                     reinterpret_cast<const float2*>(R.cs), R.sign_bits, R.dim);
+  return hipGetLastError();
+}
+
 template <int LOGB, int EL_, bool TRANSPOSE, bool Q8, typename TIn, typename TOut>
 hipError_t launch_typed(const harp_rotation& R, const void* in, void* out, int M,
                         hipStream_t stream) {
@@ -327,6 +478,13 @@ template <int LOGB>
 hipError_t launch_logb(const harp_rotation& R, const void* in, int in_dt,
                        void* out, int out_dt, int M, bool transpose,
                        hipStream_t stream) {
+  if constexpr (LOGB == 12 || LOGB == 13) {
+    // few rows of the output rotation, float32 pairs: eight workgroups per block
+    if (transpose && R.phi_codes == nullptr && M <= kSplitMaxM) {
+      if (out_dt == HARP_BF16) return launch_split<LOGB, uint16_t>(R, in, out, M, stream);
+      return launch_split<LOGB, float>(R, in, out, M, stream);
+    }
+  }
   if constexpr (LOGB == 12) {
     // few b = 4096 blocks in flight: 1024 threads per block (see Plan)
     if ((R.dim >> LOGB) * M <= 64)
