@@ -23,6 +23,8 @@
 // its code loads are in flight, then gathers its pairs from the table, so a
 // block's coefficient fetch is one byte per pair instead of eight.
 #include "launch.hpp"
+
+#include <type_traits>
 #include "device_common.hpp"
 
 namespace harp {
@@ -278,21 +280,44 @@ __global__ __launch_bounds__((Plan<LOGB, EL_>::THREADS)) void rotate_kernel(
 // workgroups.  F^T applies the stages in descending order: the first three
 // (strides B/2, B/4, B/8) mix the eight elements q + j B/8 (j = 0..7) of
 // each residue q < B/8, and every later stage stays inside one of the eight
-// sub-blocks [w B/8, (w + 1) B/8).  Workgroup w therefore applies the first
-// three stages to every residue (the whole row, which its sub-block depends
-// on), keeps element j = w of each, and finishes its sub-block alone with
-// the register rounds of rotate_kernel.  Its coefficient reads are the
-// first three stages and its own sub-block's share of the others, about a
-// third of the block's; the eight workgroups run on eight CUs instead of
-// one CU reading all of them.
+// sub-blocks [w B/8, (w + 1) B/8).  Workgroup w therefore reads the whole
+// row (its sub-block depends on all of it), applies to every residue only
+// the seven first-three-stage butterflies that lead to element j = w (all
+// four of the widest stage, the two of the next on the half holding w, the
+// one of the third), keeps that element in LDS, and finishes its sub-block
+// alone with the register rounds of rotate_kernel.  Its coefficient reads
+// are those seven pairs per residue and its own sub-block's share of the
+// other stages, about a quarter of the block's, and the eight workgroups
+// run on eight CUs instead of one CU reading all of them.
 constexpr int kSplitParts = 8;
 constexpr int kSplitThreads = 512;
 constexpr int kSplitMaxM = 8;   // rows up to this count take the split form
 
-template <int LOGB, typename TOut>
+// a where mask bits are set, else b.  The mask comes through an empty asm
+// so that the selects between register elements stay selects (the compiler
+// would otherwise fold them into one runtime-indexed array access, which it
+// places in LDS).
+__device__ __forceinline__ float bit_select(uint32_t mask, float a, float b) {
+  return __uint_as_float((mask & __float_as_uint(a)) | (~mask & __float_as_uint(b)));
+}
+
+__device__ __forceinline__ uint32_t mask_of(bool c) {
+  uint32_t m = c ? 0xffffffffu : 0u;
+  asm volatile("" : "+v"(m));
+  return m;
+}
+
+__device__ __forceinline__ void butterfly(float& a, float& b, float2 cs) {
+  const float x = a;
+  const float y = b;
+  a = fmaf(cs.x, x, cs.y * y);
+  b = fmaf(cs.y, x, -(cs.x * y));
+}
+
+template <int LOGB, bool Q8, typename TOut>
 __global__ __launch_bounds__(kSplitThreads) void rotate_out_split_kernel(
     const float* __restrict__ in, TOut* __restrict__ out, const float2* __restrict__ cs,
-    const uint32_t* __restrict__ sign, int dim) {
+    const int8_t* __restrict__ codes, float step, const uint32_t* __restrict__ sign, int dim) {
   constexpr int B = 1 << LOGB;
   constexpr int BB = B / kSplitParts;           // sub-block
   constexpr int LB = LOGB - 3;                  // stages inside a sub-block
@@ -302,16 +327,30 @@ __global__ __launch_bounds__(kSplitThreads) void rotate_out_split_kernel(
   constexpr int NRB = (LB + 2) / 3;             // their register rounds
   static_assert(QPT >= 1 && BB % kSplitThreads == 0, "sub-blocks of 512 or more");
   __shared__ float u[BB];
+  __shared__ float2 table[Q8 ? 256 : 1];        // (cos t, sin t) by code + 128
 
   const int tid = threadIdx.x;
   const int w = blockIdx.x % kSplitParts;
   const int blk = blockIdx.x / kSplitParts;
   const size_t row = blockIdx.y;
   const float* src = in + row * dim + static_cast<size_t>(blk) * B;
-  const float2* csb = cs + static_cast<size_t>(blk) * LOGB * (B / 2);
+  const size_t coff = static_cast<size_t>(blk) * LOGB * (B / 2);
+  // A coefficient is fetched as a handle (the float32 pair, or the int8
+  // code) and resolved once the code table exists.
+  using Handle = typename std::conditional<Q8, int, float2>::type;
+  auto fetch = [&](int c) -> Handle {
+    if constexpr (Q8) return codes[coff + c];
+    else return cs[coff + c];
+  };
+  auto resolve = [&](Handle h) -> float2 {
+    if constexpr (Q8) return table[h + 128];
+    else return h;
+  };
+  auto cidx = [&](int sg, int i) { return sg * (B / 2) + delete_bit(i, sg); };
 
-  // sub-block rounds: the coefficients this thread will need, issued first
-  float2 cfb[LB][E / 2];
+  // loads first: the sub-block rounds' coefficients, the row, the seven
+  // pairs per residue
+  Handle hb[LB][E / 2];
   if (tid < TB) {
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
@@ -320,54 +359,54 @@ __global__ __launch_bounds__(kSplitThreads) void rotate_out_split_kernel(
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
         if (k < R) {
-          const int sg = s0 + k;
 #pragma unroll
           for (int p = 0; p < E / 2; ++p) {
-            const int il = elem_index<E>(tid, insert_zero_bit(p, k), s0, R);
-            const int i = w * BB + il;
-            cfb[sg][p] = csb[sg * (B / 2) + delete_bit(i, sg)];
+            const int i = w * BB + elem_index<E>(tid, insert_zero_bit(p, k), s0, R);
+            hb[s0 + k][p] = fetch(cidx(s0 + k, i));
           }
         }
       }
     }
   }
-
-  // first three stages on every residue, then keep element j = w
+  const int half = w & 4;                       // elements j of the half holding w
+  float x[QPT][E];
+  Handle h2[QPT][4], h1[QPT][2], h0[QPT];
 #pragma unroll
   for (int qi = 0; qi < QPT; ++qi) {
     const int q = tid + qi * kSplitThreads;
-    float x[E];
 #pragma unroll
-    for (int j = 0; j < E; ++j) x[j] = src[q + BB * j];
-    float2 c3[3][E / 2];
+    for (int j = 0; j < E; ++j) x[qi][j] = src[q + BB * j];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const int sg = LB + k;
+    for (int p = 0; p < 4; ++p) h2[qi][p] = fetch(cidx(LB + 2, q + BB * p));
 #pragma unroll
-      for (int p = 0; p < E / 2; ++p) {
-        const int i = q + BB * insert_zero_bit(p, k);
-        c3[k][p] = csb[sg * (B / 2) + delete_bit(i, sg)];
-      }
+    for (int m = 0; m < 2; ++m) h1[qi][m] = fetch(cidx(LB + 1, q + BB * (half + m)));
+    h0[qi] = fetch(cidx(LB, q + BB * (w & 6)));
+  }
+  if constexpr (Q8) {
+    for (int i = tid; i < 256; i += kSplitThreads) {
+      float sn, cn;
+      sincosf(fmaf(static_cast<float>(i - 128), step, 0.785398163397448310f), &sn, &cn);
+      table[i] = make_float2(cn, sn);
     }
+    __syncthreads();
+  }
+
+  const uint32_t m4 = mask_of(w & 4), m2 = mask_of(w & 2), m1 = mask_of(w & 1);
 #pragma unroll
-    for (int kk = 0; kk < 3; ++kk) {
-      const int k = 2 - kk;                     // descending stages
+  for (int qi = 0; qi < QPT; ++qi) {
+    const int q = tid + qi * kSplitThreads;
+    float* v = x[qi];
 #pragma unroll
-      for (int p = 0; p < E / 2; ++p) {
-        const int j = insert_zero_bit(p, k);
-        const int j2 = j | (1 << k);
-        const float a = x[j];
-        const float b = x[j2];
-        const float c = c3[k][p].x;
-        const float sn = c3[k][p].y;
-        x[j] = fmaf(c, a, sn * b);
-        x[j2] = fmaf(sn, a, -(c * b));
-      }
-    }
-    float keep = x[0];
+    for (int p = 0; p < 4; ++p) butterfly(v[p], v[p | 4], resolve(h2[qi][p]));   // stride B/2
+    float y[4];
 #pragma unroll
-    for (int j = 1; j < E; ++j) keep = (j == w) ? x[j] : keep;
-    u[q] = keep;
+    for (int m = 0; m < 4; ++m) y[m] = bit_select(m4, v[4 + m], v[m]);
+    butterfly(y[0], y[2], resolve(h1[qi][0]));                                     // stride B/4
+    butterfly(y[1], y[3], resolve(h1[qi][1]));
+    float z0 = bit_select(m2, y[2], y[0]);
+    float z1 = bit_select(m2, y[3], y[1]);
+    butterfly(z0, z1, resolve(h0[qi]));                                            // stride B/8
+    u[q] = bit_select(m1, z1, z0);
   }
   __syncthreads();
 
@@ -385,17 +424,10 @@ __global__ __launch_bounds__(kSplitThreads) void rotate_out_split_kernel(
       for (int kk = 0; kk < 3; ++kk) {
         const int k = 2 - kk;
         if (k < R) {
-          const int sg = s0 + k;
 #pragma unroll
           for (int p = 0; p < E / 2; ++p) {
             const int j = insert_zero_bit(p, k);
-            const int j2 = j | (1 << k);
-            const float a = v[j];
-            const float b = v[j2];
-            const float c = cfb[sg][p].x;
-            const float sn = cfb[sg][p].y;
-            v[j] = fmaf(c, a, sn * b);
-            v[j2] = fmaf(sn, a, -(c * b));
+            butterfly(v[j], v[j | (1 << k)], resolve(hb[s0 + k][p]));
           }
         }
       }
@@ -414,14 +446,15 @@ __global__ __launch_bounds__(kSplitThreads) void rotate_out_split_kernel(
   }
 }
 
-template <int LOGB, typename TOut>
+template <int LOGB, bool Q8, typename TOut>
 hipError_t launch_split(const harp_rotation& R, const void* in, void* out, int M,
                         hipStream_t stream) {
   const int nblk = R.dim >> LOGB;
   const dim3 grid(nblk * kSplitParts, M);
-  hipLaunchKernelGGL((rotate_out_split_kernel<LOGB, TOut>), grid, dim3(kSplitThreads), 0,
+  hipLaunchKernelGGL((rotate_out_split_kernel<LOGB, Q8, TOut>), grid, dim3(kSplitThreads), 0,
                      stream, static_cast<const float*>(in), static_cast<TOut*>(out),
-                     reinterpret_cast<const float2*>(R.cs), R.sign_bits, R.dim);
+                     reinterpret_cast<const float2*>(R.cs), R.phi_codes, R.phi_step,
+                     R.sign_bits, R.dim);
   return hipGetLastError();
 }
 
@@ -479,10 +512,14 @@ hipError_t launch_logb(const harp_rotation& R, const void* in, int in_dt,
                        void* out, int out_dt, int M, bool transpose,
                        hipStream_t stream) {
   if constexpr (LOGB == 12 || LOGB == 13) {
-    // few rows of the output rotation, float32 pairs: eight workgroups per block
-    if (transpose && R.phi_codes == nullptr && M <= kSplitMaxM) {
-      if (out_dt == HARP_BF16) return launch_split<LOGB, uint16_t>(R, in, out, M, stream);
-      return launch_split<LOGB, float>(R, in, out, M, stream);
+    // few rows of the output rotation: eight workgroups per block
+    if (transpose && M <= kSplitMaxM) {
+      const bool ob = out_dt == HARP_BF16;
+      if (R.phi_codes != nullptr)
+        return ob ? launch_split<LOGB, true, uint16_t>(R, in, out, M, stream)
+                  : launch_split<LOGB, true, float>(R, in, out, M, stream);
+      return ob ? launch_split<LOGB, false, uint16_t>(R, in, out, M, stream)
+                : launch_split<LOGB, false, float>(R, in, out, M, stream);
     }
   }
   if constexpr (LOGB == 12) {
