@@ -185,6 +185,33 @@ def test_rotate_int8_angles(dim, b, M, xdt):
     assert report(f"rotate_out int8 {dim}/{b} M={M}", d.host(y), reft) <= BUTTERFLY_TOL
 
 
+# Output rotations of few rows at b = 4096 / 8192 run split over eight
+# workgroups per block; M = 9 is the first batch of the one-workgroup form.
+SPLIT_CASES = [
+    (4096, 4096, 1, "f32"), (4096, 4096, 8, "f32"), (4096, 4096, 9, "f32"),
+    (8192, 8192, 3, "int8"), (8192, 4096, 5, "f32"), (16384, 8192, 2, "int8"),
+    (4096, 4096, 4, "int8"),
+]
+
+
+@pytest.mark.parametrize("dim,b,M,angles", SPLIT_CASES)
+def test_rotate_out_few_rows(dim, b, M, angles):
+    """F^T y' for a few rows, float32 and bf16 outputs, both angle formats,
+    block-diagonal sides included."""
+    d = D()
+    rot = (S.rotation if angles == "f32" else S.rotation_q8)(dim, b, rng(36, dim, b))
+    R = d.dev_rotation(rot)
+    cs = rot.cs if angles == "f32" else d.cs64(rot)
+    yp = rng(37, dim, M).normal(size=(M, dim)).astype(np.float32)
+    reft = O.transpose(yp.astype(np.float64), cs, rot.sign_bits, b)
+    y = torch.empty((M, dim), dtype=torch.float32, device="cuda")
+    H().harp_rotate_out(R, d.dev(yp), y)
+    assert report(f"rotate_out {angles} {dim}/{b} M={M}", d.host(y), reft) <= BUTTERFLY_TOL
+    yb = torch.empty((M, dim), dtype=torch.bfloat16, device="cuda")
+    H().harp_rotate_out(R, d.dev(yp), yb)
+    assert_bf16_rounding_close(d.host(yb), reft, BUTTERFLY_TOL)
+
+
 @pytest.mark.parametrize("b", [16, 4096])
 def test_rotate_int8_extreme_codes(b):
     """Codes 0 (Hadamard initialisation) and +-127 at step pi/508 (pair swap
