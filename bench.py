@@ -38,7 +38,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 # when its kernel changes until the counters are taken again.
 TRAFFIC_BYTES = {
     "rotate_in_deq_gemv_2bit": 7009280,
-    "rotate_out_b4096": None,
+    "rotate_out_b4096": 590848,
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores, TFLOP/s
 WORKING_SET_BYTES = 1 << 30
