@@ -359,7 +359,8 @@ def main():
     if not args.no_mixed:
         import numpy as np
         mixed = {"workload": "harp_rotate_in_mixed (bf16 x -> float32 x~, or bf16 x~ for the "
-                             "matrix-core product) and harp_rotate_out_mixed (float32 -> float32), "
+                             "matrix-core product, with its float32 workspace) and "
+                             "harp_rotate_out_mixed (float32 -> float32), "
                              "random orthogonal blocks (float32) per stage and group"}
         for radices in ((8, 8, 8, 5, 2), (8, 8, 4, 43), (8, 8, 8, 8, 3), (8, 8, 8, 8, 7)):
             dim = int(np.prod(radices))
@@ -377,7 +378,11 @@ def main():
                 xs = [torch.randn((M, dim), device="cuda").to(idt) for _ in range(8)]
                 outs = [torch.empty((M, dim), device="cuda", dtype=odt) for _ in range(8)]
                 fn = H.harp_rotate_in_mixed if side == "in" else H.harp_rotate_out_mixed
-                ms, _ = time_graph(torch, lambda: [fn(R, a, o) for a, o in zip(xs, outs)], 5)
+                ws = None
+                if odt == torch.bfloat16:   # float32 stages in a workspace, bf16 last stage
+                    ws = torch.empty(H.harp_rotate_mixed_workspace_bytes(dim, M, odt),
+                                     dtype=torch.uint8, device="cuda")
+                ms, _ = time_graph(torch, lambda: [fn(R, a, o, ws) for a, o in zip(xs, outs)], 5)
                 us = ms * 1e3 / 8
                 nb = 4 * nblk + dim // 8 + (xs[0].element_size() + outs[0].element_size()) * M * dim
                 key = f"{side}_M{M}" + ("_bf16" if odt == torch.bfloat16 else "")

@@ -181,13 +181,26 @@ harp_status harp_rotate_out(const harp_rotation *U, const float *yt, void *y,
  * side; float32 arithmetic, a bf16 output rounds to nearest even.
  *   x  [M][dim] of x_dt;  xt [M][dim] of xt_dt;  yt [M][dim] float32;
  *   y  [M][dim] of y_dt.
+ *   workspace  optional, used only for a bf16 output: at least
+ *              harp_rotate_mixed_workspace_bytes(dim, M, HARP_BF16) bytes,
+ *              16-byte aligned (HARP_ERR_WORKSPACE if smaller).  With it the
+ *              stages run one launch each over the whole chip in float32 in
+ *              the workspace and the last stage writes the bf16 output; with
+ *              NULL one workgroup rotates each row in LDS (slower, notably
+ *              for radices that are not powers of two).  A float32 output is
+ *              its own workspace.  The contents need no initialisation;
+ *              calls that share a workspace must not overlap in time.
  */
 harp_status harp_rotate_in_mixed(const harp_mixed_rotation *R, const void *x,
                                  harp_dtype x_dt, void *xt, harp_dtype xt_dt,
-                                 int32_t M, harp_stream stream);
+                                 int32_t M, void *workspace, size_t ws_bytes,
+                                 harp_stream stream);
 harp_status harp_rotate_out_mixed(const harp_mixed_rotation *R, const float *yt,
                                   void *y, harp_dtype y_dt, int32_t M,
-                                  harp_stream stream);
+                                  void *workspace, size_t ws_bytes, harp_stream stream);
+/* Workspace bytes for M rows of dim with output dtype out_dt (0 for float32;
+ * 0 for arguments out of range). */
+size_t harp_rotate_mixed_workspace_bytes(int32_t dim, int32_t M, harp_dtype out_dt);
 
 /*
  * y'[m][n] = sum_k w_hat[n][k] x~[m][k] on the vector ALUs, float32

@@ -34,7 +34,7 @@ EXPORTED = (
     "harp_deq_gemm",
     "harp_deq_gemm_workspace_bytes", "harp_linear_workspace_bytes", "harp_linear_fused", "harp_dequant",
     "harp_rotate_weight", "harp_rotate_weight_workspace_bytes", "harp_quantize_pack",
-    "harp_rotate_in_mixed", "harp_rotate_out_mixed",
+    "harp_rotate_in_mixed", "harp_rotate_out_mixed", "harp_rotate_mixed_workspace_bytes",
     "harp_status_string", "harp_last_hip_error",
 )
 
@@ -99,8 +99,10 @@ def _load() -> ctypes.CDLL:
                                           c_size_t, c_void_p]),
         "harp_rotate_weight_workspace_bytes": (c_size_t, [c_int32, c_int32]),
         "harp_rotate_in_mixed": (c_int32, [MR, c_void_p, c_int32, c_void_p, c_int32, c_int32,
-                                            c_void_p]),
-        "harp_rotate_out_mixed": (c_int32, [MR, c_void_p, c_void_p, c_int32, c_int32, c_void_p]),
+                                            c_void_p, c_size_t, c_void_p]),
+        "harp_rotate_out_mixed": (c_int32, [MR, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
+                                             c_size_t, c_void_p]),
+        "harp_rotate_mixed_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
         "harp_quantize_pack": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p,
                                           c_void_p, c_void_p]),
         "harp_status_string": (c_char_p, [c_int32]),
@@ -133,13 +135,17 @@ def _ptr(t):
     return None if t is None else c_void_p(t.data_ptr())
 
 
-def _dtype_code(t) -> int:
+def _dtype_of(dtype) -> int:
     torch = _torch()
-    if t.dtype == torch.float32:
+    if dtype == torch.float32:
         return HARP_F32
-    if t.dtype == torch.bfloat16:
+    if dtype == torch.bfloat16:
         return HARP_BF16
-    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    raise TypeError(f"unsupported dtype {dtype} (float32 or bfloat16)")
+
+
+def _dtype_code(t) -> int:
+    return _dtype_of(t.dtype)
 
 
 def _stream(stream):
@@ -254,16 +260,31 @@ def harp_dequant(W: QWeight, out, stream=None) -> None:
            "harp_dequant")
 
 
-def harp_rotate_in_mixed(R: MixedRotation, x, xt, M: int | None = None, stream=None) -> None:
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def harp_rotate_mixed_workspace_bytes(dim: int, M: int, out_dtype) -> int:
+    return int(lib.harp_rotate_mixed_workspace_bytes(dim, M, _dtype_of(out_dtype)))
+
+
+def harp_rotate_in_mixed(R: MixedRotation, x, xt, workspace=None, M: int | None = None,
+                         stream=None) -> None:
     M = x.shape[0] if M is None else M
+    wp, wb = _ws(workspace)
     _check(lib.harp_rotate_in_mixed(ctypes.byref(R.c), _ptr(x), _dtype_code(x), _ptr(xt),
-                                    _dtype_code(xt), M, _stream(stream)), "harp_rotate_in_mixed")
+                                    _dtype_code(xt), M, wp, wb, _stream(stream)),
+           "harp_rotate_in_mixed")
 
 
-def harp_rotate_out_mixed(R: MixedRotation, yt, y, M: int | None = None, stream=None) -> None:
+def harp_rotate_out_mixed(R: MixedRotation, yt, y, workspace=None, M: int | None = None,
+                          stream=None) -> None:
     M = yt.shape[0] if M is None else M
+    wp, wb = _ws(workspace)
     _check(lib.harp_rotate_out_mixed(ctypes.byref(R.c), _ptr(yt), _ptr(y), _dtype_code(y), M,
-                                     _stream(stream)), "harp_rotate_out_mixed")
+                                     wp, wb, _stream(stream)), "harp_rotate_out_mixed")
 
 
 def harp_rotate_weight_workspace_bytes(N: int, K: int) -> int:

@@ -41,19 +41,26 @@ harp_status harp_rotate_out(const harp_rotation* U, const float* yt, void* y,
 
 harp_status harp_rotate_in_mixed(const harp_mixed_rotation* R, const void* x,
                                  harp_dtype x_dt, void* xt, harp_dtype xt_dt, int32_t M,
-                                 harp_stream stream) {
-  const harp_status st = harp::validate_rotate_mixed(R, x, x_dt, xt, xt_dt, M);
+                                 void* workspace, size_t ws_bytes, harp_stream stream) {
+  const harp_status st =
+      harp::validate_rotate_mixed(R, x, x_dt, xt, xt_dt, M, workspace, ws_bytes);
   if (st != HARP_OK || M == 0) return st;
   return from_hip(harp::launch_rotate_mixed(*R, x, x_dt, xt, xt_dt, M, false,
-                                            as_stream(stream)));
+                                            static_cast<float*>(workspace), as_stream(stream)));
 }
 
 harp_status harp_rotate_out_mixed(const harp_mixed_rotation* R, const float* yt, void* y,
-                                  harp_dtype y_dt, int32_t M, harp_stream stream) {
-  const harp_status st = harp::validate_rotate_mixed(R, yt, HARP_F32, y, y_dt, M);
+                                  harp_dtype y_dt, int32_t M, void* workspace, size_t ws_bytes,
+                                  harp_stream stream) {
+  const harp_status st =
+      harp::validate_rotate_mixed(R, yt, HARP_F32, y, y_dt, M, workspace, ws_bytes);
   if (st != HARP_OK || M == 0) return st;
   return from_hip(harp::launch_rotate_mixed(*R, yt, HARP_F32, y, y_dt, M, true,
-                                            as_stream(stream)));
+                                            static_cast<float*>(workspace), as_stream(stream)));
+}
+
+size_t harp_rotate_mixed_workspace_bytes(int32_t dim, int32_t M, harp_dtype out_dt) {
+  return harp::rotate_mixed_workspace_bytes(dim, M, out_dt);
 }
 
 harp_status harp_deq_gemv(const harp_qweight* W, const float* xt, float* yt,

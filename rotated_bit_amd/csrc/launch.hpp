@@ -17,7 +17,7 @@ hipError_t launch_rotate(const harp_rotation& R, const void* in, int in_dt,
 // Mixed-radix side: xt = F x or y = F^T y' for M rows (one workgroup per row).
 hipError_t launch_rotate_mixed(const harp_mixed_rotation& R, const void* in, int in_dt,
                                void* out, int out_dt, int M, bool transpose,
-                               hipStream_t stream);
+                               float* workspace, hipStream_t stream);
 
 // yt = w_hat xt on the vector ALUs, float32.
 hipError_t launch_gemv(const harp_qweight& W, const float* xt, float* yt,

@@ -9,15 +9,17 @@
 // gfx950 mapping.  A group of radix b takes the next power of two of b
 // lanes of one wave, lane r forming output r from the group's inputs and
 // row (or column) r of its block, so that a wave's coefficient loads are
-// contiguous.  Float32 outputs run one launch per stage, in place in the
-// output (a group's inputs and outputs are the same coordinates, and groups
-// are disjoint), spread over the whole chip; each lane keeps its block row
-// in registers for a tile of rows.  bf16 outputs have no float32 buffer to
-// pass between stages: one workgroup of 512 threads owns one row, held in
-// LDS as float32 (d <= 32768: at most 128 KB), one barrier per stage, the
-// blocks streaming from global memory where the L2 keeps them for the other
-// rows.  Register arrays are sized by the next power of two of the radix, a
-// compile-time bound chosen per stage.
+// contiguous.  The stages run one launch each over the whole chip, in place
+// in a float32 buffer (a group's inputs and outputs are the same
+// coordinates, and groups are disjoint): the output itself for a float32
+// output, the caller's workspace for a bf16 one, whose last stage writes
+// the output.  Each lane keeps its block row in registers for a tile of
+// rows.  A bf16 output without a workspace falls back to one workgroup of
+// 512 threads per row, the row held in LDS as float32 (d <= 32768: at most
+// 128 KB), one barrier per stage, the blocks streaming from global memory
+// where the L2 keeps them for the other rows.  Register arrays are sized by
+// the next power of two of the radix, a compile-time bound chosen per
+// stage.
 #include "launch.hpp"
 #include "device_common.hpp"
 
@@ -31,6 +33,8 @@ constexpr int kMixedThreads = 512;
 constexpr int kStageMaxRows = 32;     // rows per workgroup of a stage launch
 constexpr int kStageTargetWaves = 8192;  // waves a stage launch aims for
 constexpr int kStageWideM = 64;         // batches from this size use 8-wave workgroups
+constexpr int kRowFormMaxDim = 16384;   // bf16 outputs: row form limits (see launch_typed)
+constexpr int kRowFormMaxRadix = 16;
 
 struct MixedPlan {
   int dim;
@@ -164,9 +168,9 @@ __device__ __forceinline__ void read_group(const float* p, float (&xin)[BMAX]) {
   }
 }
 
-template <int BMAX, int WAVES, bool TRANSPOSE, typename TIn>
+template <int BMAX, int WAVES, bool TRANSPOSE, typename TIn, typename TOut>
 __global__ __launch_bounds__(WAVES * kWave) void mixed_stage_kernel(
-    const TIn* src, float* dst, const float* __restrict__ blk,
+    const TIn* src, TOut* dst, const float* __restrict__ blk,
     const uint32_t* __restrict__ sign, int dim, int b, int stride, int M, int rows,
     int sign_in, int sign_out) {
   __shared__ __attribute__((aligned(16))) float xsw[WAVES][kStageRB][kWave];
@@ -209,7 +213,7 @@ __global__ __launch_bounds__(WAVES * kWave) void mixed_stage_kernel(
 #pragma unroll
       for (int j = 0; j < BMAX; ++j) acc = fmaf(coef[j], xin[j], acc);
       if (act && mb + k < m1)
-        dst[static_cast<size_t>(mb + k) * dim + o] = flip_sign(acc, sgn_out);
+        store_elem(dst, static_cast<size_t>(mb + k) * dim + o, flip_sign(acc, sgn_out));
     }
   }
 }
@@ -257,8 +261,8 @@ MixedPlan make_plan(const harp_mixed_rotation& R) {
   return p;
 }
 
-template <int BMAX, int WAVES, bool TRANSPOSE, typename TIn>
-hipError_t launch_stage_waves(const TIn* src, float* dst, const float* blk, const uint32_t* sign,
+template <int BMAX, int WAVES, bool TRANSPOSE, typename TIn, typename TOut>
+hipError_t launch_stage_waves(const TIn* src, TOut* dst, const float* blk, const uint32_t* sign,
                               int dim, int b, int stride, int M, bool sign_in, bool sign_out,
                               hipStream_t stream) {
   const int groups = dim / b;
@@ -269,7 +273,7 @@ hipError_t launch_stage_waves(const TIn* src, float* dst, const float* blk, cons
   const int rows =
       std::max(1, std::min(kStageMaxRows, M * gtiles * WAVES / kStageTargetWaves));
   const dim3 grid(gtiles, (M + rows - 1) / rows);
-  hipLaunchKernelGGL((mixed_stage_kernel<BMAX, WAVES, TRANSPOSE, TIn>), grid,
+  hipLaunchKernelGGL((mixed_stage_kernel<BMAX, WAVES, TRANSPOSE, TIn, TOut>), grid,
                      dim3(WAVES * kWave), 0, stream, src, dst, blk, sign, dim, b, stride, M,
                      rows, sign_in ? 1 : 0, sign_out ? 1 : 0);
   return hipGetLastError();
@@ -278,24 +282,24 @@ hipError_t launch_stage_waves(const TIn* src, float* dst, const float* blk, cons
 // Small batches: one-wave workgroups, spread over as many compute units as
 // there are groups.  Larger batches: eight waves on neighbouring groups
 // share a compute unit, so that their strided rows share cache lines.
-template <int BMAX, bool TRANSPOSE, typename TIn>
-hipError_t launch_stage_bmax(const TIn* src, float* dst, const float* blk, const uint32_t* sign,
+template <int BMAX, bool TRANSPOSE, typename TIn, typename TOut>
+hipError_t launch_stage_bmax(const TIn* src, TOut* dst, const float* blk, const uint32_t* sign,
                              int dim, int b, int stride, int M, bool sign_in, bool sign_out,
                              hipStream_t stream) {
   if (M < kStageWideM)
-    return launch_stage_waves<BMAX, 1, TRANSPOSE, TIn>(src, dst, blk, sign, dim, b, stride, M,
-                                                       sign_in, sign_out, stream);
-  return launch_stage_waves<BMAX, 8, TRANSPOSE, TIn>(src, dst, blk, sign, dim, b, stride, M,
-                                                     sign_in, sign_out, stream);
+    return launch_stage_waves<BMAX, 1, TRANSPOSE, TIn, TOut>(src, dst, blk, sign, dim, b, stride,
+                                                             M, sign_in, sign_out, stream);
+  return launch_stage_waves<BMAX, 8, TRANSPOSE, TIn, TOut>(src, dst, blk, sign, dim, b, stride, M,
+                                                           sign_in, sign_out, stream);
 }
 
-template <bool TRANSPOSE, typename TIn>
-hipError_t launch_stage(const TIn* src, float* dst, const float* blk, const uint32_t* sign,
+template <bool TRANSPOSE, typename TIn, typename TOut>
+hipError_t launch_stage(const TIn* src, TOut* dst, const float* blk, const uint32_t* sign,
                         int dim, int b, int stride, int M, bool sign_in, bool sign_out,
                         hipStream_t stream) {
 #define HARP_STAGE(BM) \
-  launch_stage_bmax<BM, TRANSPOSE, TIn>(src, dst, blk, sign, dim, b, stride, M, sign_in, \
-                                        sign_out, stream)
+  launch_stage_bmax<BM, TRANSPOSE, TIn, TOut>(src, dst, blk, sign, dim, b, stride, M, sign_in, \
+                                              sign_out, stream)
   if (b <= 2) return HARP_STAGE(2);
   if (b <= 4) return HARP_STAGE(4);
   if (b <= 8) return HARP_STAGE(8);
@@ -305,24 +309,36 @@ hipError_t launch_stage(const TIn* src, float* dst, const float* blk, const uint
 #undef HARP_STAGE
 }
 
-// Float32 output: one launch per stage, in place in the output.
-template <bool TRANSPOSE, typename TIn>
-hipError_t launch_by_stage(const harp_mixed_rotation& R, const void* in, float* out, int M,
-                           hipStream_t stream) {
+// One launch per stage: stage 0 reads the input, the others run in place in
+// the float32 buffer ws (the output itself for a float32 output), and the
+// last writes the output.
+template <bool TRANSPOSE, typename TIn, typename TOut>
+hipError_t launch_by_stage(const harp_mixed_rotation& R, const void* in, float* ws, TOut* out,
+                           int M, hipStream_t stream) {
   const MixedPlan plan = make_plan(R);
+  const TIn* src = static_cast<const TIn*>(in);
   for (int q = 0; q < plan.n; ++q) {
     const int t = TRANSPOSE ? plan.n - 1 - q : q;
     const float* blk = R.blocks + plan.offset[t];
+    const bool first = q == 0;
+    const bool last = q == plan.n - 1;
+    const bool flip_in = first && !TRANSPOSE;
+    const bool flip_out = last && TRANSPOSE;
     hipError_t e;
-    if (q == 0) {
-      e = launch_stage<TRANSPOSE, TIn>(static_cast<const TIn*>(in), out, blk, R.sign_bits,
-                                       plan.dim, plan.radix[t], plan.stride[t], M, !TRANSPOSE,
-                                       TRANSPOSE && plan.n == 1, stream);
-    } else {
-      e = launch_stage<TRANSPOSE, float>(out, out, blk, R.sign_bits, plan.dim, plan.radix[t],
-                                         plan.stride[t], M, false,
-                                         TRANSPOSE && q == plan.n - 1, stream);
-    }
+    if (first && last)
+      e = launch_stage<TRANSPOSE, TIn, TOut>(src, out, blk, R.sign_bits, plan.dim, plan.radix[t],
+                                             plan.stride[t], M, flip_in, flip_out, stream);
+    else if (first)
+      e = launch_stage<TRANSPOSE, TIn, float>(src, ws, blk, R.sign_bits, plan.dim, plan.radix[t],
+                                              plan.stride[t], M, flip_in, flip_out, stream);
+    else if (last)
+      e = launch_stage<TRANSPOSE, float, TOut>(ws, out, blk, R.sign_bits, plan.dim,
+                                               plan.radix[t], plan.stride[t], M, flip_in, flip_out,
+                                               stream);
+    else
+      e = launch_stage<TRANSPOSE, float, float>(ws, ws, blk, R.sign_bits, plan.dim,
+                                                plan.radix[t], plan.stride[t], M, flip_in, flip_out,
+                                                stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -330,10 +346,21 @@ hipError_t launch_by_stage(const harp_mixed_rotation& R, const void* in, float* 
 
 template <bool TRANSPOSE, typename TIn, typename TOut>
 hipError_t launch_typed(const harp_mixed_rotation& R, const void* in, void* out, int M,
-                        hipStream_t stream) {
+                        float* workspace, hipStream_t stream) {
   if constexpr (std::is_same<TOut, float>::value) {
-    return launch_by_stage<TRANSPOSE, TIn>(R, in, static_cast<float*>(out), M, stream);
+    float* o = static_cast<float*>(out);
+    return launch_by_stage<TRANSPOSE, TIn, float>(R, in, o, o, M, stream);
   } else {
+    // With a workspace the stages run over the whole chip, except for large
+    // batches of small power-of-two-ish radices on rows that leave room for
+    // two workgroups per CU, where the one-workgroup-per-row form (blocks
+    // reused from the L2 across rows, one HBM pass) was measured faster.
+    int rmax = 0;
+    for (int t = 0; t < R.n_stages; ++t) rmax = std::max(rmax, R.radix[t]);
+    const bool row_form = M >= kStageWideM && R.dim <= kRowFormMaxDim && rmax <= kRowFormMaxRadix;
+    if (workspace != nullptr && !row_form)
+      return launch_by_stage<TRANSPOSE, TIn, TOut>(R, in, workspace, static_cast<TOut*>(out), M,
+                                                   stream);
     const MixedPlan plan = make_plan(R);
     const size_t shmem = sizeof(float) * static_cast<size_t>(R.dim);
     if (shmem > 65536) {   // rows above 16384 floats: raise the dynamic LDS limit
@@ -353,17 +380,18 @@ hipError_t launch_typed(const harp_mixed_rotation& R, const void* in, void* out,
 
 hipError_t launch_rotate_mixed(const harp_mixed_rotation& R, const void* in, int in_dt,
                                void* out, int out_dt, int M, bool transpose,
-                               hipStream_t stream) {
+                               float* workspace, hipStream_t stream) {
   const bool ib = in_dt == HARP_BF16;
   const bool ob = out_dt == HARP_BF16;
+  float* ws = workspace;
   if (transpose) {   // y' is float32
-    if (ob) return launch_typed<true, float, uint16_t>(R, in, out, M, stream);
-    return launch_typed<true, float, float>(R, in, out, M, stream);
+    if (ob) return launch_typed<true, float, uint16_t>(R, in, out, M, ws, stream);
+    return launch_typed<true, float, float>(R, in, out, M, ws, stream);
   }
-  if (ib && ob) return launch_typed<false, uint16_t, uint16_t>(R, in, out, M, stream);
-  if (ib) return launch_typed<false, uint16_t, float>(R, in, out, M, stream);
-  if (ob) return launch_typed<false, float, uint16_t>(R, in, out, M, stream);
-  return launch_typed<false, float, float>(R, in, out, M, stream);
+  if (ib && ob) return launch_typed<false, uint16_t, uint16_t>(R, in, out, M, ws, stream);
+  if (ib) return launch_typed<false, uint16_t, float>(R, in, out, M, ws, stream);
+  if (ob) return launch_typed<false, float, uint16_t>(R, in, out, M, ws, stream);
+  return launch_typed<false, float, float>(R, in, out, M, ws, stream);
 }
 
 }  // namespace harp

@@ -166,8 +166,15 @@ size_t rotate_weight_workspace_bytes(int32_t N, int32_t K) {
   return align256(static_cast<size_t>(N) * K * 4);
 }
 
+size_t rotate_mixed_workspace_bytes(int32_t dim, int32_t M, int out_dt) {
+  if (dim < 2 || dim > HARP_MAX_MIXED_DIM || M < 0 || M > HARP_MAX_M) return 0;
+  if (out_dt != HARP_BF16) return 0;
+  return align256(static_cast<size_t>(M) * dim * 4);
+}
+
 harp_status validate_rotate_mixed(const harp_mixed_rotation* R, const void* in, int in_dt,
-                                  const void* out, int out_dt, int32_t M) {
+                                  const void* out, int out_dt, int32_t M,
+                                  const void* workspace, size_t ws_bytes) {
   if (R == nullptr || R->blocks == nullptr || R->sign_bits == nullptr) return HARP_ERR_NULL;
   if (R->n_stages < 1 || R->n_stages > HARP_MAX_STAGES) return HARP_ERR_SHAPE;
   int64_t prod = 1;                 // capped: 16 radices of 64 would overflow
@@ -183,6 +190,10 @@ harp_status validate_rotate_mixed(const harp_mixed_rotation* R, const void* in, 
   HARP_TRY(check_m(M));
   HARP_TRY(check_data(in, M));
   HARP_TRY(check_data(out, M));
+  if (workspace != nullptr && out_dt == HARP_BF16) {
+    if (ws_bytes < rotate_mixed_workspace_bytes(R->dim, M, out_dt)) return HARP_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return HARP_ERR_ALIGN;
+  }
   return HARP_OK;
 }
 

@@ -28,8 +28,10 @@ harp_status validate_fused(const harp_rotation* V, const harp_qweight* W,
                            const void* y, int y_dt, int32_t M,
                            const void* workspace, size_t ws_bytes);
 harp_status validate_dequant(const harp_qweight* W, const void* out, int out_dt);
+size_t rotate_mixed_workspace_bytes(int32_t dim, int32_t M, int out_dt);
 harp_status validate_rotate_mixed(const harp_mixed_rotation* R, const void* in, int in_dt,
-                                  const void* out, int out_dt, int32_t M);
+                                  const void* out, int out_dt, int32_t M,
+                                  const void* workspace, size_t ws_bytes);
 harp_status validate_rotate_weight(const harp_rotation* V, const harp_rotation* U,
                                    const float* W, const float* Wp, int32_t N, int32_t K,
                                    const void* workspace, size_t ws_bytes);

@@ -304,17 +304,36 @@ def mixed(dim=40, radices=(8, 5), blocks=FAKE, sb=FAKE, n=None):
     (mixed(blocks=MISALIGNED), L.HARP_ERR_ALIGN),
 ])
 def test_mixed_rotation_checks(R, expect):
-    assert L.lib.harp_rotate_in_mixed(ctypes.byref(R), FAKE, 0, FAKE, 0, 1, None) == expect
+    assert L.lib.harp_rotate_in_mixed(ctypes.byref(R), FAKE, 0, FAKE, 0, 1, None, 0, None) == expect
 
 
 def test_mixed_rotation_other_checks():
     R = mixed()
     f_in, f_out = L.lib.harp_rotate_in_mixed, L.lib.harp_rotate_out_mixed
-    assert f_in(None, FAKE, 0, FAKE, 0, 1, None) == L.HARP_ERR_NULL
-    assert f_in(ctypes.byref(R), FAKE, 7, FAKE, 0, 1, None) == L.HARP_ERR_DTYPE
-    assert f_in(ctypes.byref(R), FAKE, 0, FAKE, 0, -2, None) == L.HARP_ERR_SHAPE
-    assert f_in(ctypes.byref(R), 0, 0, FAKE, 0, 1, None) == L.HARP_ERR_NULL
-    assert f_in(ctypes.byref(R), 0, 0, 0, 0, 0, None) == L.HARP_OK
-    assert f_out(ctypes.byref(R), FAKE, FAKE, 9, 1, None) == L.HARP_ERR_DTYPE
-    assert f_out(ctypes.byref(R), FAKE, MISALIGNED, 0, 1, None) == L.HARP_ERR_ALIGN
-    assert f_out(ctypes.byref(R), 0, 0, 0, 0, None) == L.HARP_OK
+    assert f_in(None, FAKE, 0, FAKE, 0, 1, None, 0, None) == L.HARP_ERR_NULL
+    assert f_in(ctypes.byref(R), FAKE, 7, FAKE, 0, 1, None, 0, None) == L.HARP_ERR_DTYPE
+    assert f_in(ctypes.byref(R), FAKE, 0, FAKE, 0, -2, None, 0, None) == L.HARP_ERR_SHAPE
+    assert f_in(ctypes.byref(R), 0, 0, FAKE, 0, 1, None, 0, None) == L.HARP_ERR_NULL
+    assert f_in(ctypes.byref(R), 0, 0, 0, 0, 0, None, 0, None) == L.HARP_OK
+    assert f_out(ctypes.byref(R), FAKE, FAKE, 9, 1, None, 0, None) == L.HARP_ERR_DTYPE
+    assert f_out(ctypes.byref(R), FAKE, MISALIGNED, 0, 1, None, 0, None) == L.HARP_ERR_ALIGN
+    assert f_out(ctypes.byref(R), 0, 0, 0, 0, None, 0, None) == L.HARP_OK
+
+
+def test_mixed_rotation_workspace():
+    """bf16 outputs may bring a float32 workspace of M * dim floats; float32
+    outputs need none (a given one is ignored)."""
+    ws_bytes = L.lib.harp_rotate_mixed_workspace_bytes
+    assert ws_bytes(40, 3, L.HARP_BF16) == 512            # 3 * 40 * 4 = 480, 256-aligned
+    assert ws_bytes(5120, 512, L.HARP_BF16) == 5120 * 512 * 4
+    assert ws_bytes(40, 3, L.HARP_F32) == 0
+    assert ws_bytes(1, 3, L.HARP_BF16) == 0                # out of range: 0
+    assert ws_bytes(40, -1, L.HARP_BF16) == 0
+    assert ws_bytes(40, 0, L.HARP_BF16) == 0
+    R = mixed()
+    f_in, f_out = L.lib.harp_rotate_in_mixed, L.lib.harp_rotate_out_mixed
+    bf = L.HARP_BF16
+    assert f_in(ctypes.byref(R), FAKE, 0, FAKE, bf, 3, FAKE, 511, None) == L.HARP_ERR_WORKSPACE
+    assert f_out(ctypes.byref(R), FAKE, FAKE, bf, 3, FAKE, 0, None) == L.HARP_ERR_WORKSPACE
+    assert f_in(ctypes.byref(R), FAKE, 0, FAKE, bf, 3, MISALIGNED, 512, None) == L.HARP_ERR_ALIGN
+    assert f_in(ctypes.byref(R), 0, 0, 0, bf, 0, FAKE, 0, None) == L.HARP_OK

@@ -87,6 +87,47 @@ def test_rotate_mixed_in_out(radices, M, xdt):
     assert np.all(np.abs(d.host(yb) - refb) <= ulp + delta)
 
 
+def assert_bf16_of(got, ref64):
+    """got = bf16 of a float32 result within the butterfly bar of ref64."""
+    refb = O.bf16_round(ref64)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(refb))[1] - 8)
+    delta = BUTTERFLY_TOL * np.sqrt(np.mean(ref64 ** 2))
+    assert np.all(np.abs(got - refb) <= ulp + delta)
+    assert np.mean(got != refb) < 0.01
+
+
+WS_CASES = [((8, 8, 8, 5, 2), 1), ((8, 8, 4, 43), 3), ((64, 64, 7), 70), ((43, 4, 64), 2),
+            ((5, 3), 9), ((3,), 4), ((8, 8, 8, 8, 7), 2)]
+
+
+@pytest.mark.parametrize("radices,M", WS_CASES)
+def test_rotate_mixed_bf16_workspace(radices, M):
+    """bf16 outputs with a workspace (one launch per stage in float32, the
+    last writing bf16) against the oracle and against the one-workgroup-per-
+    row path without a workspace: both apply every block in the same float32
+    order, so the bf16 outputs are equal."""
+    d = D()
+    R, blocks, signs = device_side(radices, 9)
+    dim = R.dim
+    ws = torch.empty(H().harp_rotate_mixed_workspace_bytes(dim, M, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    x = S.activations(M, dim, rng(5, dim, M), "bf16")
+    xd = d.dev_x(x, "bf16")
+    ref = O.mixed_forward(d.x_f64(x, "bf16"), radices, blocks, signs)
+    a = torch.empty((M, dim), dtype=torch.bfloat16, device="cuda")
+    b = torch.empty((M, dim), dtype=torch.bfloat16, device="cuda")
+    H().harp_rotate_in_mixed(R, xd, a, workspace=ws)
+    H().harp_rotate_in_mixed(R, xd, b)
+    assert_bf16_of(d.host(a), ref)
+    assert torch.equal(a, b)
+    yp = rng(6, dim, M).normal(size=(M, dim)).astype(np.float32)
+    reft = O.mixed_transpose(yp.astype(np.float64), radices, blocks, signs)
+    H().harp_rotate_out_mixed(R, d.dev(yp), a, workspace=ws)
+    H().harp_rotate_out_mixed(R, d.dev(yp), b)
+    assert_bf16_of(d.host(a), reft)
+    assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("radices", [(4, 4, 4, 4, 4, 4), (16, 8, 32)])
 def test_rotate_mixed_zero_parameters_is_hadamard(radices):
     """theta = 0 with power-of-two radices: F x = H_d D x / sqrt(d) (scipy)."""
