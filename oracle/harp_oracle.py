@@ -510,6 +510,29 @@ def linear(x: np.ndarray, words: np.ndarray, scale: np.ndarray,
     return transpose(yp, cs_u, signs_u, b_u)
 
 
+def linear_mixed(x: np.ndarray, words: np.ndarray, scale: np.ndarray,
+                 zero: np.ndarray, bits: int, radices_v, blocks_v, signs_v,
+                 radices_u, blocks_u, signs_u, mfma_contract: bool = False,
+                 weights_exact: bool = False) -> np.ndarray:
+    """y = F_U^T (W_hat (F_V x)) with mixed-radix sides (technical summary
+    §2.1-§2.2 for F, §2.4 for the linear); x (M, K) -> (M, N).
+
+    The same steps as ``linear``: dequantize, rotate the input with
+    ``mixed_forward``, model the matrix-core rounding points when asked,
+    contract in float64, rotate the output with ``mixed_transpose``.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    K = x.shape[-1]
+    w_hat = dequant(unpack(words, bits, K), scale, zero)
+    xt = mixed_forward(x, radices_v, blocks_v, signs_v)
+    if mfma_contract:
+        xt = bf16_round(xt)
+        if not weights_exact:
+            w_hat = bf16_round(w_hat)
+    yp = xt @ w_hat.T
+    return mixed_transpose(yp, radices_u, blocks_u, signs_u)
+
+
 def rel_l2(a: np.ndarray, ref: np.ndarray) -> float:
     """||a - ref||_2 / ||ref||_2 over the whole array."""
     a = np.asarray(a, dtype=np.float64)

@@ -145,3 +145,72 @@ def test_paper_schedule_5120_orthogonal():
     y = O.mixed_forward(x, radices, blocks, signs)
     assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-12)
     assert np.allclose(O.mixed_transpose(y, radices, blocks, signs), x, atol=1e-12)
+
+
+def packed_weight(N, K, bits, rng):
+    """Random codes, scales and zeros in the packed format (the packer is
+    pinned to hand-derived layout fixtures elsewhere)."""
+    qmax = (1 << bits) - 1
+    q = rng.integers(0, qmax + 1, size=(N, K))
+    scale = (rng.uniform(0.5, 1.5, size=(N, K // 64)) * 0.01).astype(np.float16)
+    zero = rng.integers(0, qmax + 1, size=(N, K // 64)).astype(np.float16)
+    return O.pack(q, bits), scale, zero, q
+
+
+def test_linear_mixed_all_two_is_linear():
+    """Radix-2 schedules on both sides reproduce the radix-2 linear exactly."""
+    K, N, bits = 64, 128, 3
+    rv, ru = (2,) * 6, (2,) * 7
+    pv, pu = random_params(rv, rng0), random_params(ru, rng0)
+    sv, su = random_signs(K, rng0), random_signs(N, rng0)
+    words, scale, zero, _ = packed_weight(N, K, bits, rng0)
+    cs = []
+    for radices, params in ((rv, pv), (ru, pu)):
+        t = math.pi / 4 + np.stack([params[s][:, 0] for s in range(len(radices))])[None]
+        cs.append(np.stack([np.cos(t), np.sin(t)], axis=-1))
+    x = rng0.normal(size=(3, K))
+    for contract in (False, True):
+        got = O.linear_mixed(x, words, scale, zero, bits, rv, O.mixed_blocks(rv, pv), sv,
+                             ru, O.mixed_blocks(ru, pu), su, mfma_contract=contract)
+        ref = O.linear(x, words, scale, zero, bits, cs[0], sv, K, cs[1], su, N,
+                       mfma_contract=contract)
+        assert np.allclose(got, ref, atol=1e-12, rtol=0)
+
+
+def test_linear_mixed_dense_composition():
+    """y = F_U^T W_hat F_V x with F built by digit enumeration and W_hat
+    decoded code by code (q - z) s."""
+    rv, ru = (4, 4, 4), (5, 2, 3, 4)                # K = 64 (one quantization group)
+    K, N, bits = 64, int(np.prod(ru)), 4
+    pv, pu = random_params(rv, rng0), random_params(ru, rng0)
+    bv, bu = O.mixed_blocks(rv, pv, mixer_seed=3), O.mixed_blocks(ru, pu, mixer_seed=3)
+    sv, su = random_signs(K, rng0), random_signs(N, rng0)
+    words, scale, zero, q = packed_weight(N, K, bits, rng0)
+    Fv = dense_by_enumeration(rv, bv, sv)
+    Fu = dense_by_enumeration(ru, bu, su)
+    g = np.arange(K) // 64
+    w_hat = (q - zero.astype(np.float64)[:, g]) * scale.astype(np.float64)[:, g]
+    x = rng0.normal(size=(5, K))
+    ref = x @ Fv.T @ w_hat.T @ Fu
+    got = O.linear_mixed(x, words, scale, zero, bits, rv, bv, sv, ru, bu, su)
+    assert np.allclose(got, ref, atol=1e-12, rtol=0)
+
+
+def test_linear_mixed_contract_rounds_operands():
+    """Contract mode equals the float64 product of bf16-rounded x~ and w_hat
+    (both rounded by the pinned bf16 rounding), weights_exact keeps w_hat."""
+    rv, ru = (8, 8), (5, 8)
+    K, N, bits = 64, 40, 2
+    bv = O.mixed_blocks(rv, random_params(rv, rng0))
+    bu = O.mixed_blocks(ru, random_params(ru, rng0))
+    sv, su = random_signs(K, rng0), random_signs(N, rng0)
+    words, scale, zero, q = packed_weight(N, K, bits, rng0)
+    x = rng0.normal(size=(2, K))
+    xt = O.mixed_forward(x, rv, bv, sv)
+    w_hat = O.dequant(O.unpack(words, bits, K), scale, zero)
+    for exact in (False, True):
+        w = w_hat if exact else O.bf16_round(w_hat)
+        ref = O.mixed_transpose(O.bf16_round(xt) @ w.T, ru, bu, su)
+        got = O.linear_mixed(x, words, scale, zero, bits, rv, bv, sv, ru, bu, su,
+                             mfma_contract=True, weights_exact=exact)
+        assert np.allclose(got, ref, atol=1e-12, rtol=0)
