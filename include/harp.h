@@ -254,6 +254,28 @@ size_t harp_deq_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
 size_t harp_linear_workspace_bytes(int32_t M, int32_t N, int32_t K);
 
 /*
+ * The whole linear with mixed-radix sides, y = F_U^T deq(W) F_V x
+ * (technical summary §2.4 with the stages of §2.1-2.2), for dimensions that
+ * are no power of two (e.g. 5120 = 8*8*8*5*2).  Requires V->dim == W->K and
+ * U->dim == W->N.  M < 16: float32 x~ and the vector-ALU product of
+ * harp_deq_gemv; 16 <= M <= 64: bf16 x~ and the small-batch matrix-core
+ * product; M > 64: bf16 x~ and the matrix-core GEMM with split K.  Same
+ * rounding points as harp_linear_fused.
+ *   x  [M][K] of x_dt;  y  [M][N] of y_dt.
+ *   workspace  at least harp_linear_mixed_workspace_bytes(M, N, K) bytes,
+ *              256-byte aligned, zero-filled before its first use (the
+ *              split-K counters; every call leaves them at zero).  Calls that
+ *              share a workspace must not overlap in time.
+ */
+harp_status harp_linear_fused_mixed(const harp_mixed_rotation *V, const harp_qweight *W,
+                                    const harp_mixed_rotation *U, const void *x,
+                                    harp_dtype x_dt, void *y, harp_dtype y_dt,
+                                    int32_t M, void *workspace, size_t ws_bytes,
+                                    harp_stream stream);
+/* Workspace bytes of harp_linear_fused_mixed; 0 for arguments out of range. */
+size_t harp_linear_mixed_workspace_bytes(int32_t M, int32_t N, int32_t K);
+
+/*
  * y = F_U^T deq(W) F_V x, the whole linear (technical summary §2.4 and §5).
  * M < 16 runs rotate-in (float32 x~), the vector-ALU product and rotate-out,
  * with the first two in one launch where harp_rotate_in_deq_gemv supports

@@ -7,7 +7,7 @@ importing this package fails if libharp.so has not been built.
 from ._lib import (  # noqa: F401
     HARP_BF16, HARP_F32, HarpError, MixedRotation, QWeight, Rotation, harp_dequant,
     harp_deq_gemm, harp_deq_gemm_workspace_bytes, harp_deq_gemv, harp_last_hip_error, harp_linear_fused,
-    harp_linear_workspace_bytes, harp_quantize_pack, harp_rotate_in, harp_rotate_in_deq_gemv,
+    harp_linear_fused_mixed, harp_linear_mixed_workspace_bytes, harp_linear_workspace_bytes, harp_quantize_pack, harp_rotate_in, harp_rotate_in_deq_gemv,
     harp_rotate_in_mixed, harp_rotate_mixed_workspace_bytes, harp_rotate_out, harp_rotate_out_mixed, harp_rotate_weight,
     harp_rotate_weight_workspace_bytes, lib,
     status_string,

@@ -35,6 +35,7 @@ EXPORTED = (
     "harp_deq_gemm_workspace_bytes", "harp_linear_workspace_bytes", "harp_linear_fused", "harp_dequant",
     "harp_rotate_weight", "harp_rotate_weight_workspace_bytes", "harp_quantize_pack",
     "harp_rotate_in_mixed", "harp_rotate_out_mixed", "harp_rotate_mixed_workspace_bytes",
+    "harp_linear_fused_mixed", "harp_linear_mixed_workspace_bytes",
     "harp_status_string", "harp_last_hip_error",
 )
 
@@ -103,6 +104,9 @@ def _load() -> ctypes.CDLL:
         "harp_rotate_out_mixed": (c_int32, [MR, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
                                              c_size_t, c_void_p]),
         "harp_rotate_mixed_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
+        "harp_linear_fused_mixed": (c_int32, [MR, Q, MR, c_void_p, c_int32, c_void_p, c_int32,
+                                              c_int32, c_void_p, c_size_t, c_void_p]),
+        "harp_linear_mixed_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
         "harp_quantize_pack": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p,
                                           c_void_p, c_void_p]),
         "harp_status_string": (c_char_p, [c_int32]),
@@ -285,6 +289,19 @@ def harp_rotate_out_mixed(R: MixedRotation, yt, y, workspace=None, M: int | None
     wp, wb = _ws(workspace)
     _check(lib.harp_rotate_out_mixed(ctypes.byref(R.c), _ptr(yt), _ptr(y), _dtype_code(y), M,
                                      wp, wb, _stream(stream)), "harp_rotate_out_mixed")
+
+
+def harp_linear_mixed_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib.harp_linear_mixed_workspace_bytes(M, N, K))
+
+
+def harp_linear_fused_mixed(V: MixedRotation, W: QWeight, U: MixedRotation, x, y, workspace,
+                            M: int | None = None, stream=None) -> None:
+    M = x.shape[0] if M is None else M
+    wp, wb = _ws(workspace)
+    _check(lib.harp_linear_fused_mixed(ctypes.byref(V.c), ctypes.byref(W.c), ctypes.byref(U.c),
+                                       _ptr(x), _dtype_code(x), _ptr(y), _dtype_code(y), M,
+                                       wp, wb, _stream(stream)), "harp_linear_fused_mixed")
 
 
 def harp_rotate_weight_workspace_bytes(N: int, K: int) -> int:

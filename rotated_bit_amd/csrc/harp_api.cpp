@@ -136,6 +136,42 @@ harp_status harp_linear_fused(const harp_rotation* V, const harp_qweight* W,
   return from_hip(harp::launch_rotate(*U, yp, HARP_F32, y, y_dt, M, true, s));
 }
 
+size_t harp_linear_mixed_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  return harp::mixed_workspace_bytes(M, N, K);
+}
+
+harp_status harp_linear_fused_mixed(const harp_mixed_rotation* V, const harp_qweight* W,
+                                    const harp_mixed_rotation* U, const void* x,
+                                    harp_dtype x_dt, void* y, harp_dtype y_dt, int32_t M,
+                                    void* workspace, size_t ws_bytes, harp_stream stream) {
+  const harp_status st =
+      harp::validate_fused_mixed(V, W, U, x, x_dt, y, y_dt, M, workspace, ws_bytes);
+  if (st != HARP_OK || M == 0) return st;
+  const hipStream_t s = as_stream(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int32_t N = W->N, K = W->K;
+  float* xf = reinterpret_cast<float*>(ws);
+  float* yp = reinterpret_cast<float*>(ws + harp::mixed_ws_yp_offset(M, K));
+  float* ys = reinterpret_cast<float*>(ws + harp::mixed_ws_ys_offset(M, N, K));
+  harp_status r;
+  if (M < harp::kMfmaMinM) {
+    r = from_hip(harp::launch_rotate_mixed(*V, x, x_dt, xf, HARP_F32, M, false, nullptr, s));
+    if (r != HARP_OK) return r;
+    r = from_hip(harp::launch_gemv(*W, xf, yp, M, s));
+  } else {
+    uint16_t* xb = reinterpret_cast<uint16_t*>(ws + harp::mixed_ws_xb_offset(M, K));
+    r = from_hip(harp::launch_rotate_mixed(*V, x, x_dt, xb, HARP_BF16, M, false, xf, s));
+    if (r != HARP_OK) return r;
+    if (M <= harp::kSkinnyMaxM)
+      r = from_hip(harp::launch_gemm_skinny(*W, xb, yp, M, s));
+    else
+      r = from_hip(harp::launch_gemm(*W, xb, yp, M, harp::gemm_splits(M, N, K),
+                                     ws + harp::mixed_ws_gemm_offset(M, N, K), s));
+  }
+  if (r != HARP_OK) return r;
+  return from_hip(harp::launch_rotate_mixed(*U, yp, HARP_F32, y, y_dt, M, true, ys, s));
+}
+
 harp_status harp_dequant(const harp_qweight* W, void* out, harp_dtype out_dt,
                          harp_stream stream) {
   const harp_status st = harp::validate_dequant(W, out, out_dt);

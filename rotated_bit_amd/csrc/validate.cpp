@@ -172,9 +172,7 @@ size_t rotate_mixed_workspace_bytes(int32_t dim, int32_t M, int out_dt) {
   return align256(static_cast<size_t>(M) * dim * 4);
 }
 
-harp_status validate_rotate_mixed(const harp_mixed_rotation* R, const void* in, int in_dt,
-                                  const void* out, int out_dt, int32_t M,
-                                  const void* workspace, size_t ws_bytes) {
+static harp_status check_mixed(const harp_mixed_rotation* R) {
   if (R == nullptr || R->blocks == nullptr || R->sign_bits == nullptr) return HARP_ERR_NULL;
   if (R->n_stages < 1 || R->n_stages > HARP_MAX_STAGES) return HARP_ERR_SHAPE;
   int64_t prod = 1;                 // capped: 16 radices of 64 would overflow
@@ -186,6 +184,13 @@ harp_status validate_rotate_mixed(const harp_mixed_rotation* R, const void* in, 
   if (R->dim > HARP_MAX_MIXED_DIM) return HARP_ERR_UNSUPPORTED;
   if (R->dim < 2 || prod != R->dim) return HARP_ERR_SHAPE;
   if (!aligned(R->blocks, 16) || !aligned(R->sign_bits, 16)) return HARP_ERR_ALIGN;
+  return HARP_OK;
+}
+
+harp_status validate_rotate_mixed(const harp_mixed_rotation* R, const void* in, int in_dt,
+                                  const void* out, int out_dt, int32_t M,
+                                  const void* workspace, size_t ws_bytes) {
+  HARP_TRY(check_mixed(R));
   if (bad_dtype(in_dt) || bad_dtype(out_dt)) return HARP_ERR_DTYPE;
   HARP_TRY(check_m(M));
   HARP_TRY(check_data(in, M));
@@ -194,6 +199,53 @@ harp_status validate_rotate_mixed(const harp_mixed_rotation* R, const void* in, 
     if (ws_bytes < rotate_mixed_workspace_bytes(R->dim, M, out_dt)) return HARP_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return HARP_ERR_ALIGN;
   }
+  return HARP_OK;
+}
+
+// Workspace of the mixed-radix linear: x~ as float32 (M < 16: the operand;
+// otherwise the stage buffer of the bf16 operand, which follows), y' float32,
+// the stage buffer of a bf16 output, then (M > 64) the GEMM's split-K area.
+size_t mixed_ws_xb_offset(int32_t M, int32_t K) {
+  return align256(static_cast<size_t>(M) * K * 4);
+}
+
+size_t mixed_ws_yp_offset(int32_t M, int32_t K) {
+  return mixed_ws_xb_offset(M, K) +
+         (M >= kMfmaMinM ? align256(static_cast<size_t>(M) * K * 2) : 0);
+}
+
+size_t mixed_ws_ys_offset(int32_t M, int32_t N, int32_t K) {
+  return mixed_ws_yp_offset(M, K) + align256(static_cast<size_t>(M) * N * 4);
+}
+
+size_t mixed_ws_gemm_offset(int32_t M, int32_t N, int32_t K) {
+  return mixed_ws_ys_offset(M, N, K) + align256(static_cast<size_t>(M) * N * 4);
+}
+
+size_t mixed_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  if (M < 0 || M > HARP_MAX_M || N < 2 || N > HARP_MAX_MIXED_DIM || K < 64 ||
+      K > HARP_MAX_MIXED_DIM)
+    return 0;
+  const size_t gemm = M > kSkinnyMaxM ? gemm_workspace_bytes(M, N, K) : 0;
+  return mixed_ws_gemm_offset(M, N, K) + gemm;
+}
+
+harp_status validate_fused_mixed(const harp_mixed_rotation* V, const harp_qweight* W,
+                                 const harp_mixed_rotation* U, const void* x, int x_dt,
+                                 const void* y, int y_dt, int32_t M,
+                                 const void* workspace, size_t ws_bytes) {
+  HARP_TRY(check_mixed(V));
+  HARP_TRY(check_qweight(W));
+  HARP_TRY(check_mixed(U));
+  if (V->dim != W->K || U->dim != W->N) return HARP_ERR_SHAPE;
+  if (bad_dtype(x_dt) || bad_dtype(y_dt)) return HARP_ERR_DTYPE;
+  HARP_TRY(check_m(M));
+  HARP_TRY(check_data(x, M));
+  HARP_TRY(check_data(y, M));
+  if (M == 0) return HARP_OK;
+  if (workspace == nullptr) return HARP_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return HARP_ERR_ALIGN;
+  if (ws_bytes < mixed_workspace_bytes(M, W->N, W->K)) return HARP_ERR_WORKSPACE;
   return HARP_OK;
 }
 

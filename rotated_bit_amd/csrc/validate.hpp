@@ -60,6 +60,15 @@ constexpr int32_t kMfmaMinM = 16;
 // kMfmaMinM rows and bf16 from there on.
 size_t workspace_bytes(int32_t M, int32_t N, int32_t K);
 size_t workspace_yp_offset(int32_t M, int32_t K);
+size_t mixed_ws_xb_offset(int32_t M, int32_t K);
+size_t mixed_ws_yp_offset(int32_t M, int32_t K);
+size_t mixed_ws_ys_offset(int32_t M, int32_t N, int32_t K);
+size_t mixed_ws_gemm_offset(int32_t M, int32_t N, int32_t K);
+size_t mixed_workspace_bytes(int32_t M, int32_t N, int32_t K);
+harp_status validate_fused_mixed(const harp_mixed_rotation* V, const harp_qweight* W,
+                                 const harp_mixed_rotation* U, const void* x, int x_dt,
+                                 const void* y, int y_dt, int32_t M,
+                                 const void* workspace, size_t ws_bytes);
 size_t workspace_gemm_offset(int32_t M, int32_t N, int32_t K);
 
 const char* status_string(harp_status s);

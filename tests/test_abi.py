@@ -337,3 +337,34 @@ def test_mixed_rotation_workspace():
     assert f_out(ctypes.byref(R), FAKE, FAKE, bf, 3, FAKE, 0, None) == L.HARP_ERR_WORKSPACE
     assert f_in(ctypes.byref(R), FAKE, 0, FAKE, bf, 3, MISALIGNED, 512, None) == L.HARP_ERR_ALIGN
     assert f_in(ctypes.byref(R), 0, 0, 0, bf, 0, FAKE, 0, None) == L.HARP_OK
+
+
+def test_linear_mixed_workspace_bytes():
+    f = L.lib.harp_linear_mixed_workspace_bytes
+    # M = 1: float32 x~ (20480), y' (20480), bf16-output stage buffer (20480)
+    assert f(1, 5120, 5120) == 3 * 20480
+    # M = 16: float32 stage buffer and bf16 x~ of the input, y', output buffer
+    assert f(16, 5120, 5120) == 327680 + 163840 + 327680 + 327680
+    # M = 100: plus the GEMM's split-K partials (4 slices of 40 tiles) and counters
+    assert f(100, 5120, 5120) == 4 * 2048000 - 1024000 + 4 * 40 * 128 * 128 * 4 + 256
+    assert f(1, 5120, 32) == 0            # K < 64
+    assert f(-1, 5120, 5120) == 0
+    assert f(1, 40000, 5120) == 0         # beyond the mixed-radix maximum
+
+
+def test_linear_fused_mixed_checks():
+    V, U = mixed(dim=320, radices=(8, 8, 5)), mixed(dim=40, radices=(8, 5))
+    W = qw(N=40, K=320)
+    b = ctypes.byref
+    f = L.lib.harp_linear_fused_mixed
+    need = L.lib.harp_linear_mixed_workspace_bytes(2, 40, 320)
+    assert f(None, b(W), b(U), FAKE, 0, FAKE, 0, 2, FAKE, need, None) == L.HARP_ERR_NULL
+    assert f(b(V), b(qw(N=40, K=256)), b(U), FAKE, 0, FAKE, 0, 2, FAKE, need, None) == \
+        L.HARP_ERR_SHAPE                                   # V->dim != K
+    assert f(b(V), b(W), b(V), FAKE, 0, FAKE, 0, 2, FAKE, need, None) == L.HARP_ERR_SHAPE
+    assert f(b(V), b(W), b(U), FAKE, 5, FAKE, 0, 2, FAKE, need, None) == L.HARP_ERR_DTYPE
+    assert f(b(V), b(W), b(U), FAKE, 0, FAKE, 0, 2, None, 0, None) == L.HARP_ERR_WORKSPACE
+    assert f(b(V), b(W), b(U), FAKE, 0, FAKE, 0, 2, FAKE, need - 1, None) == \
+        L.HARP_ERR_WORKSPACE
+    assert f(b(V), b(W), b(U), FAKE, 0, FAKE, 0, 2, FAKE + 16, need, None) == L.HARP_ERR_ALIGN
+    assert f(b(V), b(W), b(U), 0, 0, 0, 0, 0, None, 0, None) == L.HARP_OK

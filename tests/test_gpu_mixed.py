@@ -140,3 +140,51 @@ def test_rotate_mixed_zero_parameters_is_hadamard(radices):
     Hd = scipy.linalg.hadamard(dim) / math.sqrt(dim)
     ref = (x.astype(np.float64) * O.decode_signs(signs, dim)) @ Hd.T
     assert O.rel_l2(d.host(xt), ref) <= BUTTERFLY_TOL
+
+
+# The fused linear over mixed-radix sides.  Product paths and their rounding
+# points follow the batch size as for the radix-2 fused linear: below 16 rows
+# float32 throughout; up to 64 the codes enter the matrix cores exactly and
+# only x~ is rounded to bf16; above, x~ and w_hat are both rounded.
+FP32_PATH_TOL = 2e-5
+MFMA_PATH_TOL = 3e-4
+LINEAR_MIXED_CASES = [
+    ((8, 8, 8, 5, 2), (8, 8, 8, 5, 2), 2, 1, "f32"),
+    ((8, 8, 8, 5, 2), (8, 8, 8, 5, 2), 2, 5, "bf16"),
+    ((8, 8, 8, 8), (8, 8, 4, 43), 4, 16, "f32"),     # 4096 -> 11008
+    ((8, 8, 4, 43), (8, 8, 8, 8), 3, 40, "bf16"),    # 11008 -> 4096
+    ((8, 8, 8, 5, 2), (16, 16, 20), 2, 100, "f32"),  # 5120 -> 5120, GEMM with split K
+    ((64, 5), (40, 8), 2, 3, "bf16"),                # 320 -> 320, ragged tiles
+]
+
+
+@pytest.mark.parametrize("rv,ru,bits,M,ydt", LINEAR_MIXED_CASES)
+def test_linear_fused_mixed(rv, ru, bits, M, ydt):
+    d = D()
+    V, bv, sv = device_side(rv, 21)
+    U, bu, su = device_side(ru, 22)
+    K, N = V.dim, U.dim
+    w = S.qweight(N, K, bits, rng(7, N, K, bits))
+    W = d.dev_qweight(w)
+    x = S.activations(M, K, rng(8, K, M), "bf16", S.outlier_channels(K, rng(9, K)))
+    ws = torch.zeros(H().harp_linear_mixed_workspace_bytes(M, N, K), dtype=torch.uint8,
+                     device="cuda")
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    H().harp_linear_fused_mixed(V, W, U, d.dev_x(x, "bf16"), y, ws)
+    contract = M >= 16
+    ref = O.linear_mixed(d.x_f64(x, "bf16"), w.words, w.scale.view(np.float16),
+                         w.zero.view(np.float16), bits, rv, bv, sv, ru, bu, su,
+                         mfma_contract=contract, weights_exact=16 <= M <= 64)
+    tol = MFMA_PATH_TOL if contract else FP32_PATH_TOL
+    r = O.rel_l2(d.host(y), ref)
+    print(f"[linear mixed {rv}->{ru} {bits}-bit M={M}] rel_l2={r:.3e}", flush=True)
+    assert r <= tol
+    # a second call on the same workspace (split-K counters left at zero)
+    y2 = torch.empty_like(y)
+    H().harp_linear_fused_mixed(V, W, U, d.dev_x(x, "bf16"), y2, ws)
+    assert torch.equal(y, y2)
+    if ydt == "bf16":
+        # the bf16 output is the float32 result rounded to nearest even
+        yb = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        H().harp_linear_fused_mixed(V, W, U, d.dev_x(x, "bf16"), yb, ws)
+        assert torch.equal(yb, y.to(torch.bfloat16))
