@@ -392,6 +392,38 @@ def main():
             mixed["x".join(str(b) for b in radices)] = entry
             del R
             torch.cuda.empty_cache()
+        # the whole linear on a 5120-wide layer (8x8x8x5x2 on both sides), 2-bit
+        radices, bits = (8, 8, 8, 5, 2), 2
+        d = int(np.prod(radices))
+        nblk = sum(d * b for b in radices)
+        lin = {}
+        for M in (1, 16):
+            inst = []
+            for _ in range(32):
+                V = H.MixedRotation(torch.randn(nblk, device="cuda") * 0.1,
+                                    torch.zeros((d + 31) // 32, dtype=torch.int32, device="cuda"),
+                                    radices)
+                U = H.MixedRotation(torch.randn(nblk, device="cuda") * 0.1,
+                                    torch.zeros((d + 31) // 32, dtype=torch.int32, device="cuda"),
+                                    radices)
+                words = torch.randint(-2**31, 2**31 - 1, (d, d * bits // 32), dtype=torch.int32,
+                                      device="cuda")
+                sc = torch.full((d, d // 64), 0.01, dtype=torch.float16, device="cuda").view(torch.int16)
+                zr = torch.full((d, d // 64), 1.0, dtype=torch.float16, device="cuda").view(torch.int16)
+                W = H.QWeight(words, sc, zr, d, d, bits)
+                x = torch.randn((M, d), device="cuda").to(torch.bfloat16)
+                y = torch.empty((M, d), device="cuda")
+                ws = torch.zeros(H.harp_linear_mixed_workspace_bytes(M, d, d), dtype=torch.uint8,
+                                 device="cuda")
+                inst.append((V, W, U, x, y, ws))
+            ms, _ = time_graph(torch, lambda: [H.harp_linear_fused_mixed(*i) for i in inst], 5)
+            us = ms * 1e3 / len(inst)
+            nb = d * d * bits // 8 + d * (d // 64) * 4 + 2 * (4 * nblk + d // 8) + 2 * M * d + 4 * M * d
+            lin[f"M{M}_us"] = round(us, 2)
+            lin[f"M{M}_GB_s"] = round(nb / (us * 1e-6) / 1e9, 1)
+            del inst
+            torch.cuda.empty_cache()
+        mixed["linear_5120x5120_2bit"] = lin
         log("mixed radix: " + json.dumps(mixed))
 
     # offline preparation: W' = F_U W F_V^T, then quantize and pack (2-bit)
