@@ -218,29 +218,42 @@ __global__ __launch_bounds__(WAVES * kWave) void mixed_stage_kernel(
   }
 }
 
+// Stages 0 .. seg_n - 1 act inside contiguous sub-rows of G = b_0 ... b_{seg_n-1}
+// elements (sub-row h of a row holds the groups h G / b_t ..., whose blocks
+// start h G b_t floats into stage t's).  One workgroup takes one sub-row
+// into LDS and applies those stages (ascending for F, descending for F^T);
+// with seg_n = n and G = dim it rotates a whole row.  The sign flip is
+// applied on load for F (these stages come first) and on store for F^T
+// (they come last).
 template <bool TRANSPOSE, typename TIn, typename TOut>
 __global__ __launch_bounds__(kMixedThreads) void mixed_kernel(
     const TIn* __restrict__ in, TOut* __restrict__ out, const float* __restrict__ blocks,
-    const uint32_t* __restrict__ sign, MixedPlan plan) {
+    const uint32_t* __restrict__ sign, MixedPlan plan, int seg_n, int G) {
   extern __shared__ float u[];
   const int dim = plan.dim;
-  const size_t row = blockIdx.x;
-  const TIn* src = in + row * dim;
-  TOut* dst = out + row * dim;
-  for (int i = threadIdx.x; i < dim; i += kMixedThreads) {
+  const int subs = dim / G;
+  const size_t row = blockIdx.x / subs;
+  const int h = blockIdx.x - static_cast<int>(row) * subs;
+  const size_t base = row * dim + static_cast<size_t>(h) * G;
+  const TIn* src = in + base;
+  TOut* dst = out + base;
+  for (int i = threadIdx.x; i < G; i += kMixedThreads) {
     float v = load_elem(src, i);
-    if (!TRANSPOSE) v = flip_sign(v, (sign[i >> 5] >> (i & 31)) & 1u);
+    const int gi = h * G + i;
+    if (!TRANSPOSE) v = flip_sign(v, (sign[gi >> 5] >> (gi & 31)) & 1u);
     u[i] = v;
   }
   __syncthreads();
-  for (int q = 0; q < plan.n; ++q) {
-    const int t = TRANSPOSE ? plan.n - 1 - q : q;
-    run_stage<TRANSPOSE>(u, blocks + plan.offset[t], dim, plan.radix[t], plan.stride[t]);
+  for (int q = 0; q < seg_n; ++q) {
+    const int t = TRANSPOSE ? seg_n - 1 - q : q;
+    const float* blk = blocks + plan.offset[t] + static_cast<size_t>(h) * G * plan.radix[t];
+    run_stage<TRANSPOSE>(u, blk, G, plan.radix[t], plan.stride[t]);
     __syncthreads();
   }
-  for (int i = threadIdx.x; i < dim; i += kMixedThreads) {
+  for (int i = threadIdx.x; i < G; i += kMixedThreads) {
     float v = u[i];
-    if (TRANSPOSE) v = flip_sign(v, (sign[i >> 5] >> (i & 31)) & 1u);
+    const int gi = h * G + i;
+    if (TRANSPOSE) v = flip_sign(v, (sign[gi >> 5] >> (gi & 31)) & 1u);
     store_elem(dst, i, v);
   }
 }
@@ -309,36 +322,88 @@ hipError_t launch_stage(const TIn* src, TOut* dst, const float* blk, const uint3
 #undef HARP_STAGE
 }
 
-// One launch per stage: stage 0 reads the input, the others run in place in
-// the float32 buffer ws (the output itself for a float32 output), and the
-// last writes the output.
+// The leading stages whose radices multiply to at most kSegMaxLen act
+// inside contiguous sub-rows of that length: for small batches they run as
+// one launch, one workgroup per sub-row in LDS, when there are at least two
+// of them.
+constexpr int kSegMaxLen = 512;
+
+int lead_segment(const MixedPlan& p, int* G) {
+  int g = 1, k = 0;
+  while (k < p.n && g * p.radix[k] <= kSegMaxLen) g *= p.radix[k++];
+  *G = g;
+  return k;
+}
+
+template <bool TRANSPOSE, typename TIn, typename TOut>
+hipError_t launch_rows(const MixedPlan& plan, int seg_n, int G, const TIn* in, TOut* out,
+                       const float* blocks, const uint32_t* sign, int M, hipStream_t stream) {
+  const size_t shmem = sizeof(float) * static_cast<size_t>(G);
+  if (shmem > 65536) {   // rows above 16384 floats: raise the dynamic LDS limit
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&mixed_kernel<TRANSPOSE, TIn, TOut>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shmem));
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid(static_cast<unsigned>(static_cast<size_t>(M) * (plan.dim / G)));
+  hipLaunchKernelGGL((mixed_kernel<TRANSPOSE, TIn, TOut>), grid, dim3(kMixedThreads), shmem,
+                     stream, in, out, blocks, sign, plan, seg_n, G);
+  return hipGetLastError();
+}
+
+// Launch by launch: the fused leading segment (first for F, last for F^T)
+// and one launch per other stage.  The first launch reads the input, the
+// others run in place in the float32 buffer ws (the output itself for a
+// float32 output), and the last writes the output.
 template <bool TRANSPOSE, typename TIn, typename TOut>
 hipError_t launch_by_stage(const harp_mixed_rotation& R, const void* in, float* ws, TOut* out,
                            int M, hipStream_t stream) {
   const MixedPlan plan = make_plan(R);
+  int G = 1;
+  const int k = lead_segment(plan, &G);
+  // one workgroup per sub-row fetches its sub-row's blocks for one row only:
+  // large batches keep the per-stage launches, which reuse block rows
+  // across a tile of rows
+  const bool seg = k >= 2 && M < kStageWideM;
+  const int nops = seg ? plan.n - k + 1 : plan.n;
   const TIn* src = static_cast<const TIn*>(in);
-  for (int q = 0; q < plan.n; ++q) {
-    const int t = TRANSPOSE ? plan.n - 1 - q : q;
-    const float* blk = R.blocks + plan.offset[t];
+  for (int q = 0; q < nops; ++q) {
     const bool first = q == 0;
-    const bool last = q == plan.n - 1;
-    const bool flip_in = first && !TRANSPOSE;
-    const bool flip_out = last && TRANSPOSE;
+    const bool last = q == nops - 1;
+    const bool is_seg = seg && (TRANSPOSE ? last : first);
     hipError_t e;
-    if (first && last)
-      e = launch_stage<TRANSPOSE, TIn, TOut>(src, out, blk, R.sign_bits, plan.dim, plan.radix[t],
-                                             plan.stride[t], M, flip_in, flip_out, stream);
-    else if (first)
-      e = launch_stage<TRANSPOSE, TIn, float>(src, ws, blk, R.sign_bits, plan.dim, plan.radix[t],
-                                              plan.stride[t], M, flip_in, flip_out, stream);
-    else if (last)
-      e = launch_stage<TRANSPOSE, float, TOut>(ws, out, blk, R.sign_bits, plan.dim,
-                                               plan.radix[t], plan.stride[t], M, flip_in, flip_out,
+    if (is_seg) {
+      if (first && last)
+        e = launch_rows<TRANSPOSE, TIn, TOut>(plan, k, G, src, out, R.blocks, R.sign_bits, M,
+                                              stream);
+      else if (first)
+        e = launch_rows<TRANSPOSE, TIn, float>(plan, k, G, src, ws, R.blocks, R.sign_bits, M,
                                                stream);
-    else
-      e = launch_stage<TRANSPOSE, float, float>(ws, ws, blk, R.sign_bits, plan.dim,
-                                                plan.radix[t], plan.stride[t], M, flip_in, flip_out,
+      else
+        e = launch_rows<TRANSPOSE, float, TOut>(plan, k, G, ws, out, R.blocks, R.sign_bits, M,
                                                 stream);
+    } else {
+      const int t = TRANSPOSE ? plan.n - 1 - q : (seg ? k + q - 1 : q);
+      const float* blk = R.blocks + plan.offset[t];
+      const bool flip_in = first && !TRANSPOSE;
+      const bool flip_out = last && TRANSPOSE;
+      if (first && last)
+        e = launch_stage<TRANSPOSE, TIn, TOut>(src, out, blk, R.sign_bits, plan.dim,
+                                               plan.radix[t], plan.stride[t], M, flip_in,
+                                               flip_out, stream);
+      else if (first)
+        e = launch_stage<TRANSPOSE, TIn, float>(src, ws, blk, R.sign_bits, plan.dim,
+                                                plan.radix[t], plan.stride[t], M, flip_in,
+                                                flip_out, stream);
+      else if (last)
+        e = launch_stage<TRANSPOSE, float, TOut>(ws, out, blk, R.sign_bits, plan.dim,
+                                                 plan.radix[t], plan.stride[t], M, flip_in,
+                                                 flip_out, stream);
+      else
+        e = launch_stage<TRANSPOSE, float, float>(ws, ws, blk, R.sign_bits, plan.dim,
+                                                  plan.radix[t], plan.stride[t], M, flip_in,
+                                                  flip_out, stream);
+    }
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -362,17 +427,9 @@ hipError_t launch_typed(const harp_mixed_rotation& R, const void* in, void* out,
       return launch_by_stage<TRANSPOSE, TIn, TOut>(R, in, workspace, static_cast<TOut*>(out), M,
                                                    stream);
     const MixedPlan plan = make_plan(R);
-    const size_t shmem = sizeof(float) * static_cast<size_t>(R.dim);
-    if (shmem > 65536) {   // rows above 16384 floats: raise the dynamic LDS limit
-      const hipError_t e = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&mixed_kernel<TRANSPOSE, TIn, TOut>),
-          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shmem));
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL((mixed_kernel<TRANSPOSE, TIn, TOut>), dim3(M), dim3(kMixedThreads), shmem,
-                       stream, static_cast<const TIn*>(in), static_cast<TOut*>(out), R.blocks,
-                       R.sign_bits, plan);
-    return hipGetLastError();
+    return launch_rows<TRANSPOSE, TIn, TOut>(plan, plan.n, plan.dim, static_cast<const TIn*>(in),
+                                             static_cast<TOut*>(out), R.blocks, R.sign_bits, M,
+                                             stream);
   }
 }
 
