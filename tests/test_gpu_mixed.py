@@ -188,3 +188,33 @@ def test_linear_fused_mixed(rv, ru, bits, M, ydt):
         yb = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         H().harp_linear_fused_mixed(V, W, U, d.dev_x(x, "bf16"), yb, ws)
         assert torch.equal(yb, y.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("M", [1, 2, 64])
+def test_rotate_mixed_maximum_dim(M):
+    """d = 32768 = 64 * 64 * 8, the largest mixed-radix side: float32 outputs
+    (stage launches), bf16 with a workspace and bf16 without one (a whole row
+    of 128 KB in LDS)."""
+    radices = (64, 64, 8)
+    d = D()
+    R, blocks, signs = device_side(radices, 13)
+    dim = R.dim
+    x = S.activations(M, dim, rng(11, dim, M), "bf16")
+    xd = d.dev_x(x, "bf16")
+    ref = O.mixed_forward(d.x_f64(x, "bf16"), radices, blocks, signs)
+    xt = torch.empty((M, dim), dtype=torch.float32, device="cuda")
+    H().harp_rotate_in_mixed(R, xd, xt)
+    assert O.rel_l2(d.host(xt), ref) <= BUTTERFLY_TOL
+    ws = torch.empty(H().harp_rotate_mixed_workspace_bytes(dim, M, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    a = torch.empty((M, dim), dtype=torch.bfloat16, device="cuda")
+    b = torch.empty((M, dim), dtype=torch.bfloat16, device="cuda")
+    H().harp_rotate_in_mixed(R, xd, a, workspace=ws)
+    H().harp_rotate_in_mixed(R, xd, b)
+    assert torch.equal(a, xt.to(torch.bfloat16))
+    assert torch.equal(b, a)
+    yp = rng(12, dim, M).normal(size=(M, dim)).astype(np.float32)
+    reft = O.mixed_transpose(yp.astype(np.float64), radices, blocks, signs)
+    y = torch.empty((M, dim), dtype=torch.float32, device="cuda")
+    H().harp_rotate_out_mixed(R, d.dev(yp), y)
+    assert O.rel_l2(d.host(y), reft) <= BUTTERFLY_TOL
