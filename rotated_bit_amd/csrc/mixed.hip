@@ -14,7 +14,10 @@
 // coordinates, and groups are disjoint): the output itself for a float32
 // output, the caller's workspace for a bf16 one, whose last stage writes
 // the output.  Each lane keeps its block row in registers for a tile of
-// rows.  A bf16 output without a workspace falls back to one workgroup of
+// rows.  For small batches the leading stages whose radices multiply to at
+// most 512 act inside contiguous sub-rows and run as one launch, one
+// workgroup per sub-row in LDS.  A bf16 output without a workspace falls
+// back to one workgroup of
 // 512 threads per row, the row held in LDS as float32 (d <= 32768: at most
 // 128 KB), one barrier per stage, the blocks streaming from global memory
 // where the L2 keeps them for the other rows.  Register arrays are sized by
