@@ -17,12 +17,11 @@
 // rows.  For small batches the leading stages whose radices multiply to at
 // most 512 act inside contiguous sub-rows and run as one launch, one
 // workgroup per sub-row in LDS.  A bf16 output without a workspace falls
-// back to one workgroup of
-// 512 threads per row, the row held in LDS as float32 (d <= 32768: at most
-// 128 KB), one barrier per stage, the blocks streaming from global memory
-// where the L2 keeps them for the other rows.  Register arrays are sized by
-// the next power of two of the radix, a compile-time bound chosen per
-// stage.
+// back to one workgroup of 512 threads per row, the row held in LDS as
+// float32 (d <= 32768: at most 128 KB), one barrier per stage, the blocks
+// streaming from global memory where the L2 keeps them for the other rows.
+// Register arrays are sized by the next power of two of the radix, a
+// compile-time bound chosen per stage.
 #include "launch.hpp"
 #include "device_common.hpp"
 
