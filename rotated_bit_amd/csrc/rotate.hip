@@ -291,7 +291,10 @@ __global__ __launch_bounds__((Plan<LOGB, EL_>::THREADS)) void rotate_kernel(
 // run on eight CUs instead of one CU reading all of them.
 constexpr int kSplitParts = 8;
 constexpr int kSplitThreads = 512;
-constexpr int kSplitMaxM = 8;   // rows up to this count take the split form
+// Rows up to this count take the split form: each row is one grid row of
+// eight workgroups, so the form holds for any M; past 64 rows the block
+// kernel's shared coefficient registers read less and win.
+constexpr int kSplitMaxM = 64;
 
 // a where mask bits are set, else b.  The mask comes through an empty asm
 // so that the selects between register elements stay selects (the compiler

@@ -190,7 +190,8 @@ def test_rotate_int8_angles(dim, b, M, xdt):
 SPLIT_CASES = [
     (4096, 4096, 1, "f32"), (4096, 4096, 8, "f32"), (4096, 4096, 9, "f32"),
     (8192, 8192, 3, "int8"), (8192, 4096, 5, "f32"), (16384, 8192, 2, "int8"),
-    (4096, 4096, 4, "int8"),
+    (4096, 4096, 4, "int8"), (4096, 4096, 64, "f32"), (4096, 4096, 65, "f32"),
+    (8192, 8192, 33, "int8"),
 ]
 
 
