@@ -459,26 +459,48 @@ def main():
             torch.cuda.empty_cache()
         log("offline prep: " + json.dumps(prep))
 
-    # prefill: M = 512, 4096 x 4096 2-bit on the matrix cores
+    # prefill: M = 512 on the matrix cores, the three linears of the
+    # Qwen3-8B-shaped prefill config at 2 and 4 bits; the top-level keys are
+    # the 4096 x 4096 2-bit case
     prefill = None
     if not args.no_prefill:
-        pre = make_instances("q8b_prefill", 0, 2, 512, 8, torch, H)
-        flops = 2.0 * 512 * 4096 * 4096
-        for it in pre:
-            H.harp_rotate_in(it.V, it.x, it.xt16)
-        ms_gm, _ = time_graph(torch, lambda: [H.harp_deq_gemm(i.W, i.xt16, i.yp, i.gws) for i in pre], 10)
-        ms_fu, _ = time_graph(torch, lambda: [H.harp_linear_fused(i.V, i.W, i.U, i.x, i.y, i.ws)
-                                              for i in pre], 10)
-        us_gm, us_fu = ms_gm * 1e3 / len(pre), ms_fu * 1e3 / len(pre)
+        from synth import workloads as S
+        pcfg = S.CONFIGS["q8b_prefill"]
+        shapes = {}
+        for li_idx, lin in enumerate(pcfg.linears):
+            for bits in (2, 4):
+                count = 8 if lin.N * lin.K <= 4096 * 4096 else 4
+                pre = make_instances("q8b_prefill", li_idx, bits, 512, count, torch, H)
+                flops = 2.0 * 512 * lin.N * lin.K
+                for it in pre:
+                    H.harp_rotate_in(it.V, it.x, it.xt16)
+                ms_gm, _ = time_graph(
+                    torch, lambda: [H.harp_deq_gemm(i.W, i.xt16, i.yp, i.gws) for i in pre], 10)
+                ms_fu, _ = time_graph(
+                    torch, lambda: [H.harp_linear_fused(i.V, i.W, i.U, i.x, i.y, i.ws)
+                                    for i in pre], 10)
+                us_gm, us_fu = ms_gm * 1e3 / len(pre), ms_fu * 1e3 / len(pre)
+                tf_gm = flops / (us_gm * 1e-6) / 1e12
+                shapes[f"{lin.K}x{lin.N}_{bits}bit"] = {
+                    "K": lin.K, "N": lin.N, "bits": bits, "b_V": lin.b_v, "b_U": lin.b_u,
+                    "deq_gemm_us": round(us_gm, 2),
+                    "deq_gemm_TFLOPs": round(tf_gm, 1),
+                    "deq_gemm_frac_mfma": round(tf_gm / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "fused_us": round(us_fu, 2),
+                    "fused_frac_mfma": round(flops / (us_fu * 1e-6) / 1e12
+                                             / MFMA_BF16_PEAK_TFLOPS, 4)}
+                del pre
+                torch.cuda.empty_cache()
+        head = shapes["4096x4096_2bit"]
         prefill = {"workload": "4096x4096 2-bit M=512",
-                   "deq_gemm_us": round(us_gm, 2),
-                   "deq_gemm_TFLOPs": round(flops / (us_gm * 1e-6) / 1e12, 1),
-                   "deq_gemm_frac_mfma": round(flops / (us_gm * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                   "fused_us": round(us_fu, 2),
-                   "fused_frac_mfma": round(flops / (us_fu * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                   "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS}
+                   "deq_gemm_us": head["deq_gemm_us"],
+                   "deq_gemm_TFLOPs": head["deq_gemm_TFLOPs"],
+                   "deq_gemm_frac_mfma": head["deq_gemm_frac_mfma"],
+                   "fused_us": head["fused_us"],
+                   "fused_frac_mfma": head["fused_frac_mfma"],
+                   "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                   "shapes": shapes}
         log("prefill: " + json.dumps(prefill))
-        del pre
 
     cpu = None
     if not args.no_cpu:
