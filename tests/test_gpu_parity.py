@@ -185,8 +185,8 @@ def test_rotate_int8_angles(dim, b, M, xdt):
     assert report(f"rotate_out int8 {dim}/{b} M={M}", d.host(y), reft) <= BUTTERFLY_TOL
 
 
-# Output rotations of few rows at b = 4096 / 8192 run split over eight
-# workgroups per block; M = 9 is the first batch of the one-workgroup form.
+# Output rotations of up to 64 rows at b = 4096 / 8192 run split over eight
+# workgroups per block; M = 65 is the first batch of the one-workgroup form.
 SPLIT_CASES = [
     (4096, 4096, 1, "f32"), (4096, 4096, 8, "f32"), (4096, 4096, 9, "f32"),
     (8192, 8192, 3, "int8"), (8192, 4096, 5, "f32"), (16384, 8192, 2, "int8"),
