@@ -260,6 +260,7 @@ def main():
     log(f"step: {count} fused linears in {ms:.3f} ms "
         f"({ms * 1e3 / count:.2f} us per linear)")
     value = count * per_call / (ms * 1e-3) / 1e9
+    ms_step = ms   # the timed step; the legs below time their own work
 
     if args.calibrate_copy:
         src = torch.empty(64 << 20, dtype=torch.float32, device="cuda")
@@ -316,7 +317,7 @@ def main():
               "instances_per_step": count8, "bytes_per_call": per8,
               "us_per_linear": round(us8, 3),
               "GB_s": round(per8 / (us8 * 1e-6) / 1e9, 2),
-              "speedup_vs_f32_pairs": round((ms * 1e3 / count) / us8, 3),
+              "speedup_vs_f32_pairs": round((ms_step * 1e3 / count) / us8, 3),
               "kernels": {}}
         for name, msk, nbytes in (
                 ("rotate_in_deq_gemv_2bit_int8", ms8_rg, rotgemv_bytes(M, N, K, bits, bv, 1)),
@@ -382,8 +383,8 @@ def main():
                 if odt == torch.bfloat16:   # float32 stages in a workspace, bf16 last stage
                     ws = torch.empty(H.harp_rotate_mixed_workspace_bytes(dim, M, odt),
                                      dtype=torch.uint8, device="cuda")
-                ms, _ = time_graph(torch, lambda: [fn(R, a, o, ws) for a, o in zip(xs, outs)], 5)
-                us = ms * 1e3 / 8
+                ms_m, _ = time_graph(torch, lambda: [fn(R, a, o, ws) for a, o in zip(xs, outs)], 5)
+                us = ms_m * 1e3 / 8
                 nb = 4 * nblk + dim // 8 + (xs[0].element_size() + outs[0].element_size()) * M * dim
                 key = f"{side}_M{M}" + ("_bf16" if odt == torch.bfloat16 else "")
                 entry[f"{key}_us"] = round(us, 2)
@@ -416,8 +417,8 @@ def main():
                 ws = torch.zeros(H.harp_linear_mixed_workspace_bytes(M, d, d), dtype=torch.uint8,
                                  device="cuda")
                 inst.append((V, W, U, x, y, ws))
-            ms, _ = time_graph(torch, lambda: [H.harp_linear_fused_mixed(*i) for i in inst], 5)
-            us = ms * 1e3 / len(inst)
+            ms_m, _ = time_graph(torch, lambda: [H.harp_linear_fused_mixed(*i) for i in inst], 5)
+            us = ms_m * 1e3 / len(inst)
             nb = d * d * bits // 8 + d * (d // 64) * 4 + 2 * (4 * nblk + d // 8) + 2 * M * d + 4 * M * d
             lin[f"M{M}_us"] = round(us, 2)
             lin[f"M{M}_GB_s"] = round(nb / (us * 1e-6) / 1e9, 1)
@@ -469,8 +470,8 @@ def main():
         shapes = {}
         for li_idx, lin in enumerate(pcfg.linears):
             for bits in (2, 4):
-                count = 8 if lin.N * lin.K <= 4096 * 4096 else 4
-                pre = make_instances("q8b_prefill", li_idx, bits, 512, count, torch, H)
+                n_pre = 8 if lin.N * lin.K <= 4096 * 4096 else 4
+                pre = make_instances("q8b_prefill", li_idx, bits, 512, n_pre, torch, H)
                 flops = 2.0 * 512 * lin.N * lin.K
                 for it in pre:
                     H.harp_rotate_in(it.V, it.x, it.xt16)
@@ -517,7 +518,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -97,6 +97,21 @@ __device__ __forceinline__ void store_contig(T* p, const float (&v)[E]) {
   *reinterpret_cast<Pack<T, E>*>(p) = pk;
 }
 
+// Orders one round's LDS stores before the next round's loads.  Across a
+// workgroup that is a barrier; inside one wave, whose LDS accesses execute
+// in issue order, it is a wave-scope fence that also keeps the compiler
+// from moving the loads above the stores.
+template <bool WAVE_LOCAL>
+__device__ __forceinline__ void slot_sync() {
+  if constexpr (WAVE_LOCAL) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    __syncthreads();
+  }
+}
+
 template <int LOGB, int EL_, bool TRANSPOSE, bool Q8, typename TIn, typename TOut>
 __global__ __launch_bounds__((Plan<LOGB, EL_>::THREADS)) void rotate_kernel(
     const TIn* __restrict__ in, TOut* __restrict__ out,
@@ -108,9 +123,15 @@ __global__ __launch_bounds__((Plan<LOGB, EL_>::THREADS)) void rotate_kernel(
   constexpr int EL = P::EL;
   constexpr int L = P::L;
   constexpr int NR = P::NR;
-  extern __shared__ float lds[];
+  extern __shared__ __attribute__((aligned(16))) float lds[];
   __shared__ float2 table[Q8 ? 256 : 1];   // (cos t, sin t) by code + 128
 
+  // A block row of at most 64 threads lies inside one wave, and its LDS
+  // exchange region belongs to it alone: the rounds then only need the
+  // wave's own LDS order, not a workgroup barrier.
+  constexpr bool kWaveLocal = P::TPB <= kWave;
+  // small blocks: all slots of the workgroup share the block's pairs
+  constexpr bool kCoefLds = kWaveLocal && !Q8 && NR > 1;
   const int tid = threadIdx.x;
   const int slot = tid / P::TPB;
   const int t = tid - slot * P::TPB;
@@ -188,12 +209,25 @@ __global__ __launch_bounds__((Plan<LOGB, EL_>::THREADS)) void rotate_kernel(
       for (int q = 0; q < NR; ++q)
         for_round(q, [&](int s, int p, int) { cf[s][p] = table[qc[s][p] + 128]; });
     }
+  } else if constexpr (kCoefLds) {
+    // the block's L x B/2 pairs, fetched once per workgroup with coalesced
+    // 16-byte loads into LDS behind the slots' exchange rows; every slot
+    // then picks its own pairs from there
+    float2* csl = reinterpret_cast<float2*>(lds + P::SLOTS * B);
+    const float4* src = reinterpret_cast<const float4*>(cs + blk_off);
+    float4* dst = reinterpret_cast<float4*>(csl);
+    for (int i = tid; i < L * B / 4; i += P::THREADS) dst[i] = src[i];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kEarly; ++q)
+      for_round(q, [&](int s, int p, int c) { cf[s][p] = csl[c]; });
   } else {
     const float2* csb = cs + blk_off;
 #pragma unroll
     for (int q = 0; q < kEarly; ++q)
       for_round(q, [&](int s, int p, int c) { cf[s][p] = csb[c]; });
   }
+  static_assert(!kCoefLds || kEarly == NR, "LDS-staged pairs are all loaded up front");
   constexpr bool kPrefetchRow = Q8 || kEarly == NR;
   auto load_round = [&](int q) {
     const float2* csb = cs + blk_off;
@@ -208,7 +242,7 @@ __global__ __launch_bounds__((Plan<LOGB, EL_>::THREADS)) void rotate_kernel(
     const bool active = row < M;
     const size_t base = static_cast<size_t>(active ? row : 0) * dim +
                         static_cast<size_t>(blk) * B;
-    if (NR > 1 && it > 0) __syncthreads();   // LDS reuse across rows
+    if (NR > 1 && it > 0) slot_sync<kWaveLocal>();   // LDS reuse across rows
     if (!kPrefetchRow && it > 0) fetch(it, raw);
     float v[E];
 #pragma unroll
@@ -270,7 +304,7 @@ __global__ __launch_bounds__((Plan<LOGB, EL_>::THREADS)) void rotate_kernel(
       } else {
 #pragma unroll
         for (int j = 0; j < E; ++j) u[elem_index<E>(t, j, s0, R)] = v[j];
-        __syncthreads();
+        slot_sync<kWaveLocal>();
       }
     }
   }
@@ -468,14 +502,19 @@ hipError_t launch_typed(const harp_rotation& R, const void* in, void* out, int M
   const int nblk = R.dim >> LOGB;
   const int ygroups = (M + P::SLOTS - 1) / P::SLOTS;
   // Rows per slot: about one workgroup per CU; beyond that, a workgroup
-  // reuses its coefficient registers over several rows.
+  // reuses its coefficient registers over several rows.  Blocks of 256 or
+  // fewer fetch their pairs (at most 8 KB) once per workgroup into LDS, so
+  // they aim at about four workgroups per CU instead.
   int rps = (nblk * ygroups) / 256;
   if (rps < 1) rps = 1;
   if (rps > 8) rps = 8;
+  if (LOGB <= 8) { rps = (nblk * ygroups) / 1024; if (rps < 1) rps = 1; }
   const int need = (ygroups + 65534) / 65535;
   if (rps < need) rps = need;
   const dim3 grid(nblk, (ygroups + rps - 1) / rps);
-  const size_t shmem = P::NR > 1 ? sizeof(float) * P::SLOTS * P::B : 0;
+  size_t shmem = P::NR > 1 ? sizeof(float) * P::SLOTS * P::B : 0;
+  if (P::NR > 1 && P::TPB <= kWave && !Q8)
+    shmem += sizeof(float2) * P::L * (P::B / 2);
   hipLaunchKernelGGL((rotate_kernel<LOGB, EL_, TRANSPOSE, Q8, TIn, TOut>), grid,
                      dim3(P::THREADS), shmem, stream,
                      static_cast<const TIn*>(in), static_cast<TOut*>(out),

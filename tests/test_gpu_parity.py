@@ -128,6 +128,10 @@ ROT_CASES = [
     (4096, 4096, 17, "bf16"), (8192, 8192, 2, "bf16"), (11008, 256, 16, "bf16"),
     (28672, 256, 3, "bf16"), (12288, 256, 512, "bf16"), (4096, 4096, 512, "bf16"),
     (8192, 8192, 32, "bf16"),
+    # blocks of 64..512 (one wave per block row, pairs staged in LDS), 1024
+    # (workgroup barriers), and a ragged batch with four rows per slot
+    (192, 64, 70, "f32"), (640, 128, 21, "bf16"), (1024, 512, 37, "f32"),
+    (2048, 1024, 9, "bf16"), (28672, 256, 300, "f32"),
 ]
 
 
