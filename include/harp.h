@@ -237,9 +237,11 @@ harp_status harp_rotate_in_deq_gemv(const harp_rotation *V,
  *              at least harp_deq_gemm_workspace_bytes(M, N, K) bytes,
  *              256-byte aligned: the K dimension is split into slices that
  *              run concurrently and are summed in a fixed slice order
- *              (bitwise reproducible).  The workspace must be zero-filled
- *              before its first use; every call leaves it zero-filled.
- *              Calls that share a workspace must not overlap in time.
+ *              (bitwise reproducible).  Zero-fill the workspace before its
+ *              first use: its per-tile arrival counters must start at
+ *              zero, and every call leaves them at zero (the partial tiles
+ *              need no initialisation).  Calls that share a workspace must
+ *              not overlap in time.
  */
 harp_status harp_deq_gemm(const harp_qweight *W, const uint16_t *xt_bf16,
                           float *yt, int32_t M, void *workspace,
