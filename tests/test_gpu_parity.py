@@ -270,7 +270,7 @@ def test_rotate_max_batch_sampled():
 # a3: GEMV (float32), a4: GEMM (bf16 matrix cores)
 # ---------------------------------------------------------------------------
 
-GEMV_CASES = [(100, 320, b, m) for b in (2, 3, 4) for m in (1, 2, 3, 5, 8, 13)] + [
+GEMV_CASES = [(100, 320, b, m) for b in (2, 3, 4) for m in (1, 2, 3, 5, 8, 9, 13)] + [
     (4096, 4096, 2, 1), (11008, 4096, 2, 16), (4096, 11008, 2, 16),
     (8192, 8192, 3, 1), (2048, 8192, 4, 32), (1000, 28672, 2, 1), (64, 256, 2, 63),
 ]
