@@ -203,9 +203,11 @@ harp_status harp_rotate_out_mixed(const harp_mixed_rotation *R, const float *yt,
 size_t harp_rotate_mixed_workspace_bytes(int32_t dim, int32_t M, harp_dtype out_dt);
 
 /*
- * y'[m][n] = sum_k w_hat[n][k] x~[m][k] on the vector ALUs, float32
- * throughout: w_hat is exact in float32 and x~ is not rounded.  Meant for
- * decode batches (M < 16); any M is accepted.
+ * y'[m][n] = sum_k w_hat[n][k] x~[m][k], float32 throughout: w_hat is exact
+ * in float32 and x~ is not rounded.  Up to 8 rows on the vector ALUs, from
+ * 9 rows on in 16-row tiles on the float32 matrix cores (same products,
+ * float32 accumulation in a different order).  Meant for decode batches;
+ * any M is accepted.
  *   xt  [M][W->K] float32;  yt  [M][W->N] float32.
  */
 harp_status harp_deq_gemv(const harp_qweight *W, const float *xt, float *yt,
