@@ -54,6 +54,10 @@ size_t gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
 // kMfmaMinM rows and the bf16 matrix-core product from there on.
 constexpr int32_t kSkinnyMaxM = 64;
 constexpr int32_t kMfmaMinM = 16;
+// The fused linear folds the input rotation into the product launch up to
+// this many rows; from three rows on the two-launch form is faster (every
+// workgroup of the one-launch form rotates all rows).
+constexpr int32_t kFusedRotGemvMaxM = 2;
 
 // Workspace layout of the fused linear: x~, then y', then (M > kSkinnyMaxM)
 // the tiled GEMM's workspace, each 256-byte aligned.  x~ is float32 below
