@@ -1,6 +1,6 @@
 """GPU parity: every entry point of include/harp.h against the float64 oracle.
 
-Bars (stated in the design doc with their derivation):
+Bars (each derived from the rounding points of its path):
 * unpack / dequant (harp_dequant): bit-exact, float32 and bf16;
 * butterfly alone, float32 in and out: relative L2 <= 1e-5;
 * linear outputs: relative L2 <= 1e-3 over the whole output (the contract),
