@@ -482,6 +482,21 @@ def main():
                                     for i in pre], 10)
                 us_gm, us_fu = ms_gm * 1e3 / len(pre), ms_fu * 1e3 / len(pre)
                 tf_gm = flops / (us_gm * 1e-6) / 1e12
+                ctx = {}
+                if li_idx == 0 and bits == 2:
+                    # context, not our path: the vendor library's plain bf16
+                    # GEMM on the same x~ with the weights dequantized first
+                    wb = [torch.empty((lin.N, lin.K), dtype=torch.bfloat16, device="cuda")
+                          for _ in pre]
+                    for i, w in zip(pre, wb):
+                        H.harp_dequant(i.W, w)
+                    ms_lib, _ = time_graph(
+                        torch, lambda: [torch.matmul(i.xt16, w.t()) for i, w in zip(pre, wb)], 10)
+                    us_lib = ms_lib * 1e3 / len(pre)
+                    ctx = {"context_library_bf16_gemm_us": round(us_lib, 2),
+                           "context_library_frac_mfma": round(
+                               flops / (us_lib * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+                    del wb
                 shapes[f"{lin.K}x{lin.N}_{bits}bit"] = {
                     "K": lin.K, "N": lin.N, "bits": bits, "b_V": lin.b_v, "b_U": lin.b_u,
                     "deq_gemm_us": round(us_gm, 2),
@@ -489,7 +504,7 @@ def main():
                     "deq_gemm_frac_mfma": round(tf_gm / MFMA_BF16_PEAK_TFLOPS, 4),
                     "fused_us": round(us_fu, 2),
                     "fused_frac_mfma": round(flops / (us_fu * 1e-6) / 1e12
-                                             / MFMA_BF16_PEAK_TFLOPS, 4)}
+                                             / MFMA_BF16_PEAK_TFLOPS, 4), **ctx}
                 del pre
                 torch.cuda.empty_cache()
         head = shapes["4096x4096_2bit"]
@@ -499,6 +514,8 @@ def main():
                    "deq_gemm_frac_mfma": head["deq_gemm_frac_mfma"],
                    "fused_us": head["fused_us"],
                    "fused_frac_mfma": head["fused_frac_mfma"],
+                   "context_library_bf16_gemm_us": head.get("context_library_bf16_gemm_us"),
+                   "context_library_frac_mfma": head.get("context_library_frac_mfma"),
                    "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
                    "shapes": shapes}
         log("prefill: " + json.dumps(prefill))
