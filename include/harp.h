@@ -282,8 +282,8 @@ size_t harp_linear_mixed_workspace_bytes(int32_t M, int32_t N, int32_t K);
 /*
  * y = F_U^T deq(W) F_V x, the whole linear (technical summary §2.4 and §5).
  * M < 16 runs rotate-in (float32 x~), the float32 product of harp_deq_gemv
- * and rotate-out, with the first two in one launch for M <= 2 where
- * harp_rotate_in_deq_gemv supports the shape; M >= 16 runs rotate-in with a
+ * and rotate-out, with the first two in one launch for M <= 2 and N <= 4096
+ * where harp_rotate_in_deq_gemv supports the shape; M >= 16 runs rotate-in with a
  * bf16 x~, the matrix-core product of harp_deq_gemm and rotate-out.  Requires V->dim == W->K and
  * U->dim == W->N.
  *   x  [M][K] of x_dt;  y  [M][N] of y_dt;

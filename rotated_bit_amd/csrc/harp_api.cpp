@@ -113,7 +113,8 @@ harp_status harp_linear_fused(const harp_rotation* V, const harp_qweight* W,
   const hipStream_t s = as_stream(stream);
   char* ws = static_cast<char*>(workspace);
   float* yp = reinterpret_cast<float*>(ws + harp::workspace_yp_offset(M, W->K));
-  if (M <= harp::kFusedRotGemvMaxM && harp::gemv_rotated_supported(*V, *W, M)) {
+  if (M <= harp::kFusedRotGemvMaxM && W->N <= harp::kFusedRotGemvMaxN &&
+      harp::gemv_rotated_supported(*V, *W, M)) {
     const harp_status r = from_hip(harp::launch_gemv_rotated(*V, *W, x, x_dt, yp, M, s));
     if (r != HARP_OK) return r;
   } else if (M < harp::kMfmaMinM) {

@@ -55,9 +55,13 @@ size_t gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
 constexpr int32_t kSkinnyMaxM = 64;
 constexpr int32_t kMfmaMinM = 16;
 // The fused linear folds the input rotation into the product launch up to
-// this many rows; from three rows on the two-launch form is faster (every
-// workgroup of the one-launch form rotates all rows).
+// this many rows and output features: every workgroup of the one-launch
+// form rotates all rows itself, so it only pays off with few rows and at
+// most one workgroup (16 features) per CU.  Beyond either limit the
+// rotation runs once in its own launch (K = 4096, M = 1: N = 11008 takes
+// 16.9 us in two launches against 22.3 us in one).
 constexpr int32_t kFusedRotGemvMaxM = 2;
+constexpr int32_t kFusedRotGemvMaxN = 4096;
 
 // Workspace layout of the fused linear: x~, then y', then (M > kSkinnyMaxM)
 // the tiled GEMM's workspace, each 256-byte aligned.  x~ is float32 below
