@@ -282,13 +282,16 @@ def main():
     ms_ro, _ = time_graph(torch, lambda: [H.harp_rotate_out(i.U, i.yp, i.y) for i in inst], reps)
     ms_ri, _ = time_graph(torch, lambda: [H.harp_rotate_in(i.V, i.x, i.xt32) for i in inst], reps)
     ms_gv, _ = time_graph(torch, lambda: [H.harp_deq_gemv(i.W, i.xt32, i.yp) for i in inst], reps)
-    for name, msk, nbytes, in_path in (
-            ("rotate_in_deq_gemv_2bit", ms_rg, rotgemv_bytes(M, N, K, bits, bv), True),
-            ("rotate_out_b4096", ms_ro, rotate_bytes(M, N, bu, 4, 4), True),
-            ("rotate_in_b4096", ms_ri, rotate_bytes(M, K, bv, 2, 4), False),
-            ("deq_gemv_2bit", ms_gv, gemv_bytes(M, N, K, bits), False)):
+    # (the stand-alone rotate_in of a few rows into float32 at b = 4096 is two
+    # launches: sub-blocks, then the last three stages)
+    for name, msk, nbytes, in_path, launches in (
+            ("rotate_in_deq_gemv_2bit", ms_rg, rotgemv_bytes(M, N, K, bits, bv), True, 1),
+            ("rotate_out_b4096", ms_ro, rotate_bytes(M, N, bu, 4, 4), True, 1),
+            ("rotate_in_b4096", ms_ri, rotate_bytes(M, K, bv, 2, 4), False, 2),
+            ("deq_gemv_2bit", ms_gv, gemv_bytes(M, N, K, bits), False, 1)):
         us = msk * 1e3 / count
-        kern[name] = {"us_per_launch": round(us, 3), "alg_bytes": nbytes,
+        kern[name] = {("us_per_launch" if launches == 1 else "us_per_call"): round(us, 3),
+                      "launches_per_call": launches, "alg_bytes": nbytes,
                       "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1), "in_fused_path": in_path}
     log("kernels: " + json.dumps(kern))
     dom = max((k for k in kern if kern[k]["in_fused_path"]),

@@ -112,7 +112,11 @@ __device__ __forceinline__ void slot_sync() {
   }
 }
 
-template <int LOGB, int EL_, bool TRANSPOSE, bool Q8, typename TIn, typename TOut>
+// SUB_ = 0: blocks of b = 2^LOGB with their own pairs.  SUB_ = 3: the
+// blocks are the eight sub-blocks of a block of 8b and the stages applied
+// are that block's first LOGB stages (which never leave a sub-block); the
+// pairs are then addressed in the big block's layout.
+template <int LOGB, int EL_, bool TRANSPOSE, bool Q8, typename TIn, typename TOut, int SUB_ = 0>
 __global__ __launch_bounds__((Plan<LOGB, EL_>::THREADS)) void rotate_kernel(
     const TIn* __restrict__ in, TOut* __restrict__ out,
     const float2* __restrict__ cs, const int8_t* __restrict__ codes, float step,
@@ -131,7 +135,7 @@ __global__ __launch_bounds__((Plan<LOGB, EL_>::THREADS)) void rotate_kernel(
   // wave's own LDS order, not a workgroup barrier.
   constexpr bool kWaveLocal = P::TPB <= kWave;
   // small blocks: all slots of the workgroup share the block's pairs
-  constexpr bool kCoefLds = kWaveLocal && !Q8 && NR > 1;
+  constexpr bool kCoefLds = kWaveLocal && !Q8 && NR > 1 && SUB_ == 0;
   const int tid = threadIdx.x;
   const int slot = tid / P::TPB;
   const int t = tid - slot * P::TPB;
@@ -169,7 +173,12 @@ __global__ __launch_bounds__((Plan<LOGB, EL_>::THREADS)) void rotate_kernel(
   // next to the data (b = 8192 at 1024 threads), the last ones are loaded
   // once the first round has released its registers.
   float2 cf[L][E / 2];
-  const size_t blk_off = static_cast<size_t>(blk) * L * (B / 2);
+  // pairs of stage s of this block: blk_off + s * kStageStride + pair
+  constexpr int kStageStride = (B << SUB_) / 2;
+  const size_t blk_off =
+      SUB_ == 0 ? static_cast<size_t>(blk) * L * (B / 2)
+                : static_cast<size_t>(blk >> SUB_) * (L + SUB_) * kStageStride +
+                      static_cast<size_t>(blk & ((1 << SUB_) - 1)) * (B / 2);
   constexpr int kEarly = (L * E) > 96 ? 3 : NR;   // rounds loaded up front
   // f(s, p, c): pair p of stage s of this thread has coefficient index c.
   auto for_round = [&](int q, auto&& f) {
@@ -183,7 +192,7 @@ __global__ __launch_bounds__((Plan<LOGB, EL_>::THREADS)) void rotate_kernel(
 #pragma unroll
         for (int p = 0; p < E / 2; ++p) {
           const int i = elem_index<E>(t, insert_zero_bit(p, k), s0, R);
-          f(s, p, s * (B / 2) + delete_bit(i, s));
+          f(s, p, s * kStageStride + delete_bit(i, s));
         }
       }
     }
@@ -495,7 +504,7 @@ hipError_t launch_split(const harp_rotation& R, const void* in, void* out, int M
   return hipGetLastError();
 }
 
-template <int LOGB, int EL_, bool TRANSPOSE, bool Q8, typename TIn, typename TOut>
+template <int LOGB, int EL_, bool TRANSPOSE, bool Q8, typename TIn, typename TOut, int SUB_ = 0>
 hipError_t launch_typed(const harp_rotation& R, const void* in, void* out, int M,
                         hipStream_t stream) {
   using P = Plan<LOGB, EL_>;
@@ -513,13 +522,81 @@ hipError_t launch_typed(const harp_rotation& R, const void* in, void* out, int M
   if (rps < need) rps = need;
   const dim3 grid(nblk, (ygroups + rps - 1) / rps);
   size_t shmem = P::NR > 1 ? sizeof(float) * P::SLOTS * P::B : 0;
-  if (P::NR > 1 && P::TPB <= kWave && !Q8)
+  if (P::NR > 1 && P::TPB <= kWave && !Q8 && SUB_ == 0)
     shmem += sizeof(float2) * P::L * (P::B / 2);
-  hipLaunchKernelGGL((rotate_kernel<LOGB, EL_, TRANSPOSE, Q8, TIn, TOut>), grid,
+  hipLaunchKernelGGL((rotate_kernel<LOGB, EL_, TRANSPOSE, Q8, TIn, TOut, SUB_>), grid,
                      dim3(P::THREADS), shmem, stream,
                      static_cast<const TIn*>(in), static_cast<TOut*>(out),
                      reinterpret_cast<const float2*>(R.cs), R.phi_codes,
                      R.phi_step, R.sign_bits, R.dim, M, rps);
+  return hipGetLastError();
+}
+
+
+// Input rotation of a few rows at b = 4096 / 8192 in two launches: the first
+// LOGB - 3 stages never leave a sub-block of b/8 elements, so eight
+// workgroups per block run them (the block kernel on sub-blocks, the sign
+// flip included) into the float32 output; then this kernel applies the last
+// three stages (strides b/8, b/4, b/2) in place: residue q < b/8 owns the
+// eight elements q + (b/8) j, and stage LOGB - 3 + k pairs j with j ^ 2^k.
+// Each block's pairs are then read by a few workgroups instead of all
+// passing through one CU.
+constexpr int kTailThreads = 256;
+
+template <int LOGB, bool Q8>
+__global__ __launch_bounds__(kTailThreads) void rotate_in_tail_kernel(
+    float* __restrict__ xt, const float2* __restrict__ cs, const int8_t* __restrict__ codes,
+    float step, int dim) {
+  constexpr int B = 1 << LOGB;
+  constexpr int L = LOGB;
+  constexpr int SB = B / 8;
+  constexpr int kParts = SB / kTailThreads;   // workgroups per block row
+  static_assert(kParts >= 1 && SB % kTailThreads == 0, "sub-blocks of 256 or more");
+  __shared__ float2 table[Q8 ? 256 : 1];
+  if constexpr (Q8) {
+    float sn, cn;
+    sincosf(fmaf(static_cast<float>(static_cast<int>(threadIdx.x) - 128), step,
+                 0.785398163397448310f), &sn, &cn);
+    table[threadIdx.x] = make_float2(cn, sn);
+    __syncthreads();
+  }
+  const int blk = blockIdx.x / kParts;
+  const int q = (blockIdx.x - blk * kParts) * kTailThreads + threadIdx.x;
+  float* base = xt + static_cast<size_t>(blockIdx.y) * dim + static_cast<size_t>(blk) * B + q;
+  const size_t coff = static_cast<size_t>(blk) * L * (B / 2);
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = base[j * SB];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int s = L - 3 + k;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int j = insert_zero_bit(p, k);
+      const int j2 = j | (1 << k);
+      const size_t c = coff + static_cast<size_t>(s) * (B / 2) + delete_bit(q + SB * j, s);
+      float2 t;
+      if constexpr (Q8) t = table[codes[c] + 128];
+      else t = cs[c];
+      const float a = v[j];
+      const float b = v[j2];
+      v[j] = fmaf(t.x, a, t.y * b);
+      v[j2] = fmaf(t.y, a, -(t.x * b));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) base[j * SB] = v[j];
+}
+
+template <int LOGB, bool Q8, typename TIn>
+hipError_t launch_in_split(const harp_rotation& R, const void* in, float* out, int M,
+                           hipStream_t stream) {
+  hipError_t e = launch_typed<LOGB - 3, 3, false, Q8, TIn, float, 3>(R, in, out, M, stream);
+  if (e != hipSuccess) return e;
+  const int nblk = R.dim >> LOGB;
+  const dim3 grid(nblk * ((1 << LOGB) / 8 / kTailThreads), M);
+  hipLaunchKernelGGL((rotate_in_tail_kernel<LOGB, Q8>), grid, dim3(kTailThreads), 0, stream,
+                     out, reinterpret_cast<const float2*>(R.cs), R.phi_codes, R.phi_step, R.dim);
   return hipGetLastError();
 }
 
@@ -554,6 +631,16 @@ hipError_t launch_logb(const harp_rotation& R, const void* in, int in_dt,
                        void* out, int out_dt, int M, bool transpose,
                        hipStream_t stream) {
   if constexpr (LOGB == 12 || LOGB == 13) {
+    // few rows of the input rotation into float32: two launches (above)
+    if (!transpose && out_dt == HARP_F32 && M <= kSplitMaxM) {
+      float* o = static_cast<float*>(out);
+      const bool ib = in_dt == HARP_BF16;
+      if (R.phi_codes != nullptr)
+        return ib ? launch_in_split<LOGB, true, uint16_t>(R, in, o, M, stream)
+                  : launch_in_split<LOGB, true, float>(R, in, o, M, stream);
+      return ib ? launch_in_split<LOGB, false, uint16_t>(R, in, o, M, stream)
+                : launch_in_split<LOGB, false, float>(R, in, o, M, stream);
+    }
     // few rows of the output rotation: eight workgroups per block
     if (transpose && M <= kSplitMaxM) {
       const bool ob = out_dt == HARP_BF16;

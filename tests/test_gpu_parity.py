@@ -132,6 +132,10 @@ ROT_CASES = [
     # (workgroup barriers), and a ragged batch with four rows per slot
     (192, 64, 70, "f32"), (640, 128, 21, "bf16"), (1024, 512, 37, "f32"),
     (2048, 1024, 9, "bf16"), (28672, 256, 300, "f32"),
+    # input rotation of up to 64 rows at b = 4096 / 8192 into float32: two
+    # launches (sub-blocks, then the last three stages); 65 rows: one
+    (8192, 4096, 3, "f32"), (4096, 4096, 64, "bf16"), (4096, 4096, 65, "f32"),
+    (16384, 8192, 5, "bf16"),
 ]
 
 
