@@ -125,7 +125,11 @@ harp_status harp_linear_fused(const harp_rotation* V, const harp_qweight* W,
     if (r != HARP_OK) return r;
   } else {
     uint16_t* xt = reinterpret_cast<uint16_t*>(ws);
-    harp_status r = from_hip(harp::launch_rotate(*V, x, x_dt, xt, HARP_BF16, M, false, s));
+    // y' is not yet written: when it is at least as large as x~ in float32
+    // it holds the intermediate of the two-launch input rotation
+    harp_status r = from_hip(
+        W->N >= W->K ? harp::launch_rotate_in_scratch(*V, x, x_dt, xt, yp, M, s)
+                     : harp::launch_rotate(*V, x, x_dt, xt, HARP_BF16, M, false, s));
     if (r != HARP_OK) return r;
     if (M <= harp::kSkinnyMaxM)
       r = from_hip(harp::launch_gemm_skinny(*W, xt, yp, M, s));

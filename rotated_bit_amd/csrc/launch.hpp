@@ -15,6 +15,12 @@ hipError_t launch_rotate(const harp_rotation& R, const void* in, int in_dt,
                          hipStream_t stream);
 
 // Mixed-radix side: xt = F x or y = F^T y' for M rows (one workgroup per row).
+// x~ = F x into bf16 for M rows, with M x dim floats of scratch for the
+// float32 intermediate of the two-launch form (b = 4096 / 8192, M <= 64);
+// other shapes run launch_rotate.
+hipError_t launch_rotate_in_scratch(const harp_rotation& R, const void* in, int in_dt,
+                                    uint16_t* out, float* scratch, int M,
+                                    hipStream_t stream);
 hipError_t launch_rotate_mixed(const harp_mixed_rotation& R, const void* in, int in_dt,
                                void* out, int out_dt, int M, bool transpose,
                                float* workspace, hipStream_t stream);

@@ -543,10 +543,10 @@ hipError_t launch_typed(const harp_rotation& R, const void* in, void* out, int M
 // passing through one CU.
 constexpr int kTailThreads = 256;
 
-template <int LOGB, bool Q8>
+template <int LOGB, bool Q8, typename TOut>
 __global__ __launch_bounds__(kTailThreads) void rotate_in_tail_kernel(
-    float* __restrict__ xt, const float2* __restrict__ cs, const int8_t* __restrict__ codes,
-    float step, int dim) {
+    const float* src, TOut* dst, const float2* __restrict__ cs,
+    const int8_t* __restrict__ codes, float step, int dim) {
   constexpr int B = 1 << LOGB;
   constexpr int L = LOGB;
   constexpr int SB = B / 8;
@@ -562,11 +562,15 @@ __global__ __launch_bounds__(kTailThreads) void rotate_in_tail_kernel(
   }
   const int blk = blockIdx.x / kParts;
   const int q = (blockIdx.x - blk * kParts) * kTailThreads + threadIdx.x;
-  float* base = xt + static_cast<size_t>(blockIdx.y) * dim + static_cast<size_t>(blk) * B + q;
+  // src and dst may be the same float32 rows: each thread reads its eight
+  // elements before it writes them
+  const size_t e0 = static_cast<size_t>(blockIdx.y) * dim + static_cast<size_t>(blk) * B + q;
+  const float* sb = src + e0;
+  TOut* db = dst + e0;
   const size_t coff = static_cast<size_t>(blk) * L * (B / 2);
   float v[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = base[j * SB];
+  for (int j = 0; j < 8; ++j) v[j] = sb[j * SB];
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
     const int s = L - 3 + k;
@@ -585,19 +589,33 @@ __global__ __launch_bounds__(kTailThreads) void rotate_in_tail_kernel(
     }
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) base[j * SB] = v[j];
+  for (int j = 0; j < 8; ++j) from_f32(db[j * SB], v[j]);
 }
 
-template <int LOGB, bool Q8, typename TIn>
-hipError_t launch_in_split(const harp_rotation& R, const void* in, float* out, int M,
-                           hipStream_t stream) {
-  hipError_t e = launch_typed<LOGB - 3, 3, false, Q8, TIn, float, 3>(R, in, out, M, stream);
+// The first launch writes the float32 intermediate to scratch (M x dim
+// floats); the second writes the output (in place when out is scratch).
+template <int LOGB, bool Q8, typename TIn, typename TOut>
+hipError_t launch_in_split(const harp_rotation& R, const void* in, float* scratch, TOut* out,
+                           int M, hipStream_t stream) {
+  hipError_t e = launch_typed<LOGB - 3, 3, false, Q8, TIn, float, 3>(R, in, scratch, M, stream);
   if (e != hipSuccess) return e;
   const int nblk = R.dim >> LOGB;
   const dim3 grid(nblk * ((1 << LOGB) / 8 / kTailThreads), M);
-  hipLaunchKernelGGL((rotate_in_tail_kernel<LOGB, Q8>), grid, dim3(kTailThreads), 0, stream,
-                     out, reinterpret_cast<const float2*>(R.cs), R.phi_codes, R.phi_step, R.dim);
+  hipLaunchKernelGGL((rotate_in_tail_kernel<LOGB, Q8, TOut>), grid, dim3(kTailThreads), 0,
+                     stream, scratch, out, reinterpret_cast<const float2*>(R.cs), R.phi_codes,
+                     R.phi_step, R.dim);
   return hipGetLastError();
+}
+
+template <int LOGB, typename TOut>
+hipError_t launch_in_split_any(const harp_rotation& R, const void* in, int in_dt,
+                               float* scratch, TOut* out, int M, hipStream_t stream) {
+  const bool ib = in_dt == HARP_BF16;
+  if (R.phi_codes != nullptr)
+    return ib ? launch_in_split<LOGB, true, uint16_t, TOut>(R, in, scratch, out, M, stream)
+              : launch_in_split<LOGB, true, float, TOut>(R, in, scratch, out, M, stream);
+  return ib ? launch_in_split<LOGB, false, uint16_t, TOut>(R, in, scratch, out, M, stream)
+            : launch_in_split<LOGB, false, float, TOut>(R, in, scratch, out, M, stream);
 }
 
 template <int LOGB, int EL_, bool Q8>
@@ -634,12 +652,7 @@ hipError_t launch_logb(const harp_rotation& R, const void* in, int in_dt,
     // few rows of the input rotation into float32: two launches (above)
     if (!transpose && out_dt == HARP_F32 && M <= kSplitMaxM) {
       float* o = static_cast<float*>(out);
-      const bool ib = in_dt == HARP_BF16;
-      if (R.phi_codes != nullptr)
-        return ib ? launch_in_split<LOGB, true, uint16_t>(R, in, o, M, stream)
-                  : launch_in_split<LOGB, true, float>(R, in, o, M, stream);
-      return ib ? launch_in_split<LOGB, false, uint16_t>(R, in, o, M, stream)
-                : launch_in_split<LOGB, false, float>(R, in, o, M, stream);
+      return launch_in_split_any<LOGB, float>(R, in, in_dt, o, o, M, stream);
     }
     // few rows of the output rotation: eight workgroups per block
     if (transpose && M <= kSplitMaxM) {
@@ -661,6 +674,18 @@ hipError_t launch_logb(const harp_rotation& R, const void* in, int in_dt,
 }
 
 }  // namespace
+
+hipError_t launch_rotate_in_scratch(const harp_rotation& R, const void* in, int in_dt,
+                                    uint16_t* out, float* scratch, int M,
+                                    hipStream_t stream) {
+  if (M <= kSplitMaxM) {
+    if (R.block == 4096)
+      return launch_in_split_any<12, uint16_t>(R, in, in_dt, scratch, out, M, stream);
+    if (R.block == 8192)
+      return launch_in_split_any<13, uint16_t>(R, in, in_dt, scratch, out, M, stream);
+  }
+  return launch_rotate(R, in, in_dt, out, HARP_BF16, M, false, stream);
+}
 
 hipError_t launch_rotate(const harp_rotation& R, const void* in, int in_dt,
                          void* out, int out_dt, int M, bool transpose,

@@ -420,7 +420,8 @@ def run_fused(li, y_dtype=torch.float32):
     return y
 
 
-FUSED_CASES = [("tiny", 0, 2, 4), ("l7b_decode", 0, 2, 1)]
+FUSED_CASES = [("tiny", 0, 2, 4), ("l7b_decode", 0, 2, 1), ("l7b_decode", 0, 2, 16),
+               ("l7b_decode", 0, 2, 64)]
 FUSED_CASES += [("l7b_mlp", i, 2, m) for i in (0, 1) for m in (1, 16)]
 FUSED_CASES += [("q8b_prefill", i, b, 512) for i in (0, 1, 2) for b in (2, 4)]
 
