@@ -333,19 +333,24 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(
   floatx4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f};
   floatx4 acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
   if (gb < ge) {
-    // two register sets: the next group's loads are in flight while the
-    // current group is multiplied; a load past the range re-loads the last
+    // three register sets: the loads of the next two groups are in flight
+    // while a group is multiplied; a load past the range re-loads the last
     // group (valid memory, unused)
-    MfRegs<BITS> ra, rb;
+    MfRegs<BITS> ra, rb, rc;
+    const int gl = ge - 1;
     mf_load<BITS>(ra, gb, xrow_p, crow, srow, zrow, h);
+    mf_load<BITS>(rb, min(gb + 1, gl), xrow_p, crow, srow, zrow, h);
     int g = gb;
-    for (; g + 2 <= ge; g += 2) {
-      mf_load<BITS>(rb, g + 1, xrow_p, crow, srow, zrow, h);
+    for (; g + 3 <= ge; g += 3) {
+      mf_load<BITS>(rc, min(g + 2, gl), xrow_p, crow, srow, zrow, h);
       mf_group<BITS>(ra, h, acc0, acc1);
-      mf_load<BITS>(ra, min(g + 2, ge - 1), xrow_p, crow, srow, zrow, h);
+      mf_load<BITS>(ra, min(g + 3, gl), xrow_p, crow, srow, zrow, h);
       mf_group<BITS>(rb, h, acc0, acc1);
+      mf_load<BITS>(rb, min(g + 4, gl), xrow_p, crow, srow, zrow, h);
+      mf_group<BITS>(rc, h, acc0, acc1);
     }
     if (g < ge) mf_group<BITS>(ra, h, acc0, acc1);
+    if (g + 1 < ge) mf_group<BITS>(rb, h, acc0, acc1);
   }
   red[wave][lane] = acc0 + acc1;
   __syncthreads();
@@ -380,8 +385,8 @@ hipError_t launch_bits(const harp_qweight& W, const float* xt, float* yt, int M,
                        hipStream_t stream) {
   // Up to eight rows the vector-ALU kernel (at most two passes over the
   // weights) is faster; from nine rows on, 16-row tiles on the matrix cores
-  // (4096x4096 2-bit: 13.5 vs 12.3 us at M = 8, 14.9 vs 18.3 at M = 12,
-  // 57.5 vs 70.3 at M = 64).
+  // (4096x4096 2-bit: 13.0 vs 12.3 us at M = 8, 14.5 vs 18.3 at M = 12,
+  // 52.0 vs 70.3 at M = 64).
   if (M == 1) return launch_cfg<BITS, 1>(W, xt, yt, M, stream);
   if (M == 2) return launch_cfg<BITS, 2>(W, xt, yt, M, stream);
   if (M <= kMfMinM - 1) return launch_cfg<BITS, 4>(W, xt, yt, M, stream);
