@@ -113,6 +113,48 @@ def test_quantizer_exact_recovery(bits, arith):
     assert np.array_equal(q, q0.reshape(n, G * 64))
 
 
+def load_tie_fixtures(golden_dir):
+    """Exact-tie groups (tests/golden/quantize_ties.txt): (bits, scale,
+    zero, values[64], codes[64]); unlisted positions hold 0.0 whose code is
+    the zero-point."""
+    cases = []
+    with open(os.path.join(golden_dir, "quantize_ties.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            parts = line.split()
+            bits, scale, zero = int(parts[0]), float(parts[1]), int(parts[2])
+            vals = np.zeros(64)
+            codes = np.full(64, zero, dtype=np.uint8)
+            for i, vc in enumerate(parts[3:]):
+                v, c = vc.split(":")
+                vals[i] = float(v)
+                codes[i] = int(c)
+            cases.append((bits, scale, zero, vals, codes))
+    return cases
+
+
+@pytest.mark.parametrize("arith", ["f64", "f32"])
+def test_quantizer_tie_rule_golden(golden_dir, arith):
+    """Round half to even for both the zero-point and the codes: hand-derived
+    exact-tie groups, each of which rounding half up would change."""
+    cases = load_tie_fixtures(golden_dir)
+    assert len(cases) >= 7
+    for bits, scale, zero, vals, codes in cases:
+        q, s16, z16 = O.quantize(vals[None, :], bits, arith=arith)
+        assert float(s16[0, 0]) == scale, (bits, vals[:4])
+        assert float(z16[0, 0]) == zero, (bits, vals[:4])
+        assert np.array_equal(q[0], codes), (bits, vals[:6], q[0][:6], codes[:6])
+    # the same groups side by side in one row: each group decides alone
+    for bits in (2, 3, 4):
+        sub = [c for c in cases if c[0] == bits]
+        row = np.concatenate([c[3] for c in sub])[None, :]
+        q, s16, z16 = O.quantize(row, bits, arith=arith)
+        assert np.array_equal(q[0], np.concatenate([c[4] for c in sub]))
+        assert [float(z) for z in z16[0]] == [c[2] for c in sub]
+
+
 @pytest.mark.parametrize("arith", ["f64", "f32"])
 def test_quantizer_degenerate_group(arith):
     W = np.zeros((2, 128))
