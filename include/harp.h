@@ -168,8 +168,11 @@ harp_status harp_rotate_in(const harp_rotation *V, const void *x,
                            int32_t M, harp_stream stream);
 
 /*
- * y = F_U^T y' for each of M rows: stages L-1..0 (each stage is its own
- * transpose), then the sign flip.
+ * y = F_U^T y' for each of M rows: the output side U = F_U^T of the
+ * two-sided processor (technical summary §2.1-2.2 for the stages; §5: the
+ * processor is an exact change of basis, so U undoes the F_U applied to the
+ * weight offline).  Stages L-1..0 (each stage is its own transpose), then
+ * the sign flip; float32 arithmetic.
  *   yt  [M][U->dim] float32;  y  [M][U->dim] of y_dt (bf16: nearest even).
  */
 harp_status harp_rotate_out(const harp_rotation *U, const float *yt, void *y,
@@ -203,11 +206,14 @@ harp_status harp_rotate_out_mixed(const harp_mixed_rotation *R, const float *yt,
 size_t harp_rotate_mixed_workspace_bytes(int32_t dim, int32_t M, harp_dtype out_dt);
 
 /*
- * y'[m][n] = sum_k w_hat[n][k] x~[m][k], float32 throughout: w_hat is exact
- * in float32 and x~ is not rounded.  Up to 8 rows on the vector ALUs, from
- * 9 rows on in 16-row tiles on the float32 matrix cores (same products,
- * float32 accumulation in a different order).  Meant for decode batches;
- * any M is accepted.
+ * y'[m][n] = sum_k w_hat[n][k] x~[m][k]: the quantized matmul between the
+ * two rotations (technical summary §2.4: HARP wraps the backend's quantized
+ * linear without changing it; the backend's codebook is not on the pages,
+ * so w_hat is the stand-in per-group uniform grid described at the top of
+ * this header).  float32 throughout: w_hat is exact in float32 and x~ is
+ * not rounded.  Up to 8 rows on the vector ALUs, from 9 rows on in 16-row
+ * tiles on the float32 matrix cores (same products, float32 accumulation in
+ * a different order).  Meant for decode batches; any M is accepted.
  *   xt  [M][W->K] float32;  yt  [M][W->N] float32.
  */
 harp_status harp_deq_gemv(const harp_qweight *W, const float *xt, float *yt,
@@ -229,21 +235,27 @@ harp_status harp_rotate_in_deq_gemv(const harp_rotation *V,
                                     harp_stream stream);
 
 /*
- * y'[m][n] = sum_k bf16(w_hat[n][k]) x~[m][k] on the bf16 matrix cores with
- * float32 accumulation; bf16(w_hat) rounds to nearest even.  Any M >= 0.
- * M <= 64: one workgroup per 16 output features, each weight fetched and
- * dequantized once, no workspace (a given workspace is not used).  M > 64:
- * 128 x 128 output tiles.
+ * y'[m][n] = sum_k w_hat[n][k] x~[m][k] for batched (prefill) rows on the
+ * bf16 matrix cores with float32 accumulation: the same quantized matmul as
+ * harp_deq_gemv (technical summary §2.4; w_hat the stand-in per-group
+ * uniform grid described at the top of this header), with x~ given in bf16.
+ * Any M >= 0.
+ * M <= 64: one workgroup per 16 output features; the integer codes enter
+ * the matrix cores exactly and scale and zero are applied per group, so
+ * w_hat is not rounded; no workspace (a given workspace is not used).
+ * M > 64: 128 x 128 output tiles on bf16(w_hat) (nearest even).
  *   xt_bf16    [M][W->K] bf16;  yt  [M][W->N] float32.
- *   workspace  optional (M > 64).  NULL runs the product as one K slice.  Otherwise
- *              at least harp_deq_gemm_workspace_bytes(M, N, K) bytes,
- *              256-byte aligned: the K dimension is split into slices that
- *              run concurrently and are summed in a fixed slice order
- *              (bitwise reproducible).  Zero-fill the workspace before its
- *              first use: its per-tile arrival counters must start at
- *              zero, and every call leaves them at zero (the partial tiles
- *              need no initialisation).  Calls that share a workspace must
- *              not overlap in time.
+ *   workspace  optional (M > 64).  NULL runs the product as one K slice.
+ *              Otherwise at least harp_deq_gemm_workspace_bytes(M, N, K)
+ *              bytes, 256-byte aligned: the K dimension is split into slices
+ *              that run concurrently and are summed in a fixed slice order
+ *              (bitwise reproducible).  Its first 1024 bytes hold per-tile
+ *              arrival counters at the same offset for every shape: zero-fill
+ *              the workspace once before its first use; every call leaves the
+ *              counters at zero, so one workspace serves any sequence of
+ *              shapes it is large enough for (the partial tiles need no
+ *              initialisation).  Calls that share a workspace must not
+ *              overlap in time.
  */
 harp_status harp_deq_gemm(const harp_qweight *W, const uint16_t *xt_bf16,
                           float *yt, int32_t M, void *workspace,
@@ -254,21 +266,23 @@ harp_status harp_deq_gemm(const harp_qweight *W, const uint16_t *xt_bf16,
 size_t harp_deq_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
 
 /* Workspace bytes harp_linear_fused needs for M rows of a K -> N linear;
- * 0 when an argument is out of range. */
+ * 0 for M == 0 and when an argument is out of range. */
 size_t harp_linear_workspace_bytes(int32_t M, int32_t N, int32_t K);
 
 /*
  * The whole linear with mixed-radix sides, y = F_U^T deq(W) F_V x
  * (technical summary §2.4 with the stages of §2.1-2.2), for dimensions that
  * are no power of two (e.g. 5120 = 8*8*8*5*2).  Requires V->dim == W->K and
- * U->dim == W->N.  M < 16: float32 x~ and the vector-ALU product of
- * harp_deq_gemv; 16 <= M <= 64: bf16 x~ and the small-batch matrix-core
- * product; M > 64: bf16 x~ and the matrix-core GEMM with split K.  Same
- * rounding points as harp_linear_fused.
+ * U->dim == W->N.  The same batch ranges and rounding points as
+ * harp_linear_fused: float32 x~ below 64 rows (the product of harp_deq_gemv
+ * below 16, the small-batch matrix-core product on the two-plane bf16 split
+ * of x~ from 16), bf16 x~ from 64 rows (the small-batch product at 64, the
+ * matrix-core GEMM with split K above).
  *   x  [M][K] of x_dt;  y  [M][N] of y_dt.
  *   workspace  at least harp_linear_mixed_workspace_bytes(M, N, K) bytes,
- *              256-byte aligned, zero-filled before its first use (the
- *              split-K counters; every call leaves them at zero).  Calls that
+ *              256-byte aligned, zero-filled before its first use (its first
+ *              1024 bytes are the split-K counters, at the same offset for
+ *              every shape; every call leaves them at zero).  Calls that
  *              share a workspace must not overlap in time.
  */
 harp_status harp_linear_fused_mixed(const harp_mixed_rotation *V, const harp_qweight *W,
@@ -276,22 +290,29 @@ harp_status harp_linear_fused_mixed(const harp_mixed_rotation *V, const harp_qwe
                                     harp_dtype x_dt, void *y, harp_dtype y_dt,
                                     int32_t M, void *workspace, size_t ws_bytes,
                                     harp_stream stream);
-/* Workspace bytes of harp_linear_fused_mixed; 0 for arguments out of range. */
+/* Workspace bytes of harp_linear_fused_mixed; 0 for M == 0 and for arguments
+ * out of range. */
 size_t harp_linear_mixed_workspace_bytes(int32_t M, int32_t N, int32_t K);
 
 /*
  * y = F_U^T deq(W) F_V x, the whole linear (technical summary §2.4 and §5).
- * M < 16 runs rotate-in (float32 x~), the float32 product of harp_deq_gemv
- * and rotate-out, with the first two in one launch for M <= 2 and N <= 4096
- * where harp_rotate_in_deq_gemv supports the shape; M >= 16 runs rotate-in with a
- * bf16 x~, the matrix-core product of harp_deq_gemm and rotate-out.  Requires V->dim == W->K and
- * U->dim == W->N.
+ * Requires V->dim == W->K and U->dim == W->N.  Batch ranges:
+ *   M < 16: rotate-in to a float32 x~, the float32 product of
+ *     harp_deq_gemv, rotate-out; the first two in one launch for M <= 2 and
+ *     N <= 4096 where harp_rotate_in_deq_gemv supports the shape.
+ *   16 <= M < 64: rotate-in to a float32 x~, the small-batch matrix-core
+ *     product on x~ split exactly into two bf16 planes hi + lo
+ *     (|x~ - hi - lo| <= 2^-16 |x~|; w_hat exact), rotate-out.
+ *   M >= 64: rotate-in to a bf16 x~, the matrix-core product of
+ *     harp_deq_gemm (w_hat exact at 64 rows, bf16 above), rotate-out.
  *   x  [M][K] of x_dt;  y  [M][N] of y_dt;
  *   workspace  at least harp_linear_workspace_bytes(M, N, K) bytes, 256-byte
  *              aligned, owned by the caller.  Zero-filled before its first
- *              use (its last part holds the GEMM arrival counters, which
- *              every call leaves at zero); the rest is clobbered.  Calls
- *              that share a workspace must not overlap in time.
+ *              use: its first 1024 bytes hold the GEMM arrival counters, at
+ *              the same offset for every shape, and every call leaves them
+ *              at zero, so one workspace serves any sequence of shapes it is
+ *              large enough for; the rest is clobbered.  Calls that share a
+ *              workspace must not overlap in time.
  */
 harp_status harp_linear_fused(const harp_rotation *V, const harp_qweight *W,
                               const harp_rotation *U, const void *x,
@@ -299,11 +320,6 @@ harp_status harp_linear_fused(const harp_rotation *V, const harp_qweight *W,
                               int32_t M, void *workspace, size_t ws_bytes,
                               harp_stream stream);
 
-/*
- * Test hook, not on the hot path: writes the dense w_hat [N][K] as float32
- * (exact) or bf16 (nearest even), through the same device unpack and
- * dequant code the products use.
- */
 /*
  * Offline preparation (technical summary §2.4: the processor rotates the
  * weight before the quantization backend; §5: an exact change of basis).
@@ -336,6 +352,14 @@ harp_status harp_quantize_pack(const float *Wp, int32_t N, int32_t K, int32_t bi
                                uint32_t *qweight, uint16_t *scale, uint16_t *zero,
                                harp_stream stream);
 
+/*
+ * Test hook, not on the hot path: writes the dense w_hat [N][K] as float32
+ * (exact) or bf16 (nearest even), through the same device unpack and
+ * dequant code the products use (the stand-in per-group uniform grid
+ * described at the top of this header; technical summary §2.4 leaves the
+ * backend's codebook open).
+ *   out  [W->N][W->K] of out_dt, device, 16-byte aligned.
+ */
 harp_status harp_dequant(const harp_qweight *W, void *out, harp_dtype out_dt,
                          harp_stream stream);
 

@@ -189,9 +189,9 @@ __device__ __forceinline__ void gemm_step(
   mfma_step(sA[st], sB[st], c.wm, c.wn, c.kk0, c.frag_row, c.frag_k, acc);
 }
 
-// Split-K workspace: per slice and tile one float32 partial tile in the
-// layout the four output waves hold it (coalesced), then one uint32
-// arrival counter per tile.
+// Split K: per slice and tile one float32 partial tile in the layout the
+// four output waves hold it (coalesced), and one uint32 arrival counter per
+// tile (the caller places the counters at a fixed offset of its workspace).
 constexpr int kTileFloats = BM * BN;
 
 template <int BITS>
@@ -342,7 +342,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     // arrival; this replaces a full agent fence, whose L2 writeback and
     // invalidate would also evict the operands of tiles still running on
     // this XCD.
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt/lgkmcnt untouched
+    // vmcnt(0) only (the assembler encodes the counter fields; the LDS and
+    // export counters are left alone).
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0) {
       const uint32_t prev = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED,
@@ -402,31 +404,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 
 template <int BITS>
 hipError_t launch_bits(const harp_qweight& W, const uint16_t* xt, float* yt,
-                       int M, int splits, void* workspace, hipStream_t stream) {
+                       int M, int splits, float* partials, uint32_t* counters,
+                       hipStream_t stream) {
   const int tn = (W.N + BN - 1) / BN;
   const int tm = (M + BM - 1) / BM;
   const dim3 grid(tn, tm, splits);
-  float* partials = nullptr;
-  uint32_t* counters = nullptr;
-  if (splits > 1) {
-    partials = static_cast<float*>(workspace);
-    const size_t pbytes = static_cast<size_t>(splits) * tn * tm * kTileFloats * sizeof(float);
-    counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
-                                           ((pbytes + 255) & ~static_cast<size_t>(255)));
-  }
   hipLaunchKernelGGL((gemm_kernel<BITS>), grid, dim3(kThreads), 0, stream, W.qweight,
-                     W.scale, W.zero, xt, yt, W.N, W.K, M, partials, counters);
+                     W.scale, W.zero, xt, yt, W.N, W.K, M,
+                     splits > 1 ? partials : nullptr, splits > 1 ? counters : nullptr);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const harp_qweight& W, const uint16_t* xt, float* yt,
-                       int M, int splits, void* workspace, hipStream_t stream) {
+                       int M, int splits, float* partials, uint32_t* counters,
+                       hipStream_t stream) {
   switch (W.bits) {
-    case 2: return launch_bits<2>(W, xt, yt, M, splits, workspace, stream);
-    case 3: return launch_bits<3>(W, xt, yt, M, splits, workspace, stream);
-    case 4: return launch_bits<4>(W, xt, yt, M, splits, workspace, stream);
+    case 2: return launch_bits<2>(W, xt, yt, M, splits, partials, counters, stream);
+    case 3: return launch_bits<3>(W, xt, yt, M, splits, partials, counters, stream);
+    case 4: return launch_bits<4>(W, xt, yt, M, splits, partials, counters, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -87,8 +87,11 @@ harp_status harp_deq_gemm(const harp_qweight* W, const uint16_t* xt_bf16,
   if (M <= harp::kSkinnyMaxM)
     return from_hip(harp::launch_gemm_skinny(*W, xt_bf16, yt, M, as_stream(stream)));
   const int splits = workspace ? harp::gemm_splits(M, W->N, W->K) : 1;
-  return from_hip(harp::launch_gemm(*W, xt_bf16, yt, M, splits, workspace,
-                                    as_stream(stream)));
+  char* ws = static_cast<char*>(workspace);
+  return from_hip(harp::launch_gemm(
+      *W, xt_bf16, yt, M, splits,
+      splits > 1 ? reinterpret_cast<float*>(ws + harp::kGemmCounterBytes) : nullptr,
+      reinterpret_cast<uint32_t*>(ws), as_stream(stream)));
 }
 
 size_t harp_deq_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) {
@@ -113,31 +116,35 @@ harp_status harp_linear_fused(const harp_rotation* V, const harp_qweight* W,
   const hipStream_t s = as_stream(stream);
   char* ws = static_cast<char*>(workspace);
   float* yp = reinterpret_cast<float*>(ws + harp::workspace_yp_offset(M, W->K));
+  harp_status r;
   if (M <= harp::kFusedRotGemvMaxM && W->N <= harp::kFusedRotGemvMaxN &&
       harp::gemv_rotated_supported(*V, *W, M)) {
-    const harp_status r = from_hip(harp::launch_gemv_rotated(*V, *W, x, x_dt, yp, M, s));
+    r = from_hip(harp::launch_gemv_rotated(*V, *W, x, x_dt, yp, M, s));
+  } else if (M < harp::kBf16MinM) {
+    // float32 x~: the float32 product, or the matrix cores on its two-plane
+    // bf16 split
+    float* xt = reinterpret_cast<float*>(ws + harp::workspace_xt_offset());
+    r = from_hip(harp::launch_rotate(*V, x, x_dt, xt, HARP_F32, M, false, s));
     if (r != HARP_OK) return r;
-  } else if (M < harp::kMfmaMinM) {
-    float* xt = reinterpret_cast<float*>(ws);
-    harp_status r = from_hip(harp::launch_rotate(*V, x, x_dt, xt, HARP_F32, M, false, s));
-    if (r != HARP_OK) return r;
-    r = from_hip(harp::launch_gemv(*W, xt, yp, M, s));
-    if (r != HARP_OK) return r;
+    r = from_hip(M < harp::kSplitMinM ? harp::launch_gemv(*W, xt, yp, M, s)
+                                      : harp::launch_gemm_skinny_split(*W, xt, yp, M, s));
   } else {
-    uint16_t* xt = reinterpret_cast<uint16_t*>(ws);
+    uint16_t* xt = reinterpret_cast<uint16_t*>(ws + harp::workspace_xt_offset());
     // y' is not yet written: when it is at least as large as x~ in float32
     // it holds the intermediate of the two-launch input rotation
-    harp_status r = from_hip(
+    r = from_hip(
         W->N >= W->K ? harp::launch_rotate_in_scratch(*V, x, x_dt, xt, yp, M, s)
                      : harp::launch_rotate(*V, x, x_dt, xt, HARP_BF16, M, false, s));
     if (r != HARP_OK) return r;
     if (M <= harp::kSkinnyMaxM)
       r = from_hip(harp::launch_gemm_skinny(*W, xt, yp, M, s));
     else
-      r = from_hip(harp::launch_gemm(*W, xt, yp, M, harp::gemm_splits(M, W->N, W->K),
-                                     ws + harp::workspace_gemm_offset(M, W->N, W->K), s));
-    if (r != HARP_OK) return r;
+      r = from_hip(harp::launch_gemm(
+          *W, xt, yp, M, harp::gemm_splits(M, W->N, W->K),
+          reinterpret_cast<float*>(ws + harp::workspace_gemm_offset(M, W->N, W->K)),
+          reinterpret_cast<uint32_t*>(ws), s));
   }
+  if (r != HARP_OK) return r;
   return from_hip(harp::launch_rotate(*U, yp, HARP_F32, y, y_dt, M, true, s));
 }
 
@@ -155,14 +162,15 @@ harp_status harp_linear_fused_mixed(const harp_mixed_rotation* V, const harp_qwe
   const hipStream_t s = as_stream(stream);
   char* ws = static_cast<char*>(workspace);
   const int32_t N = W->N, K = W->K;
-  float* xf = reinterpret_cast<float*>(ws);
+  float* xf = reinterpret_cast<float*>(ws + harp::mixed_ws_xf_offset());
   float* yp = reinterpret_cast<float*>(ws + harp::mixed_ws_yp_offset(M, K));
   float* ys = reinterpret_cast<float*>(ws + harp::mixed_ws_ys_offset(M, N, K));
   harp_status r;
-  if (M < harp::kMfmaMinM) {
+  if (M < harp::kBf16MinM) {
     r = from_hip(harp::launch_rotate_mixed(*V, x, x_dt, xf, HARP_F32, M, false, nullptr, s));
     if (r != HARP_OK) return r;
-    r = from_hip(harp::launch_gemv(*W, xf, yp, M, s));
+    r = from_hip(M < harp::kSplitMinM ? harp::launch_gemv(*W, xf, yp, M, s)
+                                      : harp::launch_gemm_skinny_split(*W, xf, yp, M, s));
   } else {
     uint16_t* xb = reinterpret_cast<uint16_t*>(ws + harp::mixed_ws_xb_offset(M, K));
     r = from_hip(harp::launch_rotate_mixed(*V, x, x_dt, xb, HARP_BF16, M, false, xf, s));
@@ -170,8 +178,10 @@ harp_status harp_linear_fused_mixed(const harp_mixed_rotation* V, const harp_qwe
     if (M <= harp::kSkinnyMaxM)
       r = from_hip(harp::launch_gemm_skinny(*W, xb, yp, M, s));
     else
-      r = from_hip(harp::launch_gemm(*W, xb, yp, M, harp::gemm_splits(M, N, K),
-                                     ws + harp::mixed_ws_gemm_offset(M, N, K), s));
+      r = from_hip(harp::launch_gemm(
+          *W, xb, yp, M, harp::gemm_splits(M, N, K),
+          reinterpret_cast<float*>(ws + harp::mixed_ws_gemm_offset(M, N, K)),
+          reinterpret_cast<uint32_t*>(ws), s));
   }
   if (r != HARP_OK) return r;
   return from_hip(harp::launch_rotate_mixed(*U, yp, HARP_F32, y, y_dt, M, true, ys, s));

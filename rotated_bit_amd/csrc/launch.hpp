@@ -39,15 +39,21 @@ hipError_t launch_gemv_rotated(const harp_rotation& V, const harp_qweight& W,
                                hipStream_t stream);
 
 // yt = bf16(w_hat) xt_bf16 on the matrix cores, float32 accumulation, in
-// `splits` K slices (splits > 1 needs the GEMM workspace, zero-filled
-// before its first use and left zero-filled).
+// `splits` K slices.  splits > 1 needs `partials` (splits x tiles float32
+// tiles, no initialisation) and `counters` (one uint32 per output tile,
+// zero before the call and left zero by it).
 hipError_t launch_gemm(const harp_qweight& W, const uint16_t* xt, float* yt,
-                       int M, int splits, void* workspace, hipStream_t stream);
+                       int M, int splits, float* partials, uint32_t* counters,
+                       hipStream_t stream);
 
 // The same product for 1 <= M <= 64 with one workgroup per 16 output
-// features (no workspace, no tiles).
+// features (no workspace, no tiles); w_hat enters exactly.
 hipError_t launch_gemm_skinny(const harp_qweight& W, const uint16_t* xt, float* yt,
                               int M, hipStream_t stream);
+// The same kernel on a float32 xt, split into two bf16 planes hi + lo
+// (|xt - hi - lo| <= 2^-16 |xt|), 1 <= M <= 64.
+hipError_t launch_gemm_skinny_split(const harp_qweight& W, const float* xt, float* yt,
+                                    int M, hipStream_t stream);
 
 // Offline preparation: out [C][R] = in [R][C]^T (float32), and the packed
 // uniform grid of a float32 weight [N][K] (qweight, scale, zero in the

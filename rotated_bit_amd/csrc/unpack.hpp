@@ -189,29 +189,39 @@ __device__ __forceinline__ void chunk8_codes(uint32_t v, float (&q)[8]) {
   }
 }
 
-// The eight codes of a chunk as bf16 values 128 + q (exact: 128..143 are
-// integers of 8 significant bits), two per word, code 2i in the low half of
-// word i.  bf16 128 is 0x4300 and q fills the low mantissa bits, so each word
-// is an AND-OR of the shifted chunk.
+// The eight codes of a chunk as the bf16 values 1 + q / 2^BITS, two per
+// word, code 2i in the low half of word i.  bf16 1.0 is 0x3f80 and its
+// seven stored mantissa bits are 2^-1 .. 2^-7, so q placed in the top BITS
+// of them gives 1 + q / 2^BITS exactly: one shift and one AND-OR per word.
+// (Codes in the top bits rather than the bottom ones keep the constant part
+// of the operand small against the code part, 2^BITS : q instead of 128 : q,
+// which is what the per-group sum T - (1 + z / 2^BITS) S cancels.)
 template <int BITS>
-__device__ __forceinline__ u32x4 chunk8_bf16_offset(uint32_t v) {
-  constexpr uint32_t kBase = 0x43004300u;
+__device__ __forceinline__ u32x4 chunk8_bf16_unit(uint32_t v) {
+  constexpr uint32_t kBase = 0x3f803f80u;
+  constexpr int kTop = 7 - BITS;             // bit of the code's LSB in a half
   u32x4 out;
   if constexpr (BITS == 2) {
     const uint32_t v16 = v & 0xffffu;          // the chunk; higher bits are other codes
-    const uint32_t u = v16 | (v16 << 14);      // code 2i+1 moves to bit 4i + 16
+    const uint32_t u = v16 | (v16 << 14);      // code 2i at bit 4i, code 2i+1 at bit 4i + 16
+    constexpr uint32_t kMask = 0x00030003u << kTop;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = ((u >> (4 * i)) & 0x00030003u) | kBase;
+    for (int i = 0; i < 4; ++i) {
+      const int sh = kTop - 4 * i;             // bring bit 4i to bit kTop
+      const uint32_t w = sh >= 0 ? (u << sh) : (u >> -sh);
+      out[i] = (w & kMask) | kBase;
+    }
   } else if constexpr (BITS == 4) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t x = v >> (8 * i);
-      out[i] = (x & 0x0000000fu) | ((x & 0x000000f0u) << 12) | kBase;
+      out[i] = ((x & 0x0000000fu) << kTop) | ((x & 0x000000f0u) << (12 + kTop)) | kBase;
     }
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      out[i] = ((v >> (6 * i)) & 7u) | (((v >> (6 * i + 3)) & 7u) << 16) | kBase;
+      out[i] = (((v >> (6 * i)) & 7u) << kTop) | (((v >> (6 * i + 3)) & 7u) << (16 + kTop)) |
+               kBase;
   }
   return out;
 }

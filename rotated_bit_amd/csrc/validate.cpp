@@ -202,16 +202,20 @@ harp_status validate_rotate_mixed(const harp_mixed_rotation* R, const void* in, 
   return HARP_OK;
 }
 
-// Workspace of the mixed-radix linear: x~ as float32 (M < 16: the operand;
-// otherwise the stage buffer of the bf16 operand, which follows), y' float32,
-// the stage buffer of a bf16 output, then (M > 64) the GEMM's split-K area.
+// Workspace of the mixed-radix linear: the GEMM arrival counters (always
+// reserved, fixed offset), x~ as float32 (below kBf16MinM rows: the operand;
+// otherwise the stage buffer of the bf16 operand, which follows), y'
+// float32, the stage buffer of a bf16 output, then (M > 64) the GEMM's
+// partial tiles.
+size_t mixed_ws_xf_offset() { return kGemmCounterBytes; }
+
 size_t mixed_ws_xb_offset(int32_t M, int32_t K) {
-  return align256(static_cast<size_t>(M) * K * 4);
+  return mixed_ws_xf_offset() + align256(static_cast<size_t>(M) * K * 4);
 }
 
 size_t mixed_ws_yp_offset(int32_t M, int32_t K) {
   return mixed_ws_xb_offset(M, K) +
-         (M >= kMfmaMinM ? align256(static_cast<size_t>(M) * K * 2) : 0);
+         (M >= kBf16MinM ? align256(static_cast<size_t>(M) * K * 2) : 0);
 }
 
 size_t mixed_ws_ys_offset(int32_t M, int32_t N, int32_t K) {
@@ -226,8 +230,8 @@ size_t mixed_workspace_bytes(int32_t M, int32_t N, int32_t K) {
   if (M < 0 || M > HARP_MAX_M || N < 2 || N > HARP_MAX_MIXED_DIM || K < 64 ||
       K > HARP_MAX_MIXED_DIM)
     return 0;
-  const size_t gemm = M > kSkinnyMaxM ? gemm_workspace_bytes(M, N, K) : 0;
-  return mixed_ws_gemm_offset(M, N, K) + gemm;
+  if (M == 0) return 0;
+  return mixed_ws_gemm_offset(M, N, K) + gemm_partial_bytes(M, N, K);
 }
 
 harp_status validate_fused_mixed(const harp_mixed_rotation* V, const harp_qweight* W,
@@ -260,6 +264,7 @@ int32_t gemm_splits(int32_t M, int32_t N, int32_t K) {
   if (M <= kSkinnyMaxM || N < 1 || K < 64) return 1;
   const int64_t tiles = static_cast<int64_t>((M + kGemmTile - 1) / kGemmTile) *
                         ((N + kGemmTile - 1) / kGemmTile);
+  if (tiles > kGemmMaxSplitTiles) return 1;   // the chip is full without a split
   int32_t s = static_cast<int32_t>((256 + tiles / 2) / tiles);
   const int32_t groups = K / 64;
   if (s > 4) s = 4;
@@ -267,18 +272,25 @@ int32_t gemm_splits(int32_t M, int32_t N, int32_t K) {
   return s < 1 ? 1 : s;
 }
 
-size_t gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+size_t gemm_partial_bytes(int32_t M, int32_t N, int32_t K) {
   const int32_t s = gemm_splits(M, N, K);
   if (s <= 1) return 0;
   const size_t tiles = static_cast<size_t>((M + kGemmTile - 1) / kGemmTile) *
                        ((N + kGemmTile - 1) / kGemmTile);
-  return align256(static_cast<size_t>(s) * tiles * kGemmTile * kGemmTile * 4) +
-         align256(tiles * 4);
+  return align256(static_cast<size_t>(s) * tiles * kGemmTile * kGemmTile * 4);
 }
 
+// harp_deq_gemm's own workspace: counters, then partial tiles.
+size_t gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  const size_t p = gemm_partial_bytes(M, N, K);
+  return p == 0 ? 0 : kGemmCounterBytes + p;
+}
+
+size_t workspace_xt_offset() { return kGemmCounterBytes; }
+
 size_t workspace_yp_offset(int32_t M, int32_t K) {
-  const size_t xt_elem = M < kMfmaMinM ? 4 : 2;
-  return align256(static_cast<size_t>(M) * K * xt_elem);
+  const size_t xt_elem = M < kBf16MinM ? 4 : 2;
+  return workspace_xt_offset() + align256(static_cast<size_t>(M) * K * xt_elem);
 }
 
 size_t workspace_gemm_offset(int32_t M, int32_t N, int32_t K) {
@@ -289,8 +301,8 @@ size_t workspace_bytes(int32_t M, int32_t N, int32_t K) {
   if (M < 0 || M > HARP_MAX_M || N < 1 || N > HARP_MAX_DIM || K < 1 ||
       K > HARP_MAX_DIM)
     return 0;
-  const size_t gemm = M > kSkinnyMaxM ? gemm_workspace_bytes(M, N, K) : 0;
-  return workspace_gemm_offset(M, N, K) + gemm;
+  if (M == 0) return 0;
+  return workspace_gemm_offset(M, N, K) + gemm_partial_bytes(M, N, K);
 }
 
 const char* status_string(harp_status s) {

@@ -41,19 +41,29 @@ size_t rotate_weight_workspace_bytes(int32_t N, int32_t K);
 
 // Matrix-core GEMM tiling and its split over K: the number of K slices is
 // chosen so that about one 128 x 128 output tile slice runs per CU (256 on
-// MI355X), at most 4, each slice at least 8 quantization groups.  With
-// slices > 1 the GEMM needs a workspace: per slice and tile a float32
-// partial tile, then one uint32 arrival counter per tile.
+// MI355X), at most 4, each slice at least 8 quantization groups.  Split K
+// needs a workspace: a fixed area of per-tile uint32 arrival counters at its
+// front (a split product has at most kGemmMaxSplitTiles tiles), then per
+// slice and tile a float32 partial tile.  The counters sit at the same
+// offset for every shape, so one zero-filled workspace serves any sequence
+// of shapes that fit in it.
 constexpr int32_t kGemmTile = 128;
+constexpr int32_t kGemmMaxSplitTiles = 192;
+constexpr size_t kGemmCounterBytes = 1024;   // >= 4 * kGemmMaxSplitTiles, 256-aligned
 int32_t gemm_splits(int32_t M, int32_t N, int32_t K);
 size_t gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
+size_t gemm_partial_bytes(int32_t M, int32_t N, int32_t K);
 
-// Batch ranges of the products: harp_deq_gemm runs the small-batch
+// Batch ranges of the products.  harp_deq_gemm runs the small-batch
 // matrix-core kernel (no workspace) up to kSkinnyMaxM rows and the tiled
-// kernel above; the fused linear takes the float32 vector-ALU product below
-// kMfmaMinM rows and the bf16 matrix-core product from there on.
+// kernel above.  The fused linears keep x~ in float32 below kBf16MinM rows:
+// the vector-ALU / float32 matrix-core product below kSplitMinM, the
+// small-batch matrix-core product on the two-plane bf16 split of x~ from
+// kSplitMinM; from kBf16MinM rows on x~ is rounded to bf16 for the
+// matrix-core products.
 constexpr int32_t kSkinnyMaxM = 64;
-constexpr int32_t kMfmaMinM = 16;
+constexpr int32_t kSplitMinM = 16;
+constexpr int32_t kBf16MinM = 64;
 // The fused linear folds the input rotation into the product launch up to
 // this many rows and output features: every workgroup of the one-launch
 // form rotates all rows itself, so it only pays off with few rows and at
@@ -63,11 +73,14 @@ constexpr int32_t kMfmaMinM = 16;
 constexpr int32_t kFusedRotGemvMaxM = 2;
 constexpr int32_t kFusedRotGemvMaxN = 4096;
 
-// Workspace layout of the fused linear: x~, then y', then (M > kSkinnyMaxM)
-// the tiled GEMM's workspace, each 256-byte aligned.  x~ is float32 below
-// kMfmaMinM rows and bf16 from there on.
+// Workspace layout of the fused linear: the GEMM arrival counters
+// (kGemmCounterBytes, always reserved), x~, y', then (M > kSkinnyMaxM) the
+// GEMM's partial tiles, each part 256-byte aligned.  x~ is float32 below
+// kBf16MinM rows and bf16 from there on.
 size_t workspace_bytes(int32_t M, int32_t N, int32_t K);
+size_t workspace_xt_offset();
 size_t workspace_yp_offset(int32_t M, int32_t K);
+size_t mixed_ws_xf_offset();
 size_t mixed_ws_xb_offset(int32_t M, int32_t K);
 size_t mixed_ws_yp_offset(int32_t M, int32_t K);
 size_t mixed_ws_ys_offset(int32_t M, int32_t N, int32_t K);

@@ -194,22 +194,42 @@ class QWeight:
     zero: np.ndarray        # uint16 fp16 bits [N][K/64], integer-valued
 
 
-def qweight(N: int, K: int, bits: int, rng, w_std: float = 0.02) -> QWeight:
+def qweight(N: int, K: int, bits: int, rng, w_std: float = 0.02,
+            spread: str = "mid") -> QWeight:
     """Random packed weight with realistic group scales and zeros.
 
-    For N(0, std^2) groups of 64 the min-max range is about 4.8 std, so
-    s ~ 4.8 std / (2^B - 1), varied by a factor U(0.75, 1.25) per group.
-    Zeros are the integers nearest the middle of [0, 2^B - 1].
+    spread "mid": for N(0, std^2) groups of 64 the min-max range is about
+    4.8 std, so s ~ 4.8 std / (2^B - 1), varied by a factor U(0.75, 1.25)
+    per group; zeros are the integers nearest the middle of [0, 2^B - 1].
+
+    spread "wide" (edge coverage of the boundary format): zeros uniform over
+    the whole grid [0, 2^B - 1], the first and last group of every row pinned
+    to 0 and 2^B - 1; scales 2^e with e uniform in [-24, 4], i.e. across the
+    fp16 range from its smallest subnormal (2^-24) up, rounded to fp16, with
+    the second group of every row pinned to 2^-24 and the third to the
+    largest subnormal (1023 * 2^-24).
     """
     if bits not in (2, 3, 4) or K % 64:
         raise ValueError("bits in {2,3,4} and K % 64 == 0")
+    if spread not in ("mid", "wide"):
+        raise ValueError("spread must be 'mid' or 'wide'")
     qmax = (1 << bits) - 1
     nw = K * bits // 32
     words = rng.integers(0, 2 ** 32, size=(N, nw), dtype=np.uint64).astype(np.uint32)
     G = K // 64
-    s = (4.8 * w_std / qmax) * rng.uniform(0.75, 1.25, size=(N, G))
+    if spread == "mid":
+        s = (4.8 * w_std / qmax) * rng.uniform(0.75, 1.25, size=(N, G))
+        z = rng.integers(qmax // 2, qmax // 2 + 2, size=(N, G)).astype(np.float16)
+    else:
+        s = np.exp2(rng.uniform(-24.0, 4.0, size=(N, G)))
+        z = rng.integers(0, qmax + 1, size=(N, G)).astype(np.float16)
+        z[:, 0] = 0
+        z[:, -1] = qmax
+        if G > 1:
+            s[:, 1] = 2.0 ** -24
+        if G > 2:
+            s[:, 2] = 1023 * 2.0 ** -24
     scale = s.astype(np.float16).view(np.uint16)
-    z = rng.integers(qmax // 2, qmax // 2 + 2, size=(N, G)).astype(np.float16)
     return QWeight(N, K, bits, words, scale, z.view(np.uint16))
 
 

@@ -160,20 +160,21 @@ def test_product_data_checks():
 def test_workspace_bytes():
     f = L.harp_linear_workspace_bytes
     g = L.harp_deq_gemm_workspace_bytes
-    # M < 16: float32 x~, then y'
-    assert f(1, 4096, 4096) == 4096 * 4 + 4096 * 4
-    assert f(15, 100, 64) == 3840 + 6144         # 15*100*4 = 6000 rounds up to 6144
-    # 16 <= M <= 64: bf16 x~, y', and the small-batch product needs no workspace
-    assert f(63, 100, 64) == 8192 + 25344        # 63*64*2 = 8064 -> 8192; 25200 -> 25344
+    C = 1024   # the GEMM arrival counters, always first (fixed offset for every shape)
+    # M < 64: float32 x~, then y'
+    assert f(1, 4096, 4096) == C + 4096 * 4 + 4096 * 4
+    assert f(15, 100, 64) == C + 3840 + 6144     # 15*100*4 = 6000 rounds up to 6144
+    assert f(63, 100, 64) == C + 16128 + 25344   # 63*64*4; 25200 -> 25344
+    # M = 64: bf16 x~, y', and the small-batch product needs no workspace
     assert g(64, 4096, 4096) == 0 and g(16, 4096, 4096) == 0
-    assert f(64, 4096, 4096) == 64 * 4096 * 2 + 64 * 4096 * 4
+    assert f(64, 4096, 4096) == C + 64 * 4096 * 2 + 64 * 4096 * 4
     # M=65, 4096x4096: 32 tiles of 128x128 -> 4 K slices (8 groups each at
-    # least); partials 4*32*128*128*4 bytes, then 32 counters (256 B aligned)
-    assert g(65, 4096, 4096) == 4 * 32 * 128 * 128 * 4 + 256
-    assert f(65, 4096, 4096) == (65 * 4096 * 2 + 255) // 256 * 256 + 65 * 4096 * 4 \
-        + g(65, 4096, 4096)
+    # least): counters, then partials 4*32*128*128*4 bytes
+    assert g(65, 4096, 4096) == C + 4 * 32 * 128 * 128 * 4
+    assert f(65, 4096, 4096) == C + (65 * 4096 * 2 + 255) // 256 * 256 + 65 * 4096 * 4 \
+        + 4 * 32 * 128 * 128 * 4
     # M=512, 4096x4096: 128 tiles -> 2 slices; 12288 outputs: 384 tiles -> 1 slice
-    assert g(512, 4096, 4096) == 2 * 128 * 128 * 128 * 4 + 512
+    assert g(512, 4096, 4096) == C + 2 * 128 * 128 * 128 * 4
     assert g(512, 12288, 4096) == 0
     # K of 64 (one group) cannot be split
     assert g(512, 256, 64) == 0
@@ -341,12 +342,15 @@ def test_mixed_rotation_workspace():
 
 def test_linear_mixed_workspace_bytes():
     f = L.lib.harp_linear_mixed_workspace_bytes
+    C = 1024   # the GEMM arrival counters, always first
     # M = 1: float32 x~ (20480), y' (20480), bf16-output stage buffer (20480)
-    assert f(1, 5120, 5120) == 3 * 20480
-    # M = 16: float32 stage buffer and bf16 x~ of the input, y', output buffer
-    assert f(16, 5120, 5120) == 327680 + 163840 + 327680 + 327680
-    # M = 100: plus the GEMM's split-K partials (4 slices of 40 tiles) and counters
-    assert f(100, 5120, 5120) == 4 * 2048000 - 1024000 + 4 * 40 * 128 * 128 * 4 + 256
+    assert f(1, 5120, 5120) == C + 3 * 20480
+    # M = 16: float32 x~ (the operand, split into bf16 planes by the product),
+    # y', output buffer
+    assert f(16, 5120, 5120) == C + 327680 + 327680 + 327680
+    # M = 100: float32 stage buffer and bf16 x~ of the input, y', output
+    # buffer, then the GEMM's split-K partials (4 slices of 40 tiles)
+    assert f(100, 5120, 5120) == C + 4 * 2048000 - 1024000 + 4 * 40 * 128 * 128 * 4
     assert f(1, 5120, 32) == 0            # K < 64
     assert f(-1, 5120, 5120) == 0
     assert f(1, 40000, 5120) == 0         # beyond the mixed-radix maximum

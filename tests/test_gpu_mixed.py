@@ -171,10 +171,12 @@ def test_linear_fused_mixed(rv, ru, bits, M, ydt):
                      device="cuda")
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
     H().harp_linear_fused_mixed(V, W, U, d.dev_x(x, "bf16"), y, ws)
-    contract = M >= 16
+    # float32 x~ below 64 rows (the two-plane split from 16 on), bf16 x~ from
+    # 64 on (w_hat exact up to 64 rows, bf16 above)
+    contract = M >= 64
     ref = O.linear_mixed(d.x_f64(x, "bf16"), w.words, w.scale.view(np.float16),
                          w.zero.view(np.float16), bits, rv, bv, sv, ru, bu, su,
-                         mfma_contract=contract, weights_exact=16 <= M <= 64)
+                         mfma_contract=contract, weights_exact=M <= 64)
     tol = MFMA_PATH_TOL if contract else FP32_PATH_TOL
     r = O.rel_l2(d.host(y), ref)
     print(f"[linear mixed {rv}->{ru} {bits}-bit M={M}] rel_l2={r:.3e}", flush=True)

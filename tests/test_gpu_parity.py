@@ -32,22 +32,25 @@ FP32_PATH_TOL = 2e-5
 # p <= 2e-5 / 2^-8 ~ 5e-3, each flip one ulp (2^-8 relative), so the
 # output error is <= sqrt(p) 2^-8 ~ 2.8e-4.
 MFMA_PATH_TOL = 3e-4
-# The fused linear uses the float32 vector-ALU product below this batch and
-# the bf16 matrix-core product from it on; up to SKINNY_MAX_M rows that
-# product feeds the integer codes to the matrix cores and applies scale and
-# zero per group (w_hat exact, only x~ rounded), above it rounds both x~ and
-# w_hat to bf16.
-MFMA_MIN_M = 16
+# The fused linear keeps x~ in float32 below BF16_MIN_M rows (the contract
+# of the decode batches): the float32 product below 16 rows, then the
+# small-batch matrix-core product on the exact two-plane bf16 split of x~
+# (x~ kept to ~16 significant bits), both within the float32 bar of the
+# unrounded oracle.  From BF16_MIN_M rows on x~ is rounded to bf16; up to
+# SKINNY_MAX_M rows that product feeds the integer codes to the matrix cores
+# and applies scale and zero per group (w_hat exact, only x~ rounded), above
+# it rounds both x~ and w_hat to bf16.
+BF16_MIN_M = 64
 SKINNY_MAX_M = 64
 
 
 def path_tol(M):
-    return FP32_PATH_TOL if M < MFMA_MIN_M else MFMA_PATH_TOL
+    return FP32_PATH_TOL if M < BF16_MIN_M else MFMA_PATH_TOL
 
 
 def mode_for(M):
     """Rounding points of the product the fused linear runs at batch M."""
-    if M < MFMA_MIN_M:
+    if M < BF16_MIN_M:
         return "f32"
     return "mfma_exact_w" if M <= SKINNY_MAX_M else "mfma"
 
@@ -99,12 +102,16 @@ def report(name, got, ref):
 # a2: unpack + dequant, bit-exact
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("bits,N,K", [
-    (2, 100, 320), (3, 100, 320), (4, 100, 320),
-    (2, 4096, 4096), (3, 512, 8192), (4, 512, 8192), (2, 64, 28672),
+# "wide" weights: zero-points over the whole grid (0 and 2^B - 1 included)
+# and fp16 scales from the smallest subnormal up
+@pytest.mark.parametrize("bits,N,K,spread", [
+    (2, 100, 320, "mid"), (3, 100, 320, "mid"), (4, 100, 320, "mid"),
+    (2, 4096, 4096, "mid"), (3, 512, 8192, "mid"), (4, 512, 8192, "mid"),
+    (2, 64, 28672, "mid"), (2, 100, 320, "wide"), (3, 512, 8192, "wide"),
+    (4, 64, 28672, "wide"),
 ])
-def test_dequant_bit_exact(bits, N, K):
-    w = S.qweight(N, K, bits, rng(1, bits, N, K))
+def test_dequant_bit_exact(bits, N, K, spread):
+    w = S.qweight(N, K, bits, rng(1, bits, N, K), spread=spread)
     d = D()
     Wd = d.dev_qweight(w)
     ref = O.dequant(O.unpack(w.words, bits, K), d.scale_f16(w), d.zero_f16(w))
@@ -274,22 +281,24 @@ def test_rotate_max_batch_sampled():
 # a3: GEMV (float32), a4: GEMM (bf16 matrix cores)
 # ---------------------------------------------------------------------------
 
-GEMV_CASES = [(100, 320, b, m) for b in (2, 3, 4) for m in (1, 2, 3, 5, 8, 9, 13)] + [
-    (4096, 4096, 2, 1), (11008, 4096, 2, 16), (4096, 11008, 2, 16),
-    (8192, 8192, 3, 1), (2048, 8192, 4, 32), (1000, 28672, 2, 1), (64, 256, 2, 63),
+GEMV_CASES = [(100, 320, b, m, "mid") for b in (2, 3, 4) for m in (1, 2, 3, 5, 8, 9, 13)] + [
+    (4096, 4096, 2, 1, "mid"), (11008, 4096, 2, 16, "mid"), (4096, 11008, 2, 16, "mid"),
+    (8192, 8192, 3, 1, "mid"), (2048, 8192, 4, 32, "mid"), (1000, 28672, 2, 1, "mid"),
+    (64, 256, 2, 63, "mid"),
+    (4096, 4096, 2, 1, "wide"), (100, 320, 3, 9, "wide"), (2048, 8192, 4, 5, "wide"),
 ]
 
 
-@pytest.mark.parametrize("N,K,bits,M", GEMV_CASES)
-def test_gemv(N, K, bits, M):
+@pytest.mark.parametrize("N,K,bits,M,spread", GEMV_CASES)
+def test_gemv(N, K, bits, M, spread):
     d = D()
-    w = S.qweight(N, K, bits, rng(11, N, K, bits))
+    w = S.qweight(N, K, bits, rng(11, N, K, bits), spread=spread)
     xt = rng(12, K, M).normal(size=(M, K)).astype(np.float32)
     yt = torch.empty((M, N), dtype=torch.float32, device="cuda")
     H().harp_deq_gemv(d.dev_qweight(w), d.dev(xt), yt)
     w_hat = O.dequant(O.unpack(w.words, bits, K), d.scale_f16(w), d.zero_f16(w))
     ref = xt.astype(np.float64) @ w_hat.T
-    r = report(f"gemv {N}x{K} b{bits} M={M}", d.host(yt), ref)
+    r = report(f"gemv {N}x{K} b{bits} M={M} {spread}", d.host(yt), ref)
     assert r <= CONTRACT_TOL and r <= FP32_PATH_TOL
 
 
@@ -320,22 +329,26 @@ def test_rotate_in_deq_gemv(N, K, b, bits, M, angles, xdt):
 
 GEMM_CASES = [
     # M <= 64: the small-batch kernel (16 features per workgroup)
-    (100, 320, 2, 16), (300, 256, 3, 33), (257, 128, 4, 1), (4096, 4096, 2, 16),
-    (4096, 4096, 2, 32), (11008, 4096, 2, 16), (4096, 11008, 4, 48),
-    (1024, 28672, 3, 32), (2000, 8192, 2, 5), (1000, 1088, 4, 64), (64, 64, 2, 17),
+    (100, 320, 2, 16, "mid"), (300, 256, 3, 33, "mid"), (257, 128, 4, 1, "mid"),
+    (4096, 4096, 2, 16, "mid"), (4096, 4096, 2, 32, "mid"), (11008, 4096, 2, 16, "mid"),
+    (4096, 11008, 4, 48, "mid"), (1024, 28672, 3, 32, "mid"), (2000, 8192, 2, 5, "mid"),
+    (1000, 1088, 4, 64, "mid"), (64, 64, 2, 17, "mid"),
     # M > 64: 128 x 128 tiles, optionally split K
-    (300, 256, 3, 65), (128, 64, 2, 200),
-    (4096, 4096, 2, 512), (12288, 4096, 4, 512), (4096, 12288, 2, 512),
-    (4096, 4096, 3, 129), (1000, 1088, 2, 300), (384, 2048, 4, 64),
+    (300, 256, 3, 65, "mid"), (128, 64, 2, 200, "mid"),
+    (4096, 4096, 2, 512, "mid"), (12288, 4096, 4, 512, "mid"), (4096, 12288, 2, 512, "mid"),
+    (4096, 4096, 3, 129, "mid"), (1000, 1088, 2, 300, "mid"), (384, 2048, 4, 64, "mid"),
+    # zero-points at 0 and 2^B - 1, subnormal fp16 scales
+    (4096, 4096, 2, 16, "wide"), (300, 256, 3, 33, "wide"), (1000, 1088, 4, 64, "wide"),
+    (4096, 4096, 4, 512, "wide"), (1000, 1088, 3, 300, "wide"),
 ]
 
 
-@pytest.mark.parametrize("N,K,bits,M", GEMM_CASES)
-def test_gemm(N, K, bits, M):
+@pytest.mark.parametrize("N,K,bits,M,spread", GEMM_CASES)
+def test_gemm(N, K, bits, M, spread):
     """One K slice (no workspace) and split K (workspace) against the oracle;
     the split result is bitwise reproducible and its counters return to 0."""
     d = D()
-    w = S.qweight(N, K, bits, rng(13, N, K, bits))
+    w = S.qweight(N, K, bits, rng(13, N, K, bits), spread=spread)
     xt = S.activations(M, K, rng(14, K, M), "bf16")
     Wd, xd = d.dev_qweight(w), d.dev(xt)
     w_hat = O.dequant(O.unpack(w.words, bits, K), d.scale_f16(w), d.zero_f16(w))
@@ -348,7 +361,7 @@ def test_gemm(N, K, bits, M):
     H().harp_deq_gemm(Wd, xd, y_again)
     torch.cuda.synchronize()
     assert torch.equal(yt, y_again)
-    r = report(f"gemm {N}x{K} b{bits} M={M}", d.host(yt), ref)
+    r = report(f"gemm {N}x{K} b{bits} M={M} {spread}", d.host(yt), ref)
     assert r <= CONTRACT_TOL and r <= FP32_PATH_TOL
     ws = d.gemm_workspace(M, N, K)
     if ws is not None:
@@ -360,9 +373,8 @@ def test_gemm(N, K, bits, M):
         assert r <= CONTRACT_TOL and r <= FP32_PATH_TOL
         torch.cuda.synchronize()
         assert torch.equal(y1, y2)
-        nb = ws.numel()
         tiles = ((M + 127) // 128) * ((N + 127) // 128)
-        counters = ws[nb - ((tiles * 4 + 255) // 256) * 256:].view(torch.int32)[:tiles]
+        counters = ws[:tiles * 4].view(torch.int32)   # fixed front area
         assert int(counters.abs().sum().item()) == 0
 
 
@@ -421,6 +433,7 @@ def run_fused(li, y_dtype=torch.float32):
 
 
 FUSED_CASES = [("tiny", 0, 2, 4), ("l7b_decode", 0, 2, 1), ("l7b_decode", 0, 2, 16),
+               ("l7b_decode", 0, 2, 33), ("l7b_decode", 0, 3, 48), ("l7b_decode", 0, 4, 63),
                ("l7b_decode", 0, 2, 64)]
 FUSED_CASES += [("l7b_mlp", i, 2, m) for i in (0, 1) for m in (1, 16)]
 FUSED_CASES += [("q8b_prefill", i, b, 512) for i in (0, 1, 2) for b in (2, 4)]
@@ -437,7 +450,7 @@ def test_fused_configs(cfg, lin, bits, M):
     assert r <= path_tol(M)
 
 
-L70B_CASES = [(0, 2), (0, 3), (0, 4), (1, 2), (1, 3), (1, 4), (2, 2)]
+L70B_CASES = [(0, 2), (0, 3), (0, 4), (1, 2), (1, 3), (1, 4), (2, 2), (2, 3), (2, 4)]
 
 
 FUSED8_CASES = [("tiny", 0, 2, 4), ("l7b_decode", 0, 2, 1), ("l7b_mlp", 1, 2, 16),
@@ -456,10 +469,9 @@ def test_fused_int8_angles(cfg, lin, bits, M):
 
 @pytest.mark.parametrize("lin,bits", L70B_CASES)
 def test_fused_l70b_slice(lin, bits):
-    """Llama-70B slice at M = 1 and 32.  8192 -> 28672 checks 13 sampled
-    256-wide output blocks; 28672 -> 8192 (b = 8192 output side, so every
-    output needs all 8192 rows) is checked in full at 2 bits, the other
-    widths of the 28672-long rows being covered by 8192 -> 28672."""
+    """Llama-70B slice at M = 1 and 32, 2/3/4 bits.  8192 -> 28672 checks 13
+    sampled 256-wide output blocks; 28672 -> 8192 (b = 8192 output side, so
+    every output needs all 8192 rows) is checked in full."""
     c = S.CONFIGS["l70b_slice"]
     lis = [S.layer_inputs(c, lin, bits, M) for M in c.Ms]
     ys = [D().host(run_fused(li)) for li in lis]
@@ -469,7 +481,8 @@ def test_fused_l70b_slice(lin, bits):
         nb = L0.N // L0.b_u
         blocks = sorted(set(rng(20, lin, bits).integers(0, nb, 12).tolist()) | {nb - 1})
     # one oracle pass per batch: M = 1 takes the float32 product, M = 32 the
-    # bf16 matrix-core product, whose rounding points the oracle models
+    # matrix-core product on the two-plane split of the float32 x~; both
+    # against the unrounded oracle
     for li, y in zip(lis, ys):
         ref, rows = oracle_linear_rows(li, D().x_f64(li.x, li.x_dtype), mode_for(li.M),
                                        blocks)
@@ -538,6 +551,21 @@ def test_fused_batch_edges_and_bf16_out(M):
     assert r <= CONTRACT_TOL and r <= path_tol(M)
     assert_bf16_rounding_close(D().host(run_fused(li, torch.bfloat16)), ref,
                                path_tol(M))
+
+
+@pytest.mark.parametrize("M,bits", [(1, 2), (3, 4), (9, 3), (16, 2), (40, 4), (63, 3),
+                                    (64, 2), (100, 4)])
+def test_fused_wide_weights(M, bits):
+    """Zero-points at 0 and 2^B - 1 and subnormal fp16 scales through every
+    product of the fused linear (2048 -> 4096, b = 2048 / 4096)."""
+    cfg = S.Config(12, "wide", (S.Linear("w", 2048, 4096, 2048, 4096),), (bits,), (M,))
+    li = S.layer_inputs(cfg, 0, bits, M)
+    w = S.qweight(4096, 2048, bits, rng(50, M, bits), spread="wide")
+    li = S.LayerInputs(li.lin, bits, M, li.x, li.x_dtype, li.V, li.U, w)
+    ref, _ = oracle_linear_rows(li, D().x_f64(li.x, li.x_dtype), mode_for(M))
+    y = D().host(run_fused(li))
+    r = report(f"fused wide weights M={M} b{bits}", y, ref)
+    assert r <= CONTRACT_TOL and r <= path_tol(M)
 
 
 @pytest.mark.parametrize("M", [1, 16, 512])

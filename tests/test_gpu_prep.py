@@ -137,7 +137,16 @@ def test_prepare_then_linear():
     y = torch.empty((4, N), dtype=torch.float32, device="cuda")
     wsl = d.workspace(4, N, K)
     H().harp_linear_fused(Vd, Wq, Ud, d.dev(x), y, wsl)
+    got = y.cpu().numpy().astype(np.float64)
+    # parity: the oracle's linear on the very buffers the GPU produced
+    y_or = O.linear(x.astype(np.float64), qw.cpu().numpy().view(np.uint32),
+                    sc.cpu().numpy().view(np.float16), zr.cpu().numpy().view(np.float16), 2,
+                    V.cs, V.sign_bits, b, U.cs, U.sign_bits, b)
+    r = O.rel_l2(got, y_or)
+    print(f"[prepare+linear 2-bit] rel_l2 vs oracle on the same buffers = {r:.3e}", flush=True)
+    assert r <= 2e-5
+    # and the quantized layer approximates the dense one
     y_ref = x.astype(np.float64) @ W.astype(np.float64).T
-    err = O.rel_l2(y.cpu().numpy().astype(np.float64), y_ref)
+    err = O.rel_l2(got, y_ref)
     print(f"[prepare+linear 2-bit] rel_l2 vs W x = {err:.3f}", flush=True)
     assert err < 0.5
