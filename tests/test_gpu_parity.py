@@ -568,6 +568,32 @@ def test_fused_wide_weights(M, bits):
     assert r <= CONTRACT_TOL and r <= path_tol(M)
 
 
+def test_fused_workspace_reused_across_shapes():
+    """One workspace, sized for the largest call and zero-filled once, serves
+    M = 512, then 128, then 512 and 16 on the same 4096 x 4096 layer: the split-K
+    counters sit at a fixed offset, so no call sees another's leftovers."""
+    c = S.CONFIGS["q8b_prefill"]
+    Ms = (512, 128, 512, 16, 128)
+    lis = {M: S.layer_inputs(c, 0, 2, M) for M in set(Ms)}
+    d = D()
+    nbytes = max(H().harp_linear_workspace_bytes(M, 4096, 4096) for M in Ms)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    base = lis[512]
+    V, U, W = d.dev_rotation(base.V), d.dev_rotation(base.U), d.dev_qweight(base.W)
+    refs = {}
+    for M in Ms:
+        li = lis[M]
+        li = S.LayerInputs(base.lin, 2, M, li.x, li.x_dtype, base.V, base.U, base.W)
+        y = torch.empty((M, 4096), dtype=torch.float32, device="cuda")
+        H().harp_linear_fused(V, W, U, d.dev_x(li.x, li.x_dtype), y, ws)
+        if M not in refs:
+            refs[M] = oracle_linear_rows(li, d.x_f64(li.x, li.x_dtype), mode_for(M))[0]
+        r = report(f"reused workspace M={M}", d.host(y), refs[M])
+        assert r <= CONTRACT_TOL and r <= path_tol(M)
+    torch.cuda.synchronize()
+    assert int(ws[:1024].view(torch.int32).abs().sum().item()) == 0
+
+
 @pytest.mark.parametrize("M", [1, 16, 512])
 def test_fused_deterministic(M):
     c = S.CONFIGS["q8b_prefill"] if M == 512 else S.CONFIGS["l7b_mlp"]

@@ -1,5 +1,6 @@
 """The seeded input generators: determinism, boundary shapes and ranges."""
 import numpy as np
+import pytest
 
 from synth import workloads as S
 
@@ -37,6 +38,22 @@ def test_qweight_zero_and_scale_ranges():
         assert set(np.unique(z)) <= {qmax // 2, qmax // 2 + 1}
         s = w.scale.view(np.float16).astype(np.float64)
         assert s.min() > 0 and s.max() < 0.2
+
+
+def test_qweight_wide_spread_covers_the_format_edges():
+    for bits in (2, 3, 4):
+        qmax = (1 << bits) - 1
+        w = S.qweight(64, 1024, bits, np.random.default_rng(bits), spread="wide")
+        z = w.zero.view(np.float16).astype(np.float64)
+        s = w.scale.view(np.float16).astype(np.float64)
+        assert z.min() == 0 and z.max() == qmax and np.all(z == np.round(z))
+        assert np.all(z[:, 0] == 0) and np.all(z[:, -1] == qmax)
+        assert s.min() == 2.0 ** -24                       # smallest fp16 subnormal
+        assert np.any(s == 1023 * 2.0 ** -24)              # largest subnormal
+        assert (s < 2.0 ** -14).mean() > 0.2 and s.max() > 4.0
+        assert np.all(s > 0) and np.all(np.isfinite(s))
+    with pytest.raises(ValueError):
+        S.qweight(4, 64, 2, np.random.default_rng(0), spread="bogus")
 
 
 def test_bf16_activations_carry_outliers():
