@@ -353,6 +353,29 @@ harp_status harp_quantize_pack(const float *Wp, int32_t N, int32_t K, int32_t bi
                                harp_stream stream);
 
 /*
+ * harp_linear_fused for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, checks, results (within the path's float32 or
+ * bf16 bar) and batch ranges as harp_linear_fused, minus the workspace:
+ * x~ and y' live in a fixed device array of HARP_NOALLOC_SCRATCH_BYTES that
+ * the library holds on each GPU it runs on until the process ends.  The call
+ * allocates nothing (no hipMalloc/hipFree, no allocating library routine);
+ * its first call on a device looks up that device's array address.
+ * M > 64 runs the GEMM as one K slice (no split K), so nothing in the array
+ * needs initialisation.  Size limit: 1024 + align256(M K e) + align256(4 M N)
+ * bytes at most HARP_NOALLOC_SCRATCH_BYTES, with e = 4 for M < 64 and 2 from
+ * 64 on (align256 rounds up to a multiple of 256); larger calls return
+ * HARP_ERR_WORKSPACE and launch nothing.  Every call on one GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (other streams, other
+ * threads) race and must be serialised by the caller.
+ */
+#define HARP_NOALLOC_SCRATCH_BYTES (32u << 20)
+harp_status harp_linear_fused_noalloc(const harp_rotation *V, const harp_qweight *W,
+                                      const harp_rotation *U, const void *x,
+                                      harp_dtype x_dt, void *y, harp_dtype y_dt,
+                                      int32_t M, harp_stream stream);
+
+/*
  * Test hook, not on the hot path: writes the dense w_hat [N][K] as float32
  * (exact) or bf16 (nearest even), through the same device unpack and
  * dequant code the products use (the stand-in per-group uniform grid

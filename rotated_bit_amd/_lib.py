@@ -32,7 +32,8 @@ HARP_BF16 = 1
 EXPORTED = (
     "harp_rotate_in", "harp_rotate_out", "harp_deq_gemv", "harp_rotate_in_deq_gemv",
     "harp_deq_gemm",
-    "harp_deq_gemm_workspace_bytes", "harp_linear_workspace_bytes", "harp_linear_fused", "harp_dequant",
+    "harp_deq_gemm_workspace_bytes", "harp_linear_workspace_bytes", "harp_linear_fused",
+    "harp_linear_fused_noalloc", "harp_dequant",
     "harp_rotate_weight", "harp_rotate_weight_workspace_bytes", "harp_quantize_pack",
     "harp_rotate_in_mixed", "harp_rotate_out_mixed", "harp_rotate_mixed_workspace_bytes",
     "harp_linear_fused_mixed", "harp_linear_mixed_workspace_bytes",
@@ -95,6 +96,8 @@ def _load() -> ctypes.CDLL:
         "harp_linear_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
         "harp_linear_fused": (c_int32, [R, Q, R, c_void_p, c_int32, c_void_p, c_int32,
                                         c_int32, c_void_p, c_size_t, c_void_p]),
+        "harp_linear_fused_noalloc": (c_int32, [R, Q, R, c_void_p, c_int32, c_void_p, c_int32,
+                                                c_int32, c_void_p]),
         "harp_dequant": (c_int32, [Q, c_void_p, c_int32, c_void_p]),
         "harp_rotate_weight": (c_int32, [R, R, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
                                           c_size_t, c_void_p]),
@@ -257,6 +260,15 @@ def harp_linear_fused(V: Rotation, W: QWeight, U: Rotation, x, y, workspace,
                                  _ptr(x), _dtype_code(x), _ptr(y), _dtype_code(y), M,
                                  _ptr(workspace), ws_bytes, _stream(stream)),
            "harp_linear_fused")
+
+
+def harp_linear_fused_noalloc(V: Rotation, W: QWeight, U: Rotation, x, y,
+                              M: int | None = None, stream=None) -> None:
+    M = x.shape[0] if M is None else M
+    _check(lib.harp_linear_fused_noalloc(ctypes.byref(V.c), ctypes.byref(W.c), ctypes.byref(U.c),
+                                         _ptr(x), _dtype_code(x), _ptr(y), _dtype_code(y), M,
+                                         _stream(stream)),
+           "harp_linear_fused_noalloc")
 
 
 def harp_dequant(W: QWeight, out, stream=None) -> None:

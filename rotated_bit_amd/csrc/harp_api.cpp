@@ -2,6 +2,8 @@
 // arguments, pick the kernels, launch them on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "../../include/harp.h"
 #include "launch.hpp"
 #include "validate.hpp"
@@ -17,6 +19,75 @@ harp_status from_hip(hipError_t e) {
 }
 
 hipStream_t as_stream(harp_stream s) { return reinterpret_cast<hipStream_t>(s); }
+
+// The whole linear on a workspace laid out as harp_linear_workspace_bytes
+// describes (arguments already checked).  split_k: the M > 64 GEMM may split
+// K (needs the counters at the front of ws, zero, and the partial tiles
+// after y'); without it the GEMM runs one K slice and only the counter area,
+// x~ and y' are used (the counter area is then not read).
+harp_status fused_linear(const harp_rotation& V, const harp_qweight& W, const harp_rotation& U,
+                         const void* x, harp_dtype x_dt, void* y, harp_dtype y_dt, int32_t M,
+                         char* ws, bool split_k, hipStream_t s) {
+  float* yp = reinterpret_cast<float*>(ws + harp::workspace_yp_offset(M, W.K));
+  harp_status r;
+  if (M <= harp::kFusedRotGemvMaxM && W.N <= harp::kFusedRotGemvMaxN &&
+      harp::gemv_rotated_supported(V, W, M)) {
+    r = from_hip(harp::launch_gemv_rotated(V, W, x, x_dt, yp, M, s));
+  } else if (M < harp::kBf16MinM) {
+    // float32 x~: the float32 product, or the matrix cores on its two-plane
+    // bf16 split
+    float* xt = reinterpret_cast<float*>(ws + harp::workspace_xt_offset());
+    r = from_hip(harp::launch_rotate(V, x, x_dt, xt, HARP_F32, M, false, s));
+    if (r != HARP_OK) return r;
+    r = from_hip(M < harp::kSplitMinM ? harp::launch_gemv(W, xt, yp, M, s)
+                                      : harp::launch_gemm_skinny_split(W, xt, yp, M, s));
+  } else {
+    uint16_t* xt = reinterpret_cast<uint16_t*>(ws + harp::workspace_xt_offset());
+    // y' is not yet written: when it is at least as large as x~ in float32
+    // it holds the intermediate of the two-launch input rotation
+    r = from_hip(W.N >= W.K ? harp::launch_rotate_in_scratch(V, x, x_dt, xt, yp, M, s)
+                            : harp::launch_rotate(V, x, x_dt, xt, HARP_BF16, M, false, s));
+    if (r != HARP_OK) return r;
+    if (M <= harp::kSkinnyMaxM)
+      r = from_hip(harp::launch_gemm_skinny(W, xt, yp, M, s));
+    else
+      r = from_hip(harp::launch_gemm(
+          W, xt, yp, M, split_k ? harp::gemm_splits(M, W.N, W.K) : 1,
+          reinterpret_cast<float*>(ws + harp::workspace_gemm_offset(M, W.N, W.K)),
+          reinterpret_cast<uint32_t*>(ws), s));
+  }
+  if (r != HARP_OK) return r;
+  return from_hip(harp::launch_rotate(U, yp, HARP_F32, y, y_dt, M, true, s));
+}
+
+// Device memory of harp_linear_fused_noalloc: a file-scope array that every
+// GPU the library runs on holds until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory: its device
+// address is taken once per device with hipGetSymbolAddress (that device
+// current) and kept in scratch_ptr; only that pointer reaches kernels.
+constexpr size_t kScratchBytes = size_t{32} << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+harp_status device_scratch(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return from_hip(e);
+  if (dev < 0 || dev >= kMaxDevices) return HARP_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return from_hip(e);
+    if (p == nullptr) return HARP_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return HARP_OK;
+}
 
 }  // namespace
 
@@ -113,39 +184,26 @@ harp_status harp_linear_fused(const harp_rotation* V, const harp_qweight* W,
   const harp_status st = harp::validate_fused(V, W, U, x, x_dt, y, y_dt, M,
                                               workspace, ws_bytes);
   if (st != HARP_OK || M == 0) return st;
-  const hipStream_t s = as_stream(stream);
-  char* ws = static_cast<char*>(workspace);
-  float* yp = reinterpret_cast<float*>(ws + harp::workspace_yp_offset(M, W->K));
-  harp_status r;
-  if (M <= harp::kFusedRotGemvMaxM && W->N <= harp::kFusedRotGemvMaxN &&
-      harp::gemv_rotated_supported(*V, *W, M)) {
-    r = from_hip(harp::launch_gemv_rotated(*V, *W, x, x_dt, yp, M, s));
-  } else if (M < harp::kBf16MinM) {
-    // float32 x~: the float32 product, or the matrix cores on its two-plane
-    // bf16 split
-    float* xt = reinterpret_cast<float*>(ws + harp::workspace_xt_offset());
-    r = from_hip(harp::launch_rotate(*V, x, x_dt, xt, HARP_F32, M, false, s));
-    if (r != HARP_OK) return r;
-    r = from_hip(M < harp::kSplitMinM ? harp::launch_gemv(*W, xt, yp, M, s)
-                                      : harp::launch_gemm_skinny_split(*W, xt, yp, M, s));
-  } else {
-    uint16_t* xt = reinterpret_cast<uint16_t*>(ws + harp::workspace_xt_offset());
-    // y' is not yet written: when it is at least as large as x~ in float32
-    // it holds the intermediate of the two-launch input rotation
-    r = from_hip(
-        W->N >= W->K ? harp::launch_rotate_in_scratch(*V, x, x_dt, xt, yp, M, s)
-                     : harp::launch_rotate(*V, x, x_dt, xt, HARP_BF16, M, false, s));
-    if (r != HARP_OK) return r;
-    if (M <= harp::kSkinnyMaxM)
-      r = from_hip(harp::launch_gemm_skinny(*W, xt, yp, M, s));
-    else
-      r = from_hip(harp::launch_gemm(
-          *W, xt, yp, M, harp::gemm_splits(M, W->N, W->K),
-          reinterpret_cast<float*>(ws + harp::workspace_gemm_offset(M, W->N, W->K)),
-          reinterpret_cast<uint32_t*>(ws), s));
-  }
-  if (r != HARP_OK) return r;
-  return from_hip(harp::launch_rotate(*U, yp, HARP_F32, y, y_dt, M, true, s));
+  return fused_linear(*V, *W, *U, x, x_dt, y, y_dt, M, static_cast<char*>(workspace),
+                      true, as_stream(stream));
+}
+
+harp_status harp_linear_fused_noalloc(const harp_rotation* V, const harp_qweight* W,
+                                      const harp_rotation* U, const void* x,
+                                      harp_dtype x_dt, void* y, harp_dtype y_dt,
+                                      int32_t M, harp_stream stream) {
+  // the argument checks of harp_linear_fused with a stand-in workspace (an
+  // aligned non-null address and no size limit); then the size this call
+  // needs in the scratch: counter area, x~ and y' (one K slice, no partials)
+  harp_status st = harp::validate_fused(V, W, U, x, x_dt, y, y_dt, M,
+                                        reinterpret_cast<void*>(uintptr_t{256}), SIZE_MAX);
+  if (st != HARP_OK || M == 0) return st;
+  static_assert(kScratchBytes % 256 == 0, "scratch size");
+  if (harp::workspace_gemm_offset(M, W->N, W->K) > kScratchBytes) return HARP_ERR_WORKSPACE;
+  char* scratch_ptr = nullptr;
+  st = device_scratch(&scratch_ptr);
+  if (st != HARP_OK) return st;
+  return fused_linear(*V, *W, *U, x, x_dt, y, y_dt, M, scratch_ptr, false, as_stream(stream));
 }
 
 size_t harp_linear_mixed_workspace_bytes(int32_t M, int32_t N, int32_t K) {
