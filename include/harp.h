@@ -194,6 +194,38 @@ harp_status harp_rotate_out(const harp_rotation *U, const float *yt, void *y,
  *              its own workspace.  The contents need no initialisation;
  *              calls that share a workspace must not overlap in time.
  */
+/*
+ * Expand the learnable parameters of a mixed-radix side into the float32
+ * blocks of harp_mixed_rotation.blocks (technical summary §2.2: each block
+ * is B = Q(theta) G_b).  G_b is the fixed base mixer: H_b / sqrt(b) by
+ * Sylvester's construction for powers of two, otherwise the orthogonal
+ * factor Q of the QR factorisation of a fixed b x b Gaussian matrix, with
+ * R's diagonal made positive (technical summary §2.1-2.2: QR of a fixed
+ * Gaussian for radices that are no power of two).  Q(theta) is the Givens
+ * rotation [[cos phi, -sin phi], [sin phi, cos phi]] for b = 2 and the
+ * Cayley map (I - A)(I + A)^-1 of the skew-symmetric A for b > 2, so zero
+ * parameters give B = G_b.  Offline, host memory: float64 arithmetic
+ * (Householder QR, Gaussian elimination with partial pivoting), float32
+ * output rounded to nearest.  Synchronous; launches nothing.
+ *   n_stages, radix  as in harp_mixed_rotation (dim = prod radix)
+ *   params     host float64, the stages one after the other; stage t holds
+ *              [dim/b_t][b_t (b_t - 1) / 2]: per group the angle phi
+ *              (b_t = 2) or A's upper triangle A[r][c], r < c, row by row.
+ *   gaussians  host float64: one b_t x b_t row-major matrix for every stage
+ *              whose radix is not a power of two, in stage order (pass the
+ *              same matrix again for a repeated radix to share its mixer);
+ *              NULL allowed when every radix is a power of two.
+ *   blocks     host float32 out, 4 * dim * sum_t b_t bytes, in the layout of
+ *              harp_mixed_rotation.blocks.
+ * Errors: HARP_ERR_NULL (radix, params or blocks NULL; gaussians NULL while
+ * needed), HARP_ERR_SHAPE / HARP_ERR_UNSUPPORTED for the schedule as in the
+ * mixed-radix rotations, HARP_ERR_SHAPE for a non-finite parameter or
+ * Gaussian entry or a rank-deficient Gaussian.  blocks is written only on
+ * success.
+ */
+harp_status harp_mixed_expand(int32_t n_stages, const int32_t *radix, const double *params,
+                              const double *gaussians, float *blocks);
+
 harp_status harp_rotate_in_mixed(const harp_mixed_rotation *R, const void *x,
                                  harp_dtype x_dt, void *xt, harp_dtype xt_dt,
                                  int32_t M, void *workspace, size_t ws_bytes,

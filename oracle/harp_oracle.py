@@ -49,8 +49,9 @@ repository's design notes):
 * Mixed radix (technical summary §2.1-2.2, ``mixed_forward``): stage t acts
   on mixed-radix digit t (stride prod_{s<t} b_s); blocks Q(theta) G_b with
   Q the Cayley map (I - A)(I + A)^-1 for b > 2 and the QR factor of a fixed
-  Gaussian (positive R diagonal, numpy seed mixer_seed + b) as G_b for radices
-  that are not powers of two.
+  Gaussian (positive R diagonal; the Gaussian itself is an input, drawn once
+  per radix by the seeded generators) as G_b for radices that are not
+  powers of two.
 * int8 storage of the angles (technical summary §2.4 storage note, §4
   storage overhead; the pages give no encoding).  Each block's angle
   perturbation phi = t - pi/4 is stored as one signed 8-bit code c with one
@@ -274,34 +275,39 @@ def skew_from_params(p: np.ndarray, b: int) -> np.ndarray:
     return A - A.T
 
 
-def qr_mixer(b: int, seed: int) -> np.ndarray:
-    """Q factor of a fixed b x b Gaussian (numpy default_rng(seed)), with the
-    sign of each column chosen so that R has a positive diagonal (the unique
-    QR factorisation)."""
-    g = np.random.default_rng(seed).normal(size=(b, b))
+def qr_mixer(g: np.ndarray) -> np.ndarray:
+    """Q factor of the fixed b x b Gaussian g (an input: the random matrix the
+    method draws once), with the sign of each column chosen so that R has a
+    positive diagonal (the unique QR factorisation)."""
+    g = np.asarray(g, dtype=np.float64)
     q, r = np.linalg.qr(g)
     return q * np.sign(np.diag(r))[None, :]
 
 
-def base_mixer(b: int, seed: int) -> np.ndarray:
-    """G_b: normalised Sylvester Hadamard for powers of two, else qr_mixer."""
+def base_mixer(b: int, g=None) -> np.ndarray:
+    """G_b: normalised Sylvester Hadamard for powers of two, else the QR
+    factor of the fixed Gaussian g (b x b)."""
     if b & (b - 1) == 0:
         return sylvester_hadamard(b) / np.sqrt(b)
-    return qr_mixer(b, seed)
+    if g is None:
+        raise ValueError(f"radix {b} is not a power of two: its fixed Gaussian is needed")
+    return qr_mixer(g)
 
 
-def mixed_blocks(radices, params, mixer_seed: int = 0) -> list:
+def mixed_blocks(radices, params, gaussians=None) -> list:
     """Expand the learnable parameters into blocks, one array per stage.
 
     params[t]: shape (d / b_t, b_t (b_t - 1) / 2): per group, the Givens
     angle phi (b_t = 2) or the upper triangle of the Cayley parameter
-    (b_t > 2).  Returns [t] -> (d / b_t, b_t, b_t) float64 blocks
-    B = Q(theta) G_{b_t}; the QR mixer of radix b uses seed mixer_seed + b.
+    (b_t > 2).  gaussians[t]: the fixed b_t x b_t Gaussian whose QR factor
+    is stage t's mixer when b_t is not a power of two (None otherwise; the
+    whole list may be None when every radix is a power of two).  Returns
+    [t] -> (d / b_t, b_t, b_t) float64 blocks B = Q(theta) G_{b_t}.
     """
     d = int(np.prod(radices))
     out = []
     for t, b in enumerate(radices):
-        G = base_mixer(b, mixer_seed + b)
+        G = base_mixer(b, None if gaussians is None else gaussians[t])
         P = np.asarray(params[t], dtype=np.float64)
         if P.shape != (d // b, b * (b - 1) // 2):
             raise ValueError(f"stage {t}: params must have shape {(d // b, b * (b - 1) // 2)}")

@@ -35,7 +35,8 @@ EXPORTED = (
     "harp_deq_gemm_workspace_bytes", "harp_linear_workspace_bytes", "harp_linear_fused",
     "harp_linear_fused_noalloc", "harp_dequant",
     "harp_rotate_weight", "harp_rotate_weight_workspace_bytes", "harp_quantize_pack",
-    "harp_rotate_in_mixed", "harp_rotate_out_mixed", "harp_rotate_mixed_workspace_bytes",
+    "harp_mixed_expand", "harp_rotate_in_mixed", "harp_rotate_out_mixed",
+    "harp_rotate_mixed_workspace_bytes",
     "harp_linear_fused_mixed", "harp_linear_mixed_workspace_bytes",
     "harp_status_string", "harp_last_hip_error",
 )
@@ -102,6 +103,7 @@ def _load() -> ctypes.CDLL:
         "harp_rotate_weight": (c_int32, [R, R, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
                                           c_size_t, c_void_p]),
         "harp_rotate_weight_workspace_bytes": (c_size_t, [c_int32, c_int32]),
+        "harp_mixed_expand": (c_int32, [c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
         "harp_rotate_in_mixed": (c_int32, [MR, c_void_p, c_int32, c_void_p, c_int32, c_int32,
                                             c_void_p, c_size_t, c_void_p]),
         "harp_rotate_out_mixed": (c_int32, [MR, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
@@ -284,6 +286,33 @@ def _ws(workspace):
 
 def harp_rotate_mixed_workspace_bytes(dim: int, M: int, out_dtype) -> int:
     return int(lib.harp_rotate_mixed_workspace_bytes(dim, M, _dtype_of(out_dtype)))
+
+
+def harp_mixed_expand(radices, params, gaussians=None):
+    """Host expansion of a mixed-radix side (numpy in, numpy out).
+
+    params: per stage an array of shape (dim / b_t, b_t (b_t - 1) / 2);
+    gaussians: per stage a (b_t, b_t) array for radices that are not powers
+    of two (None entries, or None, for powers of two).  Returns the float32
+    blocks, stages concatenated, ready for MixedRotation.
+    """
+    import numpy as np
+    radices = [int(b) for b in radices]
+    dim = 1
+    for b in radices:
+        dim *= b
+    rad = np.ascontiguousarray(radices, dtype=np.int32)
+    p = np.ascontiguousarray(np.concatenate([np.asarray(a, dtype=np.float64).ravel()
+                                             for a in params]))
+    gl = [np.asarray(g, dtype=np.float64).ravel()
+          for g, b in zip(gaussians or [None] * len(radices), radices)
+          if b & (b - 1) and g is not None]
+    g = np.ascontiguousarray(np.concatenate(gl)) if gl else None
+    out = np.empty(dim * sum(radices), dtype=np.float32)
+    _check(lib.harp_mixed_expand(len(radices), rad.ctypes.data, p.ctypes.data,
+                                 None if g is None else g.ctypes.data, out.ctypes.data),
+           "harp_mixed_expand")
+    return out
 
 
 def harp_rotate_in_mixed(R: MixedRotation, x, xt, workspace=None, M: int | None = None,

@@ -6,7 +6,8 @@
 
 Every HIP source is compiled with packed-FP32 instructions disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``).  The argument checks
-(validate.cpp) are plain C++ built with g++, so they carry no HIP
+(validate.cpp) and the offline mixed-radix block expansion
+(mixed_expand.cpp) are plain C++ built with g++, so they carry no HIP
 dependency.  The library is written next to this file.
 """
 from __future__ import annotations
@@ -25,7 +26,7 @@ ARCH = os.environ.get("HARP_OFFLOAD_ARCH", "gfx950")
 
 HIP_SOURCES = ["rotate.hip", "mixed.hip", "gemv.hip", "skinny.hip", "gemm.hip", "dequant.hip",
                "prep.hip", "harp_api.cpp"]
-CXX_SOURCES = ["validate.cpp"]
+CXX_SOURCES = ["validate.cpp", "mixed_expand.cpp"]
 
 # Code object v5: loadable by the HIP runtime that ships inside torch, which
 # is the runtime the library shares with its caller (one runtime per process).

@@ -11,8 +11,9 @@ its boundary format:
   zero-initialised Givens angle), and a random sign bitmask;
 * mixed-radix rotation: per stage and group the learnable parameters
   (Givens angle or Cayley upper triangle) drawn as N(0, 0.1^2) around the
-  zero initialisation, and a random sign bitmask (the blocks themselves are
-  an offline expansion of these parameters);
+  zero initialisation, a random sign bitmask, and per radix that is not a
+  power of two the one fixed standard Gaussian matrix whose QR factor is its
+  mixer (the blocks themselves are an offline expansion of these inputs);
 * int8-stored rotation: the same angle spread drawn directly as int8 codes
   (a normal rounded to integers, clipped to [-127, 127]) with one float32
   step per side chosen so that +-127 codes span +-4 standard deviations;
@@ -168,19 +169,36 @@ def rotation_q8(dim: int, block: int, rng, theta_var: float = THETA_VAR,
 class MixedRotation:
     """One side with a mixed-radix schedule: learnable parameters per stage
     and group (Givens angle for radix 2, the b(b-1)/2 upper-triangle entries
-    of the Cayley parameter otherwise) and a random sign bitmask."""
+    of the Cayley parameter otherwise), a random sign bitmask, and per stage
+    whose radix is not a power of two the fixed b x b standard Gaussian whose
+    QR factor is that radix's mixer (None for powers of two)."""
     dim: int
     radices: tuple
     params: list            # [t] -> float64 (dim / b_t, b_t (b_t - 1) / 2)
     sign_bits: np.ndarray
+    gaussians: list = None  # [t] -> float64 (b_t, b_t) or None
 
 
-def mixed_rotation(radices, rng, scale: float = 0.1) -> MixedRotation:
+def mixer_gaussian(b: int, mixer_seed: int = 0) -> np.ndarray:
+    """The fixed b x b standard Gaussian of radix b: drawn once with numpy
+    default_rng(mixer_seed + b), so every stage and group of that radix
+    shares it."""
+    return np.random.default_rng(mixer_seed + b).normal(size=(b, b))
+
+
+def mixer_gaussians(radices, mixer_seed: int = 0) -> list:
+    """Per stage: mixer_gaussian(b_t) when b_t is not a power of two, else None."""
+    return [None if b & (b - 1) == 0 else mixer_gaussian(int(b), mixer_seed)
+            for b in radices]
+
+
+def mixed_rotation(radices, rng, scale: float = 0.1, mixer_seed: int = 0) -> MixedRotation:
     """Draw the parameters as N(0, scale^2) around the zero initialisation."""
     radices = tuple(int(b) for b in radices)
     dim = int(np.prod(radices))
     params = [rng.normal(0.0, scale, size=(dim // b, b * (b - 1) // 2)) for b in radices]
-    return MixedRotation(dim, radices, params, _sign_bits(dim, rng))
+    return MixedRotation(dim, radices, params, _sign_bits(dim, rng),
+                         mixer_gaussians(radices, mixer_seed))
 
 
 @dataclass

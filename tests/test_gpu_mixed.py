@@ -2,9 +2,10 @@
 against the float64 oracle: the pages' 5120 = 8*8*8*5*2 schedule, the
 layer dimensions of the workloads as mixed-radix products (11008, 12288,
 28672), power-of-two and tiny odd schedules, both directions, float32 and
-bf16.  The blocks are the oracle's offline expansion of seeded parameters
-(Cayley map, QR mixers), rounded to float32 for the device; the oracle
-applies the same float32 blocks.
+bf16.  The device blocks are the library's own expansion of seeded
+parameters and fixed Gaussians (harp_mixed_expand: Cayley map, QR mixers,
+float32); the oracle expands the same inputs itself in float64, so the bars
+also cover the float32 rounding of the blocks.
 """
 import math
 
@@ -44,12 +45,15 @@ def rng(*k):
 
 
 def device_side(radices, seed, zero=False):
-    side = S.mixed_rotation(radices, rng(1, seed))
+    """The device side: the library expands the seeded parameters and fixed
+    Gaussians itself (harp_mixed_expand); the oracle expands the same inputs
+    on its own, in float64, for the reference."""
+    side = S.mixed_rotation(radices, rng(1, seed), mixer_seed=seed)
     params = [np.zeros_like(p) for p in side.params] if zero else side.params
-    blocks32 = [b.astype(np.float32) for b in O.mixed_blocks(radices, params, mixer_seed=seed)]
-    flat = np.concatenate([b.ravel() for b in blocks32])
+    flat = H().harp_mixed_expand(radices, params, side.gaussians)
     R = H().MixedRotation(D().dev(flat), D().dev(side.sign_bits), radices)
-    return R, blocks32, side.sign_bits
+    blocks64 = O.mixed_blocks(radices, params, side.gaussians)
+    return R, blocks64, side.sign_bits
 
 
 CASES = [

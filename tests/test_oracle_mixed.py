@@ -13,6 +13,7 @@ import pytest
 import scipy.linalg
 
 from oracle import harp_oracle as O
+from synth import workloads as S
 
 rng0 = np.random.default_rng(777)
 
@@ -60,18 +61,20 @@ def test_skew_from_params_layout():
 
 @pytest.mark.parametrize("b", [3, 5, 7, 43])
 def test_qr_mixer_is_the_unique_qr_factor(b):
-    G = O.qr_mixer(b, seed=11)
-    g = np.random.default_rng(11).normal(size=(b, b))
+    g = S.mixer_gaussian(b, 11)
+    G = O.qr_mixer(g)
     R = G.T @ g
     assert np.allclose(G @ G.T, np.eye(b), atol=1e-12)
     assert np.allclose(np.tril(R, -1), 0.0, atol=1e-12)      # upper triangular
     assert np.all(np.diag(R) > 0)                             # positive diagonal
-    assert np.array_equal(G, O.qr_mixer(b, seed=11))          # fixed
+    assert np.array_equal(G, O.qr_mixer(S.mixer_gaussian(b, 11)))   # fixed
+    with pytest.raises(ValueError):
+        O.base_mixer(b)                                       # needs its Gaussian
 
 
 @pytest.mark.parametrize("b", [2, 4, 8, 64])
 def test_base_mixer_power_of_two_is_sylvester(b):
-    assert np.allclose(O.base_mixer(b, 0), scipy.linalg.hadamard(b) / math.sqrt(b),
+    assert np.allclose(O.base_mixer(b), scipy.linalg.hadamard(b) / math.sqrt(b),
                        atol=1e-15, rtol=0)
 
 
@@ -125,7 +128,7 @@ def dense_by_enumeration(radices, blocks, signs):
 def test_dense_brute_force_and_transpose(radices):
     d = int(np.prod(radices))
     params = random_params(radices, rng0)
-    blocks = O.mixed_blocks(radices, params, mixer_seed=5)
+    blocks = O.mixed_blocks(radices, params, S.mixer_gaussians(radices, 5))
     signs = random_signs(d, rng0)
     F = dense_by_enumeration(radices, blocks, signs)
     x = rng0.normal(size=(4, d))
@@ -139,7 +142,7 @@ def test_paper_schedule_5120_orthogonal():
     transpose inverts the forward map."""
     radices = (8, 8, 8, 5, 2)
     params = random_params(radices, rng0, 0.1)
-    blocks = O.mixed_blocks(radices, params)
+    blocks = O.mixed_blocks(radices, params, S.mixer_gaussians(radices))
     signs = random_signs(5120, rng0)
     x = rng0.normal(size=(2, 5120))
     y = O.mixed_forward(x, radices, blocks, signs)
@@ -170,8 +173,10 @@ def test_linear_mixed_all_two_is_linear():
         cs.append(np.stack([np.cos(t), np.sin(t)], axis=-1))
     x = rng0.normal(size=(3, K))
     for contract in (False, True):
-        got = O.linear_mixed(x, words, scale, zero, bits, rv, O.mixed_blocks(rv, pv), sv,
-                             ru, O.mixed_blocks(ru, pu), su, mfma_contract=contract)
+        got = O.linear_mixed(x, words, scale, zero, bits, rv,
+                             O.mixed_blocks(rv, pv, S.mixer_gaussians(rv)), sv,
+                             ru, O.mixed_blocks(ru, pu, S.mixer_gaussians(ru)), su,
+                             mfma_contract=contract)
         ref = O.linear(x, words, scale, zero, bits, cs[0], sv, K, cs[1], su, N,
                        mfma_contract=contract)
         assert np.allclose(got, ref, atol=1e-12, rtol=0)
@@ -183,7 +188,8 @@ def test_linear_mixed_dense_composition():
     rv, ru = (4, 4, 4), (5, 2, 3, 4)                # K = 64 (one quantization group)
     K, N, bits = 64, int(np.prod(ru)), 4
     pv, pu = random_params(rv, rng0), random_params(ru, rng0)
-    bv, bu = O.mixed_blocks(rv, pv, mixer_seed=3), O.mixed_blocks(ru, pu, mixer_seed=3)
+    bv = O.mixed_blocks(rv, pv, S.mixer_gaussians(rv, 3))
+    bu = O.mixed_blocks(ru, pu, S.mixer_gaussians(ru, 3))
     sv, su = random_signs(K, rng0), random_signs(N, rng0)
     words, scale, zero, q = packed_weight(N, K, bits, rng0)
     Fv = dense_by_enumeration(rv, bv, sv)
@@ -201,8 +207,8 @@ def test_linear_mixed_contract_rounds_operands():
     (both rounded by the pinned bf16 rounding), weights_exact keeps w_hat."""
     rv, ru = (8, 8), (5, 8)
     K, N, bits = 64, 40, 2
-    bv = O.mixed_blocks(rv, random_params(rv, rng0))
-    bu = O.mixed_blocks(ru, random_params(ru, rng0))
+    bv = O.mixed_blocks(rv, random_params(rv, rng0), S.mixer_gaussians(rv))
+    bu = O.mixed_blocks(ru, random_params(ru, rng0), S.mixer_gaussians(ru))
     sv, su = random_signs(K, rng0), random_signs(N, rng0)
     words, scale, zero, q = packed_weight(N, K, bits, rng0)
     x = rng0.normal(size=(2, K))
