@@ -385,6 +385,45 @@ harp_status harp_quantize_pack(const float *Wp, int32_t N, int32_t K, int32_t bi
                                harp_stream stream);
 
 /*
+ * A stack of dependent decode linears in one launch (technical summary §2.4:
+ * the rotated linear; §2.1-2.2: the stride stages of each side), the way a
+ * decoder runs them layer after layer:
+ *     y_l = F_{U,l}^T deq(W_l) F_{V,l} y_{l-1}   for l = 0 .. n_layers-1,
+ * with y_{-1} = x.  Each layer's product is the float32 product of
+ * harp_deq_gemv (x~ not rounded), so every y_l equals harp_linear_fused on
+ * the stored y_{l-1} within its float32 bar; the next layer reads y_l as
+ * stored (rounded to bf16 when y_dt is HARP_BF16).  The weights of layer
+ * l + 1 are fetched while layer l still runs, and the steps between layers
+ * are workgroup-to-workgroup handoffs on the device, not launches.
+ * Supported shapes (else HARP_ERR_UNSUPPORTED): every layer square with
+ * K = N = dim = V->block = U->block, dim 4096 or 8192; one bit width for the
+ * whole stack; angles as float32 (cos, sin) pairs; 1 <= M <= 4 for dim 4096,
+ * 1 <= M <= 2 for dim 8192 (M == 0 does nothing).
+ *   layers     host array of n_layers layers (n_layers >= 0); y of each
+ *              layer is device memory [M][dim] of y_dt.  Output buffers may
+ *              be shared between layers (ping-pong) and with x: nothing in
+ *              the stack reads a layer output back.
+ *   x          [M][dim] of x_dt, device.
+ *   workspace  at least harp_linear_chain_workspace_bytes(dim) bytes,
+ *              256-byte aligned, zero-filled once before its first use; every
+ *              call leaves it ready for the next.  Calls that share a
+ *              workspace must not overlap in time.
+ * Stacks longer than 32 layers run as one launch per 32 layers.  Every wait
+ * inside a launch is bounded; a wait that runs out (which needs a stalled
+ * device) leaves the outputs undefined and a nonzero second workspace word.
+ */
+typedef struct harp_chain_layer {
+  harp_rotation V;
+  harp_qweight W;
+  harp_rotation U;
+  void *y;
+} harp_chain_layer;
+size_t harp_linear_chain_workspace_bytes(int32_t dim);
+harp_status harp_linear_chain(const harp_chain_layer *layers, int32_t n_layers, const void *x,
+                              harp_dtype x_dt, harp_dtype y_dt, int32_t M, void *workspace,
+                              size_t ws_bytes, harp_stream stream);
+
+/*
  * harp_linear_fused for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  Same arguments, checks, results (within the path's float32 or

@@ -33,7 +33,8 @@ EXPORTED = (
     "harp_rotate_in", "harp_rotate_out", "harp_deq_gemv", "harp_rotate_in_deq_gemv",
     "harp_deq_gemm",
     "harp_deq_gemm_workspace_bytes", "harp_linear_workspace_bytes", "harp_linear_fused",
-    "harp_linear_fused_noalloc", "harp_dequant",
+    "harp_linear_fused_noalloc", "harp_linear_chain", "harp_linear_chain_workspace_bytes",
+    "harp_dequant",
     "harp_rotate_weight", "harp_rotate_weight_workspace_bytes", "harp_quantize_pack",
     "harp_mixed_expand", "harp_rotate_in_mixed", "harp_rotate_out_mixed",
     "harp_rotate_mixed_workspace_bytes",
@@ -72,6 +73,11 @@ class harp_qweight(ctypes.Structure):
                 ("zero", c_void_p)]
 
 
+class harp_chain_layer(ctypes.Structure):
+    _fields_ = [("V", harp_rotation), ("W", harp_qweight), ("U", harp_rotation),
+                ("y", c_void_p)]
+
+
 def _load() -> ctypes.CDLL:
     # torch first: its bundled HIP runtime (soname libamdhip64.so.7) must be
     # the one loaded, so that torch's streams and allocations and this
@@ -99,6 +105,10 @@ def _load() -> ctypes.CDLL:
                                         c_int32, c_void_p, c_size_t, c_void_p]),
         "harp_linear_fused_noalloc": (c_int32, [R, Q, R, c_void_p, c_int32, c_void_p, c_int32,
                                                 c_int32, c_void_p]),
+        "harp_linear_chain": (c_int32, [ctypes.POINTER(harp_chain_layer), c_int32, c_void_p,
+                                        c_int32, c_int32, c_int32, c_void_p, c_size_t,
+                                        c_void_p]),
+        "harp_linear_chain_workspace_bytes": (c_size_t, [c_int32]),
         "harp_dequant": (c_int32, [Q, c_void_p, c_int32, c_void_p]),
         "harp_rotate_weight": (c_int32, [R, R, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
                                           c_size_t, c_void_p]),
@@ -271,6 +281,26 @@ def harp_linear_fused_noalloc(V: Rotation, W: QWeight, U: Rotation, x, y,
                                          _ptr(x), _dtype_code(x), _ptr(y), _dtype_code(y), M,
                                          _stream(stream)),
            "harp_linear_fused_noalloc")
+
+
+def harp_linear_chain_workspace_bytes(dim: int) -> int:
+    return int(lib.harp_linear_chain_workspace_bytes(dim))
+
+
+def harp_linear_chain(layers, x, workspace, M: int | None = None, stream=None) -> None:
+    """layers: sequence of (V, W, U, y) with y the layer's output tensor
+    [M][dim] (float32 or bfloat16, the same for every layer)."""
+    layers = list(layers)
+    M = x.shape[0] if M is None else M
+    arr = (harp_chain_layer * max(1, len(layers)))()
+    y_dt = HARP_F32
+    for i, (V, W, U, y) in enumerate(layers):
+        arr[i] = harp_chain_layer(V.c, W.c, U.c, y.data_ptr())
+        y_dt = _dtype_code(y)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.harp_linear_chain(arr, len(layers), _ptr(x), _dtype_code(x), y_dt, M,
+                                 _ptr(workspace), ws_bytes, _stream(stream)),
+           "harp_linear_chain")
 
 
 def harp_dequant(W: QWeight, out, stream=None) -> None:

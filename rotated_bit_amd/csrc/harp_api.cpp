@@ -5,6 +5,7 @@
 #include <mutex>
 
 #include "../../include/harp.h"
+#include "chain.hpp"
 #include "launch.hpp"
 #include "validate.hpp"
 
@@ -186,6 +187,38 @@ harp_status harp_linear_fused(const harp_rotation* V, const harp_qweight* W,
   if (st != HARP_OK || M == 0) return st;
   return fused_linear(*V, *W, *U, x, x_dt, y, y_dt, M, static_cast<char*>(workspace),
                       true, as_stream(stream));
+}
+
+size_t harp_linear_chain_workspace_bytes(int32_t dim) { return harp::chain_ws_bytes(dim); }
+
+harp_status harp_linear_chain(const harp_chain_layer* layers, int32_t n_layers, const void* x,
+                              harp_dtype x_dt, harp_dtype y_dt, int32_t M, void* workspace,
+                              size_t ws_bytes, harp_stream stream) {
+  const harp_status st =
+      harp::validate_chain(layers, n_layers, x, x_dt, y_dt, M, workspace, ws_bytes);
+  if (st != HARP_OK || n_layers == 0 || M == 0) return st;
+  const int32_t dim = layers[0].V.dim;
+  const hipStream_t s = as_stream(stream);
+  // one launch per kChainMaxLayers layers; a later launch starts from the
+  // previous one's last output
+  for (int32_t l0 = 0; l0 < n_layers; l0 += harp::kChainMaxLayers) {
+    harp::ChainArgs a{};
+    a.n_layers = n_layers - l0 < harp::kChainMaxLayers ? n_layers - l0 : harp::kChainMaxLayers;
+    a.M = M;
+    a.x = l0 == 0 ? x : layers[l0 - 1].y;
+    a.x_bf16 = (l0 == 0 ? x_dt : y_dt) == HARP_BF16;
+    a.y_bf16 = y_dt == HARP_BF16;
+    a.ws = static_cast<uint32_t*>(workspace);
+    for (int32_t i = 0; i < a.n_layers; ++i) {
+      const harp_chain_layer& c = layers[l0 + i];
+      a.layer[i] = harp::ChainLayer{reinterpret_cast<const float2*>(c.V.cs), c.V.sign_bits,
+                                    c.W.qweight, c.W.scale, c.W.zero,
+                                    reinterpret_cast<const float2*>(c.U.cs), c.U.sign_bits, c.y};
+    }
+    const harp_status r = from_hip(harp::launch_chain(a, dim, layers[0].W.bits, s));
+    if (r != HARP_OK) return r;
+  }
+  return HARP_OK;
 }
 
 harp_status harp_linear_fused_noalloc(const harp_rotation* V, const harp_qweight* W,

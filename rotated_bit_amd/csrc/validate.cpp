@@ -4,6 +4,8 @@
 // batch range, data pointers (NULL when M > 0), alignment, workspace.
 #include "validate.hpp"
 
+#include "chain_layout.hpp"
+
 #include <algorithm>
 #include <cmath>
 
@@ -303,6 +305,38 @@ size_t workspace_bytes(int32_t M, int32_t N, int32_t K) {
     return 0;
   if (M == 0) return 0;
   return workspace_gemm_offset(M, N, K) + gemm_partial_bytes(M, N, K);
+}
+
+size_t chain_ws_bytes(int32_t dim) { return chain_workspace_bytes(dim); }
+
+harp_status validate_chain(const harp_chain_layer* layers, int32_t n_layers, const void* x,
+                           int x_dt, int y_dt, int32_t M, const void* workspace,
+                           size_t ws_bytes) {
+  if (n_layers < 0) return HARP_ERR_SHAPE;
+  if (n_layers == 0) return HARP_OK;
+  if (layers == nullptr) return HARP_ERR_NULL;
+  if (bad_dtype(x_dt) || bad_dtype(y_dt)) return HARP_ERR_DTYPE;
+  HARP_TRY(check_m(M));
+  const int32_t dim = layers[0].V.dim;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const harp_chain_layer& c = layers[l];
+    HARP_TRY(check_rotation(&c.V));
+    HARP_TRY(check_qweight(&c.W));
+    HARP_TRY(check_rotation(&c.U));
+    if (c.V.dim != dim || c.W.K != dim || c.W.N != dim || c.U.dim != dim) return HARP_ERR_SHAPE;
+    if (c.W.bits != layers[0].W.bits) return HARP_ERR_UNSUPPORTED;
+    if (dim != 4096 && dim != 8192) return HARP_ERR_UNSUPPORTED;
+    if (c.V.block != dim || c.U.block != dim) return HARP_ERR_UNSUPPORTED;
+    if (c.V.cs == nullptr || c.U.cs == nullptr) return HARP_ERR_UNSUPPORTED;
+    HARP_TRY(check_data(c.y, M));
+  }
+  if (M > (dim == 4096 ? 4 : 2)) return HARP_ERR_UNSUPPORTED;
+  HARP_TRY(check_data(x, M));
+  if (M == 0) return HARP_OK;
+  if (workspace == nullptr) return HARP_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return HARP_ERR_ALIGN;
+  if (ws_bytes < chain_ws_bytes(dim)) return HARP_ERR_WORKSPACE;
+  return HARP_OK;
 }
 
 const char* status_string(harp_status s) {

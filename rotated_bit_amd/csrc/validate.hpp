@@ -92,6 +92,13 @@ harp_status validate_fused_mixed(const harp_mixed_rotation* V, const harp_qweigh
                                  const void* workspace, size_t ws_bytes);
 size_t workspace_gemm_offset(int32_t M, int32_t N, int32_t K);
 
+// Decode chain: uniform square layers of dim 4096 / 8192, full-width sides,
+// float32 pairs, one bit width; M up to 4 (4096) or 2 (8192).
+size_t chain_ws_bytes(int32_t dim);
+harp_status validate_chain(const harp_chain_layer* layers, int32_t n_layers, const void* x,
+                           int x_dt, int y_dt, int32_t M, const void* workspace,
+                           size_t ws_bytes);
+
 const char* status_string(harp_status s);
 
 }  // namespace harp
