@@ -1,22 +1,34 @@
 #!/usr/bin/env python3
-"""Throughput of the HARP rotated 2-bit linear on one MI355X.
+"""Throughput of the HARP rotated low-bit linear on one MI355X.
 
-Default workload: the Llama-2-7B-shaped decode linear, 4096 -> 4096, batch
-M = 1, 2-bit group-64 weights, b = 4096 butterflies on both sides, one
-``harp_linear_fused`` call per layer.  One step is one pass over a chain of
-distinct layer instances whose combined footprint exceeds 1 GiB (four times
-the 256 MB last-level cache), captured once in a HIP graph and replayed.
-All inputs are resident in HBM before timing starts.
+Headline (the step ``--steps``/``--warmup`` time): the Llama-2-7B-shaped
+decode linear, 4096 -> 4096, batch M = 1, 2-bit group-64 weights, b = 4096
+butterflies on both sides, as 192 layers in six stacks of 32 dependent
+layers (each layer's input is the previous layer's bf16 output), one
+``harp_linear_chain`` launch per stack.  The stack's footprint (1.09 GB) exceeds four times the
+256 MB last-level cache, so every weight byte comes from HBM.  All inputs are
+resident in HBM before timing starts; the step is captured once in a HIP
+graph and replayed.
 
-value = algorithmic bytes of every call in a step / step time  (GB/s).
-Algorithmic bytes per call = packed weights + fp16 scales/zeros + float32
-(cos, sin) pairs + sign bits + bf16 x + float32 y (nothing counted for the
-intermediates).
+value = algorithmic bytes of every layer in a step / step time  (GB/s).
+Algorithmic bytes per layer = packed weights + fp16 scales/zeros + float32
+(cos, sin) pairs of both sides + sign bits + the bf16 input and output rows
+(nothing counted for the intermediates).
 
-Also reported on the same line: the roofline of the dominant kernel (its
-algorithmic bytes / its average launch duration, measured with HIP events on
-the stream it runs on), per-kernel launch durations, the M = 512 prefill
-matrix-core figure, and the float64 oracle timed on the host cores.
+Also on the same line: the roofline of the dominant kernel (its algorithmic
+bytes per launch over its average launch duration, timed with HIP events on
+the stream it runs on), the same workload as independent single-layer
+``harp_linear_fused`` calls with their per-kernel durations, every other
+configuration of the workload set (the Llama-2-7B MLP pair at M = 1 and 16,
+the Qwen3-8B-shaped prefill at M = 512, the Llama-70B-shaped slice at M = 1
+and 32 with 2/3/4-bit grids), each over its own >= 1 GiB working set, the
+int8-angle, mixed-radix and offline-preparation legs, and the float64 oracle
+timed on the host cores.
+
+Working sets: every cell builds four distinct seeded instances with the
+synthetic generators and fills the rest of its >= 1 GiB with device copies
+of them at distinct addresses (identical contents cost the same HBM traffic
+and keep host-side generation short).
 """
 from __future__ import annotations
 
@@ -31,97 +43,55 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
-
-# Memory traffic per launch of the decode-chain kernels, from two rocprofv3
-# counter passes (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000, the factors a
-# 256 MiB device copy gives) on the current kernels; set an entry to None
-# when its kernel changes until the counters are taken again.
-TRAFFIC_BYTES = {
-    "rotate_in_deq_gemv_2bit": 7009280,
-    "rotate_out_b4096": 590848,
-}
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores, TFLOP/s
 WORKING_SET_BYTES = 1 << 30
+CHAIN_LAYERS_PER_LAUNCH = 32
+DISTINCT = 4                     # seeded instances per cell; the rest are copies
+
+# HBM traffic per launch from two rocprofv3 counter passes (FETCH_SIZE and
+# WRITE_SIZE, each scaled by what the counter reads for a 256 MiB device
+# copy); None for a kernel changed since its counters were taken.
+TRAFFIC_BYTES = {
+    "chain_kernel_4096_2bit_M1_32layers": None,
+    "rotate_in_deq_gemv_2bit": None,
+    "rotate_out_b4096": None,
+}
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def side_bytes(d, b, pair_bytes=8):
+    """One side's parameters: (cos, sin) pairs (8 bytes, or one int8 code
+    plus the two float32 step values) and the sign bits."""
+    L = b.bit_length() - 1
+    steps = 4 if pair_bytes == 1 else 0
+    return pair_bytes * (d // 2) * L + steps + d // 8
+
+
+def weight_bytes(N, K, bits):
+    return N * K * bits // 8 + N * (K // 64) * 4
+
+
 def alg_bytes(M, N, K, bits, b_v, b_u, x_bytes=2, y_bytes=4, pair_bytes=8):
-    """pair_bytes: 8 for float32 (cos, sin) pairs, 1 for int8-stored angles
-    (plus the two float32 steps)."""
-    Lv, Lu = b_v.bit_length() - 1, b_u.bit_length() - 1
-    steps = 8 if pair_bytes == 1 else 0
-    return (N * K * bits // 8 + N * (K // 64) * 4
-            + pair_bytes * (K // 2 * Lv + N // 2 * Lu) + steps
-            + (K + N) // 8 + x_bytes * M * K + y_bytes * M * N)
+    return (weight_bytes(N, K, bits) + side_bytes(K, b_v, pair_bytes)
+            + side_bytes(N, b_u, pair_bytes) + x_bytes * M * K + y_bytes * M * N)
 
 
 def gemv_bytes(M, N, K, bits):
     """The product kernel alone: weights, scales/zeros, float32 x~ in, y' out."""
-    return N * K * bits // 8 + N * (K // 64) * 4 + 4 * M * K + 4 * M * N
+    return weight_bytes(N, K, bits) + 4 * M * K + 4 * M * N
 
 
 def rotgemv_bytes(M, N, K, bits, b, pair_bytes=8):
     """Input rotation + product in one kernel: weights, scales/zeros, the
     input side's angles and signs, bf16 x in, float32 y' out."""
-    L = b.bit_length() - 1
-    steps = 4 if pair_bytes == 1 else 0
-    return (N * K * bits // 8 + N * (K // 64) * 4 + pair_bytes * (K // 2) * L + steps
-            + K // 8 + 2 * M * K + 4 * M * N)
+    return weight_bytes(N, K, bits) + side_bytes(K, b, pair_bytes) + 2 * M * K + 4 * M * N
 
 
 def rotate_bytes(M, d, b, in_bytes, out_bytes, pair_bytes=8):
-    L = b.bit_length() - 1
-    steps = 4 if pair_bytes == 1 else 0
-    return pair_bytes * (d // 2) * L + steps + d // 8 + in_bytes * M * d + out_bytes * M * d
-
-
-class Instance:
-    """Device buffers of one layer instance (from the seeded generators)."""
-
-    def __init__(self, li, torch, H, y_dtype):
-        import numpy as np
-
-        def dev(a):
-            a = np.ascontiguousarray(a)
-            if a.dtype == np.uint32:
-                a = a.view(np.int32)
-            elif a.dtype == np.uint16:
-                a = a.view(np.int16)
-            return torch.from_numpy(a).cuda()
-
-        lin = li.lin
-        self.li = li
-        def rot(r):
-            if r.cs is None:
-                return H.Rotation(None, dev(r.sign_bits), r.dim, r.block,
-                                  phi_codes=dev(r.phi_codes), phi_step=r.phi_step)
-            return H.Rotation(dev(r.cs), dev(r.sign_bits), r.dim, r.block)
-
-        self.V = rot(li.V)
-        self.U = rot(li.U)
-        self.W = H.QWeight(dev(li.W.words), dev(li.W.scale), dev(li.W.zero),
-                           lin.N, lin.K, li.bits)
-        self.x = dev(li.x).view(torch.bfloat16)
-        self.y = torch.empty((li.M, lin.N), dtype=y_dtype, device="cuda")
-        # zero-filled: the GEMM arrival counters in its tail must start at 0
-        self.ws = torch.zeros(max(256, H.harp_linear_workspace_bytes(li.M, lin.N, lin.K)),
-                              dtype=torch.uint8, device="cuda")
-        gb = H.harp_deq_gemm_workspace_bytes(li.M, lin.N, lin.K)
-        self.gws = torch.zeros(gb, dtype=torch.uint8, device="cuda") if gb else None
-        self.xt32 = torch.empty((li.M, lin.K), dtype=torch.float32, device="cuda")
-        self.xt16 = torch.empty((li.M, lin.K), dtype=torch.bfloat16, device="cuda")
-        self.yp = torch.empty((li.M, lin.N), dtype=torch.float32, device="cuda")
-
-
-def make_instances(cfg_name, lin_idx, bits, M, count, torch, H, angles="f32"):
-    from synth import workloads as S
-    cfg = S.CONFIGS[cfg_name]
-    return [Instance(S.layer_inputs(cfg, lin_idx, bits, M, inst=i, angles=angles),
-                     torch, H, torch.float32)
-            for i in range(count)]
+    return side_bytes(d, b, pair_bytes) + in_bytes * M * d + out_bytes * M * d
 
 
 def time_graph(torch, fn, reps, warmup=3):
@@ -149,6 +119,109 @@ def time_graph(torch, fn, reps, warmup=3):
     return start.elapsed_time(end) / reps, g
 
 
+class Layer:
+    """Device buffers of one layer instance: both sides, the packed weight,
+    and per batch size M an input x [M][K] and an output y [M][N]."""
+
+    def __init__(self, V, W, U, xs, ys):
+        self.V, self.W, self.U, self.xs, self.ys = V, W, U, xs, ys
+
+
+def _dev(torch, a):
+    import numpy as np
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    elif a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def _rotation(torch, H, r, copy=False):
+    c = (lambda t: t.clone()) if copy else (lambda t: t)
+    if isinstance(r, H.Rotation):
+        if r.cs is None:
+            return H.Rotation(None, c(r.sign_bits), r.dim, r.block,
+                              phi_codes=c(r.phi_codes), phi_step=r.phi_step)
+        return H.Rotation(c(r.cs), c(r.sign_bits), r.dim, r.block)
+    if r.cs is None:
+        return H.Rotation(None, _dev(torch, r.sign_bits), r.dim, r.block,
+                          phi_codes=_dev(torch, r.phi_codes), phi_step=r.phi_step)
+    return H.Rotation(_dev(torch, r.cs), _dev(torch, r.sign_bits), r.dim, r.block)
+
+
+def build_layers(torch, H, cfg_name, lin_idx, bits, Ms, count, y_dtype, angles="f32"):
+    """count layer instances of one linear of a config: DISTINCT seeded ones
+    from the generators, the rest device copies of them."""
+    from synth import workloads as S
+    cfg = S.CONFIGS[cfg_name]
+    lin = cfg.linears[lin_idx]
+    base = []
+    for i in range(min(DISTINCT, count)):
+        li = S.layer_inputs(cfg, lin_idx, bits, Ms[0], inst=i, angles=angles)
+        out = S.outlier_channels(lin.K, S.rng_for(cfg.cid, S.T_OUTLIER, lin_idx, i)) \
+            if cfg.outliers else None
+        xs = {}
+        for M in Ms:
+            xa = li.x if M == Ms[0] else S.activations(
+                M, lin.K, S.rng_for(cfg.cid, S.T_X, lin_idx, i * 1000 + M), cfg.x_dtype, out)
+            xs[M] = _dev(torch, xa).view(torch.bfloat16)
+        W = H.QWeight(_dev(torch, li.W.words), _dev(torch, li.W.scale), _dev(torch, li.W.zero),
+                      lin.N, lin.K, bits)
+        base.append((_rotation(torch, H, li.V), W, _rotation(torch, H, li.U), xs))
+    layers = []
+    for i in range(count):
+        V, W, U, xs = base[i % len(base)]
+        if i >= len(base):
+            V, U = _rotation(torch, H, V, copy=True), _rotation(torch, H, U, copy=True)
+            W = H.QWeight(W.qweight.clone(), W.scale.clone(), W.zero.clone(), W.N, W.K, W.bits)
+            xs = {M: x.clone() for M, x in xs.items()}
+        ys = {M: torch.empty((M, lin.N), dtype=y_dtype, device="cuda") for M in Ms}
+        layers.append(Layer(V, W, U, xs, ys))
+    torch.cuda.synchronize()
+    return lin, layers
+
+
+def count_for(per_instance):
+    return max(DISTINCT, -(-WORKING_SET_BYTES // per_instance))
+
+
+def fused_cell(torch, H, lin, layers, M, bits, reps=5):
+    """Independent harp_linear_fused calls over the cell's instances."""
+    ws = torch.zeros(max(256, H.harp_linear_workspace_bytes(M, lin.N, lin.K)),
+                     dtype=torch.uint8, device="cuda")
+    ms, _ = time_graph(torch, lambda: [H.harp_linear_fused(L.V, L.W, L.U, L.xs[M], L.ys[M], ws)
+                                       for L in layers], reps)
+    us = ms * 1e3 / len(layers)
+    nb = alg_bytes(M, lin.N, lin.K, bits, lin.b_v, lin.b_u)
+    out = {"us_per_linear": round(us, 3), "GB_s": round(nb / (us * 1e-6) / 1e9, 1),
+           "frac_hbm": round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "TFLOPs": round(2.0 * M * lin.N * lin.K / (us * 1e-6) / 1e12, 2),
+           "bytes_per_call": nb, "instances": len(layers)}
+    del ws
+    return out
+
+
+def chain_cell(torch, H, lin, layers, M):
+    """The layers as stacks of 32 dependent layers, one harp_linear_chain
+    launch each: a stack's first layer reads the cell's input x, each next
+    one the previous layer's bf16 output.  (With the configs' N(0, 0.02^2)
+    weights and no normalisation between layers, activations grow about
+    2.7x per layer, so a stack is kept to 32 layers to stay finite.)
+    Returns (workspace, stacks, step function)."""
+    ws = torch.zeros(H.harp_linear_chain_workspace_bytes(lin.K), dtype=torch.uint8,
+                     device="cuda")
+    segs = [layers[i:i + CHAIN_LAYERS_PER_LAUNCH]
+            for i in range(0, len(layers), CHAIN_LAYERS_PER_LAUNCH)]
+    x0 = layers[0].xs[M]
+
+    def step():
+        for seg in segs:
+            H.harp_linear_chain([(L.V, L.W, L.U, L.ys[M]) for L in seg], x0, ws)
+
+    return ws, segs, step
+
+
 def cpu_baseline(li, budget_s=12.0):
     """The float64 oracle (unchanged) on the host cores, same layer inputs."""
     import numpy as np
@@ -171,11 +244,12 @@ def cpu_baseline(li, budget_s=12.0):
         if el >= budget_s or n >= 200:
             break
     per = el / n
-    b = alg_bytes(li.M, lin.N, lin.K, li.bits, lin.b_v, lin.b_u)
+    b = alg_bytes(li.M, lin.N, lin.K, li.bits, lin.b_v, lin.b_u, y_bytes=2)
     return {"value": round(b / per / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{n} full oracle linears (unpack, dequant, F_V, matvec, F_U^T) "
-                      f"of instance 0, {per * 1e3:.1f} ms each, float64 numpy"}
+            "sample": f"{n} full oracle linears (unpack, dequant, F_V, matvec, F_U^T) of "
+                      f"one 4096x4096 2-bit M=1 layer, {per * 1e3:.1f} ms each, float64 "
+                      f"numpy; GB/s over the same per-layer bytes as the headline"}
 
 
 def main():
@@ -183,18 +257,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--instances", type=int, default=0, help="layer instances (0: >= 1 GiB)")
+    ap.add_argument("--layers", type=int, default=192,
+                    help="headline stack depth (a multiple of 32 keeps launches equal)")
+    ap.add_argument("--only-headline", action="store_true",
+                    help="time the headline stack only (profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
-    ap.add_argument("--no-prefill", action="store_true", help="skip the M=512 figure")
-    ap.add_argument("--no-int8", action="store_true",
-                    help="skip the decode leg with int8-stored angles")
-    ap.add_argument("--no-batched", action="store_true",
-                    help="skip the M=16 batched-decode leg")
-    ap.add_argument("--no-prep", action="store_true",
-                    help="skip the offline-preparation leg")
-    ap.add_argument("--no-mixed", action="store_true",
-                    help="skip the mixed-radix rotation leg")
-    ap.add_argument("--eager", action="store_true", help="time eager launches, no graph")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other configurations of the workload set")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the int8-angle, mixed-radix and offline-preparation legs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (the known-size "
                          "reference for the HBM byte counters)")
@@ -212,55 +283,56 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
 
+    # ---------------- headline: the 4096-wide decode stack -----------------
     M, N, K, bits, bv, bu = 1, 4096, 4096, 2, 4096, 4096
-    per_call = alg_bytes(M, N, K, bits, bv, bu)
-    count = args.instances or -(-WORKING_SET_BYTES // per_call)
-    log(f"building {count} layer instances of 4096x4096 2-bit (>= 1 GiB)")
+    per_layer = alg_bytes(M, N, K, bits, bv, bu, y_bytes=2)
+    count = args.layers
+    log(f"building {count} layers of 4096x4096 2-bit ({count * per_layer / 1e9:.2f} GB)")
     t0 = time.time()
-    inst = make_instances("l7b_decode", 0, bits, M, count, torch, H)
-    torch.cuda.synchronize()
+    lin, layers = build_layers(torch, H, "l7b_decode", 0, bits, (M,), count, torch.bfloat16)
     log(f"  built in {time.time() - t0:.1f} s")
+    ws, segs, step = chain_cell(torch, H, lin, layers, M)
 
-    def step():
-        for it in inst:
-            H.harp_linear_fused(it.V, it.W, it.U, it.x, it.y, it.ws)
-
-    # eager reference result for the graph check
     step()
     torch.cuda.synchronize()
-    ref = [inst[0].y.clone(), inst[-1].y.clone()]
-
+    ref = [layers[0].ys[M].clone(), layers[-1].ys[M].clone()]
+    _, g = time_graph(torch, step, reps=1, warmup=0)
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    if args.eager:
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
-        start.record()
-        for _ in range(args.steps):
-            step()
-        end.record()
-        torch.cuda.synchronize()
-        ms = start.elapsed_time(end) / args.steps
-    else:
-        # capture once, replay: warmup W, then exactly K timed replays
-        _, g = time_graph(torch, step, reps=1, warmup=0)
-        for _ in range(args.warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        start.record()
-        for _ in range(args.steps):
-            g.replay()
-        end.record()
-        torch.cuda.synchronize()
-        ms = start.elapsed_time(end) / args.steps
-        for r, it in zip(ref, (inst[0], inst[-1])):
-            if not torch.equal(r, it.y):
-                raise RuntimeError("graph replay differs from eager result")
-    log(f"step: {count} fused linears in {ms:.3f} ms "
-        f"({ms * 1e3 / count:.2f} us per linear)")
-    value = count * per_call / (ms * 1e-3) / 1e9
-    ms_step = ms   # the timed step; the legs below time their own work
+    start.record()
+    for _ in range(args.steps):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    for r, L in zip(ref, (layers[0], layers[-1])):
+        if not torch.equal(r.view(torch.int16), L.ys[M].view(torch.int16)):
+            raise RuntimeError("graph replay differs from eager result")
+        if not torch.isfinite(L.ys[M]).all():
+            raise RuntimeError("non-finite layer output")
+    err = int(ws[4:8].view(torch.int32).item())
+    if err:
+        raise RuntimeError("a wait inside the chain ran out")
+    value = count * per_layer / (ms_step * 1e-3) / 1e9
+    us_layer = ms_step * 1e3 / count
+    log(f"step: {count} dependent layers in {len(segs)} launches, {ms_step:.3f} ms "
+        f"({us_layer:.2f} us per layer, {value:.1f} GB/s)")
+    # the step is the chain kernel alone (one launch per 32 layers, nothing
+    # else in the graph): its average launch duration is the step time over
+    # the launches, timed by the events above on the replay stream
+    launch_us = ms_step * 1e3 / len(segs)
+    launch_bytes = CHAIN_LAYERS_PER_LAUNCH * per_layer
+    dom = "chain_kernel_4096_2bit_M1_32layers"
+    achieved = launch_bytes / (launch_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": TRAFFIC_BYTES.get(dom),
+                "alg_bytes_per_launch": launch_bytes,
+                "us_per_launch": round(launch_us, 2)}
 
     if args.calibrate_copy:
         src = torch.empty(64 << 20, dtype=torch.float32, device="cuda")
@@ -271,257 +343,252 @@ def main():
         log("calibration: 3 x 256 MiB device copies done")
         del src, dst
 
-    # Per-kernel launch durations: each kernel alone, a graph of `count`
-    # launches on the capture stream, timed with events around the replays.
-    # The fused decode call launches rotate_in_deq_gemv then rotate_out; the
-    # stand-alone rotate_in and deq_gemv are listed for reference.
-    kern = {}
-    reps = max(3, args.steps // 10)
-    ms_rg, _ = time_graph(torch, lambda: [H.harp_rotate_in_deq_gemv(i.V, i.W, i.x, i.yp)
-                                          for i in inst], reps)
-    ms_ro, _ = time_graph(torch, lambda: [H.harp_rotate_out(i.U, i.yp, i.y) for i in inst], reps)
-    ms_ri, _ = time_graph(torch, lambda: [H.harp_rotate_in(i.V, i.x, i.xt32) for i in inst], reps)
-    ms_gv, _ = time_graph(torch, lambda: [H.harp_deq_gemv(i.W, i.xt32, i.yp) for i in inst], reps)
-    # (the stand-alone rotate_in of a few rows into float32 at b = 4096 is two
-    # launches: sub-blocks, then the last three stages)
-    for name, msk, nbytes, in_path, launches in (
-            ("rotate_in_deq_gemv_2bit", ms_rg, rotgemv_bytes(M, N, K, bits, bv), True, 1),
-            ("rotate_out_b4096", ms_ro, rotate_bytes(M, N, bu, 4, 4), True, 1),
-            ("rotate_in_b4096", ms_ri, rotate_bytes(M, K, bv, 2, 4), False, 2),
-            ("deq_gemv_2bit", ms_gv, gemv_bytes(M, N, K, bits), False, 1)):
-        us = msk * 1e3 / count
-        kern[name] = {("us_per_launch" if launches == 1 else "us_per_call"): round(us, 3),
-                      "launches_per_call": launches, "alg_bytes": nbytes,
-                      "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1), "in_fused_path": in_path}
-    log("kernels: " + json.dumps(kern))
-    dom = max((k for k in kern if kern[k]["in_fused_path"]),
-              key=lambda k: kern[k]["us_per_launch"])
-    achieved = kern[dom]["GB_s"]
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": TRAFFIC_BYTES.get(dom)}
+    headline_cfg = {"workload": "l7b_decode: 4096x4096 2-bit group-64, M=1, b=4096 both "
+                                "sides, stacks of 32 dependent layers (harp_linear_chain)",
+                    "layers_per_step": count, "launches_per_step": len(segs),
+                    "bytes_per_layer": per_layer, "us_per_layer": round(us_layer, 3),
+                    "graph": True}
 
-    # the same decode workload with int8-stored angles
-    del inst
+    # the same layers as independent single-layer calls (fused linear)
+    fused = None
+    kern = {}
+    if not args.only_headline:
+        for L in layers:
+            L.ys[M] = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        fused = fused_cell(torch, H, lin, layers, M, bits, reps=max(3, args.steps // 10))
+        fused["speedup_chain_vs_fused"] = round(fused["us_per_linear"] / us_layer, 3)
+        xt32 = torch.empty((M, K), dtype=torch.float32, device="cuda")
+        yp = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        reps = max(3, args.steps // 10)
+        ms_rg, _ = time_graph(torch, lambda: [H.harp_rotate_in_deq_gemv(L.V, L.W, L.xs[M], yp)
+                                              for L in layers], reps)
+        ms_ro, _ = time_graph(torch, lambda: [H.harp_rotate_out(L.U, yp, L.ys[M])
+                                              for L in layers], reps)
+        ms_ri, _ = time_graph(torch, lambda: [H.harp_rotate_in(L.V, L.xs[M], xt32)
+                                              for L in layers], reps)
+        ms_gv, _ = time_graph(torch, lambda: [H.harp_deq_gemv(L.W, xt32, yp) for L in layers],
+                              reps)
+        for name, msk, nbytes, launches in (
+                ("rotate_in_deq_gemv_2bit", ms_rg, rotgemv_bytes(M, N, K, bits, bv), 1),
+                ("rotate_out_b4096", ms_ro, rotate_bytes(M, N, bu, 4, 4), 1),
+                ("rotate_in_b4096", ms_ri, rotate_bytes(M, K, bv, 2, 4), 2),
+                ("deq_gemv_2bit", ms_gv, gemv_bytes(M, N, K, bits), 1)):
+            us = msk * 1e3 / count
+            kern[name] = {("us_per_launch" if launches == 1 else "us_per_call"): round(us, 3),
+                          "launches_per_call": launches, "alg_bytes": nbytes,
+                          "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                          "traffic": TRAFFIC_BYTES.get(name)}
+        fused["kernels"] = kern
+        log("fused per call: " + json.dumps(fused))
+        del xt32, yp
+    del layers, ws, g
     torch.cuda.empty_cache()
-    q8 = None
-    if not args.no_int8:
+
+    # ---------------- the other configurations ------------------------------
+    configs = {}
+    if not args.no_configs and not args.only_headline:
+        # Llama-2-7B MLP pair, M = 1 and 16
+        mlp = {}
+        for li_idx, name in ((0, "up_4096x11008"), (1, "down_11008x4096")):
+            from synth import workloads as S
+            ln = S.CONFIGS["l7b_mlp"].linears[li_idx]
+            cnt = count_for(alg_bytes(16, ln.N, ln.K, 2, ln.b_v, ln.b_u))
+            ln, ls = build_layers(torch, H, "l7b_mlp", li_idx, 2, (1, 16), cnt, torch.float32)
+            mlp[name] = {f"M{m}": fused_cell(torch, H, ln, ls, m, 2) for m in (1, 16)}
+            del ls
+            torch.cuda.empty_cache()
+        configs["l7b_mlp_2bit"] = mlp
+        log("l7b_mlp: " + json.dumps(mlp))
+
+        # Llama-70B-shaped slice, M = 1 and 32, 2/3/4 bits; the 8192-wide
+        # attention projection also as a dependent stack at M = 1
+        l70 = {}
+        from synth import workloads as S
+        for li_idx, name in ((0, "attn_8192x8192"), (1, "up_8192x28672"),
+                             (2, "down_28672x8192")):
+            for b in (2, 3, 4):
+                ln = S.CONFIGS["l70b_slice"].linears[li_idx]
+                cnt = count_for(alg_bytes(32, ln.N, ln.K, b, ln.b_v, ln.b_u))
+                if li_idx == 0:
+                    cnt = -(-cnt // CHAIN_LAYERS_PER_LAUNCH) * CHAIN_LAYERS_PER_LAUNCH
+                ln, ls = build_layers(torch, H, "l70b_slice", li_idx, b, (1, 32), cnt,
+                                      torch.float32)
+                cell = {f"M{m}": fused_cell(torch, H, ln, ls, m, b) for m in (1, 32)}
+                if li_idx == 0:
+                    for L in ls:
+                        L.ys[1] = torch.empty((1, ln.N), dtype=torch.bfloat16, device="cuda")
+                    cws, csegs, cstep = chain_cell(torch, H, ln, ls, 1)
+                    ms_c, _ = time_graph(torch, cstep, 5)
+                    if int(cws[4:8].view(torch.int32).item()):
+                        raise RuntimeError("a wait inside the 8192-wide chain ran out")
+                    nb = alg_bytes(1, ln.N, ln.K, b, ln.b_v, ln.b_u, y_bytes=2)
+                    us = ms_c * 1e3 / len(ls)
+                    cell["chain_M1"] = {"us_per_layer": round(us, 3),
+                                        "GB_s": round(nb / (us * 1e-6) / 1e9, 1),
+                                        "frac_hbm": round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                        "layers": len(ls), "launches": len(csegs)}
+                    del cws
+                l70[f"{name}_{b}bit"] = cell
+                log(f"l70b {name} {b}-bit: " + json.dumps(cell))
+                del ls
+                torch.cuda.empty_cache()
+        configs["l70b_slice"] = l70
+
+        # Qwen3-8B-shaped prefill, M = 512, 2 and 4 bits: the GEMM alone (on
+        # the rotated bf16 x~) and the whole fused linear
+        pre = {}
+        for li_idx, lnm in enumerate(("attn_4096x4096", "up_4096x12288", "down_12288x4096")):
+            for b in (2, 4):
+                ln = S.CONFIGS["q8b_prefill"].linears[li_idx]
+                Mp = 512
+                cnt = count_for(alg_bytes(Mp, ln.N, ln.K, b, ln.b_v, ln.b_u))
+                ln, ls = build_layers(torch, H, "q8b_prefill", li_idx, b, (Mp,), cnt,
+                                      torch.float32)
+                flops = 2.0 * Mp * ln.N * ln.K
+                xt16 = [torch.empty((Mp, ln.K), dtype=torch.bfloat16, device="cuda")
+                        for _ in ls]
+                for L, xt in zip(ls, xt16):
+                    H.harp_rotate_in(L.V, L.xs[Mp], xt)
+                gb = H.harp_deq_gemm_workspace_bytes(Mp, ln.N, ln.K)
+                gws = torch.zeros(gb, dtype=torch.uint8, device="cuda") if gb else None
+                ms_gm, _ = time_graph(torch, lambda: [H.harp_deq_gemm(L.W, xt, L.ys[Mp], gws)
+                                                      for L, xt in zip(ls, xt16)], 5)
+                us_gm = ms_gm * 1e3 / len(ls)
+                cell = fused_cell(torch, H, ln, ls, Mp, b)
+                tf_gm = flops / (us_gm * 1e-6) / 1e12
+                cell.update({"deq_gemm_us": round(us_gm, 2),
+                             "deq_gemm_TFLOPs": round(tf_gm, 1),
+                             "deq_gemm_frac_mfma": round(tf_gm / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "fused_frac_mfma": round(cell["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4)})
+                pre[f"{lnm}_{b}bit"] = cell
+                log(f"q8b prefill {lnm} {b}-bit: " + json.dumps(cell))
+                del ls, xt16, gws
+                torch.cuda.empty_cache()
+        configs["q8b_prefill_M512"] = pre
+
+    # ---------------- legs ---------------------------------------------------
+    legs = {}
+    if not args.no_legs and not args.only_headline:
+        import numpy as np
+        from synth import workloads as S
+        # the headline workload with int8-stored angles, per call
         per8 = alg_bytes(M, N, K, bits, bv, bu, pair_bytes=1)
-        count8 = args.instances or -(-WORKING_SET_BYTES // per8)
-        inst8 = make_instances("l7b_decode", 0, bits, M, count8, torch, H, angles="int8")
-        ms8, _ = time_graph(torch, lambda: [H.harp_linear_fused(i.V, i.W, i.U, i.x, i.y, i.ws)
-                                            for i in inst8], max(3, args.steps // 4))
-        ms8_rg, _ = time_graph(torch, lambda: [H.harp_rotate_in_deq_gemv(i.V, i.W, i.x, i.yp)
-                                               for i in inst8], reps)
-        ms8_ro, _ = time_graph(torch, lambda: [H.harp_rotate_out(i.U, i.yp, i.y) for i in inst8], reps)
-        us8 = ms8 * 1e3 / count8
-        q8 = {"workload": "l7b_decode with int8-stored angles (one byte per pair)",
-              "instances_per_step": count8, "bytes_per_call": per8,
-              "us_per_linear": round(us8, 3),
-              "GB_s": round(per8 / (us8 * 1e-6) / 1e9, 2),
-              "speedup_vs_f32_pairs": round((ms_step * 1e3 / count) / us8, 3),
-              "kernels": {}}
-        for name, msk, nbytes in (
-                ("rotate_in_deq_gemv_2bit_int8", ms8_rg, rotgemv_bytes(M, N, K, bits, bv, 1)),
-                ("rotate_out_b4096_int8", ms8_ro, rotate_bytes(M, N, bu, 4, 4, 1))):
-            us = msk * 1e3 / count8
-            q8["kernels"][name] = {"us_per_launch": round(us, 3), "alg_bytes": nbytes,
-                                   "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        ln, ls = build_layers(torch, H, "l7b_decode", 0, bits, (M,), count_for(per8),
+                              torch.float32, angles="int8")
+        q8 = fused_cell(torch, H, ln, ls, M, bits)
+        q8["bytes_per_call"] = per8
+        q8["GB_s"] = round(per8 / (q8["us_per_linear"] * 1e-6) / 1e9, 1)
+        q8["frac_hbm"] = round(q8["GB_s"] / HBM_PEAK_GBS, 4)
+        legs["int8_angles_l7b_decode_fused"] = q8
         log("int8 angles: " + json.dumps(q8))
-        del inst8
+        del ls
         torch.cuda.empty_cache()
 
-    # batched decode: the Llama-2-7B MLP pair at M = 16 (small-batch
-    # matrix-core product)
-    batched = None
-    if not args.no_batched:
-        batched = {"workload": "l7b_mlp: 4096->11008 (b_U=256) and 11008->4096 (b_V=256), "
-                               "2-bit, M=16, harp_linear_fused", "linears": {}}
-        for li_idx, name in ((0, "up_4096x11008"), (1, "down_11008x4096")):
-            bi = make_instances("l7b_mlp", li_idx, 2, 16, 16, torch, H)
-            lin = bi[0].li.lin
-            for it in bi:
-                H.harp_rotate_in(it.V, it.x, it.xt16)
-            msf, _ = time_graph(torch, lambda: [H.harp_linear_fused(i.V, i.W, i.U, i.x, i.y, i.ws)
-                                                for i in bi], 10)
-            msg, _ = time_graph(torch, lambda: [H.harp_deq_gemm(i.W, i.xt16, i.yp) for i in bi], 10)
-            usf, usg = msf * 1e3 / len(bi), msg * 1e3 / len(bi)
-            nb = alg_bytes(16, lin.N, lin.K, 2, lin.b_v, lin.b_u)
-            wb = lin.N * lin.K * 2 // 8 + lin.N * (lin.K // 64) * 4
-            batched["linears"][name] = {
-                "fused_us": round(usf, 2), "fused_GB_s": round(nb / (usf * 1e-6) / 1e9, 1),
-                "deq_gemm_us": round(usg, 2),
-                "deq_gemm_TFLOPs": round(2.0 * 16 * lin.N * lin.K / (usg * 1e-6) / 1e12, 1),
-                "deq_gemm_weight_GB_s": round(wb / (usg * 1e-6) / 1e9, 1)}
-            del bi
-            torch.cuda.empty_cache()
-        log("batched decode: " + json.dumps(batched))
+        # mixed radix: blocks expanded inside libharp from learnable
+        # parameters (orthogonal: Givens / Cayley times the fixed mixer)
+        mixed = {"workload": "full-width mixed-radix sides, blocks from harp_mixed_expand "
+                             "(parameters N(0, 0.1^2)), rotations alone and the 5120-wide "
+                             "2-bit linear"}
 
-    # mixed-radix rotation (full-width schedules instead of block-diagonal 256)
-    mixed = None
-    if not args.no_mixed:
-        import numpy as np
-        mixed = {"workload": "harp_rotate_in_mixed (bf16 x -> float32 x~, or bf16 x~ for the "
-                             "matrix-core product, with its float32 workspace) and "
-                             "harp_rotate_out_mixed (float32 -> float32), "
-                             "random orthogonal blocks (float32) per stage and group"}
+        def expand(radices, seed):
+            ms_ = S.mixed_rotation(radices, np.random.default_rng(seed))
+            blocks = H.harp_mixed_expand(radices, ms_.params, ms_.gaussians)
+            return torch.from_numpy(blocks).cuda(), _dev(torch, ms_.sign_bits)
+
         for radices in ((8, 8, 8, 5, 2), (8, 8, 4, 43), (8, 8, 8, 8, 3), (8, 8, 8, 8, 7)):
             dim = int(np.prod(radices))
             nblk = sum(dim * b for b in radices)
-            R = H.MixedRotation(torch.randn(nblk, device="cuda") * 0.1,
-                                torch.zeros((dim + 31) // 32, dtype=torch.int32, device="cuda"),
-                                radices)
+            base = [expand(radices, s) for s in range(DISTINCT)]
             entry = {}
-            legs = [("in", 1, torch.bfloat16, torch.float32),
-                    ("in", 512, torch.bfloat16, torch.float32),
-                    ("in", 512, torch.bfloat16, torch.bfloat16),
-                    ("out", 1, torch.float32, torch.float32),
-                    ("out", 512, torch.float32, torch.float32)]
-            for side, M, idt, odt in legs:
-                xs = [torch.randn((M, dim), device="cuda").to(idt) for _ in range(8)]
-                outs = [torch.empty((M, dim), device="cuda", dtype=odt) for _ in range(8)]
+            for side, Mm, idt, odt in (("in", 1, torch.bfloat16, torch.float32),
+                                       ("in", 512, torch.bfloat16, torch.float32),
+                                       ("in", 512, torch.bfloat16, torch.bfloat16),
+                                       ("out", 1, torch.float32, torch.float32),
+                                       ("out", 512, torch.float32, torch.float32)):
+                ib, ob = (2 if idt == torch.bfloat16 else 4), (2 if odt == torch.bfloat16 else 4)
+                nb = 4 * nblk + dim // 8 + (ib + ob) * Mm * dim
+                cnt = count_for(nb)
+                Rs = [H.MixedRotation(base[i % DISTINCT][0].clone(),
+                                      base[i % DISTINCT][1].clone(), radices) for i in range(cnt)]
+                xs = [torch.randn((Mm, dim), device="cuda").to(idt) for _ in range(cnt)]
+                outs = [torch.empty((Mm, dim), device="cuda", dtype=odt) for _ in range(cnt)]
                 fn = H.harp_rotate_in_mixed if side == "in" else H.harp_rotate_out_mixed
-                ws = None
-                if odt == torch.bfloat16:   # float32 stages in a workspace, bf16 last stage
-                    ws = torch.empty(H.harp_rotate_mixed_workspace_bytes(dim, M, odt),
-                                     dtype=torch.uint8, device="cuda")
-                ms_m, _ = time_graph(torch, lambda: [fn(R, a, o, ws) for a, o in zip(xs, outs)], 5)
-                us = ms_m * 1e3 / 8
-                nb = 4 * nblk + dim // 8 + (xs[0].element_size() + outs[0].element_size()) * M * dim
-                key = f"{side}_M{M}" + ("_bf16" if odt == torch.bfloat16 else "")
+                mws = None
+                if odt == torch.bfloat16:
+                    mws = torch.empty(H.harp_rotate_mixed_workspace_bytes(dim, Mm, odt),
+                                      dtype=torch.uint8, device="cuda")
+                ms_m, _ = time_graph(torch, lambda: [fn(R, a, o, mws)
+                                                     for R, a, o in zip(Rs, xs, outs)], 3)
+                us = ms_m * 1e3 / cnt
+                key = f"{side}_M{Mm}" + ("_bf16" if odt == torch.bfloat16 else "")
                 entry[f"{key}_us"] = round(us, 2)
                 entry[f"{key}_GB_s"] = round(nb / (us * 1e-6) / 1e9, 1)
-                del xs, outs
+                del Rs, xs, outs, mws
+                torch.cuda.empty_cache()
             mixed["x".join(str(b) for b in radices)] = entry
-            del R
-            torch.cuda.empty_cache()
-        # the whole linear on a 5120-wide layer (8x8x8x5x2 on both sides), 2-bit
-        radices, bits = (8, 8, 8, 5, 2), 2
+        radices, mb = (8, 8, 8, 5, 2), 2
         d = int(np.prod(radices))
         nblk = sum(d * b for b in radices)
-        lin = {}
-        for M in (1, 16):
+        base = [expand(radices, s) for s in range(2 * DISTINCT)]
+        lin5 = {}
+        for Mm in (1, 16):
+            nb = weight_bytes(d, d, mb) + 2 * (4 * nblk + d // 8) + 2 * Mm * d + 4 * Mm * d
+            cnt = count_for(nb)
+            rng = np.random.default_rng(5)
+            qw = S.qweight(d, d, mb, rng)
+            Wb = H.QWeight(_dev(torch, qw.words), _dev(torch, qw.scale), _dev(torch, qw.zero),
+                           d, d, mb)
             inst = []
-            for _ in range(32):
-                V = H.MixedRotation(torch.randn(nblk, device="cuda") * 0.1,
-                                    torch.zeros((d + 31) // 32, dtype=torch.int32, device="cuda"),
-                                    radices)
-                U = H.MixedRotation(torch.randn(nblk, device="cuda") * 0.1,
-                                    torch.zeros((d + 31) // 32, dtype=torch.int32, device="cuda"),
-                                    radices)
-                words = torch.randint(-2**31, 2**31 - 1, (d, d * bits // 32), dtype=torch.int32,
-                                      device="cuda")
-                sc = torch.full((d, d // 64), 0.01, dtype=torch.float16, device="cuda").view(torch.int16)
-                zr = torch.full((d, d // 64), 1.0, dtype=torch.float16, device="cuda").view(torch.int16)
-                W = H.QWeight(words, sc, zr, d, d, bits)
-                x = torch.randn((M, d), device="cuda").to(torch.bfloat16)
-                y = torch.empty((M, d), device="cuda")
-                ws = torch.zeros(H.harp_linear_mixed_workspace_bytes(M, d, d), dtype=torch.uint8,
-                                 device="cuda")
-                inst.append((V, W, U, x, y, ws))
-            ms_m, _ = time_graph(torch, lambda: [H.harp_linear_fused_mixed(*i) for i in inst], 5)
-            us = ms_m * 1e3 / len(inst)
-            nb = d * d * bits // 8 + d * (d // 64) * 4 + 2 * (4 * nblk + d // 8) + 2 * M * d + 4 * M * d
-            lin[f"M{M}_us"] = round(us, 2)
-            lin[f"M{M}_GB_s"] = round(nb / (us * 1e-6) / 1e9, 1)
-            del inst
+            for i in range(cnt):
+                V = H.MixedRotation(base[(2 * i) % len(base)][0].clone(),
+                                    base[(2 * i) % len(base)][1].clone(), radices)
+                U = H.MixedRotation(base[(2 * i + 1) % len(base)][0].clone(),
+                                    base[(2 * i + 1) % len(base)][1].clone(), radices)
+                W = H.QWeight(Wb.qweight.clone(), Wb.scale.clone(), Wb.zero.clone(), d, d, mb)
+                x = torch.randn((Mm, d), device="cuda").to(torch.bfloat16)
+                inst.append((V, W, U, x, torch.empty((Mm, d), device="cuda")))
+            mws = torch.zeros(H.harp_linear_mixed_workspace_bytes(Mm, d, d), dtype=torch.uint8,
+                              device="cuda")
+            ms_m, _ = time_graph(torch, lambda: [H.harp_linear_fused_mixed(*i, mws)
+                                                 for i in inst], 3)
+            us = ms_m * 1e3 / cnt
+            lin5[f"M{Mm}_us"] = round(us, 2)
+            lin5[f"M{Mm}_GB_s"] = round(nb / (us * 1e-6) / 1e9, 1)
+            del inst, mws, Wb
             torch.cuda.empty_cache()
-        mixed["linear_5120x5120_2bit"] = lin
+        mixed["linear_5120x5120_2bit"] = lin5
+        legs["mixed_radix"] = mixed
         log("mixed radix: " + json.dumps(mixed))
 
-    # offline preparation: W' = F_U W F_V^T, then quantize and pack (2-bit)
-    prep = None
-    if not args.no_prep:
-        import numpy as np
-        from synth import workloads as S
+        # offline preparation: W' = F_U W F_V^T, then quantize and pack (2-bit)
         prep = {"workload": "dense float32 W 4096x4096 (b=4096 both sides) and 8192x28672 "
                             "(b_V=256, b_U=8192): harp_rotate_weight, harp_quantize_pack 2-bit"}
-        for (N, K, bu, bv) in ((4096, 4096, 4096, 4096), (8192, 28672, 8192, 256)):
-            rV = S.rotation(K, bv, np.random.default_rng(1))
-            rU = S.rotation(N, bu, np.random.default_rng(2))
-            dv = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int32) if a.dtype == np.uint32 else a)).cuda()
-            V = H.Rotation(dv(rV.cs), dv(rV.sign_bits), K, bv)
-            U = H.Rotation(dv(rU.cs), dv(rU.sign_bits), N, bu)
-            W = torch.randn((N, K), device="cuda") * 0.02
+        for (Np, Kp, bup, bvp) in ((4096, 4096, 4096, 4096), (8192, 28672, 8192, 256)):
+            rV = S.rotation(Kp, bvp, np.random.default_rng(1))
+            rU = S.rotation(Np, bup, np.random.default_rng(2))
+            V = _rotation(torch, H, rV)
+            U = _rotation(torch, H, rU)
+            W = torch.randn((Np, Kp), device="cuda") * 0.02
             Wp = torch.empty_like(W)
-            ws = torch.empty(H.harp_rotate_weight_workspace_bytes(N, K), dtype=torch.uint8,
-                             device="cuda")
-            qw = torch.empty((N, K * 2 // 32), dtype=torch.int32, device="cuda")
-            sc = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
-            zr = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
-            ms_r, _ = time_graph(torch, lambda: H.harp_rotate_weight(V, U, W, Wp, ws), 5)
+            pws = torch.empty(H.harp_rotate_weight_workspace_bytes(Np, Kp), dtype=torch.uint8,
+                              device="cuda")
+            qw = torch.empty((Np, Kp * 2 // 32), dtype=torch.int32, device="cuda")
+            sc = torch.empty((Np, Kp // 64), dtype=torch.int16, device="cuda")
+            zr = torch.empty((Np, Kp // 64), dtype=torch.int16, device="cuda")
+            ms_r, _ = time_graph(torch, lambda: H.harp_rotate_weight(V, U, W, Wp, pws), 5)
             ms_q, _ = time_graph(torch, lambda: H.harp_quantize_pack(Wp, 2, qw, sc, zr), 5)
-            nrot = 8 * N * K + 8 * (K // 2 * (bv.bit_length() - 1) + N // 2 * (bu.bit_length() - 1))
-            nq = 4 * N * K + N * K // 4 + N * (K // 64) * 4
-            prep[f"{N}x{K}"] = {
+            nrot = 8 * Np * Kp + 8 * (Kp // 2 * (bvp.bit_length() - 1)
+                                      + Np // 2 * (bup.bit_length() - 1))
+            nq = 4 * Np * Kp + Np * Kp // 4 + Np * (Kp // 64) * 4
+            prep[f"{Np}x{Kp}"] = {
                 "rotate_weight_us": round(ms_r * 1e3, 1),
                 "rotate_weight_GB_s": round(nrot / (ms_r * 1e-3) / 1e9, 1),
                 "quantize_pack_us": round(ms_q * 1e3, 1),
                 "quantize_pack_GB_s": round(nq / (ms_q * 1e-3) / 1e9, 1)}
-            del W, Wp, ws, qw, sc, zr
+            del W, Wp, pws, qw, sc, zr
             torch.cuda.empty_cache()
+        legs["offline_prep"] = prep
         log("offline prep: " + json.dumps(prep))
-
-    # prefill: M = 512 on the matrix cores, the three linears of the
-    # Qwen3-8B-shaped prefill config at 2 and 4 bits; the top-level keys are
-    # the 4096 x 4096 2-bit case
-    prefill = None
-    if not args.no_prefill:
-        from synth import workloads as S
-        pcfg = S.CONFIGS["q8b_prefill"]
-        shapes = {}
-        for li_idx, lin in enumerate(pcfg.linears):
-            for bits in (2, 4):
-                n_pre = 8 if lin.N * lin.K <= 4096 * 4096 else 4
-                pre = make_instances("q8b_prefill", li_idx, bits, 512, n_pre, torch, H)
-                flops = 2.0 * 512 * lin.N * lin.K
-                for it in pre:
-                    H.harp_rotate_in(it.V, it.x, it.xt16)
-                ms_gm, _ = time_graph(
-                    torch, lambda: [H.harp_deq_gemm(i.W, i.xt16, i.yp, i.gws) for i in pre], 10)
-                ms_fu, _ = time_graph(
-                    torch, lambda: [H.harp_linear_fused(i.V, i.W, i.U, i.x, i.y, i.ws)
-                                    for i in pre], 10)
-                us_gm, us_fu = ms_gm * 1e3 / len(pre), ms_fu * 1e3 / len(pre)
-                tf_gm = flops / (us_gm * 1e-6) / 1e12
-                ctx = {}
-                if li_idx == 0 and bits == 2:
-                    # context, not our path: the vendor library's plain bf16
-                    # GEMM on the same x~ with the weights dequantized first
-                    wb = [torch.empty((lin.N, lin.K), dtype=torch.bfloat16, device="cuda")
-                          for _ in pre]
-                    for i, w in zip(pre, wb):
-                        H.harp_dequant(i.W, w)
-                    ms_lib, _ = time_graph(
-                        torch, lambda: [torch.matmul(i.xt16, w.t()) for i, w in zip(pre, wb)], 10)
-                    us_lib = ms_lib * 1e3 / len(pre)
-                    ctx = {"context_library_bf16_gemm_us": round(us_lib, 2),
-                           "context_library_frac_mfma": round(
-                               flops / (us_lib * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
-                    del wb
-                shapes[f"{lin.K}x{lin.N}_{bits}bit"] = {
-                    "K": lin.K, "N": lin.N, "bits": bits, "b_V": lin.b_v, "b_U": lin.b_u,
-                    "deq_gemm_us": round(us_gm, 2),
-                    "deq_gemm_TFLOPs": round(tf_gm, 1),
-                    "deq_gemm_frac_mfma": round(tf_gm / MFMA_BF16_PEAK_TFLOPS, 4),
-                    "fused_us": round(us_fu, 2),
-                    "fused_frac_mfma": round(flops / (us_fu * 1e-6) / 1e12
-                                             / MFMA_BF16_PEAK_TFLOPS, 4), **ctx}
-                del pre
-                torch.cuda.empty_cache()
-        head = shapes["4096x4096_2bit"]
-        prefill = {"workload": "4096x4096 2-bit M=512",
-                   "deq_gemm_us": head["deq_gemm_us"],
-                   "deq_gemm_TFLOPs": head["deq_gemm_TFLOPs"],
-                   "deq_gemm_frac_mfma": head["deq_gemm_frac_mfma"],
-                   "fused_us": head["fused_us"],
-                   "fused_frac_mfma": head["fused_frac_mfma"],
-                   "context_library_bf16_gemm_us": head.get("context_library_bf16_gemm_us"),
-                   "context_library_frac_mfma": head.get("context_library_frac_mfma"),
-                   "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
-                   "shapes": shapes}
-        log("prefill: " + json.dumps(prefill))
 
     cpu = None
     if not args.no_cpu:
@@ -544,19 +611,13 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "l7b_decode: 4096x4096 2-bit group-64, M=1, b=4096 both "
-                               "sides, harp_linear_fused",
-                   "instances_per_step": count, "bytes_per_call": per_call,
-                   "graph": not args.eager},
+        "config": headline_cfg,
         "frac_hbm": round(value / HBM_PEAK_GBS, 4),
         "tok_s_equiv_llama2_7b_linears": round(tok_s, 1),
         "roofline": roofline,
-        "kernels": kern,
-        "int8_angles": q8,
-        "batched_decode": batched,
-        "mixed_radix": mixed,
-        "offline_prep": prep,
-        "prefill": prefill,
+        "fused_per_call": fused,
+        "configs": configs,
+        "legs": legs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -40,14 +40,17 @@
 // Synchronisation.  A workgroup waits only for workgroups earlier in the
 // grid, which the dispatcher has started before it, so the chain makes
 // progress whatever number of workgroups fits on the chip at once (no
-// co-residency is assumed).  Data crossing workgroups is written with
-// device-coherent (sc1, write-through) stores; each writer waits for their
-// acknowledgement (vmcnt(0)), then one thread stores its flag; readers poll
-// the flags with device-scope loads and read the data with sc1 loads.  Flags
-// hold the launch's epoch (workspace word 0, plus one), so nothing needs
-// resetting: a second kernel of one thread advances the epoch after the
-// chain.  Every wait is bounded: a wait that runs out records an error in
-// workspace word 1 and ends its workgroup, so the grid always drains.
+// co-residency is assumed).  Data crossing workgroups travels through
+// device-coherent (sc1, write-through) stores and loads.  z: each rotation
+// role waits for the acknowledgement of its stores (vmcnt(0)), then stores
+// its flag in 16 copies; the product workgroups poll one copy, then load.
+// y': every value leaves as a (value, epoch) pair in one 8-byte store, and
+// the rotation roles poll the values themselves (no acknowledgement wait and
+// no flag on that side).  Flags and tags hold the launch's epoch (workspace
+// word 0, plus one), so nothing needs resetting: the last workgroup to end
+// advances the epoch for the next launch.  Every wait is bounded: a wait that
+// runs out records an error in workspace word 1 and ends its workgroup, so
+// the grid always drains.
 #include "chain.hpp"
 
 #include "device_common.hpp"
@@ -498,6 +501,16 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(ChainArgs a) {
   }
   if (!is_g) {
     rot_role(layer, idx);
+    // The last of the final rotation workgroups to end advances the epoch
+    // for the next launch.  Every other workgroup has read the epoch by
+    // then: each one feeds, through the chain of waits, the data that every
+    // final rotation workgroup has consumed.
+    __syncthreads();
+    if (tid == 0 && __hip_atomic_fetch_add(ctrl + 2, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) == static_cast<uint32_t>(nR - 1)) {
+      st_flag(ctrl + 2, 0u);
+      st_flag(ctrl, epoch);
+    }
     return;
   }
   {
@@ -672,19 +685,12 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(ChainArgs a) {
 
 }
 
-__global__ void chain_epoch_kernel(uint32_t* ctrl) {
-  st_flag(ctrl, ld_flag(ctrl) + 1u);
-}
-
 template <int LOGD, int BITS, int MT>
 hipError_t launch_chain_t(const ChainArgs& a, hipStream_t stream) {
   using P = ChainPlan<LOGD>;
   const int nR = 8 * a.M;
   const dim3 grid(a.n_layers * P::NG + nR);
   hipLaunchKernelGGL((chain_kernel<LOGD, BITS, MT>), grid, dim3(kThreadsC), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(chain_epoch_kernel, dim3(1), dim3(1), 0, stream, a.ws);
   return hipGetLastError();
 }
 
