@@ -24,8 +24,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libharp.so")
 ARCH = os.environ.get("HARP_OFFLOAD_ARCH", "gfx950")
 
-HIP_SOURCES = ["rotate.hip", "mixed.hip", "gemv.hip", "skinny.hip", "gemm.hip", "dequant.hip",
-               "prep.hip", "chain.hip", "harp_api.cpp"]
+HIP_SOURCES = ["rotate.hip", "mixed.hip", "gemv.hip", "gemv_mc.hip", "skinny.hip", "gemm.hip",
+               "dequant.hip", "prep.hip", "chain.hip", "harp_api.cpp"]
 CXX_SOURCES = ["validate.cpp", "mixed_expand.cpp"]
 
 # Code object v5: loadable by the HIP runtime that ships inside torch, which

@@ -19,6 +19,7 @@
 // is bitwise reproducible.
 #include "launch.hpp"
 #include "unpack.hpp"
+#include "validate.hpp"
 
 namespace harp {
 namespace {
@@ -743,6 +744,8 @@ hipError_t launch_gemv_rotated(const harp_rotation& V, const harp_qweight& W,
 
 hipError_t launch_gemv(const harp_qweight& W, const float* xt, float* yt, int M,
                        hipStream_t stream) {
+  if (M >= kGemvMcMinM && M <= kGemvMcMaxM && W.bits != 3)
+    return launch_gemv_mc(W, xt, yt, M, stream);
   switch (W.bits) {
     case 2: return launch_bits<2>(W, xt, yt, M, stream);
     case 3: return launch_bits<3>(W, xt, yt, M, stream);

@@ -29,6 +29,11 @@ hipError_t launch_rotate_mixed(const harp_mixed_rotation& R, const void* in, int
 hipError_t launch_gemv(const harp_qweight& W, const float* xt, float* yt,
                        int M, hipStream_t stream);
 
+// The same product on the bf16 matrix cores with x~ split into exact bf16
+// planes (gemv_mc.hip): kGemvMcMinM <= M <= kGemvMcMaxM, 2 or 4 bits.
+hipError_t launch_gemv_mc(const harp_qweight& W, const float* xt, float* yt,
+                          int M, hipStream_t stream);
+
 // yt = w_hat (F_V x) in one launch: every workgroup rotates x itself.  For
 // small batches and input sides only (gemv_rotated_supported).
 constexpr int kDecodeRotMaxM = 4;

@@ -63,6 +63,11 @@ size_t gemm_partial_bytes(int32_t M, int32_t N, int32_t K);
 // matrix-core products.
 constexpr int32_t kSkinnyMaxM = 64;
 constexpr int32_t kSplitMinM = 16;
+// The float32-x~ product below kSplitMinM: the vector-ALU kernel, except for
+// kGemvMcMinM .. kGemvMcMaxM rows at 2 and 4 bits, where the matrix cores
+// on the exact bf16 planes of x~ are faster.
+constexpr int32_t kGemvMcMinM = 3;
+constexpr int32_t kGemvMcMaxM = 8;
 constexpr int32_t kBf16MinM = 64;
 // The fused linear folds the input rotation into the product launch up to
 // this many rows and output features: every workgroup of the one-launch

@@ -302,6 +302,32 @@ def test_gemv(N, K, bits, M, spread):
     assert r <= CONTRACT_TOL and r <= FP32_PATH_TOL
 
 
+# Full-width decode products checked on sampled output features: strips of
+# two 16-feature tiles (N >= 16384) with a ragged last strip, several
+# four-group blocks per wave, uneven wave ranges (K / 64 not a multiple of
+# 8), both product kernels (M = 1, 2 and 3-bit: vector ALU; M = 3..8 at 2
+# and 4 bits: matrix cores on the bf16 planes of x~).
+WIDE_GEMV_CASES = [(16400, 8192, 2, 3), (16400, 8192, 4, 5), (16400, 8192, 4, 8),
+                   (16400, 4160, 2, 6), (16400, 8192, 2, 1), (16400, 8192, 4, 2),
+                   (4100, 8192, 4, 4), (16400, 4160, 3, 5), (16400, 8192, 2, 7)]
+
+
+@pytest.mark.parametrize("N,K,bits,M", WIDE_GEMV_CASES)
+def test_gemv_wide_sampled(N, K, bits, M):
+    d = D()
+    w = S.qweight(N, K, bits, rng(13, N, K, bits, M))
+    xt = rng(14, K, M).normal(size=(M, K)).astype(np.float32)
+    yt = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    H().harp_deq_gemv(d.dev_qweight(w), d.dev(xt), yt)
+    edges = [0, 1, 15, 16, 31, 32, 33, 63, 64, N // 2, N - 17, N - 16, N - 2, N - 1]
+    rows = np.unique(np.concatenate([edges, rng(15, N).integers(0, N, 96)]))
+    w_hat = O.dequant(O.unpack(w.words[rows], bits, K), d.scale_f16(w)[rows],
+                      d.zero_f16(w)[rows])
+    ref = xt.astype(np.float64) @ w_hat.T
+    r = report(f"gemv wide {N}x{K} b{bits} M={M}", d.host(yt)[:, rows], ref)
+    assert r <= CONTRACT_TOL and r <= FP32_PATH_TOL
+
+
 ROTGEMV_CASES = [
     (256, 256, 8, 2, 1, "f32", "f32"), (300, 256, 16, 3, 3, "int8", "bf16"),
     (4096, 4096, 4096, 2, 1, "f32", "bf16"), (4096, 4096, 4096, 2, 1, "int8", "bf16"),
