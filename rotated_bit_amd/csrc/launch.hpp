@@ -60,6 +60,15 @@ hipError_t launch_gemm_skinny(const harp_qweight& W, const uint16_t* xt, float* 
 hipError_t launch_gemm_skinny_split(const harp_qweight& W, const float* xt, float* yt,
                                     int M, hipStream_t stream);
 
+// The same products on strips of 32 or 64 features per wave
+// (skinny_wide.hip), which read x~ correspondingly fewer times: for K a
+// multiple of 4096 and N of at least 8192; the launchers above use it
+// where it applies.
+int skinny_wide_blocks(int N);
+bool skinny_wide_supported(const harp_qweight& W, int M);
+hipError_t launch_skinny_wide(const harp_qweight& W, const void* xt, bool xf32, float* yt,
+                              int M, hipStream_t stream);
+
 // Offline preparation: out [C][R] = in [R][C]^T (float32), and the packed
 // uniform grid of a float32 weight [N][K] (qweight, scale, zero in the
 // harp_qweight layout).

@@ -352,11 +352,13 @@ hipError_t launch_any(const harp_qweight& W, const void* xt, float* yt, int M,
 
 hipError_t launch_gemm_skinny(const harp_qweight& W, const uint16_t* xt, float* yt,
                               int M, hipStream_t stream) {
+  if (skinny_wide_supported(W, M)) return launch_skinny_wide(W, xt, false, yt, M, stream);
   return launch_any<false>(W, xt, yt, M, stream);
 }
 
 hipError_t launch_gemm_skinny_split(const harp_qweight& W, const float* xt, float* yt,
                                     int M, hipStream_t stream) {
+  if (skinny_wide_supported(W, M)) return launch_skinny_wide(W, xt, true, yt, M, stream);
   return launch_any<true>(W, xt, yt, M, stream);
 }
 

@@ -266,12 +266,22 @@ int32_t gemm_splits(int32_t M, int32_t N, int32_t K) {
   if (M <= kSkinnyMaxM || N < 1 || K < 64) return 1;
   const int64_t tiles = static_cast<int64_t>((M + kGemmTile - 1) / kGemmTile) *
                         ((N + kGemmTile - 1) / kGemmTile);
-  if (tiles > kGemmMaxSplitTiles) return 1;   // the chip is full without a split
-  int32_t s = static_cast<int32_t>((256 + tiles / 2) / tiles);
+  if (tiles > kGemmMaxSplitTiles) return 1;   // many rounds: the split gains little
+  // The slice count whose workgroups fill the last round of kGemmSlots
+  // best (ties to fewer slices), each slice at least 8 groups.
   const int32_t groups = K / 64;
-  if (s > 4) s = 4;
-  if (s > groups / 8) s = groups / 8;
-  return s < 1 ? 1 : s;
+  int32_t best = 1;
+  double best_fill = 0.0;
+  for (int32_t s = 1; s <= kGemmMaxSplits && groups / s >= 8; ++s) {
+    const int64_t wgs = tiles * s;
+    const int64_t rounds = (wgs + kGemmSlots - 1) / kGemmSlots;
+    const double fill = static_cast<double>(wgs) / static_cast<double>(rounds * kGemmSlots);
+    if (fill > best_fill + 1e-9) {
+      best = s;
+      best_fill = fill;
+    }
+  }
+  return best;
 }
 
 size_t gemm_partial_bytes(int32_t M, int32_t N, int32_t K) {

@@ -39,17 +39,20 @@ harp_status validate_quantize_pack(const float* Wp, int32_t N, int32_t K, int32_
                                    const void* qweight, const void* scale, const void* zero);
 size_t rotate_weight_workspace_bytes(int32_t N, int32_t K);
 
-// Matrix-core GEMM tiling and its split over K: the number of K slices is
-// chosen so that about one 128 x 128 output tile slice runs per CU (256 on
-// MI355X), at most 4, each slice at least 8 quantization groups.  Split K
-// needs a workspace: a fixed area of per-tile uint32 arrival counters at its
-// front (a split product has at most kGemmMaxSplitTiles tiles), then per
-// slice and tile a float32 partial tile.  The counters sit at the same
-// offset for every shape, so one zero-filled workspace serves any sequence
-// of shapes that fit in it.
+// Matrix-core GEMM tiling and its split over K: the number of K slices
+// (at most kGemmMaxSplits, each slice at least 8 quantization groups) is
+// the one whose workgroups best fill their last round of kGemmSlots (one
+// 128 x 128 tile slice per CU, 256 CUs on MI355X); tile counts above
+// kGemmMaxSplitTiles run unsplit.  Split K needs a workspace: a fixed area
+// of per-tile uint32 arrival counters at its front, then per slice and tile
+// a float32 partial tile.  The counters sit at the same offset for every
+// shape, so one zero-filled workspace serves any sequence of shapes that
+// fit in it.
 constexpr int32_t kGemmTile = 128;
-constexpr int32_t kGemmMaxSplitTiles = 192;
-constexpr size_t kGemmCounterBytes = 1024;   // >= 4 * kGemmMaxSplitTiles, 256-aligned
+constexpr int32_t kGemmSlots = 256;
+constexpr int32_t kGemmMaxSplits = 4;
+constexpr int32_t kGemmMaxSplitTiles = 512;
+constexpr size_t kGemmCounterBytes = 2048;   // >= 4 * kGemmMaxSplitTiles, 256-aligned
 int32_t gemm_splits(int32_t M, int32_t N, int32_t K);
 size_t gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
 size_t gemm_partial_bytes(int32_t M, int32_t N, int32_t K);

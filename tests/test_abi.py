@@ -160,7 +160,7 @@ def test_product_data_checks():
 def test_workspace_bytes():
     f = L.harp_linear_workspace_bytes
     g = L.harp_deq_gemm_workspace_bytes
-    C = 1024   # the GEMM arrival counters, always first (fixed offset for every shape)
+    C = 2048   # the GEMM split-K counters, always first (fixed offset for every shape)
     # M < 64: float32 x~, then y'
     assert f(1, 4096, 4096) == C + 4096 * 4 + 4096 * 4
     assert f(15, 100, 64) == C + 3840 + 6144     # 15*100*4 = 6000 rounds up to 6144
@@ -173,9 +173,12 @@ def test_workspace_bytes():
     assert g(65, 4096, 4096) == C + 4 * 32 * 128 * 128 * 4
     assert f(65, 4096, 4096) == C + (65 * 4096 * 2 + 255) // 256 * 256 + 65 * 4096 * 4 \
         + 4 * 32 * 128 * 128 * 4
-    # M=512, 4096x4096: 128 tiles -> 2 slices; 12288 outputs: 384 tiles -> 1 slice
+    # M=512, 4096x4096: 128 tiles -> 2 slices fill 256 CUs; 12288 outputs:
+    # 384 tiles -> 2 slices fill three rounds of 256 (one slice: 1.5 rounds)
     assert g(512, 4096, 4096) == C + 2 * 128 * 128 * 128 * 4
-    assert g(512, 12288, 4096) == 0
+    assert g(512, 12288, 4096) == C + 2 * 384 * 128 * 128 * 4
+    # 1024 tiles fill four rounds unsplit
+    assert g(1024, 16384, 4096) == 0
     # K of 64 (one group) cannot be split
     assert g(512, 256, 64) == 0
     assert f(0, 4096, 4096) == 0
@@ -342,7 +345,7 @@ def test_mixed_rotation_workspace():
 
 def test_linear_mixed_workspace_bytes():
     f = L.lib.harp_linear_mixed_workspace_bytes
-    C = 1024   # the GEMM arrival counters, always first
+    C = 2048   # the GEMM split-K counters, always first
     # M = 1: float32 x~ (20480), y' (20480), bf16-output stage buffer (20480)
     assert f(1, 5120, 5120) == C + 3 * 20480
     # M = 16: float32 x~ (the operand, split into bf16 planes by the product),

@@ -359,6 +359,10 @@ GEMM_CASES = [
     (4096, 4096, 2, 16, "mid"), (4096, 4096, 2, 32, "mid"), (11008, 4096, 2, 16, "mid"),
     (4096, 11008, 4, 48, "mid"), (1024, 28672, 3, 32, "mid"), (2000, 8192, 2, 5, "mid"),
     (1000, 1088, 4, 64, "mid"), (64, 64, 2, 17, "mid"),
+    # M <= 64 on wide strips (K a multiple of 4096, N >= 8192): 32 and 64
+    # features per wave, ragged row tiles
+    (8192, 4096, 2, 64, "mid"), (16384, 4096, 3, 33, "wide"), (16384, 4096, 4, 1, "mid"),
+    (8200, 8192, 2, 17, "wide"),
     # M > 64: 128 x 128 tiles, optionally split K
     (300, 256, 3, 65, "mid"), (128, 64, 2, 200, "mid"),
     (4096, 4096, 2, 512, "mid"), (12288, 4096, 4, 512, "mid"), (4096, 12288, 2, 512, "mid"),
@@ -399,8 +403,7 @@ def test_gemm(N, K, bits, M, spread):
         assert r <= CONTRACT_TOL and r <= FP32_PATH_TOL
         torch.cuda.synchronize()
         assert torch.equal(y1, y2)
-        tiles = ((M + 127) // 128) * ((N + 127) // 128)
-        counters = ws[:tiles * 4].view(torch.int32)   # fixed front area
+        counters = ws[:2048].view(torch.int32)   # fixed front area, left at zero
         assert int(counters.abs().sum().item()) == 0
 
 
@@ -617,7 +620,7 @@ def test_fused_workspace_reused_across_shapes():
         r = report(f"reused workspace M={M}", d.host(y), refs[M])
         assert r <= CONTRACT_TOL and r <= path_tol(M)
     torch.cuda.synchronize()
-    assert int(ws[:1024].view(torch.int32).abs().sum().item()) == 0
+    assert int(ws[:2048].view(torch.int32).abs().sum().item()) == 0
 
 
 @pytest.mark.parametrize("M", [1, 16, 512])
