@@ -281,7 +281,7 @@ harp_status harp_rotate_in_deq_gemv(const harp_rotation *V,
  *              Otherwise at least harp_deq_gemm_workspace_bytes(M, N, K)
  *              bytes, 256-byte aligned: the K dimension is split into slices
  *              that run concurrently and are summed in a fixed slice order
- *              (bitwise reproducible).  Its first 1024 bytes hold per-tile
+ *              (bitwise reproducible).  Its first 2048 bytes hold per-tile
  *              arrival counters at the same offset for every shape: zero-fill
  *              the workspace once before its first use; every call leaves the
  *              counters at zero, so one workspace serves any sequence of
@@ -313,7 +313,7 @@ size_t harp_linear_workspace_bytes(int32_t M, int32_t N, int32_t K);
  *   x  [M][K] of x_dt;  y  [M][N] of y_dt.
  *   workspace  at least harp_linear_mixed_workspace_bytes(M, N, K) bytes,
  *              256-byte aligned, zero-filled before its first use (its first
- *              1024 bytes are the split-K counters, at the same offset for
+ *              2048 bytes are the split-K counters, at the same offset for
  *              every shape; every call leaves them at zero).  Calls that
  *              share a workspace must not overlap in time.
  */
@@ -340,7 +340,7 @@ size_t harp_linear_mixed_workspace_bytes(int32_t M, int32_t N, int32_t K);
  *   x  [M][K] of x_dt;  y  [M][N] of y_dt;
  *   workspace  at least harp_linear_workspace_bytes(M, N, K) bytes, 256-byte
  *              aligned, owned by the caller.  Zero-filled before its first
- *              use: its first 1024 bytes hold the GEMM arrival counters, at
+ *              use: its first 2048 bytes hold the GEMM arrival counters, at
  *              the same offset for every shape, and every call leaves them
  *              at zero, so one workspace serves any sequence of shapes it is
  *              large enough for; the rest is clobbered.  Calls that share a
@@ -433,7 +433,7 @@ harp_status harp_linear_chain(const harp_chain_layer *layers, int32_t n_layers, 
  * allocates nothing (no hipMalloc/hipFree, no allocating library routine);
  * its first call on a device looks up that device's array address.
  * M > 64 runs the GEMM as one K slice (no split K), so nothing in the array
- * needs initialisation.  Size limit: 1024 + align256(M K e) + align256(4 M N)
+ * needs initialisation.  Size limit: 2048 + align256(M K e) + align256(4 M N)
  * bytes at most HARP_NOALLOC_SCRATCH_BYTES, with e = 4 for M < 64 and 2 from
  * 64 on (align256 rounds up to a multiple of 256); larger calls return
  * HARP_ERR_WORKSPACE and launch nothing.  Every call on one GPU shares that
