@@ -159,6 +159,12 @@ LINEAR_MIXED_CASES = [
     ((8, 8, 4, 43), (8, 8, 8, 8), 3, 40, "bf16"),    # 11008 -> 4096
     ((8, 8, 8, 5, 2), (16, 16, 20), 2, 100, "f32"),  # 5120 -> 5120, GEMM with split K
     ((64, 5), (40, 8), 2, 3, "bf16"),                # 320 -> 320, ragged tiles
+    # decode batches: the workloads' schedules, a radix-43 stage, no
+    # leading segment (64 x 64), twelve radix-2 stages
+    ((8, 8, 8, 8), (8, 8, 4, 43), 2, 2, "bf16"),     # 4096 -> 11008
+    ((8, 8, 4, 43), (8, 8, 8, 8), 4, 4, "f32"),      # 11008 -> 4096
+    ((8, 8, 8, 8, 3), (8, 8, 8, 5, 2), 3, 1, "bf16"),  # 12288 -> 5120
+    ((64, 64), (2,) * 12, 2, 3, "f32"),             # 4096 -> 4096
 ]
 
 
