@@ -334,14 +334,16 @@ size_t harp_linear_mixed_workspace_bytes(int32_t M, int32_t N, int32_t K);
  *     N <= 4096 where harp_rotate_in_deq_gemv supports the shape.
  *   16 <= M < 64: rotate-in to a float32 x~, the small-batch matrix-core
  *     product on x~ split exactly into two bf16 planes hi + lo
- *     (|x~ - hi - lo| <= 2^-16 |x~|; w_hat exact), rotate-out.
+ *     (|x~ - hi - lo| <= 2^-16 |x~|; w_hat exact), rotate-out.  Where K is
+ *     a multiple of 4096 and N at least 8192 the product may split K into
+ *     slices whose partials, summed in slice order, use the workspace.
  *   M >= 64: rotate-in to a bf16 x~, the matrix-core product of
  *     harp_deq_gemm (w_hat exact at 64 rows, bf16 above), rotate-out.
  *   x  [M][K] of x_dt;  y  [M][N] of y_dt;
  *   workspace  at least harp_linear_workspace_bytes(M, N, K) bytes, 256-byte
  *              aligned, owned by the caller.  Zero-filled before its first
- *              use: its first 2048 bytes hold the GEMM arrival counters, at
- *              the same offset for every shape, and every call leaves them
+ *              use: its first 2048 bytes hold the split-K arrival counters,
+ *              at the same offset for every shape, and every call leaves them
  *              at zero, so one workspace serves any sequence of shapes it is
  *              large enough for; the rest is clobbered.  Calls that share a
  *              workspace must not overlap in time.

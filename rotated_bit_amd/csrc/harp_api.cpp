@@ -40,8 +40,14 @@ harp_status fused_linear(const harp_rotation& V, const harp_qweight& W, const ha
     float* xt = reinterpret_cast<float*>(ws + harp::workspace_xt_offset());
     r = from_hip(harp::launch_rotate(V, x, x_dt, xt, HARP_F32, M, false, s));
     if (r != HARP_OK) return r;
-    r = from_hip(M < harp::kSplitMinM ? harp::launch_gemv(W, xt, yp, M, s)
-                                      : harp::launch_gemm_skinny_split(W, xt, yp, M, s));
+    if (M < harp::kSplitMinM)
+      r = from_hip(harp::launch_gemv(W, xt, yp, M, s));
+    else if (split_k)
+      r = from_hip(harp::launch_gemm_skinny_split_k(
+          W, xt, yp, M, reinterpret_cast<float*>(ws + harp::workspace_gemm_offset(M, W.N, W.K)),
+          reinterpret_cast<uint32_t*>(ws), s));
+    else
+      r = from_hip(harp::launch_gemm_skinny_split(W, xt, yp, M, s));
   } else {
     uint16_t* xt = reinterpret_cast<uint16_t*>(ws + harp::workspace_xt_offset());
     // y' is not yet written: when it is at least as large as x~ in float32

@@ -60,14 +60,24 @@ hipError_t launch_gemm_skinny(const harp_qweight& W, const uint16_t* xt, float* 
 hipError_t launch_gemm_skinny_split(const harp_qweight& W, const float* xt, float* yt,
                                     int M, hipStream_t stream);
 
-// The same products on strips of 32 or 64 features per wave
-// (skinny_wide.hip), which read x~ correspondingly fewer times: for K a
-// multiple of 4096 and N of at least 8192; the launchers above use it
-// where it applies.
-int skinny_wide_blocks(int N);
-bool skinny_wide_supported(const harp_qweight& W, int M);
-hipError_t launch_skinny_wide(const harp_qweight& W, const void* xt, bool xf32, float* yt,
-                              int M, hipStream_t stream);
+// The same products on strips of 16 fb features per wave
+// (skinny_wide.hip, fb 2 or 4), which read x~ correspondingly fewer times,
+// in `splits` K slices (see skinny_wide_split in validate.hpp; splits > 1
+// needs `partials`, splits x M x N floats, and zeroed `counters`, one per
+// strip and row tile, left zero).  The launchers above use it without
+// split K where it applies; launch_gemm_skinny_split_k with split K, on a
+// float32 x~ in the caller's workspace that it splits in place first.
+// xin: 0 bf16 x~, 1 float32 x~, 2 float32 x~ split in place by
+// launch_split_chunks.
+hipError_t launch_skinny_wide(const harp_qweight& W, const void* xt, int xin, float* yt,
+                              int M, int fb, int splits, float* partials, uint32_t* counters,
+                              hipStream_t stream);
+// In place over n float32 values (n a multiple of 8): each 8-value chunk
+// becomes its 8 bf16 hi values then its 8 bf16 lo values.
+hipError_t launch_split_chunks(float* xt, size_t n, hipStream_t stream);
+hipError_t launch_gemm_skinny_split_k(const harp_qweight& W, const float* xt, float* yt,
+                                      int M, float* partials, uint32_t* counters,
+                                      hipStream_t stream);
 
 // Offline preparation: out [C][R] = in [R][C]^T (float32), and the packed
 // uniform grid of a float32 weight [N][K] (qweight, scale, zero in the

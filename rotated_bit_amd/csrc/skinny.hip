@@ -29,6 +29,7 @@
 // 0..7, so the result is bitwise reproducible.
 #include "launch.hpp"
 #include "unpack.hpp"
+#include "validate.hpp"
 
 namespace harp {
 namespace {
@@ -104,14 +105,14 @@ __device__ __forceinline__ void split_bf16(const u32x4 (&f)[2], u32x4& hi, u32x4
 template <int BITS, int MB, bool XF32>
 __device__ __forceinline__ void mma_group(const ARegs<MB, XF32>& r, const uint32_t (&w)[2 * BITS],
                                           uint32_t sz, int lane, uint16_t (*xs)[16][kXsRow],
-                                          floatx4_t (&acc)[MB]) {
+                                          uint32_t base, floatx4_t (&acc)[MB]) {
   const int c = lane >> 4;
   constexpr uint32_t kOnes = 0x3f803f80u;    // two bf16 1.0
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{kOnes, kOnes, kOnes, kOnes});
   bf16x8 b[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
-    b[h] = __builtin_bit_cast(bf16x8, chunk8_bf16_unit<BITS>(chunk8<BITS>(w, h, c)));
+    b[h] = __builtin_bit_cast(bf16x8, chunk8_bf16_unit<BITS>(chunk8<BITS>(w, h, c), base));
   floatx4_t t[MB], sx[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -199,6 +200,8 @@ __global__ __launch_bounds__(kThreadsS) void skinny_kernel(
   floatx4_t acc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  uint32_t base = 0x3f803f80u;   // two bf16 1.0, kept in a register
+  asm volatile("" : "+v"(base));
 
   // This wave's groups [gb, ge), in blocks of kBlk.  The codes and scales of
   // block b+1 are in flight while block b is multiplied; the x~ of the next
@@ -230,7 +233,7 @@ __global__ __launch_bounds__(kThreadsS) void skinny_kernel(
       const uint32_t* src = &cl[buf][lane & 15][j * NW];
 #pragma unroll
       for (int i = 0; i < NW; ++i) w[i] = src[i];
-      mma_group<BITS, MB, XF32>(r, w, szl[buf][lane & 15][j], lane, xs, acc);
+      mma_group<BITS, MB, XF32>(r, w, szl[buf][lane & 15][j], lane, xs, base, acc);
     };
     auto load = [&](ARegs<MB, XF32>& r, int g) {
       load_a<MB, XF32>(r, min(g, ge - 1), arow, lane);
@@ -352,14 +355,29 @@ hipError_t launch_any(const harp_qweight& W, const void* xt, float* yt, int M,
 
 hipError_t launch_gemm_skinny(const harp_qweight& W, const uint16_t* xt, float* yt,
                               int M, hipStream_t stream) {
-  if (skinny_wide_supported(W, M)) return launch_skinny_wide(W, xt, false, yt, M, stream);
+  const WideSplit w = skinny_wide_split(M, W.N, W.K, false);
+  if (w.fb > 0) return launch_skinny_wide(W, xt, 0, yt, M, w.fb, 1, nullptr, nullptr, stream);
   return launch_any<false>(W, xt, yt, M, stream);
 }
 
 hipError_t launch_gemm_skinny_split(const harp_qweight& W, const float* xt, float* yt,
                                     int M, hipStream_t stream) {
-  if (skinny_wide_supported(W, M)) return launch_skinny_wide(W, xt, true, yt, M, stream);
+  const WideSplit w = skinny_wide_split(M, W.N, W.K, false);
+  if (w.fb > 0) return launch_skinny_wide(W, xt, 1, yt, M, w.fb, 1, nullptr, nullptr, stream);
   return launch_any<true>(W, xt, yt, M, stream);
+}
+
+hipError_t launch_gemm_skinny_split_k(const harp_qweight& W, const float* xt, float* yt,
+                                      int M, float* partials, uint32_t* counters,
+                                      hipStream_t stream) {
+  const WideSplit w = skinny_wide_split(M, W.N, W.K, true);
+  if (w.fb == 0) return launch_any<true>(W, xt, yt, M, stream);
+  // x~ is the caller's workspace here: split it once, in place, instead of
+  // in every strip's workgroup
+  const hipError_t e =
+      launch_split_chunks(const_cast<float*>(xt), static_cast<size_t>(M) * W.K, stream);
+  if (e != hipSuccess) return e;
+  return launch_skinny_wide(W, xt, 2, yt, M, w.fb, w.splits, partials, counters, stream);
 }
 
 }  // namespace harp

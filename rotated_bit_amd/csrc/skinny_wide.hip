@@ -26,6 +26,7 @@
 // in wave order 0..7, so the result is bitwise reproducible.
 #include "launch.hpp"
 #include "unpack.hpp"
+#include "validate.hpp"
 
 namespace harp {
 namespace {
@@ -72,11 +73,16 @@ __device__ __forceinline__ void split_planes(const u32x4 (&f)[2], u32x4& hi, u32
   }
 }
 
-template <int BITS, int MB, bool XF32, int FB>
+// XIN: 0 bf16 x~; 1 float32 x~, split here; 2 float32 x~ already split in
+// place by split_chunks_kernel (each 8-element chunk as 8 bf16 hi values,
+// then 8 bf16 lo values: the same 32 bytes).
+template <int BITS, int MB, int XIN, int FB>
 __global__ __launch_bounds__(kThreadsW) void skinny_wide_kernel(
     const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
     const uint16_t* __restrict__ zr, const void* __restrict__ xt,
-    float* __restrict__ yt, int N, int K, int M) {
+    float* __restrict__ yt, int N, int K, int M, float* __restrict__ partials,
+    uint32_t* __restrict__ counters) {
+  constexpr bool XF32 = XIN != 0;
   using L = WaveLds<MB, XF32, FB>;
   constexpr int P = L::P;
   constexpr int NW = 2 * BITS;
@@ -127,9 +133,13 @@ __global__ __launch_bounds__(kThreadsW) void skinny_wide_kernel(
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[fb][mb] = floatx4_w{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // This wave's groups: [gb, gb + cnt), cnt a multiple of kSzBlkW.
-  const int cnt = G / kWavesW;
-  const int gb = wave * cnt;
+  // This workgroup's K slice (blockIdx.z of gridDim.z, each a multiple of
+  // 64 groups) and this wave's groups in it: [gb, gb + cnt), cnt a
+  // multiple of kSzBlkW.
+  const int S = gridDim.z;
+  const int z = blockIdx.z;
+  const int cnt = G / S / kWavesW;
+  const int gb = z * (G / S) + wave * cnt;
   const int nblk = cnt / kSzBlkW;
 
   auto load_a = [&](WARegs<MB, XF32>& r, int g) {
@@ -165,6 +175,8 @@ __global__ __launch_bounds__(kThreadsW) void skinny_wide_kernel(
 
   constexpr uint32_t kOnes = 0x3f803f80u;   // two bf16 1.0
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{kOnes, kOnes, kOnes, kOnes});
+  uint32_t base = kOnes;   // kept in a register (one AND-OR per operand word)
+  asm volatile("" : "+v"(base));
 
   // One group (slot j of block buffer buf): x~ planes to LDS, fragments,
   // S once, then T and the scaled update for every feature block.
@@ -175,7 +187,12 @@ __global__ __launch_bounds__(kThreadsW) void skinny_wide_kernel(
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        if constexpr (XF32) {
+        if constexpr (XIN == 2) {
+          *reinterpret_cast<u32x4*>(&ld.xs[0][mb][8 * i + (lane >> 3)][8 * (lane & 7)]) =
+              r.a[mb][i][0];
+          *reinterpret_cast<u32x4*>(&ld.xs[1][mb][8 * i + (lane >> 3)][8 * (lane & 7)]) =
+              r.a[mb][i][1];
+        } else if constexpr (XF32) {
           u32x4 hi, lo;
           split_planes(r.a[mb][i], hi, lo);
           *reinterpret_cast<u32x4*>(&ld.xs[0][mb][8 * i + (lane >> 3)][8 * (lane & 7)]) = hi;
@@ -208,7 +225,7 @@ __global__ __launch_bounds__(kThreadsW) void skinny_wide_kernel(
       bf16x8 b[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        b[h] = __builtin_bit_cast(bf16x8, chunk8_bf16_unit<BITS>(chunk8<BITS>(cr.w[fb], h, c)));
+        b[h] = __builtin_bit_cast(bf16x8, chunk8_bf16_unit<BITS>(chunk8<BITS>(cr.w[fb], h, c), base));
       floatx4_w t[MB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -271,72 +288,149 @@ __global__ __launch_bounds__(kThreadsW) void skinny_wide_kernel(
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) red[wave][fb][mb][lane] = acc[fb][mb];
   __syncthreads();
-  for (int slot = tid; slot < FB * MB * kWave * 4; slot += kThreadsW) {
+  constexpr int kSlots = FB * MB * kWave * 4;
+  constexpr int kPerThread = (kSlots + kThreadsW - 1) / kThreadsW;
+  float sum[kPerThread];
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const int slot = tid + k * kThreadsW;
+    sum[k] = 0.0f;
+    if (slot < kSlots) {
+      const int v = slot & 3;
+      const int l = (slot >> 2) & (kWave - 1);
+      const int mb = (slot >> 8) % MB;
+      const int fb = (slot >> 8) / MB;
+#pragma unroll
+      for (int w = 0; w < kWavesW; ++w) sum[k] += red[w][fb][mb][l][v];
+    }
+  }
+  auto out_index = [&](int slot, int& m, int& nn) {
     const int v = slot & 3;
     const int l = (slot >> 2) & (kWave - 1);
     const int mb = (slot >> 8) % MB;
     const int fb = (slot >> 8) / MB;
-    float sum = 0.0f;
+    m = m0 + 16 * mb + 4 * (l >> 4) + v;
+    nn = n0 + 16 * fb + (l & 15);
+  };
+  if (S > 1) {
+    // Split K: every slice writes its partial strip (device-coherent
+    // stores, acknowledged before the arrival is counted); the last slice
+    // to arrive adds all S partials in slice order 0..S-1, so the result
+    // does not depend on arrival order, and resets the tile's counter.
+    __shared__ uint32_t last_flag;
+    const size_t plane = static_cast<size_t>(M) * N;
 #pragma unroll
-    for (int w = 0; w < kWavesW; ++w) sum += red[w][fb][mb][l][v];
-    const int m = m0 + 16 * mb + 4 * (l >> 4) + v;
-    const int nn = n0 + 16 * fb + (l & 15);
-    if (m < M && nn < N) yt[static_cast<size_t>(m) * N + nn] = sum;
+    for (int k = 0; k < kPerThread; ++k) {
+      const int slot = tid + k * kThreadsW;
+      int m, nn;
+      out_index(slot, m, nn);
+      if (slot < kSlots && m < M && nn < N)
+        __hip_atomic_store(&partials[z * plane + static_cast<size_t>(m) * N + nn], sum[k],
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int tile = blockIdx.y * gridDim.x + blockIdx.x;
+    if (tid == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      last_flag = prev == static_cast<uint32_t>(S - 1);
+    }
+    __syncthreads();
+    if (!last_flag) return;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+      const int slot = tid + k * kThreadsW;
+      int m, nn;
+      out_index(slot, m, nn);
+      if (slot < kSlots && m < M && nn < N) {
+        float t = 0.0f;
+        for (int zz = 0; zz < S; ++zz) {
+          const float part = __hip_atomic_load(
+              &partials[zz * plane + static_cast<size_t>(m) * N + nn], __ATOMIC_RELAXED,
+              __HIP_MEMORY_SCOPE_AGENT);
+          t = zz == 0 ? part : t + part;
+        }
+        sum[k] = t;
+      }
+    }
+    if (tid == 0)
+      __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const int slot = tid + k * kThreadsW;
+    int m, nn;
+    out_index(slot, m, nn);
+    if (slot < kSlots && m < M && nn < N) yt[static_cast<size_t>(m) * N + nn] = sum[k];
   }
 }
 
-template <int BITS, int MB, bool XF32, int FB>
-hipError_t launch_w(const harp_qweight& W, const void* xt, float* yt, int M,
-                    hipStream_t stream) {
-  const dim3 grid((W.N + 16 * FB - 1) / (16 * FB), (M + 16 * MB - 1) / (16 * MB));
-  hipLaunchKernelGGL((skinny_wide_kernel<BITS, MB, XF32, FB>), grid, dim3(kThreadsW), 0, stream,
-                     W.qweight, W.scale, W.zero, xt, yt, W.N, W.K, M);
+template <int BITS, int MB, int XIN, int FB>
+hipError_t launch_w(const harp_qweight& W, const void* xt, float* yt, int M, int S,
+                    float* partials, uint32_t* counters, hipStream_t stream) {
+  const dim3 grid((W.N + 16 * FB - 1) / (16 * FB), (M + 16 * MB - 1) / (16 * MB), S);
+  hipLaunchKernelGGL((skinny_wide_kernel<BITS, MB, XIN, FB>), grid, dim3(kThreadsW), 0, stream,
+                     W.qweight, W.scale, W.zero, xt, yt, W.N, W.K, M, partials, counters);
   return hipGetLastError();
 }
 
-template <int BITS, bool XF32, int FB>
-hipError_t launch_fb(const harp_qweight& W, const void* xt, float* yt, int M,
-                     hipStream_t stream) {
+template <int BITS, int XIN, int FB>
+hipError_t launch_fb(const harp_qweight& W, const void* xt, float* yt, int M, int S,
+                     float* partials, uint32_t* counters, hipStream_t stream) {
   // up to 16 rows in one 16-row block, more in tiles of 32 rows
-  return M <= 16 ? launch_w<BITS, 1, XF32, FB>(W, xt, yt, M, stream)
-                 : launch_w<BITS, 2, XF32, FB>(W, xt, yt, M, stream);
+  return M <= 16 ? launch_w<BITS, 1, XIN, FB>(W, xt, yt, M, S, partials, counters, stream)
+                 : launch_w<BITS, 2, XIN, FB>(W, xt, yt, M, S, partials, counters, stream);
 }
 
-template <int BITS, bool XF32>
-hipError_t launch_bits_w(const harp_qweight& W, const void* xt, float* yt, int M,
-                         hipStream_t stream) {
-  return skinny_wide_blocks(W.N) >= 4 ? launch_fb<BITS, XF32, 4>(W, xt, yt, M, stream)
-                                      : launch_fb<BITS, XF32, 2>(W, xt, yt, M, stream);
+template <int BITS, int XIN>
+hipError_t launch_bits_w(const harp_qweight& W, const void* xt, float* yt, int M, int fb,
+                         int S, float* partials, uint32_t* counters, hipStream_t stream) {
+  return fb == 4 ? launch_fb<BITS, XIN, 4>(W, xt, yt, M, S, partials, counters, stream)
+                 : launch_fb<BITS, XIN, 2>(W, xt, yt, M, S, partials, counters, stream);
+}
+
+// In place: each 8-element chunk of float32 x~ becomes 8 bf16 hi =
+// bf16(x) and then 8 bf16 lo = bf16(x - hi) (nearest even; x - hi exact), in
+// the chunk's own 32 bytes, so that the product loads both planes of a
+// chunk with the loads it would use for the float32 values.
+__global__ __launch_bounds__(256) void split_chunks_kernel(float* __restrict__ xt, size_t chunks) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= chunks) return;
+  u32x4* p = reinterpret_cast<u32x4*>(xt + 8 * i);
+  const u32x4 f[2] = {p[0], p[1]};
+  u32x4 hi, lo;
+  split_planes(f, hi, lo);
+  p[0] = hi;
+  p[1] = lo;
 }
 
 }  // namespace
 
-// Feature blocks per wave for N output features (0: use the 16-feature
-// kernel): as many as keep at least one workgroup per CU (256), at most 4.
-int skinny_wide_blocks(int N) {
-  const int blocks = N / 16;
-  if (blocks >= 4 * 256) return 4;
-  if (blocks >= 2 * 256) return 2;
-  return 0;
-}
-
-bool skinny_wide_supported(const harp_qweight& W, int M) {
-  return M >= 1 && M <= 64 && W.K % (kGroup * kWavesW * kSzBlkW) == 0 &&
-         skinny_wide_blocks(W.N) > 0;
-}
-
-hipError_t launch_skinny_wide(const harp_qweight& W, const void* xt, bool xf32, float* yt,
-                              int M, hipStream_t stream) {
-  if (!skinny_wide_supported(W, M)) return hipErrorInvalidValue;
+hipError_t launch_skinny_wide(const harp_qweight& W, const void* xt, int xin, float* yt,
+                              int M, int fb, int splits, float* partials, uint32_t* counters,
+                              hipStream_t stream) {
+  if ((fb != 2 && fb != 4) || splits < 1 || xin < 0 || xin > 2 ||
+      W.K % (kGroup * kWavesW * kSzBlkW * splits) != 0 ||
+      (splits > 1 && (partials == nullptr || counters == nullptr)))
+    return hipErrorInvalidValue;
+#define HARP_W(B, X) launch_bits_w<B, X>(W, xt, yt, M, fb, splits, partials, counters, stream)
   switch (W.bits) {
-    case 2: return xf32 ? launch_bits_w<2, true>(W, xt, yt, M, stream)
-                        : launch_bits_w<2, false>(W, xt, yt, M, stream);
-    case 3: return xf32 ? launch_bits_w<3, true>(W, xt, yt, M, stream)
-                        : launch_bits_w<3, false>(W, xt, yt, M, stream);
-    case 4: return xf32 ? launch_bits_w<4, true>(W, xt, yt, M, stream)
-                        : launch_bits_w<4, false>(W, xt, yt, M, stream);
+    case 2: return xin == 0 ? HARP_W(2, 0) : xin == 1 ? HARP_W(2, 1) : HARP_W(2, 2);
+    case 3: return xin == 0 ? HARP_W(3, 0) : xin == 1 ? HARP_W(3, 1) : HARP_W(3, 2);
+    case 4: return xin == 0 ? HARP_W(4, 0) : xin == 1 ? HARP_W(4, 1) : HARP_W(4, 2);
     default: return hipErrorInvalidValue;
   }
+#undef HARP_W
+}
+
+hipError_t launch_split_chunks(float* xt, size_t n, hipStream_t stream) {
+  if (n % 8 != 0) return hipErrorInvalidValue;
+  const size_t chunks = n / 8;
+  if (chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(split_chunks_kernel, dim3(static_cast<unsigned>((chunks + 255) / 256)),
+                     dim3(256), 0, stream, xt, chunks);
+  return hipGetLastError();
 }
 
 }  // namespace harp

@@ -196,9 +196,12 @@ __device__ __forceinline__ void chunk8_codes(uint32_t v, float (&q)[8]) {
 // (Codes in the top bits rather than the bottom ones keep the constant part
 // of the operand small against the code part, 2^BITS : q instead of 128 : q,
 // which is what the per-group sum T - (1 + z / 2^BITS) S cancels.)
+// base: two bf16 1.0 (0x3f803f80) held in a register by the caller, so
+// that mask and OR fuse into one AND-OR per word (an instruction takes at
+// most one literal).
 template <int BITS>
-__device__ __forceinline__ u32x4 chunk8_bf16_unit(uint32_t v) {
-  constexpr uint32_t kBase = 0x3f803f80u;
+__device__ __forceinline__ u32x4 chunk8_bf16_unit(uint32_t v, uint32_t base) {
+  const uint32_t kBase = base;
   constexpr int kTop = 7 - BITS;             // bit of the code's LSB in a half
   u32x4 out;
   if constexpr (BITS == 2) {

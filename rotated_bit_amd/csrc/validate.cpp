@@ -284,6 +284,29 @@ int32_t gemm_splits(int32_t M, int32_t N, int32_t K) {
   return best;
 }
 
+WideSplit skinny_wide_split(int32_t M, int32_t N, int32_t K, bool allow_split) {
+  WideSplit r{0, 1};
+  if (M < 1 || M > kSkinnyMaxM || N < 1 || K < 4096 || K % 4096 != 0) return r;
+  const int32_t G = K / 64;
+  const int64_t row_tiles = M <= 16 ? 1 : (M + 31) / 32;   // 16-row, else 32-row tiles
+  const int64_t tiles4 = (N + 63) / 64;
+  const int64_t tiles2 = (N + 31) / 32;
+  if (tiles4 >= kGemmSlots) return WideSplit{4, 1};
+  if (allow_split && tiles4 * row_tiles <= kGemmMaxSplitTiles) {
+    for (int32_t s = 2; s <= 8; ++s)
+      if (G % (64 * s) == 0 && tiles4 * s >= kGemmSlots) return WideSplit{4, s};
+  }
+  if (tiles2 >= kGemmSlots) return WideSplit{2, 1};
+  return r;
+}
+
+size_t skinny_partial_bytes(int32_t M, int32_t N, int32_t K) {
+  if (M < kSplitMinM || M >= kBf16MinM) return 0;   // the fused linear's split range
+  const WideSplit w = skinny_wide_split(M, N, K, true);
+  if (w.splits <= 1) return 0;
+  return align256(static_cast<size_t>(w.splits) * M * N * 4);
+}
+
 size_t gemm_partial_bytes(int32_t M, int32_t N, int32_t K) {
   const int32_t s = gemm_splits(M, N, K);
   if (s <= 1) return 0;
@@ -314,7 +337,8 @@ size_t workspace_bytes(int32_t M, int32_t N, int32_t K) {
       K > HARP_MAX_DIM)
     return 0;
   if (M == 0) return 0;
-  return workspace_gemm_offset(M, N, K) + gemm_partial_bytes(M, N, K);
+  return workspace_gemm_offset(M, N, K) + gemm_partial_bytes(M, N, K) +
+         skinny_partial_bytes(M, N, K);
 }
 
 size_t chain_ws_bytes(int32_t dim) { return chain_workspace_bytes(dim); }

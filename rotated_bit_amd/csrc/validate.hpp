@@ -54,6 +54,21 @@ constexpr int32_t kGemmMaxSplits = 4;
 constexpr int32_t kGemmMaxSplitTiles = 512;
 constexpr size_t kGemmCounterBytes = 2048;   // >= 4 * kGemmMaxSplitTiles, 256-aligned
 int32_t gemm_splits(int32_t M, int32_t N, int32_t K);
+
+// Small-batch product on wide strips (skinny_wide.hip): feature blocks of
+// 16 per wave (2 or 4) and K slices.  Eligible when K is a multiple of 4096
+// (every wave a whole number of eight-group blocks) and enough strips fill
+// the chip.  With split K allowed (the fused linear's workspace) four blocks
+// per wave read x~ half as often as two, and the K slices (each a multiple
+// of 64 groups, at most 8) restore at least kGemmSlots workgroups; the
+// slices' float32 partials follow y' in the workspace and use the GEMM's
+// arrival counters.  fb == 0: the 16-feature kernel runs.
+struct WideSplit {
+  int32_t fb;
+  int32_t splits;
+};
+WideSplit skinny_wide_split(int32_t M, int32_t N, int32_t K, bool allow_split);
+size_t skinny_partial_bytes(int32_t M, int32_t N, int32_t K);
 size_t gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
 size_t gemm_partial_bytes(int32_t M, int32_t N, int32_t K);
 
