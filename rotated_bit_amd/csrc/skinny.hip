@@ -367,13 +367,18 @@ hipError_t launch_gemm_skinny_split(const harp_qweight& W, const float* xt, floa
   return launch_any<true>(W, xt, yt, M, stream);
 }
 
+constexpr size_t kPresplitMinElems = size_t{1} << 17;
+
 hipError_t launch_gemm_skinny_split_k(const harp_qweight& W, const float* xt, float* yt,
                                       int M, float* partials, uint32_t* counters,
                                       hipStream_t stream) {
   const WideSplit w = skinny_wide_split(M, W.N, W.K, true);
   if (w.fb == 0) return launch_any<true>(W, xt, yt, M, stream);
   // x~ is the caller's workspace here: split it once, in place, instead of
-  // in every strip's workgroup
+  // in every strip's workgroup, where that saves more than the extra launch
+  // (measured: not at 16 x 4096)
+  if (static_cast<size_t>(M) * W.K < kPresplitMinElems)
+    return launch_skinny_wide(W, xt, 1, yt, M, w.fb, w.splits, partials, counters, stream);
   const hipError_t e =
       launch_split_chunks(const_cast<float*>(xt), static_cast<size_t>(M) * W.K, stream);
   if (e != hipSuccess) return e;
