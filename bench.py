@@ -52,7 +52,7 @@ DISTINCT = 4                     # seeded instances per cell; the rest are copie
 # WRITE_SIZE, each scaled by what the counter reads for a 256 MiB device
 # copy); None for a kernel changed since its counters were taken.
 TRAFFIC_BYTES = {
-    "chain_kernel_4096_2bit_M1_32layers": 220930764,   # FETCH 106916.2 KiB, WRITE 1920.3 KiB
+    "chain_kernel_4096_2bit_M1_32layers": None,        # changed since its counters were taken
     "rotate_in_deq_gemv_2bit": 7009280,                # FETCH 3414.5 KiB, WRITE 16.0 KiB
     "rotate_out_b4096": 590848,                        # FETCH 280.5 KiB, WRITE 16.0 KiB
 }

@@ -12,21 +12,23 @@
 // workgroup-to-workgroup handoffs (~0.5 us per flag) instead of launches.
 //
 // Work per layer l (roles by position in the 1-D grid):
-//   product (D / 16 workgroups): 16 output features each.  Before waiting,
+//   product (D / 16 workgroups): 16 output features each, the eight
+//        features q + j D/8 (j = 0..7) of two residues q, which are exactly
+//        the ones that F_U^T's widest three stages mix.  Before waiting,
 //        load the features' packed weights and the (cos, sin) pairs of the
-//        last three input stages.  Then wait for z_l (the input after its
-//        sign flip and first log2(D) - 3 stages), apply the last three stages
-//        (strides D/8, D/4, D/2; each thread owns one residue q < D/8 and its
-//        eight elements q + j D/8) into LDS, and form the float32 product
-//        y'_l for its features as the decode GEMV does (lane = quantization
-//        group, s (sum q x~ - z sum x~) per group).
+//        last three input stages and the first three output stages.  Then
+//        wait for z_l (the input after its sign flip and first log2(D) - 3
+//        stages), apply the last three stages (strides D/8, D/4, D/2; each
+//        thread owns one residue q < D/8 and its eight elements q + j D/8)
+//        into LDS, form the float32 product y'_l for its features as the
+//        decode GEMV does (lane = quantization group, s (sum q x~ - z sum x~)
+//        per group), and apply F_U^T's widest three stages to its 16 values
+//        across lanes: the value at q + j D/8 goes to sub-block j.
 //   rotation (8 roles per row): sub-block w = 0..7 of D/8 features.  Wait
-//        for all of y'_l, apply F_U^T's widest three stages only along the
-//        paths that end in sub-block w (seven butterflies per residue), then
-//        the sub-block's other stages and the sign flip: y_l[w-th eighth],
+//        for the sub-block's D/8 values, apply F_U^T's other stages (they
+//        never leave a sub-block) and the sign flip: y_l[w-th eighth],
 //        stored as the layer's output.  Then, on the same eighth, the next
-//        layer's input sign flip and first log2(D) - 3 stages (they never
-//        leave a sub-block): z_{l+1}.
+//        layer's input sign flip and first log2(D) - 3 stages: z_{l+1}.
 // The first 8 M product workgroups of layer l + 1 run layer l's rotation
 // roles before their own product (their weights are already in flight);
 // separate rotation workgroups exist only for x -> z_0 and for the last
@@ -44,9 +46,10 @@
 // device-coherent (sc1, write-through) stores and loads.  z: each rotation
 // role waits for the acknowledgement of its stores (vmcnt(0)), then stores
 // its flag in 16 copies; the product workgroups poll one copy, then load.
-// y': every value leaves as a (value, epoch) pair in one 8-byte store, and
-// the rotation roles poll the values themselves (no acknowledgement wait and
-// no flag on that side).  Flags and tags hold the launch's epoch (workspace
+// y' (after F_U^T's widest three stages): every value leaves as a (value,
+// epoch) pair in one 8-byte store, and each rotation role polls its D/8
+// values themselves, one pair per residue (no acknowledgement wait and no
+// flag on that side).  Flags and tags hold the launch's epoch (workspace
 // word 0, plus one), so nothing needs resetting: the last workgroup to end
 // advances the epoch for the next launch.  Every wait is bounded: a wait that
 // runs out records an error in workspace word 1 and ends its workgroup, so
@@ -101,15 +104,12 @@ __device__ __forceinline__ void bfly(float& a, float& b, float2 cs) {
   b = fmaf(cs.y, x, -(cs.x * y));
 }
 
-// a where mask is all ones, else b; the mask passes an empty asm so that the
-// selects stay selects between registers
-__device__ __forceinline__ float bsel(uint32_t mask, float a, float b) {
-  return __uint_as_float((mask & __float_as_uint(a)) | (~mask & __float_as_uint(b)));
-}
-__device__ __forceinline__ uint32_t maskof(bool c) {
-  uint32_t m = c ? 0xffffffffu : 0u;
-  asm volatile("" : "+v"(m));
-  return m;
+// One output of a butterfly whose two inputs sit in lanes `bit` apart: the
+// lane with `bit` clear holds the first input and keeps the first output (the
+// same arithmetic as bfly).
+__device__ __forceinline__ float bfly_lane(float v, int bit, bool high, float2 cs) {
+  const float w = shfl_xor(v, bit);
+  return high ? fmaf(cs.y, w, -(cs.x * v)) : fmaf(cs.x, v, cs.y * w);
 }
 
 // ---- device-coherent memory operations ------------------------------------
@@ -150,36 +150,38 @@ __device__ __forceinline__ void st_pair_sc1(u32x2 *p, float v, uint32_t tag) {
   d[1] = tag;
   asm volatile("global_store_dwordx2 %0, %1, off sc1" ::"v"(p), "v"(d) : "memory");
 }
-// Eight device-coherent pair loads p[0], p[s], ..., p[7 s], waited for inside
-// the asm block.
-__device__ __forceinline__ void ld8_pair_sc1(const u32x2* p, int s, u32x2 (&v)[8]) {
-  u32x2 r0, r1, r2, r3, r4, r5, r6, r7;
-  asm volatile(
-      "global_load_dwordx2 %0, %8, off sc1\n\t"
-      "global_load_dwordx2 %1, %9, off sc1\n\t"
-      "global_load_dwordx2 %2, %10, off sc1\n\t"
-      "global_load_dwordx2 %3, %11, off sc1\n\t"
-      "global_load_dwordx2 %4, %12, off sc1\n\t"
-      "global_load_dwordx2 %5, %13, off sc1\n\t"
-      "global_load_dwordx2 %6, %14, off sc1\n\t"
-      "global_load_dwordx2 %7, %15, off sc1\n\t"
-      "s_waitcnt vmcnt(0)"
-      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
-      : "v"(p), "v"(p + s), "v"(p + 2 * s), "v"(p + 3 * s), "v"(p + 4 * s), "v"(p + 5 * s),
-        "v"(p + 6 * s), "v"(p + 7 * s)
-      : "memory");
-  v[0] = r0; v[1] = r1; v[2] = r2; v[3] = r3; v[4] = r4; v[5] = r5; v[6] = r6; v[7] = r7;
+// N (1 or 2) device-coherent pair loads p[0], p[s], waited for inside the
+// asm block.
+template <int N>
+__device__ __forceinline__ void ld_pairs_sc1(const u32x2* p, int s, u32x2 (&v)[N]) {
+  static_assert(N == 1 || N == 2, "one or two pairs");
+  if constexpr (N == 1) {
+    u32x2 r0;
+    asm volatile("global_load_dwordx2 %0, %1, off sc1\n\ts_waitcnt vmcnt(0)"
+                 : "=&v"(r0) : "v"(p) : "memory");
+    v[0] = r0;
+  } else {
+    u32x2 r0, r1;
+    asm volatile(
+        "global_load_dwordx2 %0, %2, off sc1\n\t"
+        "global_load_dwordx2 %1, %3, off sc1\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(r0), "=&v"(r1) : "v"(p), "v"(p + s) : "memory");
+    v[0] = r0;
+    v[1] = r1;
+  }
 }
-// Polls p[0], p[s], ..., p[7 s] until every tag of the wave's loads holds
+// Polls p[0], p[s] (N of them) until every tag of the wave's loads holds
 // `tag`; the values in v.  False if the wait ran out.
-__device__ __forceinline__ bool poll8_pairs(const u32x2* p, int s, uint32_t tag, float (&v)[8]) {
+template <int N>
+__device__ __forceinline__ bool poll_pairs(const u32x2* p, int s, uint32_t tag, float (&v)[N]) {
   int spins = 0;
   while (true) {
-    u32x2 r[8];
-    ld8_pair_sc1(p, s, r);
+    u32x2 r[N];
+    ld_pairs_sc1<N>(p, s, r);
     bool mine = true;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < N; ++j) {
       mine = mine && r[j][1] == tag;
       v[j] = __uint_as_float(r[j][0]);
     }
@@ -283,21 +285,7 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(ChainArgs a) {
     float2 hb[kCoefLds ? 1 : LB][4];
     float2* coefl = reinterpret_cast<float2*>(smem + BB) +
                     static_cast<size_t>((uthr ? 0 : TB) + tp) * LB * 4;
-    float2 h2[QPT][4], h1[QPT][2], h0[QPT];
     uint32_t sbits = 0;
-    const int half = wsub & 4;
-    if (has_u) {
-      const float2* cs = a.layer[rl].cs_u;
-  #pragma unroll
-      for (int qi = 0; qi < QPT; ++qi) {
-        const int q = tid + kThreadsC * qi;
-  #pragma unroll
-        for (int p = 0; p < 4; ++p) h2[qi][p] = cs[cu(LOG - 1, q + BB * p)];
-  #pragma unroll
-        for (int mm = 0; mm < 2; ++mm) h1[qi][mm] = cs[cu(LOG - 2, q + BB * (half + mm))];
-        h0[qi] = cs[cu(LOG - 3, q + BB * (wsub & 6))];
-      }
-    }
     if ((uthr && has_u) || (vthr && has_v)) {
       const ChainLayer& Ls = a.layer[uthr ? rl : rl + 1];
       const float2* cs = uthr ? Ls.cs_u : Ls.cs_v;
@@ -322,33 +310,108 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(ChainArgs a) {
       const int g0 = wsub * BB + tp * 8;
       sbits = sg[g0 >> 5] >> (g0 & 31);
     }
-    auto pair = [&](int st, int p) -> float2 {
-      if constexpr (kCoefLds) return coefl[st * 4 + p];
+    // Both sides on the same wave (4096-wide layers: a side's rounds take one
+    // wave and the coefficients of both sides sit in LDS): F_U^T's last
+    // round and F_V's first one cover the same elements per thread, so they
+    // run back to back in registers.  Otherwise F_U^T on the first TB
+    // threads and F_V on the next TB.
+    constexpr bool kFuse = kCoefLds && TB <= kWave;
+    static_assert(kFuse || !kCoefLds, "LDS-staged coefficients come with one-wave rounds");
+    uint32_t vbits = sbits;
+    if constexpr (kFuse) {
+      if (uthr && has_v) {
+        const int g0 = wsub * BB + tp * 8;
+        vbits = a.layer[rl + 1].sign_v[g0 >> 5] >> (g0 & 31);
+      }
+    }
+    const float2* coef_u = reinterpret_cast<const float2*>(smem + BB) +
+                           static_cast<size_t>(tp) * LB * 4;
+    const float2* coef_v = coef_u + static_cast<size_t>(kFuse ? TB : 0) * LB * 4;
+    auto pair_u = [&](int st, int p) -> float2 {
+      if constexpr (kCoefLds) return coef_u[st * 4 + p];
       else return hb[st][p];
     };
-    // 2. the input of this sub-block: F_U^T's widest three stages on y'_l,
-    //    or the chain input x for the first phase
+    auto pair_v = [&](int st, int p) -> float2 {
+      if constexpr (kCoefLds) return coef_v[st * 4 + p];
+      else return hb[st][p];
+    };
+    auto load8 = [&](int r, float (&v)[8]) {
+  #pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = u[elem_index8(tp, j, 3 * r, round_w(r, LB))];
+    };
+    auto store8 = [&](int r, const float (&v)[8]) {
+  #pragma unroll
+      for (int j = 0; j < 8; ++j) u[elem_index8(tp, j, 3 * r, round_w(r, LB))] = v[j];
+    };
+    // F_U^T's stages of round r (descending)
+    auto u_stages = [&](int r, float (&v)[8]) {
+      const int s0 = 3 * r;
+      const int R = round_w(r, LB);
+  #pragma unroll
+      for (int kk = 0; kk < 3; ++kk) {
+        const int k = 2 - kk;
+        if (k < R) {
+  #pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const int j1 = zero_bit(p, k);
+            bfly(v[j1], v[j1 | (1 << k)], pair_u(s0 + k, p));
+          }
+        }
+      }
+    };
+    // after round 0: the sign flip and the layer output y_rl (contiguous
+    // elements 8 tp .. 8 tp + 7); the value kept is the stored one
+    auto u_out = [&](float (&v)[8]) {
+  #pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = flip_sign(v[j], (sbits >> j) & 1u);
+      const size_t off = static_cast<size_t>(m) * D + wsub * BB + tp * 8;
+      if (a.y_bf16) {
+        u32x4 pk;
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) pk[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.layer[rl].y) + off) = pk;
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[2 * j] = __uint_as_float(pk[j] << 16);
+          v[2 * j + 1] = __uint_as_float(pk[j] & 0xffff0000u);
+        }
+      } else {
+        float* yo = static_cast<float*>(a.layer[rl].y) + off;
+        *reinterpret_cast<float4*>(yo) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(yo + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    };
+    // the next layer's input sign flip (before round 0) and F_V's stages of
+    // round r (ascending)
+    auto v_stages = [&](int r, float (&v)[8]) {
+      const int s0 = 3 * r;
+      const int R = round_w(r, LB);
+      if (r == 0) {
+  #pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = flip_sign(v[j], (vbits >> j) & 1u);
+      }
+  #pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        if (k < R) {
+  #pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const int j1 = zero_bit(p, k);
+            bfly(v[j1], v[j1 | (1 << k)], pair_v(s0 + k, p));
+          }
+        }
+      }
+    };
+    // 2. the input of this sub-block: y'_l after F_U^T's widest three
+    //    stages (applied by the product workgroups), or the chain input x
+    //    for the first phase
     int failed = 0;
     if (has_u) {
       const u32x2* yp = ypbuf + (static_cast<size_t>(rl) * kChainMaxM + m) * D;
-      const uint32_t m4 = maskof(wsub & 4), m2 = maskof(wsub & 2), m1 = maskof(wsub & 1);
+      float v[QPT];
+      if (!poll_pairs<QPT>(yp + static_cast<size_t>(tid) * 8 + wsub, kThreadsC * 8, epoch, v))
+        failed = 1;
   #pragma unroll
-      for (int qi = 0; qi < QPT; ++qi) {
-        const int q = tid + kThreadsC * qi;
-        float v[8];
-        if (!poll8_pairs(yp + q, BB, epoch, v)) failed = 1;
-  #pragma unroll
-        for (int p = 0; p < 4; ++p) bfly(v[p], v[p | 4], h2[qi][p]);        // stride D/2
-        float y4[4];
-  #pragma unroll
-        for (int mm = 0; mm < 4; ++mm) y4[mm] = bsel(m4, v[4 + mm], v[mm]);
-        bfly(y4[0], y4[2], h1[qi][0]);                                      // stride D/4
-        bfly(y4[1], y4[3], h1[qi][1]);
-        float z0 = bsel(m2, y4[2], y4[0]);
-        float z1 = bsel(m2, y4[3], y4[1]);
-        bfly(z0, z1, h0[qi]);                                               // stride D/8
-        u[q] = bsel(m1, z1, z0);
-      }
+      for (int qi = 0; qi < QPT; ++qi) u[tid + kThreadsC * qi] = v[qi];
       if (failed && (tid & (kWave - 1)) == 0) st_flag(ctrl + 1, 1u);
     } else {
       for (int i = tid; i < BB; i += kThreadsC) {
@@ -358,109 +421,144 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(ChainArgs a) {
       }
     }
     if (__syncthreads_or(failed)) return false;
-    // 3. F_U^T's stages inside the sub-block (descending), the sign flip, the
-    //    rl output; the value kept for the next rl is the stored one
-    // One sub-block round per three stages; when the round's threads are a
-    // single wave (TB <= 64) only that wave's LDS order is needed between
-    // rounds, else a workgroup barrier.
-    constexpr bool kWaveRounds = TB <= kWave;
-    auto u_round = [&](int r) {
-      const int s0 = 3 * r;
-      const int R = round_w(r, LB);
-      float v[8];
+    if constexpr (kFuse) {
+      // 3-4. one wave: F_U^T's rounds (descending), the output, the next
+      //      layer's sign flip and F_V's rounds (ascending).  Each round's
+      //      (cos, sin) pairs are read from LDS during the round before, so
+      //      that a round waits only for its elements.
+      typedef float2 Coef[3][4];
+      auto load_c = [&](const float2* base, int r, Coef& c) {
   #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = u[elem_index8(tp, j, s0, R)];
+        for (int k = 0; k < 3; ++k)
+          if (k < round_w(r, LB))
   #pragma unroll
-      for (int kk = 0; kk < 3; ++kk) {
-        const int k = 2 - kk;
-        if (k < R) {
+            for (int p = 0; p < 4; ++p) c[k][p] = base[(3 * r + k) * 4 + p];
+      };
+      auto stages_c = [&](bool descending, int r, float (&v)[8], const Coef& c) {
+        const int R = round_w(r, LB);
   #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const int j1 = zero_bit(p, k);
-            bfly(v[j1], v[j1 | (1 << k)], pair(s0 + k, p));
+        for (int kk = 0; kk < 3; ++kk) {
+          const int k = descending ? 2 - kk : kk;
+          if (k < R) {
+  #pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const int j1 = zero_bit(p, k);
+              bfly(v[j1], v[j1 | (1 << k)], c[k][p]);
+            }
           }
         }
-      }
-      if (r == 0) {   // contiguous elements 8 tp .. 8 tp + 7
+      };
+      auto flip_v = [&](float (&v)[8]) {
   #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = flip_sign(v[j], (sbits >> j) & 1u);
-        const size_t off = static_cast<size_t>(m) * D + wsub * BB + tp * 8;
-        if (a.y_bf16) {
-          u32x4 pk;
+        for (int j = 0; j < 8; ++j) v[j] = flip_sign(v[j], (vbits >> j) & 1u);
+      };
+      if (uthr) {
+        float v[8];
+        Coef c, cn;
+        if (has_u) {
+          load_c(coef_u, NRB - 1, c);
   #pragma unroll
-          for (int j = 0; j < 4; ++j) pk[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
-          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.layer[rl].y) + off) = pk;
+          for (int qq = 0; qq + 1 < NRB; ++qq) {
+            const int r = NRB - 1 - qq;
+            load8(r, v);
+            load_c(coef_u, r - 1, cn);
+            stages_c(true, r, v, c);
+            store8(r, v);
   #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            v[2 * j] = __uint_as_float(pk[j] << 16);
-            v[2 * j + 1] = __uint_as_float(pk[j] & 0xffff0000u);
+            for (int k = 0; k < 3; ++k)
+  #pragma unroll
+              for (int p = 0; p < 4; ++p) c[k][p] = cn[k][p];
+            wave_sync();
           }
+          load8(0, v);
+          if (has_v) load_c(coef_v, 0, cn);
+          stages_c(true, 0, v, c);
+          u_out(v);
+          if (has_v) {
+            if (NRB > 1) load_c(coef_v, 1, c);
+            flip_v(v);
+            stages_c(false, 0, v, cn);
+          }
+          store8(0, v);
         } else {
-          float* yo = static_cast<float*>(a.layer[rl].y) + off;
-          *reinterpret_cast<float4*>(yo) = make_float4(v[0], v[1], v[2], v[3]);
-          *reinterpret_cast<float4*>(yo + 4) = make_float4(v[4], v[5], v[6], v[7]);
+          load8(0, v);
+          load_c(coef_v, 0, cn);
+          if (NRB > 1) load_c(coef_v, 1, c);
+          flip_v(v);
+          stages_c(false, 0, v, cn);
+          store8(0, v);
+        }
+        if (has_v) {
+  #pragma unroll
+          for (int r = 1; r < NRB; ++r) {
+            wave_sync();
+            load8(r, v);
+            if (r + 1 < NRB) load_c(coef_v, r + 1, cn);
+            stages_c(false, r, v, c);
+            store8(r, v);
+  #pragma unroll
+            for (int k = 0; k < 3; ++k)
+  #pragma unroll
+              for (int p = 0; p < 4; ++p) c[k][p] = cn[k][p];
+          }
         }
       }
+      __syncthreads();
+      if (!has_v) return true;
+    } else {
+      // 3. F_U^T's stages inside the sub-block (descending), the sign flip,
+      //    the rl output.  One sub-block round per three stages; when the
+      //    round's threads are a single wave (TB <= 64) only that wave's LDS
+      //    order is needed between rounds, else a workgroup barrier.
+      constexpr bool kWaveRounds = TB <= kWave;
+      auto u_round = [&](int r) {
+        float v[8];
+        load8(r, v);
+        u_stages(r, v);
+        if (r == 0) u_out(v);
+        store8(r, v);
+      };
+      if (has_u) {
+        if constexpr (kWaveRounds) {
+          if (uthr) {
   #pragma unroll
-      for (int j = 0; j < 8; ++j) u[elem_index8(tp, j, s0, R)] = v[j];
-    };
-    if (has_u) {
-      if constexpr (kWaveRounds) {
-        if (uthr) {
+            for (int qq = 0; qq < NRB; ++qq) {
+              u_round(NRB - 1 - qq);
+              if (qq + 1 < NRB) wave_sync();
+            }
+          }
+          __syncthreads();
+        } else {
   #pragma unroll
           for (int qq = 0; qq < NRB; ++qq) {
-            u_round(NRB - 1 - qq);
-            if (qq + 1 < NRB) wave_sync();
+            if (uthr) u_round(NRB - 1 - qq);
+            __syncthreads();
+          }
+        }
+      }
+      if (!has_v) return true;
+      // 4. the next rl's input sign flip and stages 0 .. LB-1 (ascending)
+      auto v_round = [&](int r) {
+        float v[8];
+        load8(r, v);
+        v_stages(r, v);
+        store8(r, v);
+      };
+      if constexpr (kWaveRounds) {
+        if (vthr) {
+  #pragma unroll
+          for (int r = 0; r < NRB; ++r) {
+            v_round(r);
+            if (r + 1 < NRB) wave_sync();
           }
         }
         __syncthreads();
       } else {
   #pragma unroll
-        for (int qq = 0; qq < NRB; ++qq) {
-          if (uthr) u_round(NRB - 1 - qq);
+        for (int r = 0; r < NRB; ++r) {
+          if (vthr) v_round(r);
           __syncthreads();
         }
-      }
-    }
-    if (!has_v) return true;
-    // 4. the next rl's input sign flip and stages 0 .. LB-1 (ascending)
-    auto v_round = [&](int r) {
-      const int s0 = 3 * r;
-      const int R = round_w(r, LB);
-      float v[8];
-  #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = u[elem_index8(tp, j, s0, R)];
-      if (r == 0) {
-  #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = flip_sign(v[j], (sbits >> j) & 1u);
-      }
-  #pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        if (k < R) {
-  #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const int j1 = zero_bit(p, k);
-            bfly(v[j1], v[j1 | (1 << k)], pair(s0 + k, p));
-          }
-        }
-      }
-  #pragma unroll
-      for (int j = 0; j < 8; ++j) u[elem_index8(tp, j, s0, R)] = v[j];
-    };
-    if constexpr (kWaveRounds) {
-      if (vthr) {
-  #pragma unroll
-        for (int r = 0; r < NRB; ++r) {
-          v_round(r);
-          if (r + 1 < NRB) wave_sync();
-        }
-      }
-      __syncthreads();
-    } else {
-  #pragma unroll
-      for (int r = 0; r < NRB; ++r) {
-        if (vthr) v_round(r);
-        __syncthreads();
       }
     }
     // 5. z_{l+1}: the sub-block to the next rl's product workgroups (256 of
@@ -518,8 +616,11 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(ChainArgs a) {
     const ChainLayer& Ly = a.layer[layer];
     const int lane = tid & (kWave - 1);
     const int wave = tid >> 6;
-    const int n0 = idx * kRowsC + wave * RW;
     constexpr int G = D / kGroup;
+    // local row j = wave RW + r is feature q + BB p of residue q = 2 idx +
+    // j / 8, p = j % 8: the eight features that F_U^T's widest three stages
+    // mix, for two residues
+    auto row_of = [&](int j) { return 2 * idx + (j >> 3) + BB * (j & 7); };
     const size_t WPR = static_cast<size_t>(D) * BITS / 32;
     // 1. this lane's groups of the wave's feature rows
     uint32_t w[GPL][RW][NWG];
@@ -528,13 +629,26 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(ChainArgs a) {
     for (int gl = 0; gl < GPL; ++gl)
 #pragma unroll
       for (int r = 0; r < RW; ++r) {
-        const int n = n0 + r;
+        const int n = row_of(wave * RW + r);
         const int g = lane + kWave * gl;
         load_group<BITS>(Ly.qw + static_cast<size_t>(n) * WPR + static_cast<size_t>(g) * NWG,
                          w[gl][r]);
         s16[gl][r] = Ly.sc[static_cast<size_t>(n) * G + g];
         z16[gl][r] = Ly.zr[static_cast<size_t>(n) * G + g];
       }
+    // F_U^T's widest three stages for lane (m, j) of wave 0, j = lane % 16:
+    // the pairs of position q + BB p at strides D/2, D/4, D/8
+    float2 hc[3];
+    if (wave == 0) {
+      const int j = lane & (kRowsC - 1);
+      const int q = 2 * idx + (j >> 3), p = j & 7;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int s = LOG - 1 - k;
+        const int plow = p & ~(4 >> k);
+        hc[k] = Ly.cs_u[s * (D / 2) + del_bit(q + BB * plow, s)];
+      }
+    }
     // 2. (the first 8 M workgroups of a layer: the previous layer's
     //    rotation role first), then z_l from the rotation role
     if (dual && !rot_role(layer - 1, idx)) return;
@@ -661,9 +775,13 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(ChainArgs a) {
       }
     }
     wave_transpose_reduce<V>(acc, lane);
-    // y'_l as (value, epoch) pairs: the rotation roles poll the values
-    // themselves, so no acknowledgement wait and no flag.  Gathered first,
-    // so that each row's 16 pairs leave as one full 128-byte line.
+    // y'_l through F_U^T's widest three stages (strides D/2, D/4, D/8),
+    // whose butterflies stay inside this workgroup's rows: lane (m, j) of
+    // wave 0 ends with position q + BB p, the input of sub-block p.  Stored
+    // as (value, epoch) pairs at [m][q][p], so that the workgroup's 16
+    // values per row leave as one full 128-byte line and sub-block p reads
+    // every eighth pair; the rotation roles poll the values themselves (no
+    // acknowledgement wait and no flag).
     float* yg = sxs + MT * G;                            // [MT][kRowsC]
 #pragma unroll
     for (int tv = 0; tv < V; ++tv) {
@@ -674,11 +792,19 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(ChainArgs a) {
       }
     }
     __syncthreads();
-    if (tid < kRowsC * a.M) {
-      const int m = tid / kRowsC;
-      const int r = tid - m * kRowsC;
-      st_pair_sc1(ypbuf + (static_cast<size_t>(layer) * kChainMaxM + m) * D + idx * kRowsC + r,
-                  yg[tid], epoch);
+    if (wave == 0) {
+      static_assert(MT * kRowsC <= kWave, "one wave holds every row of every input");
+      const int m = lane / kRowsC;
+      const int j = lane & (kRowsC - 1);
+      float v = lane < MT * kRowsC ? yg[lane] : 0.0f;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int bit = 4 >> k;
+        v = bfly_lane(v, bit, (j & bit) != 0, hc[k]);
+      }
+      if (m < a.M)
+        st_pair_sc1(ypbuf + (static_cast<size_t>(layer) * kChainMaxM + m) * D + idx * kRowsC + j,
+                    v, epoch);
     }
     return;
   }
