@@ -241,6 +241,7 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(ChainArgs a) {
   constexpr int NWG = 2 * BITS;            // uint32 words per quantization group
   constexpr int RW = kRowsC / kWavesC;     // feature rows per wave (2)
   constexpr int SEGC = BITS == 2 ? 16 : 8; // codes per inner segment
+  constexpr float kCodeScale = BITS == 3 ? 1.0f : kFp8CodeScale;  // codes as q 2^-9
   // LDS floats: the product's padded x~ and group sums, or the rotation
   // role's sub-block and (4096-wide layers) its staged (cos, sin) pairs.
   // At most 80 KB, so that two workgroups run per CU: the next layer's
@@ -729,19 +730,18 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(ChainArgs a) {
         float q[RW][SEGC];
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
+          // 2 and 4 bits: FP8 decodes of the masked codes, q 2^-9 exactly
           if constexpr (BITS == 2) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-              const uint32_t mm = opaque((w[gl][r][i] >> (2 * t)) & 0x03030303u);
-#pragma unroll
-              for (int bb = 0; bb < 4; ++bb) q[r][t + 4 * bb] = static_cast<float>((mm >> (8 * bb)) & 0xffu);
+              const uint32_t mm = (w[gl][r][i] >> (2 * t)) & 0x03030303u;
+              fp8_codes4(mm, q[r][t], q[r][t + 4], q[r][t + 8], q[r][t + 12]);
             }
           } else if constexpr (BITS == 4) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-              const uint32_t mm = opaque((w[gl][r][i] >> (4 * t)) & 0x0f0f0f0fu);
-#pragma unroll
-              for (int bb = 0; bb < 4; ++bb) q[r][t + 2 * bb] = static_cast<float>((mm >> (8 * bb)) & 0xffu);
+              const uint32_t mm = (w[gl][r][i] >> (4 * t)) & 0x0f0f0f0fu;
+              fp8_codes4(mm, q[r][t], q[r][t + 2], q[r][t + 4], q[r][t + 6]);
             }
           } else {
 #pragma unroll
@@ -771,7 +771,8 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(ChainArgs a) {
         const float z = f16_to_f32(z16[gl][r]);
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-          acc[r * MT + m] = fmaf(s, fmaf(-z, sxs[m * G + g], dot[r][m]), acc[r * MT + m]);
+          acc[r * MT + m] = fmaf(s, fmaf(-z, sxs[m * G + g], dot[r][m] * kCodeScale),
+                                 acc[r * MT + m]);
       }
     }
     wave_transpose_reduce<V>(acc, lane);

@@ -13,7 +13,8 @@
 //     per row, all issued before the staging so they are in flight together.
 // Per group the product is factored as
 //     sum_k (q_k - z) s x~_k = s (sum_k q_k x~_k - z sum_k x~_k),
-// which leaves one convert and MT fused multiply-adds per code.  A wave
+// which leaves MT fused multiply-adds per code and one convert per two
+// codes (2 and 4 bits: FP8 decodes of the masked codes).  A wave
 // needs no other wave's data: its RW*MT partial sums are combined with a
 // transposing reduction over its 64 lanes in a fixed order, so the result
 // is bitwise reproducible.
@@ -36,23 +37,27 @@ constexpr int kGStride = kGroup + 4;       // LDS floats per staged group
 // 8 codes (24 bits) for 3-bit codes.
 template <int BITS> struct Seg { static constexpr int CODES = BITS == 2 ? 16 : 8; };
 
-// Codes of segment i of a group as floats, q[j] = code (i*CODES + j).
+// Codes of segment i of a group as floats, q[j] = code (i*CODES + j) /
+// SegScale<BITS>::SCALE: 2- and 4-bit codes are masked four at a time into
+// byte lanes and decoded two per instruction as FP8 (q 2^-9, exact), 3-bit
+// codes are extracted and converted one at a time.
+template <int BITS> struct SegScale {
+  static constexpr float SCALE = BITS == 3 ? 1.0f : kFp8CodeScale;
+};
 template <int BITS>
 __device__ __forceinline__ void seg_codes(const uint32_t (&w)[2 * BITS], int i,
                                           float (&q)[Seg<BITS>::CODES]) {
   if constexpr (BITS == 2) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const uint32_t m = opaque((w[i] >> (2 * t)) & 0x03030303u);  // codes t, t+4, t+8, t+12
-#pragma unroll
-      for (int b = 0; b < 4; ++b) q[t + 4 * b] = static_cast<float>((m >> (8 * b)) & 0xffu);
+      const uint32_t m = (w[i] >> (2 * t)) & 0x03030303u;  // codes t, t+4, t+8, t+12
+      fp8_codes4(m, q[t], q[t + 4], q[t + 8], q[t + 12]);
     }
   } else if constexpr (BITS == 4) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const uint32_t m = opaque((w[i] >> (4 * t)) & 0x0f0f0f0fu);  // codes t, t+2, t+4, t+6
-#pragma unroll
-      for (int b = 0; b < 4; ++b) q[t + 2 * b] = static_cast<float>((m >> (8 * b)) & 0xffu);
+      const uint32_t m = (w[i] >> (4 * t)) & 0x0f0f0f0fu;  // codes t, t+2, t+4, t+6
+      fp8_codes4(m, q[t], q[t + 2], q[t + 4], q[t + 6]);
     }
   } else {
 #pragma unroll
@@ -174,7 +179,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
         const float z = f16_to_f32(z16[r]);
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-          acc[r * MT + m] = fmaf(s, fmaf(-z, sxs[m][lane], dot[r][m]), acc[r * MT + m]);
+          acc[r * MT + m] = fmaf(s, fmaf(-z, sxs[m][lane], dot[r][m] * SegScale<BITS>::SCALE),
+                               acc[r * MT + m]);
       }
     }
   }
@@ -669,7 +675,8 @@ __global__ __launch_bounds__(kThreads) void gemv_rot_kernel(
       const float z = f16_to_f32(z16[r]);
 #pragma unroll
       for (int m = 0; m < MT; ++m)
-        acc[r * MT + m] = fmaf(s, fmaf(-z, sxs[m][lane], dot[r][m]), acc[r * MT + m]);
+        acc[r * MT + m] = fmaf(s, fmaf(-z, sxs[m][lane], dot[r][m] * SegScale<BITS>::SCALE),
+                               acc[r * MT + m]);
     }
   }
   wave_transpose_reduce<V>(acc, lane);

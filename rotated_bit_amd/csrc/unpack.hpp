@@ -53,6 +53,23 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
   return v;
 }
 
+// Four codes below 16 in the byte lanes of m as floats q 2^-9, two per
+// instruction: the packed FP8 (OCP e4m3) decode maps byte values 0..15 to
+// exactly q 2^-9 (subnormal below 8, the first binade from 8 to 15).  A
+// product formed from them is exactly 2^-9 times the one formed from q
+// (every rounding scales with it), so scaling the sum by kFp8CodeScale
+// restores it bit for bit.
+constexpr float kFp8CodeScale = 512.0f;
+__device__ __forceinline__ void fp8_codes4(uint32_t m, float& q0, float& q1, float& q2,
+                                           float& q3) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(m), false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(m), true);
+  q0 = lo[0];
+  q1 = lo[1];
+  q2 = hi[0];
+  q3 = hi[1];
+}
+
 // Codes of one 32-code run as floats.  2- and 4-bit codes are masked four
 // at a time into byte lanes, each then a single byte-to-float convert.
 template <int BITS>
