@@ -409,7 +409,7 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(ChainArgs a) {
     if (has_u) {
       const u32x2* yp = ypbuf + (static_cast<size_t>(rl) * kChainMaxM + m) * D;
       float v[QPT];
-      if (!poll_pairs<QPT>(yp + static_cast<size_t>(tid) * 8 + wsub, kThreadsC * 8, epoch, v))
+      if (!poll_pairs<QPT>(yp + static_cast<size_t>(wsub) * BB + tid, kThreadsC, epoch, v))
         failed = 1;
   #pragma unroll
       for (int qi = 0; qi < QPT; ++qi) u[tid + kThreadsC * qi] = v[qi];
@@ -779,10 +779,10 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(ChainArgs a) {
     // y'_l through F_U^T's widest three stages (strides D/2, D/4, D/8),
     // whose butterflies stay inside this workgroup's rows: lane (m, j) of
     // wave 0 ends with position q + BB p, the input of sub-block p.  Stored
-    // as (value, epoch) pairs at [m][q][p], so that the workgroup's 16
-    // values per row leave as one full 128-byte line and sub-block p reads
-    // every eighth pair; the rotation roles poll the values themselves (no
-    // acknowledgement wait and no flag).
+    // as (value, epoch) pairs in position order, so that sub-block p reads
+    // one contiguous run of BB pairs (polling a strided eighth of every line
+    // took ~0.5 us longer to see the last value); the rotation roles poll
+    // the values themselves (no acknowledgement wait and no flag).
     float* yg = sxs + MT * G;                            // [MT][kRowsC]
 #pragma unroll
     for (int tv = 0; tv < V; ++tv) {
@@ -804,7 +804,8 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(ChainArgs a) {
         v = bfly_lane(v, bit, (j & bit) != 0, hc[k]);
       }
       if (m < a.M)
-        st_pair_sc1(ypbuf + (static_cast<size_t>(layer) * kChainMaxM + m) * D + idx * kRowsC + j,
+        st_pair_sc1(ypbuf + (static_cast<size_t>(layer) * kChainMaxM + m) * D +
+                        static_cast<size_t>(j & 7) * BB + 2 * idx + (j >> 3),
                     v, epoch);
     }
     return;

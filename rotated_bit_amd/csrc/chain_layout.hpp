@@ -14,8 +14,7 @@ constexpr int kChainFlagCopies = 16;  // copies of each rotation flag (spread po
 // out, word 2 the final workgroups' arrival count), per-phase rotation flags
 // [phase][copy][32], then the data: float32 z [phase][kChainMaxM][dim] for
 // phases 0..kChainMaxLayers, and y' after the output side's widest three
-// stages as (float32 value, uint32 epoch) pairs [layer][kChainMaxM][dim/8
-// residues][8 sub-blocks].
+// stages as (float32 value, uint32 epoch) pairs [layer][kChainMaxM][dim].
 constexpr size_t kChainFlagsOffset = 64;
 constexpr size_t kChainDataOffset =
     (kChainFlagsOffset + size_t{kChainMaxLayers + 1} * kChainFlagCopies * 32 + 63) / 64 * 64;
