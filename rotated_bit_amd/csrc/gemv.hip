@@ -10,7 +10,8 @@
 //     while staging (16 lanes per group, fixed butterfly order);
 //   * lane l of every wave takes group l of the chunk: one contiguous
 //     16/24/32-byte load of packed codes per row and one fp16 scale and zero
-//     per row, all issued before the staging so they are in flight together.
+//     per row, issued one chunk ahead (right after the chunk's x~ loads), so
+//     that they stream in while the current chunk is staged and multiplied.
 // Per group the product is factored as
 //     sum_k (q_k - z) s x~_k = s (sum_k q_k x~_k - z sum_k x~_k),
 // which leaves MT fused multiply-adds per code and one convert per two
@@ -99,37 +100,61 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.0f;
 
-  for (int g0 = 0; g0 < G; g0 += GC) {
-    const int ng = min(GC, G - g0);
-    const int g = g0 + lane;
-    const bool active = lane < ng;
-
-    // This lane's group of every row: in flight during the staging below.
+  // This lane's group of every row for one chunk.  The loads are never
+  // conditional (lanes past the chunk's end and the prefetch after the last
+  // chunk re-read a valid group), so the compiler's waits stay partial.
+  struct ChunkRegs {
     uint32_t w[RW][NWG];
     uint16_t s16[RW], z16[RW];
-    if (active) {
+  };
+  auto load_chunk = [&](int g0, ChunkRegs& R) {
+    const int g = min(g0 + lane, G - 1);
 #pragma unroll
-      for (int r = 0; r < RW; ++r) {
-        load_group<BITS>(wrow[r] + static_cast<size_t>(g) * NWG, w[r]);
-        s16[r] = srow[r][g];
-        z16[r] = zrow[r][g];
-      }
+    for (int r = 0; r < RW; ++r) {
+      load_group<BITS>(wrow[r] + static_cast<size_t>(g) * NWG, R.w[r]);
+      R.s16[r] = srow[r][g];
+      R.z16[r] = zrow[r][g];
     }
-
-    // Stage x~[m][64*g0 .. 64*(g0+ng)) and its per-group sums.
-    __syncthreads();   // the previous chunk is no longer read
+  };
+  // One chunk: its x~ loads first, then the next chunk's codes (in flight
+  // during this chunk's staging and product), then x~ staged in LDS with
+  // its per-group sums, then the product on the codes loaded one chunk ago.
+  auto chunk = [&](int g0, const ChunkRegs& cur, ChunkRegs& nxt) {
+    const int ng = min(GC, G - g0);
+    const bool active = lane < ng;
+    constexpr int H = GC * 16 / kThreads;          // float4 per thread per row
+    float4 xv4[MT][H];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const int mm = min(m0 + m, M - 1);   // rows past M: staged, never stored
       const float4* src = reinterpret_cast<const float4*>(
           xt + static_cast<size_t>(mm) * K + static_cast<size_t>(g0) * kGroup);
 #pragma unroll
-      for (int h = 0; h < GC * 16 / kThreads; ++h) {
+      for (int h = 0; h < H; ++h) {
         const int f = tid + h * kThreads;   // float4 index; 16 per group
+        xv4[m][h] = src[min(f, ng * 16 - 1)];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_chunk(min(g0 + GC, G - 1), nxt);
+    // x~ arrives here, with the prefetch still in flight; the empty asm pins
+    // each value so that no load is re-issued behind the prefetch
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int h = 0; h < H; ++h)
+        asm volatile("" : "+v"(xv4[m][h].x), "+v"(xv4[m][h].y), "+v"(xv4[m][h].z),
+                     "+v"(xv4[m][h].w));
+    __syncthreads();   // the previous chunk is no longer read
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+      for (int h = 0; h < H; ++h) {
+        const int f = tid + h * kThreads;
         const int gi = f >> 4;
+        const float4 v = xv4[m][h];
         float part = 0.0f;
         if (gi < ng) {
-          const float4 v = src[f];
           *reinterpret_cast<float4*>(&xs[m][gi * kGStride + (f & 15) * 4]) = v;
           part = (v.x + v.y) + (v.z + v.w);
         }
@@ -154,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
         // Codes of both rows once; then x~ one batch row at a time.
         float q[RW][SEG];
 #pragma unroll
-        for (int r = 0; r < RW; ++r) seg_codes<BITS>(w[r], i, q[r]);
+        for (int r = 0; r < RW; ++r) seg_codes<BITS>(cur.w[r], i, q[r]);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           float xv[SEG];
@@ -175,14 +200,20 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
       }
 #pragma unroll
       for (int r = 0; r < RW; ++r) {
-        const float s = f16_to_f32(s16[r]);
-        const float z = f16_to_f32(z16[r]);
+        const float s = f16_to_f32(cur.s16[r]);
+        const float z = f16_to_f32(cur.z16[r]);
 #pragma unroll
         for (int m = 0; m < MT; ++m)
           acc[r * MT + m] = fmaf(s, fmaf(-z, sxs[m][lane], dot[r][m] * SegScale<BITS>::SCALE),
                                acc[r * MT + m]);
       }
     }
+  };
+  ChunkRegs ra, rb;
+  load_chunk(0, ra);
+  for (int g0 = 0; g0 < G; g0 += 2 * GC) {
+    chunk(g0, ra, rb);
+    if (g0 + GC < G) chunk(g0 + GC, rb, ra);
   }
 
   wave_transpose_reduce<V>(acc, lane);
