@@ -52,9 +52,9 @@ DISTINCT = 4                     # seeded instances per cell; the rest are copie
 # WRITE_SIZE, each scaled by what the counter reads for a 256 MiB device
 # copy); None for a kernel changed since its counters were taken.
 TRAFFIC_BYTES = {
-    "chain_kernel_4096_2bit_M1_32layers": None,        # changed since its counters were taken
-    "rotate_in_deq_gemv_2bit": 7009280,                # FETCH 3414.5 KiB, WRITE 16.0 KiB
-    "rotate_out_b4096": 590848,                        # FETCH 280.5 KiB, WRITE 16.0 KiB
+    "chain_kernel_4096_2bit_M1_32layers": 213233601,   # FETCH 102662.5 KiB, WRITE 2944.3 KiB
+    "rotate_in_deq_gemv_2bit": 7006096,                # FETCH 3413.5 KiB, WRITE 16.0 KiB
+    "rotate_out_b4096": 590755,                        # FETCH 280.5 KiB, WRITE 16.0 KiB
 }
 
 
