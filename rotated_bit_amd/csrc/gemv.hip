@@ -33,6 +33,7 @@ constexpr int kRowsPerWg = kWaves * RW;    // 16
 constexpr int KC = 4096;                   // inputs per staged chunk
 constexpr int GC = KC / kGroup;            // groups per chunk: one per lane
 constexpr int kGStride = kGroup + 4;       // LDS floats per staged group
+constexpr int kPersistBlocks = 512;        // workgroups of a persistent grid
 
 // Codes per segment of the inner loop: one word for 2- and 4-bit codes,
 // 8 codes (24 bits) for 3-bit codes.
@@ -82,19 +83,19 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid >> 6;
-  const int rbase = blockIdx.x * kRowsPerWg + wave * RW;
   const int m0 = blockIdx.y * MT;
-
-  const uint32_t* wrow[RW];
-  const uint16_t* srow[RW];
-  const uint16_t* zrow[RW];
-#pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    const int n = min(rbase + r, N - 1);        // rows past N: loaded, never stored
-    wrow[r] = qw + static_cast<size_t>(n) * WPR;
-    srow[r] = sc + static_cast<size_t>(n) * G;
-    zrow[r] = zr + static_cast<size_t>(n) * G;
-  }
+  // Work items (row block, chunk): this workgroup takes row blocks
+  // blockIdx.x, blockIdx.x + gridDim.x, ... (one each when the grid covers
+  // every block; a smaller grid keeps the code prefetch running across its
+  // blocks), every chunk of each.
+  const int nrb = (N + kRowsPerWg - 1) / kRowsPerWg;
+  const int nch = (G + GC - 1) / GC;
+  const int nit = (nrb - static_cast<int>(blockIdx.x) + static_cast<int>(gridDim.x) - 1) /
+                  static_cast<int>(gridDim.x) * nch;
+  auto item_rbase = [&](int it) {
+    return (static_cast<int>(blockIdx.x) + it / nch * static_cast<int>(gridDim.x)) * kRowsPerWg +
+           wave * RW;
+  };
 
   float acc[V];
 #pragma unroll
@@ -107,19 +108,23 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     uint32_t w[RW][NWG];
     uint16_t s16[RW], z16[RW];
   };
-  auto load_chunk = [&](int g0, ChunkRegs& R) {
-    const int g = min(g0 + lane, G - 1);
+  auto load_item = [&](int it, ChunkRegs& R) {
+    const int g = min((it % nch) * GC + lane, G - 1);
+    const int rbase = item_rbase(it);
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
-      load_group<BITS>(wrow[r] + static_cast<size_t>(g) * NWG, R.w[r]);
-      R.s16[r] = srow[r][g];
-      R.z16[r] = zrow[r][g];
+      const int n = min(rbase + r, N - 1);      // rows past N: loaded, never stored
+      load_group<BITS>(qw + static_cast<size_t>(n) * WPR + static_cast<size_t>(g) * NWG, R.w[r]);
+      R.s16[r] = sc[static_cast<size_t>(n) * G + g];
+      R.z16[r] = zr[static_cast<size_t>(n) * G + g];
     }
   };
-  // One chunk: its x~ loads first, then the next chunk's codes (in flight
-  // during this chunk's staging and product), then x~ staged in LDS with
-  // its per-group sums, then the product on the codes loaded one chunk ago.
-  auto chunk = [&](int g0, const ChunkRegs& cur, ChunkRegs& nxt) {
+  // One item: its x~ loads first, then the next item's codes (in flight
+  // during this item's staging and product), then x~ staged in LDS with its
+  // per-group sums, then the product on the codes loaded one item ago; the
+  // last chunk of a row block stores the block's rows.
+  auto chunk = [&](int it, const ChunkRegs& cur, ChunkRegs& nxt) {
+    const int g0 = (it % nch) * GC;
     const int ng = min(GC, G - g0);
     const bool active = lane < ng;
     constexpr int H = GC * 16 / kThreads;          // float4 per thread per row
@@ -136,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    load_chunk(min(g0 + GC, G - 1), nxt);
+    load_item(min(it + 1, nit - 1), nxt);
     // x~ arrives here, with the prefetch still in flight; the empty asm pins
     // each value so that no load is re-issued behind the prefetch
 #pragma unroll
@@ -208,31 +213,44 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
                                acc[r * MT + m]);
       }
     }
+    if (g0 + GC >= G) {
+      float out[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        out[i] = acc[i];
+        acc[i] = 0.0f;
+      }
+      wave_transpose_reduce<V>(out, lane);
+      // Lane lane_of_value(t) holds value t = r * MT + m.
+      const int rbase = item_rbase(it);
+#pragma unroll
+      for (int t = 0; t < V; ++t) {
+        if (lane == lane_of_value<V>(t)) {
+          const int r = t / MT;
+          const int m = t - r * MT;
+          const int n = rbase + r;
+          if (n < N && m0 + m < M) yt[static_cast<size_t>(m0 + m) * N + n] = out[0];
+        }
+      }
+    }
   };
   ChunkRegs ra, rb;
-  load_chunk(0, ra);
-  for (int g0 = 0; g0 < G; g0 += 2 * GC) {
-    chunk(g0, ra, rb);
-    if (g0 + GC < G) chunk(g0 + GC, rb, ra);
-  }
-
-  wave_transpose_reduce<V>(acc, lane);
-  // Lane lane_of_value(t) holds value t = r * MT + m.
-#pragma unroll
-  for (int t = 0; t < V; ++t) {
-    if (lane == lane_of_value<V>(t)) {
-      const int r = t / MT;
-      const int m = t - r * MT;
-      const int n = rbase + r;
-      if (n < N && m0 + m < M) yt[static_cast<size_t>(m0 + m) * N + n] = acc[0];
-    }
+  load_item(0, ra);
+  for (int it = 0; it < nit; it += 2) {
+    chunk(it, ra, rb);
+    if (it + 1 < nit) chunk(it + 1, rb, ra);
   }
 }
 
 template <int BITS, int MT>
 hipError_t launch_cfg(const harp_qweight& W, const float* xt, float* yt, int M,
                       hipStream_t stream) {
-  const dim3 grid((W.N + kRowsPerWg - 1) / kRowsPerWg, (M + MT - 1) / MT);
+  // Row blocks beyond kPersistBlocks per launch are taken in turn by a grid
+  // of kPersistBlocks workgroups (two per CU), so that short rows (one or
+  // two chunks) do not expose each workgroup's first code load.
+  const int nrb = (W.N + kRowsPerWg - 1) / kRowsPerWg;
+  const int gx = (M <= MT && nrb > 2 * kPersistBlocks) ? kPersistBlocks : nrb;
+  const dim3 grid(gx, (M + MT - 1) / MT);
   hipLaunchKernelGGL((gemv_kernel<BITS, MT>), grid, dim3(kThreads), 0, stream,
                      W.qweight, W.scale, W.zero, xt, yt, W.N, W.K, M);
   return hipGetLastError();

@@ -309,7 +309,11 @@ def test_gemv(N, K, bits, M, spread):
 # and 4 bits: matrix cores on the bf16 planes of x~).
 WIDE_GEMV_CASES = [(16400, 8192, 2, 3), (16400, 8192, 4, 5), (16400, 8192, 4, 8),
                    (16400, 4160, 2, 6), (16400, 8192, 2, 1), (16400, 8192, 4, 2),
-                   (4100, 8192, 4, 4), (16400, 4160, 3, 5), (16400, 8192, 2, 7)]
+                   (4100, 8192, 4, 4), (16400, 4160, 3, 5), (16400, 8192, 2, 7),
+                   # one row over more than 1024 row blocks: a persistent grid
+                   # of 512 workgroups, each taking several blocks (ragged
+                   # last block, a partial second chunk, odd item counts)
+                   (16420, 4160, 3, 1), (28680, 4096, 4, 1)]
 
 
 @pytest.mark.parametrize("N,K,bits,M", WIDE_GEMV_CASES)
