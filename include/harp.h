@@ -410,7 +410,7 @@ harp_status harp_quantize_pack(const float *Wp, int32_t N, int32_t K, int32_t bi
  *              256-byte aligned, zero-filled once before its first use; every
  *              call leaves it ready for the next.  Calls that share a
  *              workspace must not overlap in time.
- * Stacks longer than 32 layers run as one launch per 32 layers.  Every wait
+ * Stacks longer than 48 layers run as one launch per 48 layers.  Every wait
  * inside a launch is bounded; a wait that runs out (which needs a stalled
  * device) leaves the outputs undefined and a nonzero second workspace word.
  */

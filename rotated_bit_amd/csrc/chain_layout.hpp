@@ -6,7 +6,7 @@
 
 namespace harp {
 
-constexpr int kChainMaxLayers = 32;   // layers per launch (kernel arguments by value)
+constexpr int kChainMaxLayers = 48;   // layers per launch (kernel arguments by value, 3 KB)
 constexpr int kChainMaxM = 4;
 constexpr int kChainFlagCopies = 16;  // copies of each rotation flag (spread polling)
 
