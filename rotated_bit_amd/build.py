@@ -24,7 +24,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libharp.so")
 ARCH = os.environ.get("HARP_OFFLOAD_ARCH", "gfx950")
 
-HIP_SOURCES = ["rotate.hip", "mixed.hip", "gemv.hip", "gemv_mc.hip", "skinny.hip", "skinny_wide.hip", "gemm.hip",
+HIP_SOURCES = ["rotate.hip", "mixed.hip", "gemv.hip", "gemv_f4.hip", "gemv_mc.hip", "skinny.hip", "skinny_wide.hip", "gemm.hip",
                "dequant.hip", "prep.hip", "chain.hip", "harp_api.cpp"]
 CXX_SOURCES = ["validate.cpp", "mixed_expand.cpp"]
 

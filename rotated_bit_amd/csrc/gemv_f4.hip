@@ -1,0 +1,424 @@
+// One-row decode product of 2-bit codes on the FP4 x FP8 matrix cores:
+//     y'[n] = sum_g s[n][g] (sum_{k in g} q[n][k] x~[k] - z[n][g] sum_{k in g} x~[k]).
+//
+// gfx950 has a block-scaled matrix-core instruction whose operands are
+// FP8 / FP6 / FP4 values (v_mfma_scale_f32_16x16x128_f8f6f4: a 16 x 128
+// times 128 x 16 product, float32 accumulation, one power-of-two scale per
+// row or column and 32 inputs).  Both factors of q x~ map onto it exactly:
+//   * a 2-bit code q is the FP4 (e2m1) value q / 2 when its two bits sit at
+//     the bottom of a nibble: a code word masked with 0x33333333 and its
+//     copy shifted right by two give sixteen FP4 values with two
+//     instructions each, and the column scale 2^1 restores q;
+//   * x~ (float32, not rounded) is carried as eight FP8 (e4m3) planes of
+//     signed 4-bit digits, one exponent per quantization group and plane,
+//     which reproduce x~ to 2^-32 of the group maximum (see build_step).
+// A small kernel builds the planes once per call; each product workgroup
+// copies its K slice of them into LDS and streams the codes of its rows.
+//
+// Operand roles of one matrix-core step (128 inputs, two quantization
+// groups): the planes are the 16 x 128 operand, one row per (plane p,
+// group half h) so that row p + 8h carries plane p of the step's group h and
+// zeros over the other group; the codes are the 128 x 16 operand, one
+// column per output row.  Lane l then holds the four planes
+// 4(l/16 % 2) .. +3 of group half (l/16) / 2 for output row l % 16: all four
+// share that row's scale and zero, so the epilogue is one sum, one
+// multiply-add for the zero point and one for the scale per step and lane.
+//
+// Lane layouts (checked on the device): FP4 operand lane l holds row or
+// column l % 16 and inputs 32 (l/16) .. +31 in nibble order; FP8 operand
+// lane l holds row or column l % 16 and inputs 16 (l/16) .. +15 (bytes
+// 0..15) and 64 + 16 (l/16) .. +15 (bytes 16..31); the scale of row/column
+// r and input block b comes from lane r + 16 b; result lane l holds column
+// l % 16, rows 4 (l/16) .. +3.
+//
+// Inputs in operand order.  Steps come in pairs (2t, 2t + 1) over the 256
+// inputs of groups 4t .. 4t+3: step 2t + e takes group 4t + e in its first
+// group half and group 4t + 2 + e in its second, so block b of the step (a
+// half group) is inputs 256 t + 128 (b/2) + 64 e + 32 (b%2) .. +31.  Within
+// a block, operand offset o = 8 v + j (nibble j of code register v) is
+// input pi(o) = 16 (v/2) + 2 j + (v % 2), because register v holds the even
+// (v even) or odd codes of one code word.  Each lane loads one whole group
+// (16 bytes) per pair, lanes 16 apart exchange half groups
+// (v_permlane16_swap), and every row's 128-byte line of codes is read by
+// four lanes of one load.
+#include "launch.hpp"
+#include "unpack.hpp"
+#include "validate.hpp"
+
+namespace harp {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kF4WgWaves = 8;                      // one 16-row tile per wave
+constexpr int kF4Threads = kF4WgWaves * kWave;     // 512
+constexpr int kPlanes = 8;
+
+// ---- planes ----------------------------------------------------------------
+// Lane reductions over one 16-lane row with DPP moves (quad swaps, then the
+// half-row and row mirrors): every lane of the row ends with the result,
+// formed in the same order in each.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, dpp<0xb1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp<0x4e>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp<0x141>(v));   // row_half_mirror
+  return fmaxf(v, dpp<0x140>(v));   // row_mirror
+}
+__device__ __forceinline__ float row_sum(float v) {
+  v += dpp<0xb1>(v);
+  v += dpp<0x4e>(v);
+  v += dpp<0x141>(v);
+  return v + dpp<0x140>(v);
+}
+
+constexpr int kStepLds = 1024 + 16;       // LDS bytes per step: planes, then 16 zero bytes
+
+// Planes of one step of 128 inputs, built by one wave into LDS.  One
+// 16-lane row per 32-input block b, two inputs per lane (block offsets
+// u = j and j + 16 for lane j of the row); rows 0-1 and rows 2-3 are the
+// step's two quantization groups.  Per group, with 2^E <= max |x~| < 2^(E+1),
+// plane p holds the signed digit d_p = rint(r_p / 2^(E-3-4p)) of every input
+// (r_0 = x~, r_{p+1} = r_p - d_p 2^(E-3-4p), each step exact), so
+// |d_0| <= 16, |d_p| <= 8 after that, and the eight planes carry x~ to
+// 2^(E-32).  Digits are small integers, exact in FP8, and one plane of one
+// group shares one scale: every product the matrix cores sum for a result
+// is an integer of at most 48 times that scale (their sums are exact; with
+// products spread over the whole FP8 range the instruction's sum was
+// measured to lose bits about 2^-11 below its largest term).  Planes whose
+// scale would fall below 2^-127 (groups below about 2^-96) stay zero.
+// xs: the step's inputs (x~ + 256 t + 64 e for step 2t + e).  Planes go to
+// pl[lane][16] in operand order: block offset u becomes operand offset
+// o = pi^-1(u) and lands in operand lane (p + 8h) + 16 g, byte o % 16, with
+// h = b / 2 and g = 2 (b % 2) + o / 16; bytes 1024..1039 are zeroed.  The
+// scale byte of plane p (E - 3 - 4p + 127) goes to psc[lane] for the lanes
+// that supply operand row p + 8h's scale of the group's blocks; the rows of
+// the other group half get 127 (their operand bytes there are zero).  The
+// sums of x~ over the step's groups 4t + e and 4t + 2 + e (fixed order) go
+// to sx[0] and sx[2].
+__device__ __forceinline__ void build_step(const float* __restrict__ xs, uint8_t* pl,
+                                           uint8_t* psc, float* sx, int lane) {
+  const int j = lane & 15;
+  const int b = lane >> 4;
+  const int k0 = 128 * (b >> 1) + 32 * (b & 1) + j;
+  float ra = xs[k0];
+  float rb = xs[k0 + 16];
+  {
+    const float t = row_sum(ra + rb);
+    // rows 1 and 3 add lane 15 of rows 0 and 2 (row_bcast:15)
+    const float g2 = t + __int_as_float(__builtin_amdgcn_update_dpp(
+                             0, __float_as_int(t), 0x142, 0xa, 0xf, false));
+    if (j == 15 && (b & 1)) sx[2 * (b >> 1)] = g2;
+  }
+  if (lane < 4) reinterpret_cast<uint32_t*>(pl + 1024)[lane] = 0u;
+  // group maximum: row maximum, then rows 0 <-> 1 and 2 <-> 3 exchanged
+  float m = row_max(fmaxf(fabsf(ra), fabsf(rb)));
+  {
+    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m),
+                                                     false, false);
+    m = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  }
+  const int E = static_cast<int>((__float_as_uint(m) >> 23) & 0xff) - 127;   // floor(log2 m)
+  const int o = 8 * (j & 1) + (j >> 1);   // operand offset of u = j (u = j + 16: o + 16)
+  const int h = b >> 1;
+  uint8_t* dst = pl + 2 * (b & 1) * 256 + o;
+  uint8_t* sdst = psc + 16 * b;
+#pragma unroll
+  for (int p = 0; p < kPlanes; ++p) {
+    const int sb = E - 3 - 4 * p + 127;   // scale byte of this plane
+    const bool live = m > 0.0f && sb >= 0;
+    uint32_t enc = 0;
+    if (live) {
+      const float da = rintf(ldexpf(ra, 127 - sb));
+      const float db = rintf(ldexpf(rb, 127 - sb));
+      enc = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(da, db, 0, false));
+      ra -= ldexpf(da, sb - 127);
+      rb -= ldexpf(db, sb - 127);
+    }
+    dst[(p + 8 * h) * 16] = static_cast<uint8_t>(enc & 0xffu);
+    dst[256 + (p + 8 * h) * 16] = static_cast<uint8_t>((enc >> 8) & 0xffu);
+    if (j == 0) sdst[p + 8 * h] = static_cast<uint8_t>(live ? sb : 127);
+    if (j == 1) sdst[p + 8 * (1 - h)] = 127;
+  }
+}
+
+// One wave per step: the step's planes, scale bytes and group sums built
+// into LDS by build_step, then written out with one 16-byte store per lane
+// (planes, f4 region layout pl[step][lane][16]), one 4-byte store per lane
+// of the first 16 (scale bytes, psc[step][lane]) and two floats (group
+// sums, sx[group]).
+__global__ __launch_bounds__(256) void f4_planes_kernel(const float* __restrict__ xt, int K,
+                                                        u32x4* __restrict__ pl,
+                                                        uint32_t* __restrict__ psc,
+                                                        float* __restrict__ sx) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[4][kStepLds + kWave];
+  __shared__ float ssx[4][4];
+  const int s = (blockIdx.x * 256 + threadIdx.x) >> 6;
+  if (s >= K / kF4Step) return;   // whole waves
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x >> 6;
+  build_step(xt + 256 * (s >> 1) + 64 * (s & 1), stage[w], stage[w] + kStepLds, ssx[w], lane);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  pl[static_cast<size_t>(s) * kWave + lane] = reinterpret_cast<const u32x4*>(stage[w])[lane];
+  if (lane < 16)
+    psc[static_cast<size_t>(s) * 16 + lane] =
+        reinterpret_cast<const uint32_t*>(stage[w] + kStepLds)[lane];
+  if (lane < 2) sx[4 * (s >> 1) + 2 * lane + (s & 1)] = ssx[w][2 * lane];
+}
+
+// ---- product ---------------------------------------------------------------
+// Grid (ceil(tiles / 8), slices): wave w of workgroup (x, y) owns rows
+// 16 (8x + w) .. +15 over the K slice y (step pairs [pa, pb)).  The first
+// chunk's codes are requested before the slice's planes, scale bytes and
+// group sums (from f4_planes_kernel) and the workgroup's scales and zeros
+// (row-contiguous reads) are copied into LDS.  The codes then stream in
+// chunks of kPairs step pairs through two register sets (the next chunk is
+// requested before the current one is used); the steps of a chunk are
+// issued 2 kBatchPairs matrix instructions at a time before their
+// epilogues, with no branch inside (steps past the slice's end repeat its
+// last step with the scale zeroed).
+//
+// LDS keeps each step's 1024 plane bytes followed by 16 zero bytes, so a
+// lane forms its operand (plane bytes in one half, zeros in the other) from
+// two reads at the same immediate offset and no selects.
+constexpr int kPairs = 8;                 // step pairs per chunk
+constexpr int kSzStride = kF4MaxSliceSteps + 1;   // LDS dwords per row of scales / zeros
+constexpr int kBatchPairs = 2;            // step pairs per batch of matrix instructions
+
+__global__ __launch_bounds__(kF4Threads, 1) void gemv_f4_kernel(
+    const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
+    const uint16_t* __restrict__ zr, const u32x4* __restrict__ gpl,
+    const uint32_t* __restrict__ gps, const float* __restrict__ gsx, float* __restrict__ yt,
+    float* __restrict__ partials, uint32_t* __restrict__ counters, int N, int K, int slices) {
+  __shared__ __attribute__((aligned(16))) uint8_t lpl[kF4MaxSliceSteps * kStepLds];
+  __shared__ uint8_t lpsc[kF4MaxSliceSteps * kWave];
+  __shared__ float lsx[2 * kF4MaxSliceSteps];
+  // scales and zeros of the workgroup's rows over the slice: per row one
+  // dword per (step pair, group half), rows kSzStride dwords apart (odd, so
+  // that the 16 rows of a wave read distinct banks)
+  __shared__ uint32_t lsc[kF4WgWaves * 16 * kSzStride];
+  __shared__ uint32_t lzr[kF4WgWaves * 16 * kSzStride];
+
+  const int pairs = K / (2 * kF4Step);
+  const int pa = static_cast<int>(blockIdx.y) * pairs / slices;
+  const int pb = (static_cast<int>(blockIdx.y) + 1) * pairs / slices;
+  const int np = pb - pa;                 // step pairs of this slice
+  const int ns = 2 * np;                  // steps
+  const int sa = 2 * pa;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
+  const int tiles = N / 16;
+  const int tile = static_cast<int>(blockIdx.x) * kF4WgWaves + wave;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int h = g >> 1;                    // group half of this lane's results
+  const bool zlane = (g & 1) == 0;         // planes 0..3: carries the zero-point term
+  const int row = min(tile, tiles - 1) * 16 + n;   // waves past the last tile load it, then leave
+  const u32x4* qrow = reinterpret_cast<const u32x4*>(qw + static_cast<size_t>(row) * (K / 16)) + g;
+
+  // one register set: per step pair this lane's group of codes (16 bytes,
+  // group 4t + g); pairs past the slice re-read its last pair (one cached
+  // line per lane)
+  struct Chunk {
+    u32x4 c[kPairs];
+  };
+  auto load = [&](int c, Chunk& ch) {
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i) ch.c[i] = qrow[4 * (pa + min(c * kPairs + i, np - 1))];
+  };
+  const int nch = (np + kPairs - 1) / kPairs;
+  Chunk A, B;
+  load(0, A);
+  {
+    // planes: at most 8 16-byte vectors per thread; scale bytes: ns * 16
+    // <= 2 * kF4Threads dwords; group sums: 2 ns <= kF4Threads floats
+    constexpr int kPer = kF4MaxSliceSteps * kWave / kF4Threads;
+    constexpr int kPsPer = kF4MaxSliceSteps * 16 / kF4Threads;
+    static_assert(kPsPer * kF4Threads == kF4MaxSliceSteps * 16 &&
+                  2 * kF4MaxSliceSteps <= kF4Threads, "LDS fill shares");
+    const u32x4* ppl = gpl + static_cast<size_t>(sa) * kWave;
+    const int nv = ns * kWave;
+    u32x4 v[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) v[q] = ppl[min(tid + q * kF4Threads, nv - 1)];
+    uint32_t ps[kPsPer];
+#pragma unroll
+    for (int q = 0; q < kPsPer; ++q) ps[q] = gps[sa * 16 + min(tid + q * kF4Threads, ns * 16 - 1)];
+    const float sxv = gsx[2 * sa + min(tid, 2 * ns - 1)];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int i = tid + q * kF4Threads;
+      if (i < nv)
+        *reinterpret_cast<u32x4*>(lpl + (i >> 6) * kStepLds + (i & 63) * 16) = v[q];
+    }
+    if (tid < ns)
+      *reinterpret_cast<u32x4*>(lpl + tid * kStepLds + 1024) = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < kPsPer; ++q)
+      if (tid + q * kF4Threads < ns * 16)
+        reinterpret_cast<uint32_t*>(lpsc)[tid + q * kF4Threads] = ps[q];
+    if (tid < 2 * ns) lsx[tid] = sxv;
+    // scales and zeros: np 8-byte words (four groups) per row, consecutive
+    // threads along a row; rows past N re-read the last row
+    const int row0 = static_cast<int>(blockIdx.x) * kF4WgWaves * 16;
+    const int nw = kF4WgWaves * 16 * np;
+    for (int i = tid; i < nw; i += kF4Threads) {
+      const int r = i / np;
+      const int q = i - r * np;
+      const size_t gi = static_cast<size_t>(min(row0 + r, N - 1)) * (K / (4 * kGroup)) + pa + q;
+      const uint2 sv = reinterpret_cast<const uint2*>(sc)[gi];
+      const uint2 zv = reinterpret_cast<const uint2*>(zr)[gi];
+      lsc[r * kSzStride + 2 * q] = sv.x;
+      lsc[r * kSzStride + 2 * q + 1] = sv.y;
+      lzr[r * kSzStride + 2 * q] = zv.x;
+      lzr[r * kSzStride + 2 * q + 1] = zv.y;
+    }
+  }
+  __syncthreads();
+  if (tile >= tiles) return;
+
+  // operand halves: rows p + 8h with h = 1 carry their planes in bytes
+  // 16..31, the others in bytes 0..15; the other half reads the zeros
+  const bool upper = (lane & 8) != 0;
+  const uint8_t* lo_base = lpl + (upper ? 1024 : lane * 16);
+  const uint8_t* hi_base = lpl + (upper ? lane * 16 : 1024);
+  const float* sx_base = lsx + 2 * h;
+  const uint32_t* sc_base = lsc + (wave * 16 + n) * kSzStride + h;
+  const uint32_t* zr_base = lzr + (wave * 16 + n) * kSzStride + h;
+  const float zmask = zlane ? 1.0f : 0.0f;
+
+  float acc = 0.0f;
+  auto process = [&](const Chunk& ch, int c) {
+#pragma unroll
+    for (int half = 0; half < kPairs / kBatchPairs; ++half) {
+      floatx4 Dv[2 * kBatchPairs];
+#pragma unroll
+      for (int i = 0; i < 2 * kBatchPairs; ++i) {
+        const int pi = half * kBatchPairs + i / 2;    // pair within the chunk
+        const int e = i & 1;                           // step within the pair
+        const int ls = min(2 * (c * kPairs + pi) + e, ns - 1);
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(lo_base + ls * kStepLds);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(hi_base + ls * kStepLds);
+        const i32x8 Aop = {static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z),
+                           static_cast<int>(lo.w), static_cast<int>(hi.x), static_cast<int>(hi.y),
+                           static_cast<int>(hi.z), static_cast<int>(hi.w)};
+        // half groups exchanged between lanes 16 apart: afterwards words
+        // 0-1 belong to step 2t and words 2-3 to step 2t + 1 in every lane
+        u32x4 w = ch.c[pi];
+        {
+          const auto s0 = __builtin_amdgcn_permlane16_swap(w.x, w.z, false, false);
+          const auto s1 = __builtin_amdgcn_permlane16_swap(w.y, w.w, false, false);
+          w.x = s0[0];
+          w.z = s0[1];
+          w.y = s1[0];
+          w.w = s1[1];
+        }
+        const uint32_t w0 = e ? w.z : w.x;
+        const uint32_t w1 = e ? w.w : w.y;
+        const i32x8 Bop = {static_cast<int>(w0 & 0x33333333u),
+                           static_cast<int>((w0 >> 2) & 0x33333333u),
+                           static_cast<int>(w1 & 0x33333333u),
+                           static_cast<int>((w1 >> 2) & 0x33333333u), 0, 0, 0, 0};
+        Dv[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            Aop, Bop, floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 4, 0,
+            static_cast<int>(lpsc[ls * kWave + lane]), 0, 128);
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * kBatchPairs; ++i) {
+        const int pi = half * kBatchPairs + i / 2;
+        const int e = i & 1;
+        const int ls = 2 * (c * kPairs + pi) + e;
+        const float live = ls < ns ? 1.0f : 0.0f;
+        const float dsum = (Dv[i][0] + Dv[i][1]) + (Dv[i][2] + Dv[i][3]);
+        // the row's scale and zero of group 4t + 2h + e
+        const int lp = min(c * kPairs + pi, np - 1);
+        const float sf = live * f16_to_f32(static_cast<uint16_t>(sc_base[2 * lp] >> (16 * e)));
+        const float zf = f16_to_f32(static_cast<uint16_t>(zr_base[2 * lp] >> (16 * e)));
+        // group sum of group 4t + 2h + e (local group 2 ls + 2h - e), on
+        // the lanes that carry the zero-point term
+        const float sxg = zmask * sx_base[2 * min(ls, ns - 1) - e];
+        acc = fmaf(sf, fmaf(-zf, sxg, dsum), acc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // chunk c: request chunk c + 1 into the other register set, then use
+  // chunk c (requested one chunk earlier)
+  auto chunk = [&](int c, const Chunk& cur, Chunk& nxt) {
+    load(c + 1, nxt);   // pairs past the slice all re-read its last pair
+    process(cur, c);
+  };
+  // unconditional second half (past the last chunk every step is zeroed):
+  // under a branch the loads into B would be sunk behind the use of A
+  for (int c = 0; c < nch; c += 2) {
+    chunk(c, A, B);
+    chunk(c + 1, B, A);
+  }
+  // the four lanes of row n: (g0 + g1) + (g2 + g3), the same bits in each
+  acc += shfl_xor(acc, 16);
+  acc += shfl_xor(acc, 32);
+
+  if (slices == 1) {
+    if (g == 0) yt[row] = acc;
+    return;
+  }
+  // Split K: each slice stores its partial (device-coherent stores,
+  // acknowledged before the arrival is counted); the last slice to arrive
+  // adds the partials in slice order, so the result does not depend on the
+  // arrival order, and resets the tile's counter.
+  if (g == 0)
+    __hip_atomic_store(&partials[static_cast<size_t>(blockIdx.y) * N + row], acc,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  uint32_t prev = 0;
+  if (lane == 0)
+    prev = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  prev = __shfl(prev, 0, kWave);
+  if (prev != static_cast<uint32_t>(slices - 1)) return;
+  if (g == 0) {
+    float t = 0.0f;
+    for (int j = 0; j < slices; ++j) {
+      const float part = __hip_atomic_load(&partials[static_cast<size_t>(j) * N + row],
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      t = j == 0 ? part : t + part;
+    }
+    yt[row] = t;
+  }
+  if (lane == 0)
+    __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace
+
+hipError_t launch_gemv_f4(const harp_qweight& W, const float* xt, float* yt, uint8_t* f4,
+                          uint32_t* counters, int slices, hipStream_t stream) {
+  const int steps = W.K / kF4Step;
+  const int pairs = steps / 2;
+  if (W.bits != 2 || W.N % 16 != 0 || W.K % (2 * kF4Step) != 0 || slices < 1 ||
+      slices > kF4MaxSplits || (pairs + slices - 1) / slices * 2 > kF4MaxSliceSteps ||
+      f4 == nullptr || (slices > 1 && (counters == nullptr || W.N / 16 > kF4MaxSplitTiles)))
+    return hipErrorInvalidValue;
+  u32x4* pl = reinterpret_cast<u32x4*>(f4);
+  uint32_t* psc = reinterpret_cast<uint32_t*>(f4 + f4_psc_offset(W.K));
+  float* sx = reinterpret_cast<float*>(f4 + f4_sx_offset(W.K));
+  hipLaunchKernelGGL(f4_planes_kernel, dim3((steps + 3) / 4), dim3(256), 0, stream, xt, W.K, pl,
+                     psc, sx);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int tiles = W.N / 16;
+  const dim3 grid((tiles + kF4WgWaves - 1) / kF4WgWaves, slices);
+  hipLaunchKernelGGL(gemv_f4_kernel, grid, dim3(kF4Threads), 0, stream, W.qweight, W.scale,
+                     W.zero, pl, psc, sx, yt,
+                     reinterpret_cast<float*>(f4 + f4_partial_offset(W.K)), counters, W.N, W.K,
+                     slices);
+  return hipGetLastError();
+}
+
+}  // namespace harp

@@ -22,10 +22,11 @@ harp_status from_hip(hipError_t e) {
 hipStream_t as_stream(harp_stream s) { return reinterpret_cast<hipStream_t>(s); }
 
 // The whole linear on a workspace laid out as harp_linear_workspace_bytes
-// describes (arguments already checked).  split_k: the M > 64 GEMM may split
-// K (needs the counters at the front of ws, zero, and the partial tiles
-// after y'); without it the GEMM runs one K slice and only the counter area,
-// x~ and y' are used (the counter area is then not read).
+// describes (arguments already checked).  split_k: the M > 64 GEMM and the
+// one-row FP4 product may split K (needs the counters at the front of ws,
+// zero, and the partials after y' or in the f4 region); without it they run
+// one K slice and only the counter area, x~, y' and (one-row FP4 product)
+// the f4 region's planes are used (the counter area is then not read).
 harp_status fused_linear(const harp_rotation& V, const harp_qweight& W, const harp_rotation& U,
                          const void* x, harp_dtype x_dt, void* y, harp_dtype y_dt, int32_t M,
                          char* ws, bool split_k, hipStream_t s) {
@@ -40,7 +41,12 @@ harp_status fused_linear(const harp_rotation& V, const harp_qweight& W, const ha
     float* xt = reinterpret_cast<float*>(ws + harp::workspace_xt_offset());
     r = from_hip(harp::launch_rotate(V, x, x_dt, xt, HARP_F32, M, false, s));
     if (r != HARP_OK) return r;
-    if (M < harp::kSplitMinM)
+    const int32_t f4_slices = harp::f4_slices(M, W.N, W.K, W.bits, split_k);
+    if (f4_slices > 0)
+      r = from_hip(harp::launch_gemv_f4(
+          W, xt, yp, reinterpret_cast<uint8_t*>(ws + harp::workspace_f4_offset(M, W.N, W.K)),
+          reinterpret_cast<uint32_t*>(ws), f4_slices, s));
+    else if (M < harp::kSplitMinM)
       r = from_hip(harp::launch_gemv(W, xt, yp, M, s));
     else if (split_k)
       r = from_hip(harp::launch_gemm_skinny_split_k(
@@ -233,12 +239,17 @@ harp_status harp_linear_fused_noalloc(const harp_rotation* V, const harp_qweight
                                       int32_t M, harp_stream stream) {
   // the argument checks of harp_linear_fused with a stand-in workspace (an
   // aligned non-null address and no size limit); then the size this call
-  // needs in the scratch: counter area, x~ and y' (one K slice, no partials)
+  // needs in the scratch: counter area, x~ and y' (one K slice, no
+  // partials), and the f4 region's planes when the one-row FP4 product runs
   harp_status st = harp::validate_fused(V, W, U, x, x_dt, y, y_dt, M,
                                         reinterpret_cast<void*>(uintptr_t{256}), SIZE_MAX);
   if (st != HARP_OK || M == 0) return st;
   static_assert(kScratchBytes % 256 == 0, "scratch size");
-  if (harp::workspace_gemm_offset(M, W->N, W->K) > kScratchBytes) return HARP_ERR_WORKSPACE;
+  const int32_t f4s = harp::f4_slices(M, W->N, W->K, W->bits, false);
+  const size_t need = f4s > 0 ? harp::workspace_f4_offset(M, W->N, W->K) +
+                                    harp::f4_region_bytes(W->N, W->K, f4s)
+                              : harp::workspace_gemm_offset(M, W->N, W->K);
+  if (need > kScratchBytes) return HARP_ERR_WORKSPACE;
   char* scratch_ptr = nullptr;
   st = device_scratch(&scratch_ptr);
   if (st != HARP_OK) return st;

@@ -29,6 +29,14 @@ hipError_t launch_rotate_mixed(const harp_mixed_rotation& R, const void* in, int
 hipError_t launch_gemv(const harp_qweight& W, const float* xt, float* yt,
                        int M, hipStream_t stream);
 
+// One row of 2-bit codes on the FP4 x FP8 matrix cores (gemv_f4.hip): x~
+// is turned into digit planes in the f4 region (f4_region_bytes in
+// validate.hpp), then the product runs in `slices` K slices (f4_slices);
+// slices > 1 needs zeroed `counters` (one uint32 per 16-row tile, left
+// zero) and the partials that follow the planes in the region.
+hipError_t launch_gemv_f4(const harp_qweight& W, const float* xt, float* yt, uint8_t* f4,
+                          uint32_t* counters, int slices, hipStream_t stream);
+
 // The same product on the bf16 matrix cores with x~ split into exact bf16
 // planes (gemv_mc.hip): kGemvMcMinM <= M <= kGemvMcMaxM, 2 or 4 bits.
 hipError_t launch_gemv_mc(const harp_qweight& W, const float* xt, float* yt,

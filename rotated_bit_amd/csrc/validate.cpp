@@ -332,13 +332,45 @@ size_t workspace_gemm_offset(int32_t M, int32_t N, int32_t K) {
   return workspace_yp_offset(M, K) + align256(static_cast<size_t>(M) * N * 4);
 }
 
+int32_t f4_slices(int32_t M, int32_t N, int32_t K, int32_t bits, bool allow_split) {
+  if (M != 1 || bits != 2 || N < 16 || N % 16 != 0 || K < 2 * kF4Step || K % (2 * kF4Step) != 0 ||
+      static_cast<int64_t>(N) * K < kF4MinWeights)
+    return 0;
+  // slices are whole step pairs; the largest of them must fit in LDS
+  const int32_t pairs = K / (2 * kF4Step);
+  const int32_t tiles = N / 16;
+  const auto fits = [&](int32_t s) { return (pairs + s - 1) / s * 2 <= kF4MaxSliceSteps; };
+  if (!allow_split || tiles > kF4MaxSplitTiles) return fits(1) ? 1 : 0;
+  int32_t s = (kF4Waves + tiles - 1) / tiles;
+  s = std::min(s, kF4MaxSplits);
+  s = std::min(s, std::max(1, pairs / 2));   // at least 2 step pairs per slice
+  while (!fits(s)) ++s;
+  return s <= kF4MaxSplits ? s : 0;
+}
+
+size_t f4_psc_offset(int32_t K) { return static_cast<size_t>(K / kF4Step) * 1024; }
+size_t f4_sx_offset(int32_t K) { return f4_psc_offset(K) + static_cast<size_t>(K / kF4Step) * 64; }
+size_t f4_partial_offset(int32_t K) {
+  return align256(f4_sx_offset(K) + static_cast<size_t>(K / 64) * 4);   // one float per group
+}
+size_t f4_region_bytes(int32_t N, int32_t K, int32_t slices) {
+  if (slices <= 0) return 0;
+  return f4_partial_offset(K) + (slices > 1 ? align256(static_cast<size_t>(slices) * N * 4) : 0);
+}
+
+size_t workspace_f4_offset(int32_t M, int32_t N, int32_t K) {
+  return workspace_gemm_offset(M, N, K) + gemm_partial_bytes(M, N, K) +
+         skinny_partial_bytes(M, N, K);
+}
+
 size_t workspace_bytes(int32_t M, int32_t N, int32_t K) {
   if (M < 0 || M > HARP_MAX_M || N < 1 || N > HARP_MAX_DIM || K < 1 ||
       K > HARP_MAX_DIM)
     return 0;
   if (M == 0) return 0;
-  return workspace_gemm_offset(M, N, K) + gemm_partial_bytes(M, N, K) +
-         skinny_partial_bytes(M, N, K);
+  // the f4 region is reserved for every bit width (the size query does not
+  // know it)
+  return workspace_f4_offset(M, N, K) + f4_region_bytes(N, K, f4_slices(M, N, K, 2, true));
 }
 
 size_t chain_ws_bytes(int32_t dim) { return chain_workspace_bytes(dim); }

@@ -96,9 +96,40 @@ constexpr int32_t kBf16MinM = 64;
 constexpr int32_t kFusedRotGemvMaxM = 2;
 constexpr int32_t kFusedRotGemvMaxN = 4096;
 
+// One-row decode product of 2-bit codes on the FP4 x FP8 matrix cores
+// (gemv_f4.hip).  x~ is first turned into FP8 planes of 4-bit digits (one
+// exponent per quantization group and plane) in the "f4 region" of the
+// workspace; each workgroup holds one K slice of them in LDS, at most
+// kF4MaxSliceSteps steps of kF4Step inputs (slices are whole pairs of
+// steps).  Eligible: M == 1, 2-bit codes, N a multiple of 16, K a multiple
+// of 2 kF4Step, at least kF4MinWeights weights (below that the vector-ALU
+// kernel is faster).  f4_slices returns the number of K slices (0: not
+// eligible).  With split K allowed it aims at kF4Waves one-tile waves (16
+// rows each) and splits only up to kF4MaxSplitTiles tiles (the slices then
+// meet on the arrival counters at the workspace's front, their float32
+// partials in the f4 region); without it every K must fit one slice.
+constexpr int32_t kF4Step = 128;
+constexpr int32_t kF4MaxSliceSteps = 64;
+constexpr int64_t kF4MinWeights = int64_t{1} << 27;
+constexpr int32_t kF4Waves = 2048;
+constexpr int32_t kF4MaxSplits = 8;
+constexpr int32_t kF4MaxSplitTiles = 512;   // <= kGemmCounterBytes / 4
+int32_t f4_slices(int32_t M, int32_t N, int32_t K, int32_t bits, bool allow_split);
+// The f4 region: planes (K/128 steps x 64 lanes x 16 bytes), scale bytes
+// (K/128 x 64 bytes), group sums of x~ (K/64 floats), then `slices` x N
+// float32 partials when slices > 1; offsets within it.
+size_t f4_region_bytes(int32_t N, int32_t K, int32_t slices);
+size_t f4_psc_offset(int32_t K);
+size_t f4_sx_offset(int32_t K);
+size_t f4_partial_offset(int32_t K);
+// Offset of the f4 region in the fused linear's workspace (after every
+// other part).
+size_t workspace_f4_offset(int32_t M, int32_t N, int32_t K);
+
 // Workspace layout of the fused linear: the GEMM arrival counters
 // (kGemmCounterBytes, always reserved), x~, y', then (M > kSkinnyMaxM) the
-// GEMM's partial tiles, each part 256-byte aligned.  x~ is float32 below
+// GEMM's partial tiles, then (M == 1, shapes f4_slices admits) the f4
+// region, each part 256-byte aligned.  x~ is float32 below
 // kBf16MinM rows and bf16 from there on.
 size_t workspace_bytes(int32_t M, int32_t N, int32_t K);
 size_t workspace_xt_offset();

@@ -1,0 +1,161 @@
+"""GPU parity of the one-row 2-bit decode product on the FP4 x FP8 matrix
+cores (the fused linear at M = 1 on layers of at least 2^27 weights, HARP
+technical summary §2.4 with the per-group uniform grid standing in for the
+quantizer).
+
+x~ is not rounded on this path (eight FP8 residual planes per 32-input
+block carry it to about 2^-32 of the block maximum), so every case meets the
+float32 bar of the decode product against the unrounded oracle.  The cases
+cover each way the K dimension is cut (one slice; split K over 4 and 8
+slices, equal and ragged), x~ with zero, tiny, subnormal and outlier
+blocks, the edge
+weight format (zero-points 0 and 2^B - 1, subnormal fp16 scales), a
+workspace reused across shapes and products (the split-K counters end at
+zero), repeatability, and the no-allocation entry point.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import harp_oracle as O
+from synth import workloads as S
+
+pytestmark = pytest.mark.gpu
+
+FP32_PATH_TOL = 2e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rotated_bit_amd  # noqa: F401
+    yield
+
+
+def H():
+    import rotated_bit_amd
+    return rotated_bit_amd
+
+
+def D():
+    import devbuf
+    return devbuf
+
+
+def rng(*k):
+    return np.random.default_rng(np.random.SeedSequence([4417, *k]))
+
+
+def oracle_yp(li, xt, chunk=2048):
+    """Unrounded oracle product y' = w_hat x~, rows of w_hat in chunks."""
+    lin, w = li.lin, li.W
+    yp = np.empty((xt.shape[0], lin.N))
+    s16, z16 = w.scale.view(np.float16), w.zero.view(np.float16)
+    for r0 in range(0, lin.N, chunk):
+        rr = slice(r0, min(r0 + chunk, lin.N))
+        wh = O.dequant(O.unpack(w.words[rr], w.bits, lin.K), s16[rr], z16[rr])
+        yp[:, rr] = xt @ wh.T
+    return yp
+
+
+def oracle_y(li, x64):
+    """Unrounded oracle linear: x~ = F_V x, y' = w_hat x~, y = F_U^T y'."""
+    lin = li.lin
+    xt = O.forward(x64, D().cs64(li.V), li.V.sign_bits, lin.b_v)
+    return O.transpose(oracle_yp(li, xt), D().cs64(li.U), li.U.sign_bits, lin.b_u)
+
+
+def run(li, ws=None, noalloc=False):
+    d = D()
+    lin = li.lin
+    V, U, W = d.dev_rotation(li.V), d.dev_rotation(li.U), d.dev_qweight(li.W)
+    x = d.dev_x(li.x, li.x_dtype)
+    y = torch.empty((li.M, lin.N), dtype=torch.float32, device="cuda")
+    if noalloc:
+        H().harp_linear_fused_noalloc(V, W, U, x, y)
+    else:
+        H().harp_linear_fused(V, W, U, x, y, d.workspace(li.M, lin.N, lin.K) if ws is None else ws)
+    torch.cuda.synchronize()
+    return y
+
+
+def check(name, li, y):
+    ref = oracle_y(li, D().x_f64(li.x, li.x_dtype))
+    r = O.rel_l2(D().host(y), ref)
+    print(f"[{name}] rel_l2={r:.3e}", flush=True)
+    assert r <= FP32_PATH_TOL
+    return r
+
+
+def layer(K, N, b_v, b_u, seed, bits=2, xdt="bf16"):
+    cfg = S.Config(60 + seed, "f4", (S.Linear("f", K, N, b_v, b_u),), (bits,), (1,),
+                   x_dtype=xdt)
+    return S.layer_inputs(cfg, 0, bits, 1)
+
+
+# (K, N, b_v, b_u), all at least 2^27 weights: one slice of 64 steps (1024
+# tiles); split K 4 ways (512 tiles, 32 steps each); 4 ragged slices of
+# 16-17 step pairs; 8 ragged slices of 17 step pairs (256 tiles)
+F4_SHAPES = [(8192, 16384, 8192, 256), (16384, 8192, 256, 8192), (16640, 8192, 256, 256),
+             (34816, 4096, 256, 4096)]
+
+
+@pytest.mark.parametrize("K,N,b_v,b_u", F4_SHAPES)
+def test_f4_shapes(K, N, b_v, b_u):
+    li = layer(K, N, b_v, b_u, seed=K % 97)
+    check(f"f4 {K}->{N}", li, run(li))
+
+
+def test_f4_special_inputs():
+    """x~ blocks of zeros, of tiny normal and subnormal float32 values, with
+    a single large outlier, and of mixed magnitudes (b_V = 2, so each block
+    of x reaches x~ mixed only within pairs)."""
+    li = layer(8192, 16384, 2, 256, seed=3, xdt="f32")
+    g = rng(1)
+    x = g.standard_normal((1, 8192)).astype(np.float32)
+    x[0, 0:64] = 0.0                                   # a whole group of zeros
+    x[0, 64:96] = 1e-35 * g.standard_normal(32)        # tiny normals
+    x[0, 96:128] = 3e-41 * np.sign(g.standard_normal(32))   # float32 subnormals
+    x[0, 128:160] = 1e-3 * g.standard_normal(32)
+    x[0, 140] = 3e4                                    # one outlier in that block
+    x[0, 160:192] = np.ldexp(g.standard_normal(32), g.integers(-60, 40, 32))
+    li = S.LayerInputs(li.lin, 2, 1, x, "f32", li.V, li.U, li.W)
+    check("f4 special x", li, run(li))
+
+
+def test_f4_wide_weights():
+    """Zero-points at 0 and 3 and subnormal fp16 scales on the split path."""
+    li = layer(16384, 8192, 256, 8192, seed=4)
+    w = S.qweight(8192, 16384, 2, rng(2), spread="wide")
+    li = S.LayerInputs(li.lin, 2, 1, li.x, li.x_dtype, li.V, li.U, w)
+    check("f4 wide weights", li, run(li))
+
+
+def test_f4_repeatable_and_counters_left_zero():
+    """Two calls on one workspace are bitwise equal; a larger batch on the
+    same workspace in between (its own split K) disturbs nothing; the
+    counter area ends at zero."""
+    li1 = layer(16384, 8192, 256, 8192, seed=5)
+    cfg16 = S.Config(65, "f4", (li1.lin,), (2,), (16,))
+    li16 = S.layer_inputs(cfg16, 0, 2, 16)
+    li16 = S.LayerInputs(li1.lin, 2, 16, li16.x, li16.x_dtype, li1.V, li1.U, li1.W)
+    nbytes = max(H().harp_linear_workspace_bytes(M, 8192, 16384) for M in (1, 16))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    a = run(li1, ws).clone()
+    y16 = run(li16, ws)
+    b = run(li1, ws)
+    assert torch.equal(a, b)
+    check("f4 after reuse", li1, b)
+    ref16 = oracle_y(li16, D().x_f64(li16.x, li16.x_dtype))
+    assert O.rel_l2(D().host(y16), ref16) <= FP32_PATH_TOL
+    assert int(ws[:2048].view(torch.int32).abs().sum().item()) == 0
+
+
+@pytest.mark.parametrize("K,N,b_v,b_u", [(8192, 16384, 8192, 256), (16384, 8192, 256, 8192)])
+def test_f4_noalloc(K, N, b_v, b_u):
+    """No-allocation entry point: one K slice (no counters) on the FP4 path
+    (8192 -> 16384); 16384 -> 8192 needs split K, so it takes the vector-ALU
+    product there."""
+    li = layer(K, N, b_v, b_u, seed=6)
+    check(f"f4 noalloc {K}->{N}", li, run(li, noalloc=True))
