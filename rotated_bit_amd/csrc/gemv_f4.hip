@@ -186,7 +186,7 @@ __global__ __launch_bounds__(256) void f4_planes_kernel(const float* __restrict_
 // LDS keeps each step's 1024 plane bytes followed by 16 zero bytes, so a
 // lane forms its operand (plane bytes in one half, zeros in the other) from
 // two reads at the same immediate offset and no selects.
-constexpr int kPairs = 8;                 // step pairs per chunk
+constexpr int kPairs = 2;                 // step pairs per chunk
 constexpr int kSzStride = kF4MaxSliceSteps + 1;   // LDS dwords per row of scales / zeros
 constexpr int kBatchPairs = 2;            // step pairs per batch of matrix instructions
 
@@ -265,19 +265,32 @@ __global__ __launch_bounds__(kF4Threads, 1) void gemv_f4_kernel(
         reinterpret_cast<uint32_t*>(lpsc)[tid + q * kF4Threads] = ps[q];
     if (tid < 2 * ns) lsx[tid] = sxv;
     // scales and zeros: np 8-byte words (four groups) per row, consecutive
-    // threads along a row; rows past N re-read the last row
+    // threads along a row, every load issued before the first LDS write;
+    // rows past N re-read the last row
+    constexpr int kSzPer = kF4WgWaves * 16 * (kF4MaxSliceSteps / 2) / kF4Threads;
     const int row0 = static_cast<int>(blockIdx.x) * kF4WgWaves * 16;
     const int nw = kF4WgWaves * 16 * np;
-    for (int i = tid; i < nw; i += kF4Threads) {
+    uint2 sv[kSzPer], zv[kSzPer];
+#pragma unroll
+    for (int q = 0; q < kSzPer; ++q) {
+      const int i = min(tid + q * kF4Threads, nw - 1);
       const int r = i / np;
-      const int q = i - r * np;
-      const size_t gi = static_cast<size_t>(min(row0 + r, N - 1)) * (K / (4 * kGroup)) + pa + q;
-      const uint2 sv = reinterpret_cast<const uint2*>(sc)[gi];
-      const uint2 zv = reinterpret_cast<const uint2*>(zr)[gi];
-      lsc[r * kSzStride + 2 * q] = sv.x;
-      lsc[r * kSzStride + 2 * q + 1] = sv.y;
-      lzr[r * kSzStride + 2 * q] = zv.x;
-      lzr[r * kSzStride + 2 * q + 1] = zv.y;
+      const size_t gi =
+          static_cast<size_t>(min(row0 + r, N - 1)) * (K / (4 * kGroup)) + pa + (i - r * np);
+      sv[q] = reinterpret_cast<const uint2*>(sc)[gi];
+      zv[q] = reinterpret_cast<const uint2*>(zr)[gi];
+    }
+#pragma unroll
+    for (int q = 0; q < kSzPer; ++q) {
+      const int i = tid + q * kF4Threads;
+      if (i < nw) {
+        const int r = i / np;
+        const int o = r * kSzStride + 2 * (i - r * np);
+        lsc[o] = sv[q].x;
+        lsc[o + 1] = sv[q].y;
+        lzr[o] = zv[q].x;
+        lzr[o + 1] = zv[q].y;
+      }
     }
   }
   __syncthreads();
@@ -349,13 +362,14 @@ __global__ __launch_bounds__(kF4Threads, 1) void gemv_f4_kernel(
     }
   };
   // chunk c: request chunk c + 1 into the other register set, then use
-  // chunk c (requested one chunk earlier)
+  // chunk c (pairs past the slice all re-read its last pair).  One small
+  // chunk ahead measured faster than two, or than larger chunks.  The second
+  // half is unconditional (past the last chunk every step is zeroed): under
+  // a branch its loads would be sunk behind the first half's use
   auto chunk = [&](int c, const Chunk& cur, Chunk& nxt) {
-    load(c + 1, nxt);   // pairs past the slice all re-read its last pair
+    load(c + 1, nxt);
     process(cur, c);
   };
-  // unconditional second half (past the last chunk every step is zeroed):
-  // under a branch the loads into B would be sunk behind the use of A
   for (int c = 0; c < nch; c += 2) {
     chunk(c, A, B);
     chunk(c + 1, B, A);
