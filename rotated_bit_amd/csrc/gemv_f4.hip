@@ -10,8 +10,8 @@
 //     copy shifted right by two give sixteen FP4 values with two
 //     instructions each, and the column scale 2^1 restores q;
 //   * x~ (float32, not rounded) is carried as eight FP8 (e4m3) planes of
-//     signed 4-bit digits, one exponent per quantization group and plane,
-//     which reproduce x~ to 2^-32 of the group maximum (see build_step).
+//     signed base-16 digits, one exponent per quantization group and plane,
+//     which reproduce x~ to 2^-28 of the group maximum (see build_step).
 // A small kernel builds the planes once per call; each product workgroup
 // copies its K slice of them into LDS and streams the codes of its rows.
 //
@@ -81,20 +81,21 @@ constexpr int kStepLds = 1024 + 16;       // LDS bytes per step: planes, then 16
 // 16-lane row per 32-input block b, two inputs per lane (block offsets
 // u = j and j + 16 for lane j of the row); rows 0-1 and rows 2-3 are the
 // step's two quantization groups.  Per group, with 2^E <= max |x~| < 2^(E+1),
-// plane p holds the signed digit d_p = rint(r_p / 2^(E-3-4p)) of every input
-// (r_0 = x~, r_{p+1} = r_p - d_p 2^(E-3-4p), each step exact), so
-// |d_0| <= 16, |d_p| <= 8 after that, and the eight planes carry x~ to
-// 2^(E-32).  Digits are small integers, exact in FP8, and one plane of one
-// group shares one scale: every product the matrix cores sum for a result
-// is an integer of at most 48 times that scale (their sums are exact; with
-// products spread over the whole FP8 range the instruction's sum was
-// measured to lose bits about 2^-11 below its largest term).  Planes whose
-// scale would fall below 2^-127 (groups below about 2^-96) stay zero.
+// every input becomes the integer X = rint(x~ 2^(27-E)) (|X| < 2^28, error
+// at most 2^(E-28)), written in balanced base 16, X = sum_i d_i 16^i with
+// digits d_i in [-8, 7] (the nibbles of X + 0x88888888, less 8), and plane
+// p holds digit 7 - p, whose weight is 2^(E+1-4p).  Digits are small
+// integers, exact in FP8, and one plane of one group shares one scale:
+// every product the matrix cores sum for a result is an integer of at most
+// 24 times that scale, so their sums are exact (with products spread over
+// the whole FP8 range the instruction's sum was measured to lose bits about
+// 2^-11 below its largest term).  Groups below 2^-100 (a plane's scale
+// would fall below 2^-127) are left as zero.
 // xs: the step's inputs (x~ + 256 t + 64 e for step 2t + e).  Planes go to
 // pl[lane][16] in operand order: block offset u becomes operand offset
 // o = pi^-1(u) and lands in operand lane (p + 8h) + 16 g, byte o % 16, with
 // h = b / 2 and g = 2 (b % 2) + o / 16; bytes 1024..1039 are zeroed.  The
-// scale byte of plane p (E - 3 - 4p + 127) goes to psc[lane] for the lanes
+// scale byte of plane p (E + 1 - 4p + 127) goes to psc[lane] for the lanes
 // that supply operand row p + 8h's scale of the group's blocks; the rows of
 // the other group half get 127 (their operand bytes there are zero).  The
 // sums of x~ over the step's groups 4t + e and 4t + 2 + e (fixed order) go
@@ -104,8 +105,8 @@ __device__ __forceinline__ void build_step(const float* __restrict__ xs, uint8_t
   const int j = lane & 15;
   const int b = lane >> 4;
   const int k0 = 128 * (b >> 1) + 32 * (b & 1) + j;
-  float ra = xs[k0];
-  float rb = xs[k0 + 16];
+  const float ra = xs[k0];
+  const float rb = xs[k0 + 16];
   {
     const float t = row_sum(ra + rb);
     // rows 1 and 3 add lane 15 of rows 0 and 2 (row_bcast:15)
@@ -122,25 +123,24 @@ __device__ __forceinline__ void build_step(const float* __restrict__ xs, uint8_t
     m = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
   }
   const int E = static_cast<int>((__float_as_uint(m) >> 23) & 0xff) - 127;   // floor(log2 m)
+  const bool live = m > 0.0f && E >= -100;
+  const uint32_t ya = live ? static_cast<uint32_t>(__float2int_rn(ldexpf(ra, 27 - E))) + 0x88888888u
+                           : 0x88888888u;
+  const uint32_t yb = live ? static_cast<uint32_t>(__float2int_rn(ldexpf(rb, 27 - E))) + 0x88888888u
+                           : 0x88888888u;
   const int o = 8 * (j & 1) + (j >> 1);   // operand offset of u = j (u = j + 16: o + 16)
   const int h = b >> 1;
   uint8_t* dst = pl + 2 * (b & 1) * 256 + o;
   uint8_t* sdst = psc + 16 * b;
 #pragma unroll
   for (int p = 0; p < kPlanes; ++p) {
-    const int sb = E - 3 - 4 * p + 127;   // scale byte of this plane
-    const bool live = m > 0.0f && sb >= 0;
-    uint32_t enc = 0;
-    if (live) {
-      const float da = rintf(ldexpf(ra, 127 - sb));
-      const float db = rintf(ldexpf(rb, 127 - sb));
-      enc = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(da, db, 0, false));
-      ra -= ldexpf(da, sb - 127);
-      rb -= ldexpf(db, sb - 127);
-    }
+    const int sh = 4 * (kPlanes - 1 - p);
+    const float da = static_cast<float>(static_cast<int>((ya >> sh) & 15u) - 8);
+    const float db = static_cast<float>(static_cast<int>((yb >> sh) & 15u) - 8);
+    const uint32_t enc = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(da, db, 0, false));
     dst[(p + 8 * h) * 16] = static_cast<uint8_t>(enc & 0xffu);
     dst[256 + (p + 8 * h) * 16] = static_cast<uint8_t>((enc >> 8) & 0xffu);
-    if (j == 0) sdst[p + 8 * h] = static_cast<uint8_t>(live ? sb : 127);
+    if (j == 0) sdst[p + 8 * h] = static_cast<uint8_t>(live ? E + 1 - 4 * p + 127 : 127);
     if (j == 1) sdst[p + 8 * (1 - h)] = 127;
   }
 }
