@@ -202,6 +202,27 @@ def fused_cell(torch, H, lin, layers, M, bits, reps=5):
     return out
 
 
+def product_cell(torch, H, lin, layers, reps=5):
+    """The one-row product alone over the cell's instances, on one float32
+    x~: harp_deq_gemv_ws with its workspace (the FP4 x FP8 matrix-core
+    product where it applies) and without (the vector-ALU product)."""
+    xt = torch.randn((1, lin.K), dtype=torch.float32, device="cuda")
+    yp = torch.empty((1, lin.N), dtype=torch.float32, device="cuda")
+    nb = gemv_bytes(1, lin.N, lin.K, layers[0].W.bits)
+    out = {"alg_bytes": nb, "instances": len(layers)}
+    wsb = H.harp_deq_gemv_workspace_bytes(1, lin.N, lin.K)
+    ws = torch.zeros(max(256, wsb), dtype=torch.uint8, device="cuda")
+    for name, w in (("fp4", ws if wsb else None), ("vector", None)):
+        ms, _ = time_graph(torch, lambda: [H.harp_deq_gemv_ws(L.W, xt, yp, w) for L in layers],
+                           reps)
+        us = ms * 1e3 / len(layers)
+        out[f"{name}_us"] = round(us, 3)
+        out[f"{name}_GB_s"] = round(nb / (us * 1e-6) / 1e9, 1)
+        out[f"{name}_frac_hbm"] = round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    del ws, xt, yp
+    return out
+
+
 def chain_cell(torch, H, lin, layers, M):
     """The layers as stacks of 48 dependent layers, one harp_linear_chain
     launch each: a stack's first layer reads the cell's input x, each next
@@ -414,6 +435,8 @@ def main():
                 ln, ls = build_layers(torch, H, "l70b_slice", li_idx, b, (1, 32), cnt,
                                       torch.float32)
                 cell = {f"M{m}": fused_cell(torch, H, ln, ls, m, b) for m in (1, 32)}
+                if li_idx > 0 and b == 2:
+                    cell["product_M1"] = product_cell(torch, H, ln, ls)
                 if li_idx == 0:
                     for L in ls:
                         L.ys[1] = torch.empty((1, ln.N), dtype=torch.bfloat16, device="cuda")

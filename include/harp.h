@@ -252,6 +252,30 @@ harp_status harp_deq_gemv(const harp_qweight *W, const float *xt, float *yt,
                           int32_t M, harp_stream stream);
 
 /*
+ * harp_deq_gemv with an optional workspace (the same product, reading
+ * and contract: float32, x~ not rounded).  With a workspace, one row
+ * (M = 1) of 2-bit codes on a layer of at least 2^27 weights (N a multiple
+ * of 16, K of 256) runs on the FP4 x FP8 matrix cores: the codes enter as
+ * exact FP4 values and x~ as eight FP8 planes of base-16 digits per
+ * quantization group (x~ carried to 2^-28 of its group maximum, every
+ * matrix-core sum exact), K split into slices summed in a fixed order
+ * (bitwise reproducible).  Other calls, and NULL, run harp_deq_gemv.
+ *   xt  [M][W->K] float32;  yt  [M][W->N] float32.
+ *   workspace  optional: NULL, or at least harp_deq_gemv_workspace_bytes(M,
+ *              N, K) bytes, 256-byte aligned, zero-filled before its first
+ *              use (its first 2048 bytes are arrival counters that every
+ *              call leaves at zero; the rest needs no initialisation).
+ *              Calls that share a workspace must not overlap in time.
+ */
+harp_status harp_deq_gemv_ws(const harp_qweight *W, const float *xt, float *yt,
+                             int32_t M, void *workspace, size_t ws_bytes,
+                             harp_stream stream);
+
+/* Workspace bytes harp_deq_gemv_ws uses for M rows of a K -> N product (0:
+ * it uses none for this shape); 0 for out-of-range sizes. */
+size_t harp_deq_gemv_workspace_bytes(int32_t M, int32_t N, int32_t K);
+
+/*
  * y' = w_hat (F_V x) for small batches in one launch: every workgroup applies
  * the input rotation (technical summary §2.1-2.2, as harp_rotate_in with a
  * float32 x~) to the whole input row in its local memory while its weights

@@ -30,7 +30,8 @@ HARP_F32 = 0
 HARP_BF16 = 1
 
 EXPORTED = (
-    "harp_rotate_in", "harp_rotate_out", "harp_deq_gemv", "harp_rotate_in_deq_gemv",
+    "harp_rotate_in", "harp_rotate_out", "harp_deq_gemv", "harp_deq_gemv_ws",
+    "harp_deq_gemv_workspace_bytes", "harp_rotate_in_deq_gemv",
     "harp_deq_gemm",
     "harp_deq_gemm_workspace_bytes", "harp_linear_workspace_bytes", "harp_linear_fused",
     "harp_linear_fused_noalloc", "harp_linear_chain", "harp_linear_chain_workspace_bytes",
@@ -95,6 +96,9 @@ def _load() -> ctypes.CDLL:
         "harp_rotate_in": (c_int32, [R, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p]),
         "harp_rotate_out": (c_int32, [R, c_void_p, c_void_p, c_int32, c_int32, c_void_p]),
         "harp_deq_gemv": (c_int32, [Q, c_void_p, c_void_p, c_int32, c_void_p]),
+        "harp_deq_gemv_ws": (c_int32, [Q, c_void_p, c_void_p, c_int32, c_void_p, c_size_t,
+                                       c_void_p]),
+        "harp_deq_gemv_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
         "harp_rotate_in_deq_gemv": (c_int32, [R, Q, c_void_p, c_int32, c_void_p, c_int32,
                                                c_void_p]),
         "harp_deq_gemm": (c_int32, [Q, c_void_p, c_void_p, c_int32, c_void_p, c_size_t,
@@ -238,6 +242,18 @@ def harp_deq_gemv(W: QWeight, xt, yt, M: int | None = None, stream=None) -> None
     M = xt.shape[0] if M is None else M
     _check(lib.harp_deq_gemv(ctypes.byref(W.c), _ptr(xt), _ptr(yt), M, _stream(stream)),
            "harp_deq_gemv")
+
+
+def harp_deq_gemv_ws(W: QWeight, xt, yt, workspace=None, M: int | None = None,
+                     stream=None) -> None:
+    M = xt.shape[0] if M is None else M
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.harp_deq_gemv_ws(ctypes.byref(W.c), _ptr(xt), _ptr(yt), M, _ptr(workspace),
+                                ws_bytes, _stream(stream)), "harp_deq_gemv_ws")
+
+
+def harp_deq_gemv_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib.harp_deq_gemv_workspace_bytes(M, N, K))
 
 
 def harp_rotate_in_deq_gemv(V: Rotation, W: QWeight, x, yt, M: int | None = None,

@@ -154,6 +154,29 @@ harp_status harp_deq_gemv(const harp_qweight* W, const float* xt, float* yt,
   return from_hip(harp::launch_gemv(*W, xt, yt, M, as_stream(stream)));
 }
 
+harp_status harp_deq_gemv_ws(const harp_qweight* W, const float* xt, float* yt, int32_t M,
+                             void* workspace, size_t ws_bytes, harp_stream stream) {
+  const harp_status st = harp::validate_gemv_ws(W, xt, yt, M, workspace, ws_bytes);
+  if (st != HARP_OK || M == 0) return st;
+  const int32_t slices =
+      workspace != nullptr ? harp::f4_slices(M, W->N, W->K, W->bits, true) : 0;
+  if (slices > 0) {
+    char* ws = static_cast<char*>(workspace);
+    return from_hip(harp::launch_gemv_f4(*W, xt, yt,
+                                         reinterpret_cast<uint8_t*>(ws + harp::kGemmCounterBytes),
+                                         reinterpret_cast<uint32_t*>(ws), slices,
+                                         as_stream(stream)));
+  }
+  return from_hip(harp::launch_gemv(*W, xt, yt, M, as_stream(stream)));
+}
+
+size_t harp_deq_gemv_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  if (M < 0 || M > HARP_MAX_M || N < 1 || N > HARP_MAX_DIM || K < 64 ||
+      K > HARP_MAX_DIM)
+    return 0;
+  return harp::gemv_workspace_bytes(M, N, K);
+}
+
 harp_status harp_rotate_in_deq_gemv(const harp_rotation* V, const harp_qweight* W,
                                     const void* x, harp_dtype x_dt, float* yt,
                                     int32_t M, harp_stream stream) {

@@ -109,6 +109,15 @@ harp_status validate_rotate_gemv(const harp_rotation* V, const harp_qweight* W,
   return HARP_OK;
 }
 
+harp_status validate_gemv_ws(const harp_qweight* W, const void* xt, const void* yt,
+                             int32_t M, const void* workspace, size_t ws_bytes) {
+  HARP_TRY(validate_gemv(W, xt, yt, M));
+  if (M == 0 || workspace == nullptr) return HARP_OK;   // no workspace: harp_deq_gemv
+  if (!aligned(workspace, 256)) return HARP_ERR_ALIGN;
+  if (ws_bytes < gemv_workspace_bytes(M, W->N, W->K)) return HARP_ERR_WORKSPACE;
+  return HARP_OK;
+}
+
 harp_status validate_gemm(const harp_qweight* W, const void* xt, const void* yt,
                           int32_t M, const void* workspace, size_t ws_bytes) {
   HARP_TRY(validate_gemv(W, xt, yt, M));
@@ -356,6 +365,12 @@ size_t f4_partial_offset(int32_t K) {
 size_t f4_region_bytes(int32_t N, int32_t K, int32_t slices) {
   if (slices <= 0) return 0;
   return f4_partial_offset(K) + (slices > 1 ? align256(static_cast<size_t>(slices) * N * 4) : 0);
+}
+
+size_t gemv_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  // the size query does not know the bit width: sized for 2-bit codes
+  const int32_t s = f4_slices(M, N, K, 2, true);
+  return s > 0 ? kGemmCounterBytes + f4_region_bytes(N, K, s) : 0;
 }
 
 size_t workspace_f4_offset(int32_t M, int32_t N, int32_t K) {

@@ -21,6 +21,8 @@ harp_status validate_gemv(const harp_qweight* W, const void* xt, const void* yt,
                           int32_t M);
 harp_status validate_rotate_gemv(const harp_rotation* V, const harp_qweight* W,
                                 const void* x, int x_dt, const void* yt, int32_t M);
+harp_status validate_gemv_ws(const harp_qweight* W, const void* xt, const void* yt,
+                             int32_t M, const void* workspace, size_t ws_bytes);
 harp_status validate_gemm(const harp_qweight* W, const void* xt, const void* yt,
                           int32_t M, const void* workspace, size_t ws_bytes);
 harp_status validate_fused(const harp_rotation* V, const harp_qweight* W,
@@ -70,6 +72,9 @@ struct WideSplit {
 WideSplit skinny_wide_split(int32_t M, int32_t N, int32_t K, bool allow_split);
 size_t skinny_partial_bytes(int32_t M, int32_t N, int32_t K);
 size_t gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
+// harp_deq_gemv_ws's workspace: the counter area (kGemmCounterBytes), then
+// the f4 region; 0 when the FP4 product does not apply to the shape.
+size_t gemv_workspace_bytes(int32_t M, int32_t N, int32_t K);
 size_t gemm_partial_bytes(int32_t M, int32_t N, int32_t K);
 
 // Batch ranges of the products.  harp_deq_gemm runs the small-batch

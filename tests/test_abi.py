@@ -157,6 +157,49 @@ def test_product_data_checks():
     assert L.lib.harp_dequant(ctypes.byref(W), FAKE, 3, None) == L.HARP_ERR_DTYPE
 
 
+def test_deq_gemv_ws_checks():
+    """harp_deq_gemv_ws: harp_deq_gemv's checks, then (a workspace given)
+    alignment and size; the size query is 0 where the FP4 product does not
+    apply."""
+    gw = L.lib.harp_deq_gemv_ws
+    W = qw()
+    assert gw(None, FAKE, FAKE, 1, None, 0, None) == L.HARP_ERR_NULL
+    assert gw(ctypes.byref(W), 0, FAKE, 1, None, 0, None) == L.HARP_ERR_NULL
+    assert gw(ctypes.byref(W), FAKE, MISALIGNED, 3, None, 0, None) == L.HARP_ERR_ALIGN
+    assert gw(ctypes.byref(W), FAKE, FAKE, -2, None, 0, None) == L.HARP_ERR_SHAPE
+    assert gw(ctypes.byref(W), 0, 0, 0, FAKE + 16, 0, None) == L.HARP_OK
+    big = qw(N=28672, K=8192)
+    need = L.harp_deq_gemv_workspace_bytes(1, 28672, 8192)
+    assert need > 0
+    assert gw(ctypes.byref(big), FAKE, FAKE, 1, FAKE + 16, need, None) == L.HARP_ERR_ALIGN
+    assert gw(ctypes.byref(big), FAKE, FAKE, 1, FAKE, need - 1, None) == L.HARP_ERR_WORKSPACE
+    assert gw(ctypes.byref(big), 0, FAKE, 1, FAKE, need, None) == L.HARP_ERR_NULL
+
+
+def test_deq_gemv_workspace_bytes():
+    """Counter area (2048 bytes), then planes (1 KB per 128 inputs), scale
+    bytes (64 per 128 inputs), group sums (4 per 64 inputs, to a 256-byte
+    boundary) and, with split K, slices x N float32 partials."""
+    g = L.harp_deq_gemv_workspace_bytes
+    C = 2048
+    up = (8192 // 128) * 1088 + 8192 // 64 * 4          # 70144, already 256-aligned
+    # 28672 x 8192: 1792 row tiles, one K slice (no partials)
+    assert g(1, 28672, 8192) == C + up
+    # 8192 x 28672: 512 tiles; 2048 waves want 4 slices (56 steps each <= 64)
+    down = (28672 // 128) * 1088 + 28672 // 64 * 4
+    assert g(1, 8192, 28672) == C + (down + 255) // 256 * 256 + 4 * 8192 * 4
+    # 4096 x 34816: 256 tiles -> 8 slices of 17 step pairs
+    k = 34816
+    assert g(1, 4096, k) == C + ((k // 128) * 1088 + k // 64 * 4 + 255) // 256 * 256 \
+        + 8 * 4096 * 4
+    # below 2^27 weights, more than one row, ragged N or K: none
+    assert g(1, 8192, 8192) == 0
+    assert g(2, 28672, 8192) == 0
+    assert g(1, 28680, 8192) == 0
+    assert g(1, 28672, 8320) == 0
+    assert g(0, 28672, 8192) == 0 and g(-1, 28672, 8192) == 0
+
+
 def test_workspace_bytes():
     f = L.harp_linear_workspace_bytes
     g = L.harp_deq_gemm_workspace_bytes

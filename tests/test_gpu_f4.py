@@ -3,12 +3,13 @@ cores (the fused linear at M = 1 on layers of at least 2^27 weights, HARP
 technical summary §2.4 with the per-group uniform grid standing in for the
 quantizer).
 
-x~ is not rounded on this path (eight FP8 residual planes per 32-input
-block carry it to about 2^-32 of the block maximum), so every case meets the
-float32 bar of the decode product against the unrounded oracle.  The cases
+x~ is not rounded on this path (eight FP8 planes of base-16 digits per
+quantization group carry it to 2^-28 of the group maximum, and every
+matrix-core sum is exact), so every case meets the float32 bar of the
+decode product against the unrounded oracle.  The cases
 cover each way the K dimension is cut (one slice; split K over 4 and 8
-slices, equal and ragged), x~ with zero, tiny, subnormal and outlier
-blocks, the edge
+slices, equal and ragged), the product alone through harp_deq_gemv_ws, x~
+with zero, tiny, subnormal and outlier blocks, the edge
 weight format (zero-points 0 and 2^B - 1, subnormal fp16 scales), a
 workspace reused across shapes and products (the split-K counters end at
 zero), repeatability, and the no-allocation entry point.
@@ -105,6 +106,38 @@ F4_SHAPES = [(8192, 16384, 8192, 256), (16384, 8192, 256, 8192), (16640, 8192, 2
 def test_f4_shapes(K, N, b_v, b_u):
     li = layer(K, N, b_v, b_u, seed=K % 97)
     check(f"f4 {K}->{N}", li, run(li))
+
+
+@pytest.mark.parametrize("K,N", [(8192, 28672), (28672, 8192), (34816, 4096)])
+def test_f4_deq_gemv_ws(K, N):
+    """The product alone (harp_deq_gemv_ws with a workspace: one K slice at
+    28672 rows, 4 and 8 slices below) against the oracle product on the
+    same float32 x~ (random, with a zero group and an outlier); twice on one
+    workspace, bitwise equal, counters left at zero; without a workspace the
+    vector-ALU product, within the same bar."""
+    li = layer(K, N, 256, 256, seed=N % 89)
+    g = rng(3, K)
+    xt = g.standard_normal((1, K)).astype(np.float32)
+    xt[0, 128:192] = 0.0
+    xt[0, 1000] = 500.0
+    d = D()
+    W = d.dev_qweight(li.W)
+    ws = torch.zeros(H().harp_deq_gemv_workspace_bytes(1, N, K), dtype=torch.uint8,
+                     device="cuda")
+    x_d = d.dev(xt)
+    outs = []
+    for w in (ws, ws, None):
+        yt = torch.empty((1, N), dtype=torch.float32, device="cuda")
+        H().harp_deq_gemv_ws(W, x_d, yt, w)
+        outs.append(yt)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    assert int(ws[:2048].view(torch.int32).abs().sum().item()) == 0
+    ref = oracle_yp(li, xt.astype(np.float64))
+    for name, y in (("FP4", outs[0]), ("vector", outs[2])):
+        r = O.rel_l2(d.host(y), ref)
+        print(f"[f4 deq_gemv_ws {K}->{N} {name}] rel_l2={r:.3e}", flush=True)
+        assert r <= FP32_PATH_TOL
 
 
 def test_f4_special_inputs():
