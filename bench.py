@@ -285,6 +285,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other configurations of the workload set")
+    ap.add_argument("--configs", default="l7b_mlp,l70b_slice,q8b_prefill",
+                    help="comma-separated configurations to run (profiling runs)")
     ap.add_argument("--no-legs", action="store_true",
                     help="skip the int8-angle, mixed-radix and offline-preparation legs")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -408,9 +410,11 @@ def main():
     # ---------------- the other configurations ------------------------------
     configs = {}
     if not args.no_configs and not args.only_headline:
+        wanted = set(args.configs.split(","))
         # Llama-2-7B MLP pair, M = 1 and 16
         mlp = {}
-        for li_idx, name in ((0, "up_4096x11008"), (1, "down_11008x4096")):
+        for li_idx, name in (((0, "up_4096x11008"), (1, "down_11008x4096"))
+                             if "l7b_mlp" in wanted else ()):
             from synth import workloads as S
             ln = S.CONFIGS["l7b_mlp"].linears[li_idx]
             cnt = count_for(alg_bytes(16, ln.N, ln.K, 2, ln.b_v, ln.b_u))
@@ -418,15 +422,16 @@ def main():
             mlp[name] = {f"M{m}": fused_cell(torch, H, ln, ls, m, 2) for m in (1, 16)}
             del ls
             torch.cuda.empty_cache()
-        configs["l7b_mlp_2bit"] = mlp
+        if mlp:
+            configs["l7b_mlp_2bit"] = mlp
         log("l7b_mlp: " + json.dumps(mlp))
 
         # Llama-70B-shaped slice, M = 1 and 32, 2/3/4 bits; the 8192-wide
         # attention projection also as a dependent stack at M = 1
         l70 = {}
         from synth import workloads as S
-        for li_idx, name in ((0, "attn_8192x8192"), (1, "up_8192x28672"),
-                             (2, "down_28672x8192")):
+        for li_idx, name in (((0, "attn_8192x8192"), (1, "up_8192x28672"),
+                              (2, "down_28672x8192")) if "l70b_slice" in wanted else ()):
             for b in (2, 3, 4):
                 ln = S.CONFIGS["l70b_slice"].linears[li_idx]
                 cnt = count_for(alg_bytes(32, ln.N, ln.K, b, ln.b_v, ln.b_u))
@@ -455,12 +460,14 @@ def main():
                 log(f"l70b {name} {b}-bit: " + json.dumps(cell))
                 del ls
                 torch.cuda.empty_cache()
-        configs["l70b_slice"] = l70
+        if l70:
+            configs["l70b_slice"] = l70
 
         # Qwen3-8B-shaped prefill, M = 512, 2 and 4 bits: the GEMM alone (on
         # the rotated bf16 x~) and the whole fused linear
         pre = {}
-        for li_idx, lnm in enumerate(("attn_4096x4096", "up_4096x12288", "down_12288x4096")):
+        for li_idx, lnm in enumerate(("attn_4096x4096", "up_4096x12288", "down_12288x4096")
+                                     if "q8b_prefill" in wanted else ()):
             for b in (2, 4):
                 ln = S.CONFIGS["q8b_prefill"].linears[li_idx]
                 Mp = 512
@@ -487,7 +494,8 @@ def main():
                 log(f"q8b prefill {lnm} {b}-bit: " + json.dumps(cell))
                 del ls, xt16, gws
                 torch.cuda.empty_cache()
-        configs["q8b_prefill_M512"] = pre
+        if pre:
+            configs["q8b_prefill_M512"] = pre
 
     # ---------------- legs ---------------------------------------------------
     legs = {}
