@@ -243,9 +243,11 @@ size_t harp_rotate_mixed_workspace_bytes(int32_t dim, int32_t M, harp_dtype out_
  * linear without changing it; the backend's codebook is not on the pages,
  * so w_hat is the stand-in per-group uniform grid described at the top of
  * this header).  float32 throughout: w_hat is exact in float32 and x~ is
- * not rounded.  Up to 8 rows on the vector ALUs, from 9 rows on in 16-row
- * tiles on the float32 matrix cores (same products, float32 accumulation in
- * a different order).  Meant for decode batches; any M is accepted.
+ * not rounded.  One or two rows (and 3-bit codes up to 8 rows) on the
+ * vector ALUs; 3..8 rows of 2- and 4-bit codes on the bf16 matrix cores
+ * with x~ split into exact bf16 planes; from 9 rows on in 16-row tiles on
+ * the float32 matrix cores (same products, float32 accumulation in a
+ * different order).  Meant for decode batches; any M is accepted.
  *   xt  [M][W->K] float32;  yt  [M][W->N] float32.
  */
 harp_status harp_deq_gemv(const harp_qweight *W, const float *xt, float *yt,
