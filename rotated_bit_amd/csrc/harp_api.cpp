@@ -39,13 +39,17 @@ harp_status fused_linear(const harp_rotation& V, const harp_qweight& W, const ha
     // float32 x~: the float32 product, or the matrix cores on its two-plane
     // bf16 split
     float* xt = reinterpret_cast<float*>(ws + harp::workspace_xt_offset());
-    r = from_hip(harp::launch_rotate(V, x, x_dt, xt, HARP_F32, M, false, s));
-    if (r != HARP_OK) return r;
+    // one row on the FP4 product: with a b = 4096 / 8192 input side the
+    // rotation's last launch writes the product's planes itself
     const int32_t f4_slices = harp::f4_slices(M, W.N, W.K, W.bits, split_k);
+    uint8_t* f4r = reinterpret_cast<uint8_t*>(ws + harp::workspace_f4_offset(M, W.N, W.K));
+    const bool fold = f4_slices > 0 && harp::rotate_in_f4_supported(V, M);
+    r = from_hip(fold ? harp::launch_rotate_in_f4(V, x, x_dt, xt, f4r, s)
+                      : harp::launch_rotate(V, x, x_dt, xt, HARP_F32, M, false, s));
+    if (r != HARP_OK) return r;
     if (f4_slices > 0)
-      r = from_hip(harp::launch_gemv_f4(
-          W, xt, yp, reinterpret_cast<uint8_t*>(ws + harp::workspace_f4_offset(M, W.N, W.K)),
-          reinterpret_cast<uint32_t*>(ws), f4_slices, s));
+      r = from_hip(harp::launch_gemv_f4(W, xt, yp, f4r, reinterpret_cast<uint32_t*>(ws),
+                                        f4_slices, fold, s));
     else if (M < harp::kSplitMinM)
       r = from_hip(harp::launch_gemv(W, xt, yp, M, s));
     else if (split_k)
@@ -164,7 +168,7 @@ harp_status harp_deq_gemv_ws(const harp_qweight* W, const float* xt, float* yt, 
     char* ws = static_cast<char*>(workspace);
     return from_hip(harp::launch_gemv_f4(*W, xt, yt,
                                          reinterpret_cast<uint8_t*>(ws + harp::kGemmCounterBytes),
-                                         reinterpret_cast<uint32_t*>(ws), slices,
+                                         reinterpret_cast<uint32_t*>(ws), slices, false,
                                          as_stream(stream)));
   }
   return from_hip(harp::launch_gemv(*W, xt, yt, M, as_stream(stream)));

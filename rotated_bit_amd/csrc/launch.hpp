@@ -34,8 +34,19 @@ hipError_t launch_gemv(const harp_qweight& W, const float* xt, float* yt,
 // validate.hpp), then the product runs in `slices` K slices (f4_slices);
 // slices > 1 needs zeroed `counters` (one uint32 per 16-row tile, left
 // zero) and the partials that follow the planes in the region.
+// planes_ready: the planes are already in the region (launch_rotate_in_f4)
+// and x~ is not read.
 hipError_t launch_gemv_f4(const harp_qweight& W, const float* xt, float* yt, uint8_t* f4,
-                          uint32_t* counters, int slices, hipStream_t stream);
+                          uint32_t* counters, int slices, bool planes_ready,
+                          hipStream_t stream);
+
+// One row of x~ = F x at b = 4096 / 8192 finished straight into that
+// product's planes in the f4 region (two launches: the sub-blocks into the
+// float32 scratch, then the last three stages and the planes); x~ itself is
+// not written.
+bool rotate_in_f4_supported(const harp_rotation& R, int M);
+hipError_t launch_rotate_in_f4(const harp_rotation& R, const void* in, int in_dt,
+                               float* scratch, uint8_t* f4r, hipStream_t stream);
 
 // The same product on the bf16 matrix cores with x~ split into exact bf16
 // planes (gemv_mc.hip): kGemvMcMinM <= M <= kGemvMcMaxM, 2 or 4 bits.

@@ -22,7 +22,9 @@
 // evaluates (cos t, sin t) once for all 256 codes into an LDS table while
 // its code loads are in flight, then gathers its pairs from the table, so a
 // block's coefficient fetch is one byte per pair instead of eight.
+#include "f4_planes.hpp"
 #include "launch.hpp"
+#include "validate.hpp"
 
 #include <type_traits>
 #include "device_common.hpp"
@@ -543,34 +545,17 @@ hipError_t launch_typed(const harp_rotation& R, const void* in, void* out, int M
 // passing through one CU.
 constexpr int kTailThreads = 256;
 
-template <int LOGB, bool Q8, typename TOut>
-__global__ __launch_bounds__(kTailThreads) void rotate_in_tail_kernel(
-    const float* src, TOut* dst, const float2* __restrict__ cs,
-    const int8_t* __restrict__ codes, float step, int dim) {
+// The last three stages of residue q of block blk on the eight elements v[j]
+// = element q + (b/8) j (tab: the int8 angle table when Q8).
+template <int LOGB, bool Q8>
+__device__ __forceinline__ void tail_stages(float (&v)[8], int q, int blk,
+                                            const float2* __restrict__ cs,
+                                            const int8_t* __restrict__ codes,
+                                            const float2* tab) {
   constexpr int B = 1 << LOGB;
   constexpr int L = LOGB;
   constexpr int SB = B / 8;
-  constexpr int kParts = SB / kTailThreads;   // workgroups per block row
-  static_assert(kParts >= 1 && SB % kTailThreads == 0, "sub-blocks of 256 or more");
-  __shared__ float2 table[Q8 ? 256 : 1];
-  if constexpr (Q8) {
-    float sn, cn;
-    sincosf(fmaf(static_cast<float>(static_cast<int>(threadIdx.x) - 128), step,
-                 0.785398163397448310f), &sn, &cn);
-    table[threadIdx.x] = make_float2(cn, sn);
-    __syncthreads();
-  }
-  const int blk = blockIdx.x / kParts;
-  const int q = (blockIdx.x - blk * kParts) * kTailThreads + threadIdx.x;
-  // src and dst may be the same float32 rows: each thread reads its eight
-  // elements before it writes them
-  const size_t e0 = static_cast<size_t>(blockIdx.y) * dim + static_cast<size_t>(blk) * B + q;
-  const float* sb = src + e0;
-  TOut* db = dst + e0;
   const size_t coff = static_cast<size_t>(blk) * L * (B / 2);
-  float v[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = sb[j * SB];
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
     const int s = L - 3 + k;
@@ -580,7 +565,7 @@ __global__ __launch_bounds__(kTailThreads) void rotate_in_tail_kernel(
       const int j2 = j | (1 << k);
       const size_t c = coff + static_cast<size_t>(s) * (B / 2) + delete_bit(q + SB * j, s);
       float2 t;
-      if constexpr (Q8) t = table[codes[c] + 128];
+      if constexpr (Q8) t = tab[codes[c] + 128];
       else t = cs[c];
       const float a = v[j];
       const float b = v[j2];
@@ -588,8 +573,94 @@ __global__ __launch_bounds__(kTailThreads) void rotate_in_tail_kernel(
       v[j2] = fmaf(t.y, a, -(t.x * b));
     }
   }
+}
+
+template <int LOGB, bool Q8>
+__device__ __forceinline__ void tail_table(float2* table, float step) {
+  if constexpr (Q8) {
+    float sn, cn;
+    sincosf(fmaf(static_cast<float>(static_cast<int>(threadIdx.x) - 128), step,
+                 0.785398163397448310f), &sn, &cn);
+    table[threadIdx.x] = make_float2(cn, sn);
+    __syncthreads();
+  }
+}
+
+template <int LOGB, bool Q8, typename TOut>
+__global__ __launch_bounds__(kTailThreads) void rotate_in_tail_kernel(
+    const float* src, TOut* dst, const float2* __restrict__ cs,
+    const int8_t* __restrict__ codes, float step, int dim) {
+  constexpr int B = 1 << LOGB;
+  constexpr int SB = B / 8;
+  constexpr int kParts = SB / kTailThreads;   // workgroups per block row
+  static_assert(kParts >= 1 && SB % kTailThreads == 0, "sub-blocks of 256 or more");
+  __shared__ float2 table[Q8 ? 256 : 1];
+  tail_table<LOGB, Q8>(table, step);
+  const int blk = blockIdx.x / kParts;
+  const int q = (blockIdx.x - blk * kParts) * kTailThreads + threadIdx.x;
+  // src and dst may be the same float32 rows: each thread reads its eight
+  // elements before it writes them
+  const size_t e0 = static_cast<size_t>(blockIdx.y) * dim + static_cast<size_t>(blk) * B + q;
+  const float* sb = src + e0;
+  TOut* db = dst + e0;
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = sb[j * SB];
+  tail_stages<LOGB, Q8>(v, q, blk, cs, codes, table);
 #pragma unroll
   for (int j = 0; j < 8; ++j) from_f32(db[j * SB], v[j]);
+}
+
+// The same last three stages for one row, finished into the planes of the
+// one-row FP4 matrix-core product (f4_planes.hpp) instead of float32 x~: a
+// workgroup's residues q0 .. q0 + 255 hold, for j = 0..7, the 256
+// consecutive inputs blk b + (b/8) j + q0 .. +255, i.e. one pair of product
+// steps each.  Its first four waves apply the stages and leave the values
+// in LDS; then each of its sixteen waves builds and writes one step.
+constexpr int kTailF4Threads = 16 * kWave;
+
+template <int LOGB, bool Q8>
+__global__ __launch_bounds__(kTailF4Threads) void rotate_in_tail_f4_kernel(
+    const float* src, const float2* __restrict__ cs, const int8_t* __restrict__ codes,
+    float step, u32x4* __restrict__ pl, uint32_t* __restrict__ psc, float* __restrict__ gsx) {
+  constexpr int B = 1 << LOGB;
+  constexpr int SB = B / 8;
+  constexpr int kParts = SB / kTailThreads;
+  static_assert(kParts >= 1 && SB % kTailThreads == 0 && kTailThreads == 256,
+                "sub-blocks of 256 or more, one step pair per residue span");
+  __shared__ float2 table[Q8 ? 256 : 1];
+  __shared__ float xl[8][kTailThreads];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[16][f4::kStepLds + kWave];
+  __shared__ float ssx[16][4];
+  const int blk = blockIdx.x / kParts;
+  const int part = blockIdx.x - blk * kParts;
+  if constexpr (Q8) {
+    if (threadIdx.x < 256) {
+      float sn, cn;
+      sincosf(fmaf(static_cast<float>(static_cast<int>(threadIdx.x) - 128), step,
+                   0.785398163397448310f), &sn, &cn);
+      table[threadIdx.x] = make_float2(cn, sn);
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x < kTailThreads) {
+    const int q = part * kTailThreads + threadIdx.x;
+    const float* sb = src + static_cast<size_t>(blk) * B + q;
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = sb[j * SB];
+    tail_stages<LOGB, Q8>(v, q, blk, cs, codes, table);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xl[j][threadIdx.x] = v[j];
+  }
+  __syncthreads();
+  const int w = threadIdx.x >> 6;   // step w of the sixteen
+  const int lane = threadIdx.x & (kWave - 1);
+  const int j = w >> 1;
+  const int e = w & 1;
+  const int s = 2 * ((blk * B + SB * j + kTailThreads * part) / 256) + e;
+  f4::build_step(&xl[j][64 * e], stage[w], stage[w] + f4::kStepLds, ssx[w], lane);
+  f4::emit_step(stage[w], ssx[w], s, pl, psc, gsx, lane);
 }
 
 // The first launch writes the float32 intermediate to scratch (M x dim
@@ -616,6 +687,32 @@ hipError_t launch_in_split_any(const harp_rotation& R, const void* in, int in_dt
               : launch_in_split<LOGB, true, float, TOut>(R, in, scratch, out, M, stream);
   return ib ? launch_in_split<LOGB, false, uint16_t, TOut>(R, in, scratch, out, M, stream)
             : launch_in_split<LOGB, false, float, TOut>(R, in, scratch, out, M, stream);
+}
+
+template <int LOGB, bool Q8, typename TIn>
+hipError_t launch_in_split_f4(const harp_rotation& R, const void* in, float* scratch,
+                              uint8_t* f4r, hipStream_t stream) {
+  hipError_t e = launch_typed<LOGB - 3, 3, false, Q8, TIn, float, 3>(R, in, scratch, 1, stream);
+  if (e != hipSuccess) return e;
+  const int nblk = R.dim >> LOGB;
+  const dim3 grid(nblk * ((1 << LOGB) / 8 / kTailThreads), 1);
+  hipLaunchKernelGGL((rotate_in_tail_f4_kernel<LOGB, Q8>), grid, dim3(kTailF4Threads), 0, stream,
+                     scratch, reinterpret_cast<const float2*>(R.cs), R.phi_codes, R.phi_step,
+                     reinterpret_cast<u32x4*>(f4r),
+                     reinterpret_cast<uint32_t*>(f4r + f4_psc_offset(R.dim)),
+                     reinterpret_cast<float*>(f4r + f4_sx_offset(R.dim)));
+  return hipGetLastError();
+}
+
+template <int LOGB>
+hipError_t launch_in_split_f4_any(const harp_rotation& R, const void* in, int in_dt,
+                                  float* scratch, uint8_t* f4r, hipStream_t stream) {
+  const bool ib = in_dt == HARP_BF16;
+  if (R.phi_codes != nullptr)
+    return ib ? launch_in_split_f4<LOGB, true, uint16_t>(R, in, scratch, f4r, stream)
+              : launch_in_split_f4<LOGB, true, float>(R, in, scratch, f4r, stream);
+  return ib ? launch_in_split_f4<LOGB, false, uint16_t>(R, in, scratch, f4r, stream)
+            : launch_in_split_f4<LOGB, false, float>(R, in, scratch, f4r, stream);
 }
 
 template <int LOGB, int EL_, bool Q8>
@@ -685,6 +782,17 @@ hipError_t launch_rotate_in_scratch(const harp_rotation& R, const void* in, int 
       return launch_in_split_any<13, uint16_t>(R, in, in_dt, scratch, out, M, stream);
   }
   return launch_rotate(R, in, in_dt, out, HARP_BF16, M, false, stream);
+}
+
+bool rotate_in_f4_supported(const harp_rotation& R, int M) {
+  return M == 1 && (R.block == 4096 || R.block == 8192);
+}
+
+hipError_t launch_rotate_in_f4(const harp_rotation& R, const void* in, int in_dt,
+                               float* scratch, uint8_t* f4r, hipStream_t stream) {
+  if (R.block == 4096) return launch_in_split_f4_any<12>(R, in, in_dt, scratch, f4r, stream);
+  if (R.block == 8192) return launch_in_split_f4_any<13>(R, in, in_dt, scratch, f4r, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_rotate(const harp_rotation& R, const void* in, int in_dt,

@@ -8,7 +8,9 @@ quantization group carry it to 2^-28 of the group maximum, and every
 matrix-core sum is exact), so every case meets the float32 bar of the
 decode product against the unrounded oracle.  The cases
 cover each way the K dimension is cut (one slice; split K over 4 and 8
-slices, equal and ragged), the product alone through harp_deq_gemv_ws, x~
+slices, equal and ragged), planes written by the input rotation's last
+launch (b_V = 4096 / 8192, both angle formats), the product alone through
+harp_deq_gemv_ws, x~
 with zero, tiny, subnormal and outlier blocks, the edge
 weight format (zero-points 0 and 2^B - 1, subnormal fp16 scales), a
 workspace reused across shapes and products (the split-K counters end at
@@ -89,10 +91,10 @@ def check(name, li, y):
     return r
 
 
-def layer(K, N, b_v, b_u, seed, bits=2, xdt="bf16"):
+def layer(K, N, b_v, b_u, seed, bits=2, xdt="bf16", angles="f32"):
     cfg = S.Config(60 + seed, "f4", (S.Linear("f", K, N, b_v, b_u),), (bits,), (1,),
                    x_dtype=xdt)
-    return S.layer_inputs(cfg, 0, bits, 1)
+    return S.layer_inputs(cfg, 0, bits, 1, angles=angles)
 
 
 # (K, N, b_v, b_u), all at least 2^27 weights: one slice of 64 steps (1024
@@ -106,6 +108,17 @@ F4_SHAPES = [(8192, 16384, 8192, 256), (16384, 8192, 256, 8192), (16640, 8192, 2
 def test_f4_shapes(K, N, b_v, b_u):
     li = layer(K, N, b_v, b_u, seed=K % 97)
     check(f"f4 {K}->{N}", li, run(li))
+
+
+@pytest.mark.parametrize("K,N,b_v,angles,xdt", [
+    (4096, 32768, 4096, "int8", "f32"), (4096, 32768, 4096, "f32", "bf16"),
+    (16384, 8192, 8192, "int8", "bf16"), (8192, 16384, 8192, "f32", "f32")])
+def test_f4_planes_from_rotation(K, N, b_v, angles, xdt):
+    """b_V = 4096 / 8192 input sides: the rotation's last launch writes the
+    product's planes itself (float32 and int8-stored angles, bf16 and
+    float32 x, one and two blocks)."""
+    li = layer(K, N, b_v, 256, seed=b_v % 83 + K % 7, xdt=xdt, angles=angles)
+    check(f"f4 planes from rotation {K}->{N} b_v={b_v} {angles} {xdt}", li, run(li))
 
 
 @pytest.mark.parametrize("K,N", [(8192, 28672), (28672, 8192), (34816, 4096)])
