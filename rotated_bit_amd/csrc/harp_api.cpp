@@ -39,8 +39,8 @@ harp_status fused_linear(const harp_rotation& V, const harp_qweight& W, const ha
     // float32 x~: the float32 product, or the matrix cores on its two-plane
     // bf16 split
     float* xt = reinterpret_cast<float*>(ws + harp::workspace_xt_offset());
-    // one row on the FP4 product: with a b = 4096 / 8192 input side the
-    // rotation's last launch writes the product's planes itself
+    // one row on the FP4 product: with a b = 256 / 4096 / 8192 input side
+    // the rotation's last launch writes the product's planes itself
     const int32_t f4_slices = harp::f4_slices(M, W.N, W.K, W.bits, split_k);
     uint8_t* f4r = reinterpret_cast<uint8_t*>(ws + harp::workspace_f4_offset(M, W.N, W.K));
     const bool fold = f4_slices > 0 && harp::rotate_in_f4_supported(V, M);

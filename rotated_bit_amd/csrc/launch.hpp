@@ -40,10 +40,10 @@ hipError_t launch_gemv_f4(const harp_qweight& W, const float* xt, float* yt, uin
                           uint32_t* counters, int slices, bool planes_ready,
                           hipStream_t stream);
 
-// One row of x~ = F x at b = 4096 / 8192 finished straight into that
-// product's planes in the f4 region (two launches: the sub-blocks into the
-// float32 scratch, then the last three stages and the planes); x~ itself is
-// not written.
+// One row of x~ = F x at b = 256 / 4096 / 8192 finished straight into that
+// product's planes in the f4 region (b = 256: one launch; b = 4096 / 8192:
+// the sub-blocks into the float32 scratch, then the last three stages and
+// the planes); x~ itself is not written.
 bool rotate_in_f4_supported(const harp_rotation& R, int M);
 hipError_t launch_rotate_in_f4(const harp_rotation& R, const void* in, int in_dt,
                                float* scratch, uint8_t* f4r, hipStream_t stream);

@@ -663,6 +663,66 @@ __global__ __launch_bounds__(kTailF4Threads) void rotate_in_tail_f4_kernel(
   f4::emit_step(stage[w], ssx[w], s, pl, psc, gsx, lane);
 }
 
+// x~ = F x for one row at b = 256, finished into the planes of the one-row
+// FP4 matrix-core product (f4_planes.hpp) instead of float32 x~: one
+// workgroup per block, which is one pair of product steps.  The sign flip
+// and the eight stages run in LDS (thread t < 128 takes pair t of each
+// stage; its eight coefficients are requested first), then two waves build
+// the block's two steps.
+template <bool Q8, typename TIn>
+__global__ __launch_bounds__(256) void rotate_in_b256_f4_kernel(
+    const TIn* __restrict__ x, const float2* __restrict__ cs, const int8_t* __restrict__ codes,
+    float step, const uint32_t* __restrict__ sign, u32x4* __restrict__ pl,
+    uint32_t* __restrict__ psc, float* __restrict__ gsx) {
+  constexpr int B = 256;
+  constexpr int L = 8;
+  __shared__ float2 table[Q8 ? 256 : 1];
+  __shared__ float xl[B];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[2][f4::kStepLds + kWave];
+  __shared__ float ssx[2][4];
+  const int blk = blockIdx.x;
+  const int t = threadIdx.x;
+  if constexpr (Q8) {
+    float sn, cn;
+    sincosf(fmaf(static_cast<float>(t - 128), step, 0.785398163397448310f), &sn, &cn);
+    table[t] = make_float2(cn, sn);
+  }
+  const int g = blk * B + t;
+  const size_t coff = static_cast<size_t>(blk) * L * (B / 2);
+  float2 c[L];
+  int8_t qc[L];
+  if (t < B / 2) {
+#pragma unroll
+    for (int st = 0; st < L; ++st) {
+      if constexpr (Q8) qc[st] = codes[coff + st * (B / 2) + t];
+      else c[st] = cs[coff + st * (B / 2) + t];
+    }
+  }
+  xl[t] = flip_sign(to_f32(x[g]), (sign[g >> 5] >> (g & 31)) & 1u);
+  __syncthreads();
+#pragma unroll
+  for (int st = 0; st < L; ++st) {
+    if (t < B / 2) {
+      float2 cf;
+      if constexpr (Q8) cf = table[qc[st] + 128];
+      else cf = c[st];
+      const int i = insert_zero_bit(t, st);
+      const int i2 = i | (1 << st);
+      const float a = xl[i];
+      const float b = xl[i2];
+      xl[i] = fmaf(cf.x, a, cf.y * b);
+      xl[i2] = fmaf(cf.y, a, -(cf.x * b));
+    }
+    __syncthreads();
+  }
+  if (t < 2 * kWave) {
+    const int w = t >> 6;
+    const int lane = t & (kWave - 1);
+    f4::build_step(&xl[64 * w], stage[w], stage[w] + f4::kStepLds, ssx[w], lane);
+    f4::emit_step(stage[w], ssx[w], 2 * blk + w, pl, psc, gsx, lane);
+  }
+}
+
 // The first launch writes the float32 intermediate to scratch (M x dim
 // floats); the second writes the output (in place when out is scratch).
 template <int LOGB, bool Q8, typename TIn, typename TOut>
@@ -785,11 +845,38 @@ hipError_t launch_rotate_in_scratch(const harp_rotation& R, const void* in, int 
 }
 
 bool rotate_in_f4_supported(const harp_rotation& R, int M) {
-  return M == 1 && (R.block == 4096 || R.block == 8192);
+  return M == 1 && (R.block == 256 || R.block == 4096 || R.block == 8192);
 }
 
 hipError_t launch_rotate_in_f4(const harp_rotation& R, const void* in, int in_dt,
                                float* scratch, uint8_t* f4r, hipStream_t stream) {
+  if (R.block == 256) {
+    u32x4* pl = reinterpret_cast<u32x4*>(f4r);
+    uint32_t* psc = reinterpret_cast<uint32_t*>(f4r + f4_psc_offset(R.dim));
+    float* sx = reinterpret_cast<float*>(f4r + f4_sx_offset(R.dim));
+    const float2* cs = reinterpret_cast<const float2*>(R.cs);
+    const dim3 grid(R.dim / 256);
+    const bool ib = in_dt == HARP_BF16;
+    if (R.phi_codes != nullptr) {
+      if (ib)
+        hipLaunchKernelGGL((rotate_in_b256_f4_kernel<true, uint16_t>), grid, dim3(256), 0,
+                           stream, static_cast<const uint16_t*>(in), cs, R.phi_codes,
+                           R.phi_step, R.sign_bits, pl, psc, sx);
+      else
+        hipLaunchKernelGGL((rotate_in_b256_f4_kernel<true, float>), grid, dim3(256), 0, stream,
+                           static_cast<const float*>(in), cs, R.phi_codes, R.phi_step,
+                           R.sign_bits, pl, psc, sx);
+    } else if (ib) {
+      hipLaunchKernelGGL((rotate_in_b256_f4_kernel<false, uint16_t>), grid, dim3(256), 0,
+                         stream, static_cast<const uint16_t*>(in), cs, R.phi_codes, R.phi_step,
+                         R.sign_bits, pl, psc, sx);
+    } else {
+      hipLaunchKernelGGL((rotate_in_b256_f4_kernel<false, float>), grid, dim3(256), 0, stream,
+                         static_cast<const float*>(in), cs, R.phi_codes, R.phi_step,
+                         R.sign_bits, pl, psc, sx);
+    }
+    return hipGetLastError();
+  }
   if (R.block == 4096) return launch_in_split_f4_any<12>(R, in, in_dt, scratch, f4r, stream);
   if (R.block == 8192) return launch_in_split_f4_any<13>(R, in, in_dt, scratch, f4r, stream);
   return hipErrorInvalidValue;

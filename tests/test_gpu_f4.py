@@ -9,7 +9,7 @@ matrix-core sum is exact), so every case meets the float32 bar of the
 decode product against the unrounded oracle.  The cases
 cover each way the K dimension is cut (one slice; split K over 4 and 8
 slices, equal and ragged), planes written by the input rotation's last
-launch (b_V = 4096 / 8192, both angle formats), the product alone through
+launch (b_V = 256 / 4096 / 8192, both angle formats), the product alone through
 harp_deq_gemv_ws, x~
 with zero, tiny, subnormal and outlier blocks, the edge
 weight format (zero-points 0 and 2^B - 1, subnormal fp16 scales), a
@@ -112,11 +112,12 @@ def test_f4_shapes(K, N, b_v, b_u):
 
 @pytest.mark.parametrize("K,N,b_v,angles,xdt", [
     (4096, 32768, 4096, "int8", "f32"), (4096, 32768, 4096, "f32", "bf16"),
-    (16384, 8192, 8192, "int8", "bf16"), (8192, 16384, 8192, "f32", "f32")])
+    (16384, 8192, 8192, "int8", "bf16"), (8192, 16384, 8192, "f32", "f32"),
+    (28672, 8192, 256, "int8", "f32"), (16384, 8192, 256, "f32", "bf16")])
 def test_f4_planes_from_rotation(K, N, b_v, angles, xdt):
-    """b_V = 4096 / 8192 input sides: the rotation's last launch writes the
-    product's planes itself (float32 and int8-stored angles, bf16 and
-    float32 x, one and two blocks)."""
+    """b_V = 256 / 4096 / 8192 input sides: the rotation's last launch writes
+    the product's planes itself (float32 and int8-stored angles, bf16 and
+    float32 x, one to 112 blocks)."""
     li = layer(K, N, b_v, 256, seed=b_v % 83 + K % 7, xdt=xdt, angles=angles)
     check(f"f4 planes from rotation {K}->{N} b_v={b_v} {angles} {xdt}", li, run(li))
 
