@@ -91,11 +91,23 @@ constexpr int kPairs = 2;                 // step pairs per chunk
 constexpr int kSzStride = kF4MaxSliceSteps + 1;   // LDS dwords per row of scales / zeros
 constexpr int kBatchPairs = 2;            // step pairs per batch of matrix instructions
 
+// Output side folded into the product (FOLD 1: float32 y, 2: bf16 y): a
+// block-diagonal F_U with 256-output blocks, one K slice.
+struct F4Out {
+  const float2* cs;
+  const int8_t* codes;
+  float step;
+  const uint32_t* sign;
+  void* y;
+};
+
+template <int FOLD, bool Q8U>
 __global__ __launch_bounds__(kF4Threads, 1) void gemv_f4_kernel(
     const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
     const uint16_t* __restrict__ zr, const u32x4* __restrict__ gpl,
     const uint32_t* __restrict__ gps, const float* __restrict__ gsx, float* __restrict__ yt,
-    float* __restrict__ partials, uint32_t* __restrict__ counters, int N, int K, int slices) {
+    float* __restrict__ partials, uint32_t* __restrict__ counters, int N, int K, int slices,
+    F4Out out) {
   __shared__ __attribute__((aligned(16))) uint8_t lpl[kF4MaxSliceSteps * kStepLds];
   __shared__ uint8_t lpsc[kF4MaxSliceSteps * kWave];
   __shared__ float lsx[2 * kF4MaxSliceSteps];
@@ -279,6 +291,68 @@ __global__ __launch_bounds__(kF4Threads, 1) void gemv_f4_kernel(
   acc += shfl_xor(acc, 16);
   acc += shfl_xor(acc, 32);
 
+  if constexpr (FOLD != 0) {
+    // The output rotation of this workgroup's 256-output block (two
+    // workgroups of 128 rows): y' is stored device-coherent and acknowledged
+    // before the workgroup's arrival is counted; the second workgroup of the
+    // block to arrive reads the block's y', applies the transposed stages
+    // 7 .. 0 and the signs in LDS, writes y and resets the counter.
+    __shared__ uint32_t last;
+    if (g == 0)
+      __hip_atomic_store(&yt[row], acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int ob = static_cast<int>(blockIdx.x) >> 1;
+    if (tid == 0)
+      last = __hip_atomic_fetch_add(&counters[ob], 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) == 1u;
+    __syncthreads();
+    if (!last) return;
+    float* xl = reinterpret_cast<float*>(lpl);                // the planes are no longer read
+    float2* tab = reinterpret_cast<float2*>(lpl + 256 * sizeof(float));
+    const size_t coff = static_cast<size_t>(ob) * 8 * 128;
+    float2 cf[8];
+    int8_t qc[8];
+    if (tid < 128) {
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        if constexpr (Q8U) qc[st] = out.codes[coff + st * 128 + tid];
+        else cf[st] = out.cs[coff + st * 128 + tid];
+      }
+    }
+    if (tid < 256) {
+      xl[tid] = __hip_atomic_load(&yt[ob * 256 + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if constexpr (Q8U) {
+        float sn, cn;
+        sincosf(fmaf(static_cast<float>(tid - 128), out.step, 0.785398163397448310f), &sn, &cn);
+        tab[tid] = make_float2(cn, sn);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int st = 7; st >= 0; --st) {
+      if (tid < 128) {
+        float2 c;
+        if constexpr (Q8U) c = tab[qc[st] + 128];
+        else c = cf[st];
+        const int i = ((tid >> st) << (st + 1)) | (tid & ((1 << st) - 1));
+        const int i2 = i | (1 << st);
+        const float a = xl[i];
+        const float b = xl[i2];
+        xl[i] = fmaf(c.x, a, c.y * b);
+        xl[i2] = fmaf(c.y, a, -(c.x * b));
+      }
+      __syncthreads();
+    }
+    if (tid < 256) {
+      const int o = ob * 256 + tid;
+      const float v = flip_sign(xl[tid], (out.sign[o >> 5] >> (o & 31)) & 1u);
+      if constexpr (FOLD == 1) static_cast<float*>(out.y)[o] = v;
+      else static_cast<uint16_t*>(out.y)[o] = f32_to_bf16(v);
+    }
+    if (tid == 0) __hip_atomic_store(&counters[ob], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   if (slices == 1) {
     if (g == 0) yt[row] = acc;
     return;
@@ -314,12 +388,14 @@ __global__ __launch_bounds__(kF4Threads, 1) void gemv_f4_kernel(
 
 hipError_t launch_gemv_f4(const harp_qweight& W, const float* xt, float* yt, uint8_t* f4,
                           uint32_t* counters, int slices, bool planes_ready,
-                          hipStream_t stream) {
+                          hipStream_t stream, const harp_rotation* U, void* y, int y_dt) {
   const int steps = W.K / kF4Step;
   const int pairs = steps / 2;
   if (W.bits != 2 || W.N % 16 != 0 || W.K % (2 * kF4Step) != 0 || slices < 1 ||
       slices > kF4MaxSplits || (pairs + slices - 1) / slices * 2 > kF4MaxSliceSteps ||
-      f4 == nullptr || (slices > 1 && (counters == nullptr || W.N / 16 > kF4MaxSplitTiles)))
+      f4 == nullptr || (slices > 1 && (counters == nullptr || W.N / 16 > kF4MaxSplitTiles)) ||
+      (U != nullptr && !gemv_f4_fold_supported(*U, W, slices)) ||
+      (U != nullptr && (counters == nullptr || y == nullptr)))
     return hipErrorInvalidValue;
   u32x4* pl = reinterpret_cast<u32x4*>(f4);
   uint32_t* psc = reinterpret_cast<uint32_t*>(f4 + f4_psc_offset(W.K));
@@ -332,11 +408,27 @@ hipError_t launch_gemv_f4(const harp_qweight& W, const float* xt, float* yt, uin
   }
   const int tiles = W.N / 16;
   const dim3 grid((tiles + kF4WgWaves - 1) / kF4WgWaves, slices);
-  hipLaunchKernelGGL(gemv_f4_kernel, grid, dim3(kF4Threads), 0, stream, W.qweight, W.scale,
-                     W.zero, pl, psc, sx, yt,
-                     reinterpret_cast<float*>(f4 + f4_partial_offset(W.K)), counters, W.N, W.K,
-                     slices);
+  float* part = reinterpret_cast<float*>(f4 + f4_partial_offset(W.K));
+  F4Out out{};
+  if (U != nullptr)
+    out = F4Out{reinterpret_cast<const float2*>(U->cs), U->phi_codes, U->phi_step, U->sign_bits,
+                y};
+#define HARP_F4(FO, Q)                                                                        \
+  hipLaunchKernelGGL((gemv_f4_kernel<FO, Q>), grid, dim3(kF4Threads), 0, stream, W.qweight,    \
+                     W.scale, W.zero, pl, psc, sx, yt, part, counters, W.N, W.K, slices, out)
+  if (U == nullptr) HARP_F4(0, false);
+  else if (U->phi_codes != nullptr) {
+    if (y_dt == HARP_BF16) HARP_F4(2, true);
+    else HARP_F4(1, true);
+  } else if (y_dt == HARP_BF16) HARP_F4(2, false);
+  else HARP_F4(1, false);
+#undef HARP_F4
   return hipGetLastError();
+}
+
+bool gemv_f4_fold_supported(const harp_rotation& U, const harp_qweight& W, int slices) {
+  return slices == 1 && U.block == 256 && U.dim == W.N && W.N % 256 == 0 &&
+         W.N / 256 <= kF4MaxSplitTiles;
 }
 
 }  // namespace harp

@@ -47,6 +47,11 @@ harp_status fused_linear(const harp_rotation& V, const harp_qweight& W, const ha
     r = from_hip(fold ? harp::launch_rotate_in_f4(V, x, x_dt, xt, f4r, s)
                       : harp::launch_rotate(V, x, x_dt, xt, HARP_F32, M, false, s));
     if (r != HARP_OK) return r;
+    // and with a b = 256 output side (one K slice, a zeroed workspace) the
+    // product's last workgroup of each 256-output block applies F_U^T
+    if (f4_slices > 0 && split_k && harp::gemv_f4_fold_supported(U, W, f4_slices))
+      return from_hip(harp::launch_gemv_f4(W, xt, yp, f4r, reinterpret_cast<uint32_t*>(ws),
+                                           f4_slices, fold, s, &U, y, y_dt));
     if (f4_slices > 0)
       r = from_hip(harp::launch_gemv_f4(W, xt, yp, f4r, reinterpret_cast<uint32_t*>(ws),
                                         f4_slices, fold, s));

@@ -35,10 +35,15 @@ hipError_t launch_gemv(const harp_qweight& W, const float* xt, float* yt,
 // slices > 1 needs zeroed `counters` (one uint32 per 16-row tile, left
 // zero) and the partials that follow the planes in the region.
 // planes_ready: the planes are already in the region (launch_rotate_in_f4)
-// and x~ is not read.
+// and x~ is not read.  U non-null (gemv_f4_fold_supported): the output
+// rotation is applied in the same launch, y (y_dt) is written and yt holds
+// y' only as an intermediate; needs zeroed counters (one per 256 outputs,
+// left zero).
 hipError_t launch_gemv_f4(const harp_qweight& W, const float* xt, float* yt, uint8_t* f4,
                           uint32_t* counters, int slices, bool planes_ready,
-                          hipStream_t stream);
+                          hipStream_t stream, const harp_rotation* U = nullptr,
+                          void* y = nullptr, int y_dt = HARP_F32);
+bool gemv_f4_fold_supported(const harp_rotation& U, const harp_qweight& W, int slices);
 
 // One row of x~ = F x at b = 256 / 4096 / 8192 finished straight into that
 // product's planes in the f4 region (b = 256: one launch; b = 4096 / 8192:

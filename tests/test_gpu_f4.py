@@ -9,8 +9,9 @@ matrix-core sum is exact), so every case meets the float32 bar of the
 decode product against the unrounded oracle.  The cases
 cover each way the K dimension is cut (one slice; split K over 4 and 8
 slices, equal and ragged), planes written by the input rotation's last
-launch (b_V = 256 / 4096 / 8192, both angle formats), the product alone through
-harp_deq_gemv_ws, x~
+launch (b_V = 256 / 4096 / 8192, both angle formats), the output rotation
+applied by the product (b_U = 256, float32 and bf16 y), the product alone
+through harp_deq_gemv_ws, x~
 with zero, tiny, subnormal and outlier blocks, the edge
 weight format (zero-points 0 and 2^B - 1, subnormal fp16 scales), a
 workspace reused across shapes and products (the split-K counters end at
@@ -120,6 +121,30 @@ def test_f4_planes_from_rotation(K, N, b_v, angles, xdt):
     float32 x, one to 112 blocks)."""
     li = layer(K, N, b_v, 256, seed=b_v % 83 + K % 7, xdt=xdt, angles=angles)
     check(f"f4 planes from rotation {K}->{N} b_v={b_v} {angles} {xdt}", li, run(li))
+
+
+@pytest.mark.parametrize("angles", ["f32", "int8"])
+def test_f4_output_rotation_in_product(angles):
+    """b_U = 256 with one K slice: the product's second workgroup of each
+    256-output block applies F_U^T.  float32 output against the oracle; the
+    bf16 output is the float32 output rounded to nearest even, bit for bit;
+    repeated calls on one workspace agree and leave the counters at zero."""
+    li = layer(8192, 16384, 8192, 256, seed=9, angles=angles)
+    d = D()
+    V, U, W = d.dev_rotation(li.V), d.dev_rotation(li.U), d.dev_qweight(li.W)
+    x = d.dev_x(li.x, li.x_dtype)
+    ws = d.workspace(1, 16384, 8192)
+    y32 = torch.empty((1, 16384), dtype=torch.float32, device="cuda")
+    y16 = torch.empty((1, 16384), dtype=torch.bfloat16, device="cuda")
+    y32b = torch.empty_like(y32)
+    H().harp_linear_fused(V, W, U, x, y32, ws)
+    H().harp_linear_fused(V, W, U, x, y16, ws)
+    H().harp_linear_fused(V, W, U, x, y32b, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y32, y32b)
+    assert torch.equal(y16, y32.to(torch.bfloat16))
+    assert int(ws[:2048].view(torch.int32).abs().sum().item()) == 0
+    check(f"f4 output rotation in the product {angles}", li, y32)
 
 
 @pytest.mark.parametrize("K,N", [(8192, 28672), (28672, 8192), (34816, 4096)])
