@@ -296,20 +296,13 @@ __global__ __launch_bounds__(kF4Threads, 1) void gemv_f4_kernel(
     // workgroups of 128 rows): y' is stored device-coherent and acknowledged
     // before the workgroup's arrival is counted; the second workgroup of the
     // block to arrive reads the block's y', applies the transposed stages
-    // 7 .. 0 and the signs in LDS, writes y and resets the counter.
+    // 7 .. 0 and the signs in LDS, writes y and resets the counter.  Both
+    // workgroups request the block's (cos, sin) pairs or angle codes and
+    // sign words (and evaluate the angle table) before the acknowledgement
+    // wait, so that the last one starts its stages one memory round trip
+    // earlier.
     __shared__ uint32_t last;
-    if (g == 0)
-      __hip_atomic_store(&yt[row], acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
     const int ob = static_cast<int>(blockIdx.x) >> 1;
-    if (tid == 0)
-      last = __hip_atomic_fetch_add(&counters[ob], 1u, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT) == 1u;
-    __syncthreads();
-    if (!last) return;
-    float* xl = reinterpret_cast<float*>(lpl);                // the planes are no longer read
-    float2* tab = reinterpret_cast<float2*>(lpl + 256 * sizeof(float));
     const size_t coff = static_cast<size_t>(ob) * 8 * 128;
     float2 cf[8];
     int8_t qc[8];
@@ -320,13 +313,29 @@ __global__ __launch_bounds__(kF4Threads, 1) void gemv_f4_kernel(
         else cf[st] = out.cs[coff + st * 128 + tid];
       }
     }
+    uint32_t sgn = 0;
+    if (tid < 256) sgn = out.sign[(ob * 256 + tid) >> 5];
+    if (g == 0)
+      __hip_atomic_store(&yt[row], acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    float2 tv = make_float2(0.0f, 0.0f);
+    if constexpr (Q8U) {
+      float sn, cn;
+      sincosf(fmaf(static_cast<float>((tid & 255) - 128), out.step, 0.785398163397448310f), &sn,
+              &cn);
+      tv = make_float2(cn, sn);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0)
+      last = __hip_atomic_fetch_add(&counters[ob], 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) == 1u;
+    __syncthreads();
+    if (!last) return;
+    float* xl = reinterpret_cast<float*>(lpl);                // the planes are no longer read
+    float2* tab = reinterpret_cast<float2*>(lpl + 256 * sizeof(float));
     if (tid < 256) {
       xl[tid] = __hip_atomic_load(&yt[ob * 256 + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if constexpr (Q8U) {
-        float sn, cn;
-        sincosf(fmaf(static_cast<float>(tid - 128), out.step, 0.785398163397448310f), &sn, &cn);
-        tab[tid] = make_float2(cn, sn);
-      }
+      if constexpr (Q8U) tab[tid] = tv;
     }
     __syncthreads();
 #pragma unroll
@@ -346,7 +355,7 @@ __global__ __launch_bounds__(kF4Threads, 1) void gemv_f4_kernel(
     }
     if (tid < 256) {
       const int o = ob * 256 + tid;
-      const float v = flip_sign(xl[tid], (out.sign[o >> 5] >> (o & 31)) & 1u);
+      const float v = flip_sign(xl[tid], (sgn >> (o & 31)) & 1u);
       if constexpr (FOLD == 1) static_cast<float*>(out.y)[o] = v;
       else static_cast<uint16_t*>(out.y)[o] = f32_to_bf16(v);
     }
