@@ -42,6 +42,7 @@
 // (v_permlane16_swap), and every row's 128-byte line of codes is read by
 // four lanes of one load.
 #include "f4_planes.hpp"
+#include "fold256.hpp"
 #include "launch.hpp"
 #include "unpack.hpp"
 #include "validate.hpp"
@@ -92,14 +93,7 @@ constexpr int kSzStride = kF4MaxSliceSteps + 1;   // LDS dwords per row of scale
 constexpr int kBatchPairs = 2;            // step pairs per batch of matrix instructions
 
 // Output side folded into the product (FOLD 1: float32 y, 2: bf16 y): a
-// block-diagonal F_U with 256-output blocks, one K slice.
-struct F4Out {
-  const float2* cs;
-  const int8_t* codes;
-  float step;
-  const uint32_t* sign;
-  void* y;
-};
+// block-diagonal F_U with 256-output blocks, one K slice (fold256.hpp).
 
 template <int FOLD, bool Q8U>
 __global__ __launch_bounds__(kF4Threads, 1) void gemv_f4_kernel(
@@ -107,7 +101,7 @@ __global__ __launch_bounds__(kF4Threads, 1) void gemv_f4_kernel(
     const uint16_t* __restrict__ zr, const u32x4* __restrict__ gpl,
     const uint32_t* __restrict__ gps, const float* __restrict__ gsx, float* __restrict__ yt,
     float* __restrict__ partials, uint32_t* __restrict__ counters, int N, int K, int slices,
-    F4Out out) {
+    Fold256Out out) {
   __shared__ __attribute__((aligned(16))) uint8_t lpl[kF4MaxSliceSteps * kStepLds];
   __shared__ uint8_t lpsc[kF4MaxSliceSteps * kWave];
   __shared__ float lsx[2 * kF4MaxSliceSteps];
@@ -293,73 +287,16 @@ __global__ __launch_bounds__(kF4Threads, 1) void gemv_f4_kernel(
 
   if constexpr (FOLD != 0) {
     // The output rotation of this workgroup's 256-output block (two
-    // workgroups of 128 rows): y' is stored device-coherent and acknowledged
-    // before the workgroup's arrival is counted; the second workgroup of the
-    // block to arrive reads the block's y', applies the transposed stages
-    // 7 .. 0 and the signs in LDS, writes y and resets the counter.  Both
-    // workgroups request the block's (cos, sin) pairs or angle codes and
-    // sign words (and evaluate the angle table) before the acknowledgement
-    // wait, so that the last one starts its stages one memory round trip
-    // earlier.
+    // workgroups of 128 rows), the second to arrive applying it.
     __shared__ uint32_t last;
     const int ob = static_cast<int>(blockIdx.x) >> 1;
-    const size_t coff = static_cast<size_t>(ob) * 8 * 128;
-    float2 cf[8];
-    int8_t qc[8];
-    if (tid < 128) {
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        if constexpr (Q8U) qc[st] = out.codes[coff + st * 128 + tid];
-        else cf[st] = out.cs[coff + st * 128 + tid];
-      }
-    }
-    uint32_t sgn = 0;
-    if (tid < 256) sgn = out.sign[(ob * 256 + tid) >> 5];
+    Fold256Regs fr;
+    fold256_prefetch<Q8U>(out, ob, tid, fr);
     if (g == 0)
       __hip_atomic_store(&yt[row], acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    float2 tv = make_float2(0.0f, 0.0f);
-    if constexpr (Q8U) {
-      float sn, cn;
-      sincosf(fmaf(static_cast<float>((tid & 255) - 128), out.step, 0.785398163397448310f), &sn,
-              &cn);
-      tv = make_float2(cn, sn);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (tid == 0)
-      last = __hip_atomic_fetch_add(&counters[ob], 1u, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT) == 1u;
-    __syncthreads();
-    if (!last) return;
-    float* xl = reinterpret_cast<float*>(lpl);                // the planes are no longer read
-    float2* tab = reinterpret_cast<float2*>(lpl + 256 * sizeof(float));
-    if (tid < 256) {
-      xl[tid] = __hip_atomic_load(&yt[ob * 256 + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if constexpr (Q8U) tab[tid] = tv;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int st = 7; st >= 0; --st) {
-      if (tid < 128) {
-        float2 c;
-        if constexpr (Q8U) c = tab[qc[st] + 128];
-        else c = cf[st];
-        const int i = ((tid >> st) << (st + 1)) | (tid & ((1 << st) - 1));
-        const int i2 = i | (1 << st);
-        const float a = xl[i];
-        const float b = xl[i2];
-        xl[i] = fmaf(c.x, a, c.y * b);
-        xl[i2] = fmaf(c.y, a, -(c.x * b));
-      }
-      __syncthreads();
-    }
-    if (tid < 256) {
-      const int o = ob * 256 + tid;
-      const float v = flip_sign(xl[tid], (sgn >> (o & 31)) & 1u);
-      if constexpr (FOLD == 1) static_cast<float*>(out.y)[o] = v;
-      else static_cast<uint16_t*>(out.y)[o] = f32_to_bf16(v);
-    }
-    if (tid == 0) __hip_atomic_store(&counters[ob], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the planes are no longer read once every wave has arrived
+    fold256_finish<FOLD, Q8U>(out, ob, tid, fr, yt, counters, 2u, reinterpret_cast<float*>(lpl),
+                              reinterpret_cast<float2*>(lpl + 256 * sizeof(float)), &last);
     return;
   }
   if (slices == 1) {
@@ -418,9 +355,9 @@ hipError_t launch_gemv_f4(const harp_qweight& W, const float* xt, float* yt, uin
   const int tiles = W.N / 16;
   const dim3 grid((tiles + kF4WgWaves - 1) / kF4WgWaves, slices);
   float* part = reinterpret_cast<float*>(f4 + f4_partial_offset(W.K));
-  F4Out out{};
+  Fold256Out out{};
   if (U != nullptr)
-    out = F4Out{reinterpret_cast<const float2*>(U->cs), U->phi_codes, U->phi_step, U->sign_bits,
+    out = Fold256Out{reinterpret_cast<const float2*>(U->cs), U->phi_codes, U->phi_step, U->sign_bits,
                 y};
 #define HARP_F4(FO, Q)                                                                        \
   hipLaunchKernelGGL((gemv_f4_kernel<FO, Q>), grid, dim3(kF4Threads), 0, stream, W.qweight,    \
