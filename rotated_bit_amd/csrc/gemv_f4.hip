@@ -1,4 +1,5 @@
-// One-row decode product of 2-bit codes on the FP4 x FP8 matrix cores:
+// One-row decode product of 2-bit codes on the FP4 x FP8 matrix cores (and
+// of 4-bit codes as FP8 values, transpose4 below):
 //     y'[n] = sum_g s[n][g] (sum_{k in g} q[n][k] x~[k] - z[n][g] sum_{k in g} x~[k]).
 //
 // gfx950 has a block-scaled matrix-core instruction whose operands are
@@ -95,7 +96,40 @@ constexpr int kBatchPairs = 2;            // step pairs per batch of matrix inst
 // Output side folded into the product (FOLD 1: float32 y, 2: bf16 y): a
 // block-diagonal F_U with 256-output blocks, one K slice (fold256.hpp).
 
-template <int FOLD, bool Q8U>
+// 4-bit codes as FP8 (e4m3) values: a code q in the low nibble of a byte
+// is q 2^-9 exactly (subnormal below 8, the first binade from 8), restored
+// by the column scale 2^9.  The FP8 operand layout gives lane l (g = l/16)
+// the inputs 16g .. 16g+15 of the step's two groups, in the order the planes
+// use (even inputs in bytes 0..7, odd ones in bytes 8..15 of each half).
+// Each lane loads one whole group (32 bytes) of its row per step pair; the
+// four lanes of a row then exchange 16-input runs (a 4 x 4 transpose over
+// lanes 16 apart: lanes 32 apart swap the runs whose upper index bit differs
+// from theirs, then lanes 16 apart the rest), so that lane g holds run g of
+// groups 4t .. 4t+3.
+struct T4 {
+  uint2 p[4];
+};
+__device__ __forceinline__ T4 transpose4(const u32x4 (&c)[2]) {
+  // runs 0..3 of the lane's own group: (c0.x, c0.y), (c0.z, c0.w), ...
+  const auto a0 = __builtin_amdgcn_permlane32_swap(c[0].x, c[1].x, false, false);
+  const auto a1 = __builtin_amdgcn_permlane32_swap(c[0].y, c[1].y, false, false);
+  const auto a2 = __builtin_amdgcn_permlane32_swap(c[0].z, c[1].z, false, false);
+  const auto a3 = __builtin_amdgcn_permlane32_swap(c[0].w, c[1].w, false, false);
+  // now (a0[0], a1[0]) / (a0[1], a1[1]): run 2 g1 of the groups with upper
+  // bit 0 / 1 and lower bit g0; (a2, a3) the same for run 2 g1 + 1
+  const auto b0 = __builtin_amdgcn_permlane16_swap(a0[0], a2[0], false, false);
+  const auto b1 = __builtin_amdgcn_permlane16_swap(a1[0], a3[0], false, false);
+  const auto b2 = __builtin_amdgcn_permlane16_swap(a0[1], a2[1], false, false);
+  const auto b3 = __builtin_amdgcn_permlane16_swap(a1[1], a3[1], false, false);
+  T4 t;
+  t.p[0] = make_uint2(b0[0], b1[0]);
+  t.p[1] = make_uint2(b0[1], b1[1]);
+  t.p[2] = make_uint2(b2[0], b3[0]);
+  t.p[3] = make_uint2(b2[1], b3[1]);
+  return t;
+}
+
+template <int BITS, int FOLD, bool Q8U>
 __global__ __launch_bounds__(kF4Threads, 1) void gemv_f4_kernel(
     const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
     const uint16_t* __restrict__ zr, const u32x4* __restrict__ gpl,
@@ -127,17 +161,23 @@ __global__ __launch_bounds__(kF4Threads, 1) void gemv_f4_kernel(
   const int h = g >> 1;                    // group half of this lane's results
   const bool zlane = (g & 1) == 0;         // planes 0..3: carries the zero-point term
   const int row = min(tile, tiles - 1) * 16 + n;   // waves past the last tile load it, then leave
-  const u32x4* qrow = reinterpret_cast<const u32x4*>(qw + static_cast<size_t>(row) * (K / 16)) + g;
+  // 2 bits: 16 bytes per group; 4 bits: 32 bytes per group (two vectors)
+  constexpr int kVec = BITS / 2;
+  const u32x4* qrow =
+      reinterpret_cast<const u32x4*>(qw + static_cast<size_t>(row) * (K * BITS / 32)) + kVec * g;
 
   // one register set: per step pair this lane's group of codes (16 bytes,
   // group 4t + g); pairs past the slice re-read its last pair (one cached
   // line per lane)
   struct Chunk {
-    u32x4 c[kPairs];
+    u32x4 c[kPairs][kVec];
   };
   auto load = [&](int c, Chunk& ch) {
 #pragma unroll
-    for (int i = 0; i < kPairs; ++i) ch.c[i] = qrow[4 * (pa + min(c * kPairs + i, np - 1))];
+    for (int i = 0; i < kPairs; ++i)
+#pragma unroll
+      for (int v = 0; v < kVec; ++v)
+        ch.c[i][v] = qrow[4 * kVec * (pa + min(c * kPairs + i, np - 1)) + v];
   };
   const int nch = (np + kPairs - 1) / kPairs;
   Chunk A, B;
@@ -228,26 +268,45 @@ __global__ __launch_bounds__(kF4Threads, 1) void gemv_f4_kernel(
         const i32x8 Aop = {static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z),
                            static_cast<int>(lo.w), static_cast<int>(hi.x), static_cast<int>(hi.y),
                            static_cast<int>(hi.z), static_cast<int>(hi.w)};
-        // half groups exchanged between lanes 16 apart: afterwards words
-        // 0-1 belong to step 2t and words 2-3 to step 2t + 1 in every lane
-        u32x4 w = ch.c[pi];
-        {
-          const auto s0 = __builtin_amdgcn_permlane16_swap(w.x, w.z, false, false);
-          const auto s1 = __builtin_amdgcn_permlane16_swap(w.y, w.w, false, false);
-          w.x = s0[0];
-          w.z = s0[1];
-          w.y = s1[0];
-          w.w = s1[1];
+        if constexpr (BITS == 2) {
+          // half groups exchanged between lanes 16 apart: afterwards words
+          // 0-1 belong to step 2t and words 2-3 to step 2t + 1 in every lane
+          u32x4 w = ch.c[pi][0];
+          {
+            const auto s0 = __builtin_amdgcn_permlane16_swap(w.x, w.z, false, false);
+            const auto s1 = __builtin_amdgcn_permlane16_swap(w.y, w.w, false, false);
+            w.x = s0[0];
+            w.z = s0[1];
+            w.y = s1[0];
+            w.w = s1[1];
+          }
+          const uint32_t w0 = e ? w.z : w.x;
+          const uint32_t w1 = e ? w.w : w.y;
+          const i32x8 Bop = {static_cast<int>(w0 & 0x33333333u),
+                             static_cast<int>((w0 >> 2) & 0x33333333u),
+                             static_cast<int>(w1 & 0x33333333u),
+                             static_cast<int>((w1 >> 2) & 0x33333333u), 0, 0, 0, 0};
+          Dv[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              Aop, Bop, floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 4, 0,
+              static_cast<int>(lpsc[ls * kWave + lane]), 0, 128);
+        } else {
+          const T4 t = transpose4(ch.c[pi]);
+          // bytes 0..15: the even, then the odd inputs of the lane's run of
+          // group 4t + e; bytes 16..31: the same run of group 4t + 2 + e
+          const uint2 ra = e ? t.p[1] : t.p[0];
+          const uint2 rb = e ? t.p[3] : t.p[2];
+          const i32x8 Bop = {static_cast<int>(ra.x & 0x0f0f0f0fu),
+                             static_cast<int>(ra.y & 0x0f0f0f0fu),
+                             static_cast<int>((ra.x >> 4) & 0x0f0f0f0fu),
+                             static_cast<int>((ra.y >> 4) & 0x0f0f0f0fu),
+                             static_cast<int>(rb.x & 0x0f0f0f0fu),
+                             static_cast<int>(rb.y & 0x0f0f0f0fu),
+                             static_cast<int>((rb.x >> 4) & 0x0f0f0f0fu),
+                             static_cast<int>((rb.y >> 4) & 0x0f0f0f0fu)};
+          Dv[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              Aop, Bop, floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0,
+              static_cast<int>(lpsc[ls * kWave + lane]), 0, 127 + 9);
         }
-        const uint32_t w0 = e ? w.z : w.x;
-        const uint32_t w1 = e ? w.w : w.y;
-        const i32x8 Bop = {static_cast<int>(w0 & 0x33333333u),
-                           static_cast<int>((w0 >> 2) & 0x33333333u),
-                           static_cast<int>(w1 & 0x33333333u),
-                           static_cast<int>((w1 >> 2) & 0x33333333u), 0, 0, 0, 0};
-        Dv[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            Aop, Bop, floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 4, 0,
-            static_cast<int>(lpsc[ls * kWave + lane]), 0, 128);
       }
 #pragma unroll
       for (int i = 0; i < 2 * kBatchPairs; ++i) {
@@ -337,7 +396,7 @@ hipError_t launch_gemv_f4(const harp_qweight& W, const float* xt, float* yt, uin
                           hipStream_t stream, const harp_rotation* U, void* y, int y_dt) {
   const int steps = W.K / kF4Step;
   const int pairs = steps / 2;
-  if (W.bits != 2 || W.N % 16 != 0 || W.K % (2 * kF4Step) != 0 || slices < 1 ||
+  if ((W.bits != 2 && W.bits != 4) || W.N % 16 != 0 || W.K % (2 * kF4Step) != 0 || slices < 1 ||
       slices > kF4MaxSplits || (pairs + slices - 1) / slices * 2 > kF4MaxSliceSteps ||
       f4 == nullptr || (slices > 1 && (counters == nullptr || W.N / 16 > kF4MaxSplitTiles)) ||
       (U != nullptr && !gemv_f4_fold_supported(*U, W, slices)) ||
@@ -359,15 +418,22 @@ hipError_t launch_gemv_f4(const harp_qweight& W, const float* xt, float* yt, uin
   if (U != nullptr)
     out = Fold256Out{reinterpret_cast<const float2*>(U->cs), U->phi_codes, U->phi_step, U->sign_bits,
                 y};
-#define HARP_F4(FO, Q)                                                                        \
-  hipLaunchKernelGGL((gemv_f4_kernel<FO, Q>), grid, dim3(kF4Threads), 0, stream, W.qweight,    \
+#define HARP_F4(B, FO, Q)                                                                     \
+  hipLaunchKernelGGL((gemv_f4_kernel<B, FO, Q>), grid, dim3(kF4Threads), 0, stream, W.qweight, \
                      W.scale, W.zero, pl, psc, sx, yt, part, counters, W.N, W.K, slices, out)
-  if (U == nullptr) HARP_F4(0, false);
-  else if (U->phi_codes != nullptr) {
-    if (y_dt == HARP_BF16) HARP_F4(2, true);
-    else HARP_F4(1, true);
-  } else if (y_dt == HARP_BF16) HARP_F4(2, false);
-  else HARP_F4(1, false);
+#define HARP_F4_BITS(B)                           \
+  if (U == nullptr) HARP_F4(B, 0, false);         \
+  else if (U->phi_codes != nullptr) {             \
+    if (y_dt == HARP_BF16) HARP_F4(B, 2, true);   \
+    else HARP_F4(B, 1, true);                     \
+  } else if (y_dt == HARP_BF16) HARP_F4(B, 2, false); \
+  else HARP_F4(B, 1, false);
+  if (W.bits == 2) {
+    HARP_F4_BITS(2)
+  } else {
+    HARP_F4_BITS(4)
+  }
+#undef HARP_F4_BITS
 #undef HARP_F4
   return hipGetLastError();
 }

@@ -168,7 +168,7 @@ harp_status harp_deq_gemv_ws(const harp_qweight* W, const float* xt, float* yt, 
   const harp_status st = harp::validate_gemv_ws(W, xt, yt, M, workspace, ws_bytes);
   if (st != HARP_OK || M == 0) return st;
   const int32_t slices =
-      workspace != nullptr ? harp::f4_slices(M, W->N, W->K, W->bits, true) : 0;
+      workspace != nullptr && W->bits == 2 ? harp::f4_slices(M, W->N, W->K, W->bits, true) : 0;
   if (slices > 0) {
     char* ws = static_cast<char*>(workspace);
     return from_hip(harp::launch_gemv_f4(*W, xt, yt,

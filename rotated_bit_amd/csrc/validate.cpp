@@ -342,7 +342,7 @@ size_t workspace_gemm_offset(int32_t M, int32_t N, int32_t K) {
 }
 
 int32_t f4_slices(int32_t M, int32_t N, int32_t K, int32_t bits, bool allow_split) {
-  if (M != 1 || bits != 2 || N < 16 || N % 16 != 0 || K < 2 * kF4Step || K % (2 * kF4Step) != 0 ||
+  if (M != 1 || (bits != 2 && bits != 4) || N < 16 || N % 16 != 0 || K < 2 * kF4Step || K % (2 * kF4Step) != 0 ||
       static_cast<int64_t>(N) * K < kF4MinWeights)
     return 0;
   // slices are whole step pairs; the largest of them must fit in LDS

@@ -106,7 +106,8 @@ constexpr int32_t kFusedRotGemvMaxN = 4096;
 // exponent per quantization group and plane) in the "f4 region" of the
 // workspace; each workgroup holds one K slice of them in LDS, at most
 // kF4MaxSliceSteps steps of kF4Step inputs (slices are whole pairs of
-// steps).  Eligible: M == 1, 2-bit codes, N a multiple of 16, K a multiple
+// steps).  Eligible: M == 1, 2-bit codes (FP4 operands) or 4-bit codes (FP8
+// operands), N a multiple of 16, K a multiple
 // of 2 kF4Step, at least kF4MinWeights weights (below that the vector-ALU
 // kernel is faster).  f4_slices returns the number of K slices (0: not
 // eligible).  With split K allowed it aims at kF4Waves one-tile waves (16

@@ -1,7 +1,8 @@
-"""GPU parity of the one-row 2-bit decode product on the FP4 x FP8 matrix
-cores (the fused linear at M = 1 on layers of at least 2^27 weights, HARP
+"""GPU parity of the one-row 2- and 4-bit decode product on the block-scaled
+matrix cores (the fused linear at M = 1 on layers of at least 2^27 weights, HARP
 technical summary §2.4 with the per-group uniform grid standing in for the
-quantizer).
+quantizer).  2-bit codes enter as FP4 values, 4-bit codes (fused linear
+only) as FP8 values.
 
 x~ is not rounded on this path (eight FP8 planes of base-16 digits per
 quantization group carry it to 2^-28 of the group maximum, and every
@@ -111,6 +112,26 @@ def test_f4_shapes(K, N, b_v, b_u):
     check(f"f4 {K}->{N}", li, run(li))
 
 
+# 4-bit codes on the same product as FP8 values: one slice with the output
+# rotation in the launch (8192 -> 28672 shape family), split K 4 ways, 8
+# ragged slices; wide zero-points (0 and 15) and subnormal fp16 scales
+F4_SHAPES_4BIT = [(8192, 16384, 8192, 256, "f32"), (16384, 8192, 256, 8192, "int8"),
+                  (34816, 4096, 256, 4096, "f32")]
+
+
+@pytest.mark.parametrize("K,N,b_v,b_u,angles", F4_SHAPES_4BIT)
+def test_f4_shapes_4bit(K, N, b_v, b_u, angles):
+    li = layer(K, N, b_v, b_u, seed=K % 89 + 4, bits=4, angles=angles)
+    check(f"f4 4-bit {K}->{N} {angles}", li, run(li))
+
+
+def test_f4_wide_weights_4bit():
+    li = layer(16384, 8192, 256, 8192, seed=7, bits=4)
+    w = S.qweight(8192, 16384, 4, rng(5), spread="wide")
+    li = S.LayerInputs(li.lin, 4, 1, li.x, li.x_dtype, li.V, li.U, w)
+    check("f4 4-bit wide weights", li, run(li))
+
+
 @pytest.mark.parametrize("K,N,b_v,angles,xdt", [
     (4096, 32768, 4096, "int8", "f32"), (4096, 32768, 4096, "f32", "bf16"),
     (16384, 8192, 8192, "int8", "bf16"), (8192, 16384, 8192, "f32", "f32"),
@@ -147,14 +168,17 @@ def test_f4_output_rotation_in_product(angles):
     check(f"f4 output rotation in the product {angles}", li, y32)
 
 
-@pytest.mark.parametrize("K,N", [(8192, 28672), (28672, 8192), (34816, 4096)])
-def test_f4_deq_gemv_ws(K, N):
+@pytest.mark.parametrize("K,N,bits", [(8192, 28672, 2), (28672, 8192, 2), (34816, 4096, 2),
+                                      (28672, 8192, 4)])
+def test_f4_deq_gemv_ws(K, N, bits):
     """The product alone (harp_deq_gemv_ws with a workspace: one K slice at
     28672 rows, 4 and 8 slices below) against the oracle product on the
     same float32 x~ (random, with a zero group and an outlier); twice on one
     workspace, bitwise equal, counters left at zero; without a workspace the
-    vector-ALU product, within the same bar."""
-    li = layer(K, N, 256, 256, seed=N % 89)
+    vector-ALU product, within the same bar.  4-bit codes take the vector
+    product here even with a workspace (the matrix-core form is no faster
+    alone; the fused linear uses it)."""
+    li = layer(K, N, 256, 256, seed=N % 89, bits=bits)
     g = rng(3, K)
     xt = g.standard_normal((1, K)).astype(np.float32)
     xt[0, 128:192] = 0.0
@@ -175,7 +199,7 @@ def test_f4_deq_gemv_ws(K, N):
     ref = oracle_yp(li, xt.astype(np.float64))
     for name, y in (("FP4", outs[0]), ("vector", outs[2])):
         r = O.rel_l2(d.host(y), ref)
-        print(f"[f4 deq_gemv_ws {K}->{N} {name}] rel_l2={r:.3e}", flush=True)
+        print(f"[f4 deq_gemv_ws {K}->{N} {bits}-bit {name}] rel_l2={r:.3e}", flush=True)
         assert r <= FP32_PATH_TOL
 
 
