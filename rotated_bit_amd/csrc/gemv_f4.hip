@@ -115,8 +115,8 @@ __device__ __forceinline__ T4 transpose4(const u32x4 (&c)[2]) {
   const auto a1 = __builtin_amdgcn_permlane32_swap(c[0].y, c[1].y, false, false);
   const auto a2 = __builtin_amdgcn_permlane32_swap(c[0].z, c[1].z, false, false);
   const auto a3 = __builtin_amdgcn_permlane32_swap(c[0].w, c[1].w, false, false);
-  // now (a0[0], a1[0]) / (a0[1], a1[1]): run 2 g1 of the groups with upper
-  // bit 0 / 1 and lower bit g0; (a2, a3) the same for run 2 g1 + 1
+  // with g = 2 g1 + g0: now (a0[0], a1[0]) / (a0[1], a1[1]) hold run 2 g1
+  // of groups 4t + g0 / 4t + 2 + g0, and (a2, a3) the same for run 2 g1 + 1
   const auto b0 = __builtin_amdgcn_permlane16_swap(a0[0], a2[0], false, false);
   const auto b1 = __builtin_amdgcn_permlane16_swap(a1[0], a3[0], false, false);
   const auto b2 = __builtin_amdgcn_permlane16_swap(a0[1], a2[1], false, false);
