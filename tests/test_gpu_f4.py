@@ -197,7 +197,7 @@ def test_f4_deq_gemv_ws(K, N, bits):
     assert torch.equal(outs[0], outs[1])
     assert int(ws[:2048].view(torch.int32).abs().sum().item()) == 0
     ref = oracle_yp(li, xt.astype(np.float64))
-    for name, y in (("FP4", outs[0]), ("vector", outs[2])):
+    for name, y in (("with workspace", outs[0]), ("no workspace", outs[2])):
         r = O.rel_l2(d.host(y), ref)
         print(f"[f4 deq_gemv_ws {K}->{N} {bits}-bit {name}] rel_l2={r:.3e}", flush=True)
         assert r <= FP32_PATH_TOL
@@ -248,10 +248,12 @@ def test_f4_repeatable_and_counters_left_zero():
     assert int(ws[:2048].view(torch.int32).abs().sum().item()) == 0
 
 
-@pytest.mark.parametrize("K,N,b_v,b_u", [(8192, 16384, 8192, 256), (16384, 8192, 256, 8192)])
-def test_f4_noalloc(K, N, b_v, b_u):
-    """No-allocation entry point: one K slice (no counters) on the FP4 path
-    (8192 -> 16384); 16384 -> 8192 needs split K, so it takes the vector-ALU
-    product there."""
-    li = layer(K, N, b_v, b_u, seed=6)
-    check(f"f4 noalloc {K}->{N}", li, run(li, noalloc=True))
+@pytest.mark.parametrize("K,N,b_v,b_u,bits", [(8192, 16384, 8192, 256, 2),
+                                             (16384, 8192, 256, 8192, 2),
+                                             (8192, 16384, 8192, 256, 4)])
+def test_f4_noalloc(K, N, b_v, b_u, bits):
+    """No-allocation entry point: one K slice (no counters) on the
+    block-scaled path (8192 -> 16384, 2- and 4-bit codes); 16384 -> 8192
+    needs split K, so it takes the vector-ALU product there."""
+    li = layer(K, N, b_v, b_u, seed=6, bits=bits)
+    check(f"f4 noalloc {K}->{N} {bits}-bit", li, run(li, noalloc=True))
