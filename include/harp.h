@@ -358,6 +358,13 @@ size_t harp_linear_mixed_workspace_bytes(int32_t M, int32_t N, int32_t K);
  *   M < 16: rotate-in to a float32 x~, the float32 product of
  *     harp_deq_gemv, rotate-out; the first two in one launch for M <= 2 and
  *     N <= 4096 where harp_rotate_in_deq_gemv supports the shape.
+ *     M == 1 with 2- or 4-bit codes on a layer of at least 2^27 weights
+ *     (N a multiple of 16, K of 256): the block-scaled matrix-core product
+ *     (2-bit codes as FP4, 4-bit codes as FP8 values, x~ as FP8 digit planes
+ *     exact to 2^-28 of each group's largest value, written by the input
+ *     rotation's last launch for b_V = 256 / 4096 / 8192), K cut into
+ *     slices summed in slice order; with a b_U = 256 output side and one K
+ *     slice the output rotation runs inside the product's launch.
  *   16 <= M < 64: rotate-in to a float32 x~, the small-batch matrix-core
  *     product on x~ split exactly into two bf16 planes hi + lo
  *     (|x~ - hi - lo| <= 2^-16 |x~|; w_hat exact), rotate-out.  Where K is
